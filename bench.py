@@ -1,0 +1,241 @@
+"""Benchmark of the SageSLA attention forward on one MI355X.
+
+One step = one sla_attention_fwd call (every stage: block statistics, K mean,
+INT8 quantisation, top-k selection, linear-branch staging and state, the
+block-sparse kernel with the fused linear branch and combine) over the whole
+workload, inputs resident in HBM, bf16 output, workspace preallocated.
+
+Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload wan14b720]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SLA attn fwd ms/call + effective TOPS (% MFMA peak), Wan-14B-720p shape"
+PEAK_I8_OPS = 5.0e15        # MI355X dense INT8 MFMA
+PEAK_F16_FLOPS = 2.5e15     # MI355X dense fp16/bf16 MFMA
+PEAK_HBM = 8.0e12           # MI355X HBM3E bytes/s
+STAGES = ["stats", "kmean", "quantize", "topk", "linear_prep", "linear_final", "sparse"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the launch stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(ev.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def work_counts(idx: np.ndarray, N: int, d: int, BH: int, keep_all: bool, linear: bool,
+                direct: bool):
+    """Algorithmic operation counts of one call from the selection idx [B,H,Nb,k].
+
+    Valid-row products only (the ragged last block counts its real rows).
+    Returns (int8 ops of Q.K^T, 16-bit flops of the sparse kernel)."""
+    nb = idx.shape[2]
+    rows = np.full(nb, 64, dtype=np.int64)
+    rows[-1] = N - 64 * (nb - 1)
+    kept_rows = rows[idx.reshape(-1, idx.shape[-1])].sum(axis=1)          # per (bh, i)
+    ni = np.tile(rows, idx.shape[0] * idx.shape[1])
+    kept_pairs_rows = float((ni * kept_rows).sum())                         # sum_i n_i sum_j n_j
+    qk = 2.0 * d * kept_pairs_rows
+    pv = 2.0 * d * kept_pairs_rows
+    lin = 0.0
+    if linear:
+        if direct:
+            lin = 2 * 2.0 * d * float((ni * (N - kept_rows)).sum())
+        else:
+            lin = 2 * 2.0 * d * kept_pairs_rows + 2.0 * d * d * N * BH     # kept share + phi(Q)H
+    return qk, pv + lin
+
+
+def cpu_baseline(Q, K, V, wl, keep, phi, n_blocks_sample=160):
+    """The fp64 oracle on one head and a sample of its query blocks, scaled to ms/call."""
+    from oracle import sla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    nb = O.n_blocks(wl.N, 64)
+    sample = sorted(set(np.linspace(0, nb - 1, n_blocks_sample + 1).astype(int).tolist()))
+    t0 = time.perf_counter()
+    O.sla_forward_head(Q[0, 0], K[0, 0], V[0, 0], 64, keep, phi, query_blocks=sample[:1])
+    t1 = time.perf_counter()
+    O.sla_forward_head(Q[0, 0], K[0, 0], V[0, 0], 64, keep, phi, query_blocks=sample)
+    t2 = time.perf_counter()
+    per_block = max((t2 - t1) - (t1 - t0), 0.0) / (len(sample) - 1)
+    setup = max((t1 - t0) - per_block, 0.0)
+    ms_call = 1e3 * wl.B * wl.H * (setup + nb * per_block)
+    return {"value": ms_call, "unit": "ms/call", "cores": int(cores), "kind": "oracle",
+            "sample": (f"head 0 of {wl.name}: per-head setup (selection, K mean, quantisation) "
+                       f"{setup:.2f} s + {len(sample) - 1} sampled query blocks at "
+                       f"{per_block * 1e3:.1f} ms each, scaled to {wl.B * wl.H} heads x {nb} "
+                       f"query blocks; {t2 - t0:.1f} s of CPU work")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b720")
+    ap.add_argument("--keep", type=float, default=None)
+    ap.add_argument("--phi", default="elu1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the SageSLA forward is sharded by heads with no "
+              f"communication, so --gpus {args.gpus} is not run here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_linear_attention_sagesla_amd as sla
+    from sparse_linear_attention_sagesla_amd import _lib
+    from sparse_linear_attention_sagesla_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    keep = wl.keep[0] if args.keep is None else args.keep
+    phi = args.phi
+    if keep >= 1.0:
+        phi = "none"
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    log(f"[bench] workload {wl.name} B={B} H={H} N={N} keep={keep} phi={phi}")
+    t = time.perf_counter()
+    Q, K, V = make_inputs(wl)
+    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def to_dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    op = sla.SLAAttention(B, H, N, keep=keep, phi=phi, out_dtype=torch.bfloat16, device=dev)
+    lib = _lib.load()
+    ph = _lib.PHI[phi]
+    stream = torch.cuda.current_stream(dev)
+
+    def call(events=None):
+        ev = (ctypes.c_void_p * len(events))(*events) if events else None
+        rc = lib.sla_attention_fwd_timed(
+            _lib._ptr(q), _lib._ptr(k), _lib._ptr(v), B, H, N, d, 64, float(keep), ph,
+            _lib._ptr(op.out), 0, None, _lib._ptr(op.workspace), op.workspace.numel(),
+            ctypes.c_void_p(stream.cuda_stream), ev)
+        if rc != 0:
+            raise RuntimeError(lib.sla_status_string(rc).decode())
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    hip = HipEvents()
+    evs = [hip.create(2 * len(STAGES)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        call(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step")
+
+    nb = sla.n_blocks(N)
+    kk = sla.topk_count(nb, keep)
+    linear = phi != "none" and kk < nb
+    direct = linear and (nb - kk) <= kk
+    skipped = set()
+    if kk == 0:
+        skipped |= {0, 1, 2, 3}
+    if not linear or direct:
+        skipped.add(5)
+    stage_ms = {}
+    for si, name in enumerate(STAGES):
+        if si in skipped:
+            continue
+        stage_ms[name] = float(np.mean([hip.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]))
+    for e in evs:
+        hip.destroy(e)
+
+    if kk > 0:
+        idx = sla.block_select(q, k, keep).cpu().numpy()
+        ops_i8, ops_16 = work_counts(idx, N, d, B * H, kk == nb, linear, direct)
+    else:
+        ops_i8, ops_16 = 0.0, 2.0 * d * d * N * B * H * 2
+    t_sparse = stage_ms["sparse"] * 1e-3
+    f16_equiv = ops_i8 * (PEAK_F16_FLOPS / PEAK_I8_OPS) + ops_16
+    achieved = f16_equiv / t_sparse / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_FLOPS / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / (PEAK_F16_FLOPS / 1e12), 4),
+                "traffic": None, "kernel": "sparse_fwd_kernel",
+                "note": "fp16-equivalent: INT8 ops weighted 0.5 (INT8 peak is 2x the fp16 peak)"}
+    bytes_io = {
+        "stats": 2 * B * H * N * d * 2,
+        "quantize": 2 * B * H * N * d * 2 + 2 * B * H * nb * 64 * d,
+        "linear_prep": 2 * B * H * N * d * 2 + (2 if linear else 1) * B * H * nb * 64 * d * 2,
+    }
+    bw = {n: round(bytes_io[n] / (stage_ms[n] * 1e-3) / 1e9, 1) for n in bytes_io if n in stage_ms}
+    eff_tops = (ops_i8 + ops_16) / (ms_step * 1e-3) / 1e12
+    dense_equiv = 4.0 * N * N * d * B * H / (ms_step * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(ms_step, 4), "unit": "ms/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8+f16 (bf16 in/out)", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "d": d, "block": 64,
+                   "keep": keep, "k": kk, "phi": phi, "grid": wl.grid},
+        "effective_tops": round(eff_tops, 2), "dense_equiv_tops": round(dense_equiv, 2),
+        "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "stage_hbm_gbps": bw,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(Q, K, V, wl, keep, phi)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * sla.h -- C ABI of libsla.so, the MI355X (gfx950) SageSLA attention forward.
+ *
+ * SageSLA is the SageAttention-based fast forward pass of sparse-linear
+ * attention (SLA): tool digest "TurboDiffusion", section "使用方式与安装".
+ * Each query block of `block` tokens keeps its top `keep` fraction of key
+ * blocks (the pipeline knob sla_topk=0.1 of tutorial "TurboDiffusion技术架构解析：
+ * 稀疏线性注意力应用实战" §3.2; "about 10% kept" in commentary "清华开源
+ * TurboDiffusion加速框架：视频生成提升200倍，迈入秒级时代", section
+ * "SageAttention与稀疏计算") and runs exact softmax attention softmax(QK^T/sqrt(d))V
+ * on them (tutorial §2.1, standard attention) with Q.K^T on INT8 codes
+ * (commentary, same section: low-bit SageAttention).  The remaining key blocks
+ * are summarised by normalised linear attention phi(Q)(phi(K)^T V) with phi =
+ * elu+1 or ReLU (tutorial §2.1, linear attention), and the two outputs are
+ * summed.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are device pointers (memory from hipMalloc / torch on the GPU),
+ *    contiguous row-major [B, H, N, d] with d fastest, 16-byte aligned.
+ *    bf16 tensors are passed as raw 16-bit patterns (`const void*`).
+ *  - Supported shapes: block == 64 and d == 128 (SLA_ERR_UNSUPPORTED
+ *    otherwise); B, H, N >= 1; N <= 2^20; 0 <= keep <= 1.
+ *  - Blocks: Nb = ceil(N / 64); the last block may be ragged; rows past N
+ *    ("pad rows") never take part in any sum, maximum or softmax.
+ *  - The caller allocates and owns every buffer, including the workspace
+ *    (size from sla_workspace_size).  The library allocates nothing and keeps
+ *    no mutable global state; calls on different streams are independent as
+ *    long as their workspaces differ.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *    the call returns without synchronising.  Arguments are validated before
+ *    anything is enqueued: on any error status nothing has been enqueued.
+ *    SLA_ERR_DEVICE reports a failed kernel launch (hipGetLastError).
+ *  - Outputs must not alias inputs or the workspace.
+ *  - Numeric range: inputs must be finite.  The linear branch stages
+ *    phi(Q)/16 and phi(K)/16 in fp16 and the softmax branch stages V in
+ *    fp16, so |V| <= 65504 and phi values <= 360 (|Q|, |K| below about 359)
+ *    keep every staged value in range.
+ */
+#ifndef SLA_H_
+#define SLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLA_BLOCK 64
+#define SLA_HEAD_DIM 128
+#define SLA_MAX_TOKENS (1 << 20)
+
+typedef enum sla_status {
+  SLA_OK = 0,
+  SLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, keep outside [0,1], ... */
+  SLA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement     */
+  SLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  SLA_ERR_DEVICE = 4       /* a HIP call or kernel launch failed              */
+} sla_status;
+
+typedef enum sla_phi {
+  SLA_PHI_NONE = 0, /* linear branch off                          */
+  SLA_PHI_ELU1 = 1, /* phi(x) = x + 1 for x > 0, exp(x) otherwise */
+  SLA_PHI_RELU = 2  /* phi(x) = max(x, 0)                         */
+} sla_phi;
+
+typedef enum sla_out_dtype {
+  SLA_OUT_BF16 = 0, /* bf16 output, round-to-nearest-even of the fp32 result */
+  SLA_OUT_F32 = 1   /* fp32 output                                           */
+} sla_out_dtype;
+
+typedef enum sla_op {
+  SLA_OP_QUANTIZE = 0,
+  SLA_OP_SELECT = 1,
+  SLA_OP_ATTENTION = 2
+} sla_op;
+
+/* Number of key blocks every query block keeps: 0 if keep <= 0, n_blocks if
+ * keep >= 1, else min(n_blocks, max(1, ceil(keep * n_blocks - 1e-9))).  The
+ * pages give the fraction (sla_topk, "top k%") but not the rounding; this
+ * rounds up so at least the requested fraction is kept.  Pure host function;
+ * returns -1 if n_blocks < 1 or keep is NaN. */
+int32_t sla_topk_count(int32_t n_blocks, double keep);
+
+/* Workspace bytes `op` needs for this shape, written to *bytes.  `keep` and
+ * `phi` matter only for SLA_OP_ATTENTION (pass 0 otherwise).  Pure host
+ * function; validates like the op itself. */
+sla_status sla_workspace_size(int op, int B, int H, int N, int d, int block,
+                              double keep, int phi, size_t *bytes);
+
+/* Per-block INT8 quantisation of Q and of mean-smoothed K (low-bit
+ * SageAttention, commentary section "SageAttention与稀疏计算"; the K channel
+ * mean is subtracted before quantising, which leaves each softmax row
+ * unchanged since q.(k - mu) = q.k - q.mu is constant along the row).
+ *   q, k      bf16 [B,H,N,128]                                    (in)
+ *   k_mean    fp32 [B,H,128]: mu_c = fp32((sum over all N rows of K[.,c],
+ *             fp64, rows ascending within blocks, blocks ascending) / N)  (out)
+ *   q_i8,k_i8 int8 [B,H,Nb*64,128]; pad rows are 0                  (out)
+ *   q_scale,k_scale fp32 [B,H,Nb]                                   (out)
+ * Per block, on x = fp32(Q) or x = fp32(K) - mu (one fp32 subtraction):
+ *   a = max |x| over valid rows and all channels; scale = fp32(a/127);
+ *   code = clamp(rint_half_even(fp32(x * fp32(127/a))), -127, 127);
+ *   a == 0 gives scale 0 and zero codes.
+ * Workspace: sla_workspace_size(SLA_OP_QUANTIZE, ...). */
+sla_status sla_quantize_qk(const void *q, const void *k, int B, int H, int N,
+                           int d, int block, int8_t *q_i8, int8_t *k_i8,
+                           float *q_scale, float *k_scale, float *k_mean,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Key-block selection T_k (tutorial §2.1): for every query block i, the
+ * k = sla_topk_count(Nb, keep) key blocks j with the largest score
+ *   s_ij = sum_c qbar_ic * kbar_jc   (fp64, channels ascending),
+ * where qbar/kbar are the fp32-rounded block means of the raw Q and K
+ * (fp64 row sums / valid rows).  Equal scores go to the lower j.
+ *   kblock_idx  int32 [B,H,Nb,k], ascending within each row           (out)
+ *   kblock_mask uint32 [B,H,Nb,ceil(Nb/32)] bit j%32 of word j/32 set iff j
+ *               is kept; may be NULL                                  (out)
+ * keep must be > 0 (k >= 1).  Workspace: SLA_OP_SELECT. */
+sla_status sla_block_select(const void *q, const void *k, int B, int H, int N,
+                            int d, int block, double keep, int32_t *kblock_idx,
+                            uint32_t *kblock_mask, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* The SageSLA forward.  For query t of block i with kept set S_i:
+ *   softmax branch: softmax over the valid keys u of S_i of
+ *       acc_tu * q_scale_i * k_scale_j / sqrt(128)   (acc: exact int32 dot
+ *       product of the INT8 codes), applied to V (P and V in fp16 on the
+ *       matrix cores, fp32 accumulation, normaliser summed from the fp16 P);
+ *       zero when k == 0;
+ *   linear branch (phi != NONE): over the valid keys U of the other blocks,
+ *       phi(q)^T (sum_U phi(k_u) v_u^T) / phi(q)^T (sum_U phi(k_u)), phi on
+ *       the raw Q and K; zero when U is empty or the denominator vanishes;
+ *   out = softmax branch + linear branch.
+ *   q, k, v     bf16 [B,H,N,128]                                       (in)
+ *   keep        kept fraction, 0..1; keep == 0 requires phi != NONE
+ *   phi         sla_phi
+ *   out         [B,H,N,128], bf16 or fp32 per out_dtype                 (out)
+ *   out_linear  fp32 [B,H,N,128] linear branch alone; may be NULL       (out)
+ * Workspace: SLA_OP_ATTENTION (holds codes, selection, fp16 staging and the
+ * linear state, about 3 bytes/element of Q). */
+sla_status sla_attention_fwd(const void *q, const void *k, const void *v,
+                             int B, int H, int N, int d, int block, double keep,
+                             int phi, void *out, int out_dtype,
+                             float *out_linear, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Stages of sla_attention_fwd, in launch order (see sla_attention_fwd_timed). */
+typedef enum sla_stage {
+  SLA_STAGE_STATS = 0,        /* fp64 block sums, pooled block means of Q and K   */
+  SLA_STAGE_KMEAN = 1,        /* K channel mean                                   */
+  SLA_STAGE_QUANTIZE = 2,     /* INT8 codes and scales of Q and smoothed K        */
+  SLA_STAGE_TOPK = 3,         /* block scores and top-k key-block selection       */
+  SLA_STAGE_LINEAR_PREP = 4,  /* fp16 staging of V and phi(K), partial phi(K)^T V */
+  SLA_STAGE_LINEAR_FINAL = 5, /* whole-head phi(K)^T V and sum phi(K)             */
+  SLA_STAGE_SPARSE = 6,       /* block-sparse attention + linear branch + combine */
+  SLA_N_STAGES = 7
+} sla_stage;
+
+/* sla_attention_fwd that also records caller-created HIP events (hipEvent_t,
+ * same device) on `stream`: stage_events[2*s] just before stage s is
+ * enqueued and stage_events[2*s+1] just after.  stage_events may be NULL and
+ * any entry may be NULL; stages that a call skips (selection when keep == 0,
+ * linear stages when phi == NONE) record nothing.  Same arguments, ownership
+ * and errors as sla_attention_fwd; a failed hipEventRecord gives
+ * SLA_ERR_DEVICE. */
+sla_status sla_attention_fwd_timed(const void *q, const void *k, const void *v,
+                                   int B, int H, int N, int d, int block,
+                                   double keep, int phi, void *out,
+                                   int out_dtype, float *out_linear, void *ws,
+                                   size_t ws_bytes, void *stream,
+                                   void *const *stage_events);
+
+/* Integer Q.K^T tiles from the attention kernel's INT8 matrix-core path, for
+ * checking accumulators bit for bit.  pairs: int32 [n_pairs,4] device array
+ * of (b, h, query block i, key block j); acc: int32 [n_pairs,64,64],
+ * acc[p][r][c] = sum_e q_i8[b,h,64i+r,e] * k_i8[b,h,64j+c,e] (pad rows
+ * included).  No workspace. */
+sla_status sla_debug_qk_i32(const int8_t *q_i8, const int8_t *k_i8, int B,
+                            int H, int N, int d, int block,
+                            const int32_t *pairs, int n_pairs, int32_t *acc,
+                            void *stream);
+
+/* Static string naming a status code. */
+const char *sla_status_string(int status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int sla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H_ */

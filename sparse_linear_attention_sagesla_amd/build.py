@@ -1,0 +1,70 @@
+"""Builds libsla.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Usage: python -m sparse_linear_attention_sagesla_amd.build [-v]
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libsla.so")
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # no packed fp32 VALU instructions anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE fp32 division (the quantiser scales depend on it)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-fast-math", "-Wall", "-Wno-unused-function",
+    f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+]
+
+SOURCES = {
+    # statistics / quantiser / selection must follow a fixed rounding order
+    "sla_prep.hip": ["-ffp-contract=off"],
+    "sla_sparse.hip": [],
+    "sla_api.cpp": ["-x", "hip", "-ffp-contract=off"],
+}
+
+
+def _compile(src: str, extra: list[str], verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
+    if verbose and res.stderr.strip():
+        print(res.stderr, file=sys.stderr)
+    return obj
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libsla.so next to this file."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), SOURCES.items()))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose="-v" in sys.argv))

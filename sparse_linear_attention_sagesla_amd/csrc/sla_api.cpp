@@ -1,0 +1,257 @@
+// C ABI of libsla.so: argument validation, workspace carving and the launch
+// sequence of the SageSLA forward.  Nothing is enqueued unless every argument
+// checks out; kernels run on the caller's stream without host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/sla.h"
+#include "sla_internal.h"
+
+namespace {
+
+using sla::Shape;
+using sla::Workspace;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sla_status check_shape(int B, int H, int N, int d, int block) {
+  if (B < 1 || H < 1 || N < 1) return SLA_ERR_INVALID_ARG;
+  if (d != SLA_HEAD_DIM || block != SLA_BLOCK) return SLA_ERR_UNSUPPORTED;
+  if (N > SLA_MAX_TOKENS) return SLA_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1 << 20)) return SLA_ERR_UNSUPPORTED;
+  return SLA_OK;
+}
+
+Shape make_shape(int B, int H, int N, int k) {
+  Shape s;
+  s.B = B;
+  s.H = H;
+  s.N = N;
+  s.BH = B * H;
+  s.Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
+  s.Np = s.Nb * SLA_BLOCK;
+  s.k = k;
+  return s;
+}
+
+// Carves the workspace for `op`; with base == nullptr only the size is computed.
+size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> unsigned char* {
+    unsigned char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  const size_t BH = (size_t)s.BH, Nb = (size_t)s.Nb, Np = (size_t)s.Np, D = SLA_HEAD_DIM;
+  Workspace tmp;
+  Workspace& ws = w ? *w : tmp;
+  ws.ksum = reinterpret_cast<double*>(take(BH * Nb * D * sizeof(double)));
+  ws.qbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+  ws.kbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+  if (op == SLA_OP_ATTENTION) {
+    ws.mu = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
+    ws.q8 = reinterpret_cast<int8_t*>(take(BH * Np * D));
+    ws.k8 = reinterpret_cast<int8_t*>(take(BH * Np * D));
+    ws.sq = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
+    ws.sk = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
+    ws.idx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.k > 0 ? s.k : 1) * sizeof(int32_t)));
+    ws.v16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+    if (phi != SLA_PHI_NONE && s.k < s.Nb && sla::linear_direct(s)) {
+      ws.uidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.Nb - s.k) * sizeof(int32_t)));
+      ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+    } else if (phi != SLA_PHI_NONE && s.k < s.Nb) {
+      ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+      ws.hpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * D * sizeof(float)));
+      ws.zpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * sizeof(float)));
+      ws.h16t = reinterpret_cast<uint16_t*>(take(BH * D * D * sizeof(uint16_t)));
+      ws.hscale = reinterpret_cast<float*>(take(BH * sizeof(float)));
+      ws.z = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
+    }
+  }
+  return off;
+}
+
+sla_status device_status(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t sla_topk_count(int32_t n_blocks, double keep) {
+  if (n_blocks < 1 || std::isnan(keep)) return -1;
+  if (keep <= 0.0) return 0;
+  if (keep >= 1.0) return n_blocks;
+  const double c = std::ceil(keep * (double)n_blocks - 1e-9);
+  int32_t k = (int32_t)c;
+  if (k < 1) k = 1;
+  if (k > n_blocks) k = n_blocks;
+  return k;
+}
+
+sla_status sla_workspace_size(int op, int B, int H, int N, int d, int block, double keep,
+                              int phi, size_t* bytes) {
+  if (!bytes) return SLA_ERR_INVALID_ARG;
+  *bytes = 0;
+  const sla_status st = check_shape(B, H, N, d, block);
+  if (st != SLA_OK) return st;
+  if (op < SLA_OP_QUANTIZE || op > SLA_OP_ATTENTION) return SLA_ERR_INVALID_ARG;
+  int k = 0;
+  if (op == SLA_OP_ATTENTION) {
+    if (std::isnan(keep) || keep < 0.0 || keep > 1.0) return SLA_ERR_INVALID_ARG;
+    if (phi < SLA_PHI_NONE || phi > SLA_PHI_RELU) return SLA_ERR_INVALID_ARG;
+    k = sla_topk_count((N + SLA_BLOCK - 1) / SLA_BLOCK, keep);
+  }
+  *bytes = carve(op, make_shape(B, H, N, k), phi, nullptr, nullptr);
+  return SLA_OK;
+}
+
+sla_status sla_quantize_qk(const void* q, const void* k, int B, int H, int N, int d, int block,
+                           int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale,
+                           float* k_mean, void* ws, size_t ws_bytes, void* stream) {
+  sla_status st = check_shape(B, H, N, d, block);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !q_i8 || !k_i8 || !q_scale || !k_scale || !k_mean) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8))
+    return SLA_ERR_INVALID_ARG;
+  const Shape s = make_shape(B, H, N, 0);
+  const size_t need = carve(SLA_OP_QUANTIZE, s, SLA_PHI_NONE, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  Workspace w;
+  carve(SLA_OP_QUANTIZE, s, SLA_PHI_NONE, static_cast<unsigned char*>(ws), &w);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, hs);
+  if (e == hipSuccess) e = sla::launch_key_mean(w.ksum, s, k_mean, hs);
+  if (e == hipSuccess) e = sla::launch_quantize(qb, kb, k_mean, s, q_i8, k_i8, q_scale, k_scale, hs);
+  return device_status(e);
+}
+
+sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, int d, int block,
+                            double keep, int32_t* kblock_idx, uint32_t* kblock_mask, void* ws,
+                            size_t ws_bytes, void* stream) {
+  sla_status st = check_shape(B, H, N, d, block);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !kblock_idx) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k)) return SLA_ERR_INVALID_ARG;
+  if (std::isnan(keep) || keep <= 0.0 || keep > 1.0) return SLA_ERR_INVALID_ARG;
+  const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
+  const Shape s = make_shape(B, H, N, sla_topk_count(Nb, keep));
+  int R = 1;
+  if (sla::topk_lds_bytes(Nb, &R) > 160 * 1024) return SLA_ERR_UNSUPPORTED;
+  const size_t need = carve(SLA_OP_SELECT, s, SLA_PHI_NONE, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  Workspace w;
+  carve(SLA_OP_SELECT, s, SLA_PHI_NONE, static_cast<unsigned char*>(ws), &w);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, hs);
+  if (e == hipSuccess)
+    e = sla::launch_block_topk(w.qbar, w.kbar, s, kblock_idx, kblock_mask, nullptr, hs);
+  return device_status(e);
+}
+
+sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, int B, int H,
+                                   int N, int d, int block, double keep, int phi, void* out,
+                                   int out_dtype, float* out_linear, void* ws, size_t ws_bytes,
+                                   void* stream, void* const* stage_events) {
+  sla_status st = check_shape(B, H, N, d, block);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !v || !out) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (out_linear && !aligned16(out_linear)))
+    return SLA_ERR_INVALID_ARG;
+  if (std::isnan(keep) || keep < 0.0 || keep > 1.0) return SLA_ERR_INVALID_ARG;
+  if (phi < SLA_PHI_NONE || phi > SLA_PHI_RELU) return SLA_ERR_INVALID_ARG;
+  if (out_dtype != SLA_OUT_BF16 && out_dtype != SLA_OUT_F32) return SLA_ERR_INVALID_ARG;
+  const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
+  const int kk = sla_topk_count(Nb, keep);
+  if (kk == 0 && phi == SLA_PHI_NONE) return SLA_ERR_INVALID_ARG;
+  int R = 1;
+  if (kk > 0 && sla::topk_lds_bytes(Nb, &R) > 160 * 1024) return SLA_ERR_UNSUPPORTED;
+  const Shape s = make_shape(B, H, N, kk);
+  const size_t need = carve(SLA_OP_ATTENTION, s, phi, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  Workspace w;
+  carve(SLA_OP_ATTENTION, s, phi, static_cast<unsigned char*>(ws), &w);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  const auto* vb = static_cast<const uint16_t*>(v);
+  // the linear branch exists only when some key block is left out
+  const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
+  const bool direct = phi_eff != SLA_PHI_NONE && sla::linear_direct(s);
+  hipError_t e = hipSuccess;
+  // runs one stage between its two optional events
+  auto stage = [&](int id, auto&& launch) {
+    if (e != hipSuccess) return;
+    if (stage_events && stage_events[2 * id])
+      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id]), hs);
+    if (e == hipSuccess) e = launch();
+    if (e == hipSuccess && stage_events && stage_events[2 * id + 1])
+      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + 1]), hs);
+  };
+  if (kk > 0) {
+    stage(SLA_STAGE_STATS, [&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, hs); });
+    stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
+    stage(SLA_STAGE_QUANTIZE,
+          [&] { return sla::launch_quantize(qb, kb, w.mu, s, w.q8, w.k8, w.sq, w.sk, hs); });
+    stage(SLA_STAGE_TOPK, [&] {
+      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr, hs);
+    });
+  }
+  stage(SLA_STAGE_LINEAR_PREP, [&] {
+    return sla::launch_linear_prep(kb, vb, s, phi_eff, !direct, w.fk16, w.v16, w.hpart, w.zpart, hs);
+  });
+  if (phi_eff != SLA_PHI_NONE && !direct)
+    stage(SLA_STAGE_LINEAR_FINAL,
+          [&] { return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs); });
+  stage(SLA_STAGE_SPARSE, [&] {
+    return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
+                                  out_linear, hs);
+  });
+  return device_status(e);
+}
+
+sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B, int H, int N,
+                             int d, int block, double keep, int phi, void* out, int out_dtype,
+                             float* out_linear, void* ws, size_t ws_bytes, void* stream) {
+  return sla_attention_fwd_timed(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, out_linear,
+                                 ws, ws_bytes, stream, nullptr);
+}
+
+sla_status sla_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                            int block, const int32_t* pairs, int n_pairs, int32_t* acc,
+                            void* stream) {
+  sla_status st = check_shape(B, H, N, d, block);
+  if (st != SLA_OK) return st;
+  if (!q_i8 || !k_i8 || !pairs || !acc || n_pairs < 0) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q_i8) || !aligned16(k_i8)) return SLA_ERR_INVALID_ARG;
+  if (n_pairs == 0) return SLA_OK;
+  const Shape s = make_shape(B, H, N, 0);
+  return device_status(sla::launch_debug_qk(q_i8, k_i8, s, pairs, n_pairs, acc,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+const char* sla_status_string(int status) {
+  switch (status) {
+    case SLA_OK: return "SLA_OK";
+    case SLA_ERR_INVALID_ARG: return "SLA_ERR_INVALID_ARG: invalid argument";
+    case SLA_ERR_UNSUPPORTED: return "SLA_ERR_UNSUPPORTED: shape or option not supported";
+    case SLA_ERR_WORKSPACE: return "SLA_ERR_WORKSPACE: workspace missing or too small";
+    case SLA_ERR_DEVICE: return "SLA_ERR_DEVICE: HIP launch failed";
+    default: return "unknown sla_status";
+  }
+}
+
+int sla_version(void) { return 100; }
+
+}  // extern "C"

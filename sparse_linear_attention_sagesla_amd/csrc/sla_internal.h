@@ -1,0 +1,70 @@
+// Internal declarations shared by the libsla host code and its HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace sla {
+
+constexpr int kBlk = 64;        // tokens per query / key block
+constexpr int kD = 128;         // head dimension
+constexpr int kLinChunks = 32;  // key-block chunks per head in the linear-state reduction
+constexpr float kPhiScale = 0.0625f;  // phi(Q), phi(K) are staged in fp16 as phi/16
+
+enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiRelu = 2 };
+
+struct Shape {
+  int B, H, N;
+  int BH;   // B * H
+  int Nb;   // ceil(N / 64)
+  int Np;   // Nb * 64 (rows of the padded code / staging buffers)
+  int k;    // kept key blocks per query block
+};
+
+// Device buffers carved out of the caller's workspace (null when unused).
+struct Workspace {
+  double* ksum = nullptr;     // [BH, Nb, D]   fp64 K block sums (for the K mean)
+  float* qbar = nullptr;      // [BH, Nb, D]   fp32 Q block means
+  float* kbar = nullptr;      // [BH, Nb, D]   fp32 K block means
+  float* mu = nullptr;        // [BH, D]       K channel mean
+  int8_t* q8 = nullptr;       // [BH, Np, D]   INT8 codes
+  int8_t* k8 = nullptr;       // [BH, Np, D]
+  float* sq = nullptr;        // [BH, Nb]      block scales
+  float* sk = nullptr;        // [BH, Nb]
+  int32_t* idx = nullptr;     // [BH, Nb, k]   kept key blocks, ascending
+  int32_t* uidx = nullptr;    // [BH, Nb, Nb-k] the other key blocks (direct linear mode)
+  uint16_t* fk16 = nullptr;   // [BH, Np, D]   fp16 phi(K)/16, row-major, pad rows 0
+  uint16_t* v16 = nullptr;    // [BH, Nb, D, 64] fp16 V per block, [channel][permuted key]
+  float* hpart = nullptr;     // [BH, kLinChunks, D, D] partial phi(K)^T V
+  float* zpart = nullptr;     // [BH, kLinChunks, D]    partial sum phi(K)
+  uint16_t* h16t = nullptr;   // [BH, D(out), D(in)] fp16 H^T * 2^-s
+  float* hscale = nullptr;    // [BH] 2^s
+  float* z = nullptr;         // [BH, D] fp32 sum phi(K)/16
+};
+
+// Stage launchers (all enqueue on `s`, return the launch status).
+hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
+                              double* ksum, float* qbar, float* kbar, hipStream_t s);
+hipError_t launch_key_mean(const double* ksum, const Shape& sh, float* mu, hipStream_t s);
+hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu,
+                           const Shape& sh, int8_t* q8, int8_t* k8, float* sq, float* sk,
+                           hipStream_t s);
+hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
+                             int32_t* idx, uint32_t* mask, int32_t* uidx, hipStream_t s);
+size_t topk_lds_bytes(int Nb, int* rows_per_group);
+hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
+                              bool reduce, uint16_t* fk16, uint16_t* v16, float* hpart,
+                              float* zpart, hipStream_t s);
+hipError_t launch_linear_final(const float* hpart, const float* zpart, const Shape& sh,
+                               uint16_t* h16t, float* hscale, float* z, hipStream_t s);
+// Linear-branch form: with few unselected blocks (Nb - k <= k) the branch is
+// summed directly over them; otherwise as whole-head sums minus the kept share.
+inline bool linear_direct(const Shape& sh) { return sh.Nb - sh.k <= sh.k; }
+hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
+                             void* out, int out_f32, float* out_linear, hipStream_t s);
+hipError_t launch_debug_qk(const int8_t* q8, const int8_t* k8, const Shape& sh,
+                           const int32_t* pairs, int n_pairs, int32_t* acc, hipStream_t s);
+
+}  // namespace sla

@@ -1,0 +1,558 @@
+// Bandwidth-bound stages of the SageSLA forward on gfx950:
+//   block statistics (fp64 block sums, pooled means), K channel mean,
+//   INT8 quantisation of Q and smoothed K, block scores + top-k selection,
+//   and the linear-branch staging / global state.
+//
+// This translation unit is compiled with -ffp-contract=off: the quantiser and
+// the statistics must reproduce a fixed fp32/fp64 operation order bit for bit.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+
+#include "sla_internal.h"
+
+namespace sla {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// 8 consecutive bf16 values packed in a uint4 -> 8 floats.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* x) {
+  x[0] = __uint_as_float(u.x << 16);
+  x[1] = __uint_as_float(u.x & 0xffff0000u);
+  x[2] = __uint_as_float(u.y << 16);
+  x[3] = __uint_as_float(u.y & 0xffff0000u);
+  x[4] = __uint_as_float(u.z << 16);
+  x[5] = __uint_as_float(u.z & 0xffff0000u);
+  x[6] = __uint_as_float(u.w << 16);
+  x[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ float phi_apply(float x, int phi) {
+  if (phi == kPhiElu1) return x > 0.0f ? x + 1.0f : __expf(x);
+  return fmaxf(x, 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Block statistics.  One workgroup covers 8 consecutive blocks of one (b,h);
+// 16 lanes per (block, tensor) each own 8 channels and add the valid rows in
+// ascending order in fp64.  Outputs: Q/K block means rounded to fp32 and the
+// fp64 K block sums (for the K channel mean).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void block_stats_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int N, int Nb,
+    double* __restrict__ ksum, float* __restrict__ qbar, float* __restrict__ kbar) {
+  const int t = threadIdx.x;
+  const int blk = blockIdx.x * 8 + (t >> 5);
+  const int tensor = (t >> 4) & 1;
+  const int cg = t & 15;
+  const int bh = blockIdx.y;
+  if (blk >= Nb) return;
+  const int rows = min(kBlk, N - blk * kBlk);
+  const uint16_t* src = (tensor == 0 ? q : k) +
+                        ((size_t)bh * N + (size_t)blk * kBlk) * kD + cg * 8;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll 4
+  for (int r = 0; r < rows; ++r) {
+    const uint4 u = *reinterpret_cast<const uint4*>(src + (size_t)r * kD);
+    float x[8];
+    unpack_bf16x8(u, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (double)x[e];
+  }
+  const size_t o = ((size_t)bh * Nb + blk) * kD + cg * 8;
+  const double n = (double)rows;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float mean = (float)(acc[e] / n);
+    if (tensor == 0) {
+      qbar[o + e] = mean;
+    } else {
+      kbar[o + e] = mean;
+      ksum[o + e] = acc[e];
+    }
+  }
+}
+
+// K channel mean: blocks ascending, one fp64 division by N, rounded to fp32.
+__global__ __launch_bounds__(128) void key_mean_kernel(const double* __restrict__ ksum,
+                                                       int N, int Nb, float* __restrict__ mu) {
+  const int c = threadIdx.x;
+  const int bh = blockIdx.x;
+  const double* p = ksum + (size_t)bh * Nb * kD + c;
+  double s = 0.0;
+  for (int i = 0; i < Nb; ++i) s += p[(size_t)i * kD];
+  mu[(size_t)bh * kD + c] = (float)(s / (double)N);
+}
+
+// ---------------------------------------------------------------------------
+// INT8 quantiser.  One workgroup per (block, b*h, tensor).  Lane t owns
+// channels 8*(t%16).. of rows t/16 + 16m.  a = max|x| over valid rows;
+// scale = a/127, inv = 127/a (IEEE fp32 division); code = rint(x*inv)
+// clamped to [-127,127]; pad rows are written as 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ mu, int N, int Nb, int8_t* __restrict__ q8,
+    int8_t* __restrict__ k8, float* __restrict__ sq, float* __restrict__ sk) {
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const bool isk = blockIdx.z == 1;
+  const int cc = t & 15;
+  const int rr = t >> 4;
+  const int rows = min(kBlk, N - blk * kBlk);
+  const uint16_t* src = (isk ? k : q) + ((size_t)bh * N + (size_t)blk * kBlk) * kD + cc * 8;
+  float m8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m8[e] = isk ? mu[(size_t)bh * kD + cc * 8 + e] : 0.0f;
+  float x[4][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = rr + 16 * m;
+    if (r < rows) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src + (size_t)r * kD);
+      unpack_bf16x8(u, x[m]);
+      if (isk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[m][e] = x[m][e] - m8[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[m][e]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[m][e] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float scale = 0.0f, inv = 0.0f;
+  if (a > 0.0f) {
+    scale = a / 127.0f;
+    inv = 127.0f / a;
+  }
+  int8_t* dst = (isk ? k8 : q8) + ((size_t)bh * Nb * kBlk + (size_t)blk * kBlk) * kD + cc * 8;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = rr + 16 * m;
+    uint32_t w[2] = {0u, 0u};
+    if (r < rows && a > 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float y = rintf(x[m][e] * inv);
+        y = fminf(fmaxf(y, -127.0f), 127.0f);
+        const uint32_t b = (uint32_t)(int32_t)y & 0xffu;
+        w[e >> 2] |= b << (8 * (e & 3));
+      }
+    }
+    *reinterpret_cast<uint2*>(dst + (size_t)r * kD) = make_uint2(w[0], w[1]);
+  }
+  if (t == 0) (isk ? sk : sq)[(size_t)bh * Nb + blk] = scale;
+}
+
+// ---------------------------------------------------------------------------
+// Block scores and top-k.  A workgroup owns R query blocks of one (b,h).
+// Phase 1: lane j computes s_ij = sum_c qbar_ic kbar_jc for its key block j
+// and all R rows (fp64 fma, channels ascending; the fp32 x fp32 product is
+// exact in fp64 so each step rounds once) and stores an order-preserving
+// 64-bit key of s_ij in LDS.  Phase 2: one wave per row runs an MSB-first
+// radix select (8-bit digits) for the k-th largest key T, then keeps every
+// key > T plus the lowest-indexed keys == T, writing indices ascending.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t score_key(double s) {
+  if (s == 0.0) s = 0.0;  // -0 and +0 rank equal
+  const uint64_t u = (uint64_t)__double_as_longlong(s);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void block_topk_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int Nb, int k,
+    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, int32_t* __restrict__ uidx) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  double* qs = reinterpret_cast<double*>(smem);                           // [R][128]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + R * kD * 8);        // [4][256]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem + R * kD * 8 + 4096); // [R][Nb]
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int bh = blockIdx.y;
+  const int i0 = blockIdx.x * R;
+  const float* kb = kbar + (size_t)bh * Nb * kD;
+
+  for (int e = t; e < R * kD; e += 256) {
+    const int r = e / kD;
+    const int i = min(i0 + r, Nb - 1);
+    qs[e] = (double)qbar[((size_t)bh * Nb + i) * kD + (e % kD)];
+  }
+  __syncthreads();
+
+  for (int j = t; j < Nb; j += 256) {
+    double acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0;
+    const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * kD);
+    for (int c4 = 0; c4 < kD / 4; ++c4) {
+      const float4 kv = kr[c4];
+      const double kd[4] = {(double)kv.x, (double)kv.y, (double)kv.z, (double)kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * kD + 4 * c4 + e], kd[e], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) keys[(size_t)r * Nb + j] = score_key(acc[r]);
+  }
+  __syncthreads();
+
+  uint32_t* h = hist + wave * 256;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = wave; r < R; r += 4) {
+    const int i = i0 + r;
+    if (i >= Nb) break;  // wave-uniform; no block barrier follows
+    const uint64_t* kr = keys + (size_t)r * Nb;
+    uint64_t prefix = 0, pmask = 0;
+    uint32_t kk = (uint32_t)k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[lane * 4 + q] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      for (int j = lane; j < Nb; j += 64) {
+        const uint64_t key = kr[j];
+        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      uint32_t cnt[4];
+      uint32_t local = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cnt[q] = h[255 - 4 * lane - q];
+        local += cnt[q];
+      }
+      uint32_t incl = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      uint32_t before = incl - local;
+      int digit = -1;
+      uint32_t newkk = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (digit < 0 && before < kk && before + cnt[q] >= kk) {
+          digit = 255 - 4 * lane - q;
+          newkk = kk - before;
+        }
+        before += cnt[q];
+      }
+      const uint64_t found = __ballot(digit >= 0);
+      const int src = __ffsll((unsigned long long)found) - 1;
+      digit = __shfl(digit, src);
+      kk = __shfl(newkk, src);
+      prefix |= (uint64_t)digit << shift;
+      pmask |= 0xffull << shift;
+      __builtin_amdgcn_wave_barrier();
+    }
+    const uint64_t T = prefix;
+    const uint32_t need_ties = kk;
+    int32_t* out = idx + ((size_t)bh * Nb + i) * k;
+    uint32_t* mrow = mask ? mask + ((size_t)bh * Nb + i) * ((Nb + 31) / 32) : nullptr;
+    int32_t* urow = uidx ? uidx + ((size_t)bh * Nb + i) * (Nb - k) : nullptr;
+    uint32_t base = 0, ties = 0, ubase = 0;
+    for (int jb = 0; jb < Nb; jb += 64) {
+      const int j = jb + lane;
+      const bool valid = j < Nb;
+      const uint64_t key = valid ? kr[j] : 0ull;
+      const bool gt = valid && key > T;
+      const bool eq = valid && key == T;
+      const uint64_t eqb = __ballot(eq);
+      const uint32_t eq_rank = ties + (uint32_t)__popcll(eqb & lt_mask);
+      const bool sel = gt || (eq && eq_rank < need_ties);
+      const uint64_t sb = __ballot(sel);
+      const uint32_t pos = base + (uint32_t)__popcll(sb & lt_mask);
+      if (sel && pos < (uint32_t)k) out[pos] = j;
+      if (urow) {
+        const uint64_t ub = __ballot(valid && !sel);
+        const uint32_t upos = ubase + (uint32_t)__popcll(ub & lt_mask);
+        if (valid && !sel && upos < (uint32_t)(Nb - k)) urow[upos] = j;
+        ubase += (uint32_t)__popcll(ub);
+      }
+      if (mrow) {
+        const int w0 = jb >> 5;
+        if (lane == 0) mrow[w0] = (uint32_t)sb;
+        if (lane == 1 && w0 + 1 < (Nb + 31) / 32) mrow[w0 + 1] = (uint32_t)(sb >> 32);
+      }
+      base += (uint32_t)__popcll(sb);
+      ties += (uint32_t)__popcll(eqb);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Linear-branch staging.  A workgroup walks a contiguous chunk of key blocks
+// of one (b,h).  For every block it
+//   * writes phi(K)/16 as fp16, row-major [key][channel] (pad rows 0),
+//   * writes V as fp16 in the per-block layout [channel][permuted key] that
+//     the attention kernel reads as a matrix-core operand (pad keys 0),
+//   * accumulates H = sum phi(K)^T V and z = sum phi(K) for the chunk
+//     (fp16 operands, fp32 accumulation, blocks in ascending order).
+// Permuted key order inside each 32-key half: position 8g+s holds key
+// 4g+s (s<4) or 16+4g+(s-4) (s>=4), matching the transposed score tiles
+// that feed the P.V product.
+// kMode: 0 = V staging only, 1 = V and phi(K) staging, 2 = staging plus the
+// H, z partial sums.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int perm_pos(int key) {
+  const int h = key >> 5, r = key & 31;
+  return 32 * h + 8 * ((r & 15) >> 2) + (r & 3) + 4 * (r >> 4);
+}
+
+template <int kMode>
+__global__ __launch_bounds__(256) void linear_prep_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int Nb, int phi,
+    uint16_t* __restrict__ fk16, uint16_t* __restrict__ v16, float* __restrict__ hpart,
+    float* __restrict__ zpart) {
+  // LDS: transposed tiles [128 channels][64 positions] fp16, 16 KB each
+  __shared__ __align__(16) _Float16 fkT[kD * kBlk];
+  __shared__ __align__(16) _Float16 vT[kD * kBlk];
+  constexpr bool kLinear = kMode >= 1;
+  constexpr bool kReduce = kMode >= 2;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int chunk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int j0 = (int)(((long long)chunk * Nb) / kLinChunks);
+  const int j1 = (int)(((long long)(chunk + 1) * Nb) / kLinChunks);
+  // lane t: keys 4a..4a+3, channels 8cc..8cc+7
+  const int a = t >> 4;
+  const int cc = t & 15;
+
+  float4v acc[2][8];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 8; ++y) acc[x][y] = float4v{0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.0f;
+
+  for (int j = j0; j < j1; ++j) {
+    const int rows = min(kBlk, N - j * kBlk);
+    const size_t row0 = (size_t)bh * N + (size_t)j * kBlk;
+    _Float16 fv[4][8], vv[4][8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = 4 * a + m;
+      float xv[8], xk[8];
+      if (r < rows) {
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(v + (row0 + r) * kD + cc * 8), xv);
+        if (kLinear)
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(k + (row0 + r) * kD + cc * 8), xk);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = xk[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vv[m][e] = (_Float16)xv[e];
+        if (kLinear) fv[m][e] = (r < rows) ? (_Float16)(phi_apply(xk[e], phi) * kPhiScale) : (_Float16)0.0f;
+      }
+      if (kLinear) {
+        half8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fv[m][e];
+        *reinterpret_cast<half8*>(fk16 + (((size_t)bh * Nb + j) * kBlk + r) * kD + cc * 8) = o;
+      }
+    }
+    // transposed LDS writes: 4 consecutive keys -> 4 consecutive positions
+    const int p0 = perm_pos(4 * a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = cc * 8 + e;
+      half4 hv = {vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
+      *reinterpret_cast<half4*>(&vT[c * kBlk + p0]) = hv;
+      if (kLinear) {
+        half4 hf = {fv[0][e], fv[1][e], fv[2][e], fv[3][e]};
+        *reinterpret_cast<half4*>(&fkT[c * kBlk + p0]) = hf;
+      }
+    }
+    __syncthreads();
+    // V staging copy-out: 16 KB contiguous per block
+    {
+      const uint4* srcv = reinterpret_cast<const uint4*>(vT);
+      uint4* dstv = reinterpret_cast<uint4*>(v16 + ((size_t)bh * Nb + j) * kD * kBlk);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dstv[t + 256 * m] = srcv[t + 256 * m];
+    }
+    if (kReduce) {
+      // H[c][e] += sum_pos fkT[c][pos] vT[e][pos]; wave owns c-tiles 2w, 2w+1
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        half8 af[2], bf[8];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          af[x] = *reinterpret_cast<const half8*>(&fkT[(16 * (2 * wave + x) + l16) * kBlk + 32 * kc + 8 * g]);
+#pragma unroll
+        for (int y = 0; y < 8; ++y)
+          bf[y] = *reinterpret_cast<const half8*>(&vT[(16 * y + l16) * kBlk + 32 * kc + 8 * g]);
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int y = 0; y < 8; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[x], bf[y], acc[x][y], 0, 0, 0);
+      }
+      if (t < kD) {
+        const half8* row = reinterpret_cast<const half8*>(&fkT[t * kBlk]);
+        for (int p = 0; p < kBlk / 8; ++p) {
+          const half8 hv = row[p];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) zacc += (float)hv[e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (kReduce) {
+    float* hp = hpart + ((size_t)bh * kLinChunks + chunk) * kD * kD;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 8; ++y)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hp[(size_t)(16 * (2 * wave + x) + 4 * g + r) * kD + 16 * y + l16] = acc[x][y][r];
+    if (t < kD) zpart[((size_t)bh * kLinChunks + chunk) * kD + t] = zacc;
+  }
+}
+
+// Sum the chunk partials in order; store H^T as fp16 scaled by 2^-s so that
+// max|H| * 2^-s lies in [2^14, 2^15), plus 2^s and z.
+__global__ __launch_bounds__(256) void linear_final_kernel(
+    const float* __restrict__ hpart, const float* __restrict__ zpart,
+    uint16_t* __restrict__ h16t, float* __restrict__ hscale, float* __restrict__ z) {
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int bh = blockIdx.x;
+  const float* hp = hpart + (size_t)bh * kLinChunks * kD * kD;
+  float hv[64];
+  float mx = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 64; ++m) {
+    const int e = t + 256 * m;
+    float s = 0.0f;
+    for (int c = 0; c < kLinChunks; ++c) s += hp[(size_t)c * kD * kD + e];
+    hv[m] = s;
+    mx = fmaxf(mx, fabsf(s));
+  }
+  if (t < kD) {
+    float s = 0.0f;
+    for (int c = 0; c < kLinChunks; ++c) s += zpart[((size_t)bh * kLinChunks + c) * kD + t];
+    z[(size_t)bh * kD + t] = s;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int s = 0;
+  if (mx > 0.0f) s = ilogbf(mx) - 14;
+  const float down = ldexpf(1.0f, -s);
+  if (t == 0) hscale[bh] = ldexpf(1.0f, s);
+  _Float16* out = reinterpret_cast<_Float16*>(h16t) + (size_t)bh * kD * kD;
+#pragma unroll
+  for (int m = 0; m < 64; ++m) {
+    const int e = t + 256 * m;       // H[c][o] with c = e / 128, o = e % 128
+    const int c = e >> 7, o = e & 127;
+    out[(size_t)o * kD + c] = (_Float16)(hv[m] * down);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
+                              double* ksum, float* qbar, float* kbar, hipStream_t s) {
+  dim3 grid((sh.Nb + 7) / 8, sh.BH);
+  block_stats_kernel<<<grid, 256, 0, s>>>(q, k, sh.N, sh.Nb, ksum, qbar, kbar);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_mean(const double* ksum, const Shape& sh, float* mu, hipStream_t s) {
+  key_mean_kernel<<<sh.BH, 128, 0, s>>>(ksum, sh.N, sh.Nb, mu);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu,
+                           const Shape& sh, int8_t* q8, int8_t* k8, float* sq, float* sk,
+                           hipStream_t s) {
+  dim3 grid(sh.Nb, sh.BH, 2);
+  quantize_kernel<<<grid, 256, 0, s>>>(q, k, mu, sh.N, sh.Nb, q8, k8, sq, sk);
+  return hipGetLastError();
+}
+
+size_t topk_lds_bytes(int Nb, int* rows_per_group) {
+  int R = 8;
+  while (R > 1 && (size_t)R * Nb * 8 + (size_t)R * kD * 8 + 4096 > 64 * 1024) R >>= 1;
+  if (rows_per_group) *rows_per_group = R;
+  return (size_t)R * Nb * 8 + (size_t)R * kD * 8 + 4096;
+}
+
+hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
+                             int32_t* idx, uint32_t* mask, int32_t* uidx, hipStream_t s) {
+  int R = 1;
+  const size_t lds = topk_lds_bytes(sh.Nb, &R);
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const int big = 160 * 1024;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<1>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
+  });
+  dim3 grid((sh.Nb + R - 1) / R, sh.BH);
+  switch (R) {
+    case 8: block_topk_kernel<8><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
+    case 4: block_topk_kernel<4><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
+    case 2: block_topk_kernel<2><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
+    default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
+                              bool reduce, uint16_t* fk16, uint16_t* v16, float* hpart,
+                              float* zpart, hipStream_t s) {
+  dim3 grid(kLinChunks, sh.BH);
+  if (phi == kPhiNone)
+    linear_prep_kernel<0><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, hpart, zpart);
+  else if (!reduce)
+    linear_prep_kernel<1><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, hpart, zpart);
+  else
+    linear_prep_kernel<2><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, hpart, zpart);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_final(const float* hpart, const float* zpart, const Shape& sh,
+                               uint16_t* h16t, float* hscale, float* z, hipStream_t s) {
+  linear_final_kernel<<<sh.BH, 256, 0, s>>>(hpart, zpart, h16t, hscale, z);
+  return hipGetLastError();
+}
+
+}  // namespace sla

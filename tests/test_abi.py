@@ -1,0 +1,127 @@
+"""Host-side checks of libsla.so: it loads, exports every declared symbol, and
+every entry point rejects bad arguments before touching a device.  No test
+here launches a kernel, so the file runs on a machine without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import sla_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla.h")
+
+from sparse_linear_attention_sagesla_amd import _lib  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libsla.so not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced on error paths
+MISALIGNED = ctypes.c_void_p(0x100008)
+NULL = ctypes.c_void_p(0)
+
+
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_are_exported():
+    names = set(re.findall(r"\b(sla_[a-z0-9_]+)\s*\(", open(HEADER).read()))
+    assert {"sla_quantize_qk", "sla_block_select", "sla_attention_fwd"} <= names
+    L = lib()
+    for n in sorted(names):
+        assert hasattr(L, n), f"libsla.so does not export {n}"
+
+
+def test_version_and_status_strings():
+    L = lib()
+    assert L.sla_version() >= 100
+    for s in range(5):
+        assert L.sla_status_string(s).decode().startswith("SLA_")
+    assert b"unknown" in L.sla_status_string(99)
+
+
+@pytest.mark.parametrize("nb", [1, 2, 7, 30, 32, 512, 1182, 4096])
+def test_topk_count_matches_oracle(nb):
+    for keep in (0.0, 1e-6, 0.01, 0.05, 0.1, 0.15, 0.2, 0.333, 0.5, 0.99, 1.0, 1.5, -0.1):
+        assert _lib.topk_count(nb, keep) == O.topk_count(nb, keep)
+    assert lib().sla_topk_count(0, 0.1) == -1
+    assert lib().sla_topk_count(nb, float("nan")) == -1
+
+
+def _ws(op, B=1, H=2, N=2048, d=128, block=64, keep=0.1, phi=1):
+    out = ctypes.c_size_t(0)
+    st = lib().sla_workspace_size(op, B, H, N, d, block, keep, phi, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_validation_and_growth():
+    assert _ws(2)[0] == OK and _ws(2)[1] > 0
+    assert _ws(2, d=64)[0] == UNSUPPORTED
+    assert _ws(2, block=128)[0] == UNSUPPORTED
+    assert _ws(2, N=0)[0] == INVALID
+    assert _ws(2, B=0)[0] == INVALID
+    assert _ws(2, N=(1 << 20) + 1)[0] == UNSUPPORTED
+    assert _ws(2, keep=1.5)[0] == INVALID
+    assert _ws(2, phi=7)[0] == INVALID
+    assert _ws(9)[0] == INVALID
+    assert lib().sla_workspace_size(2, 1, 1, 64, 128, 64, 0.1, 1, None) == INVALID
+    s_small, s_big = _ws(2, N=2048)[1], _ws(2, N=75600)[1]
+    assert s_big > s_small
+    assert _ws(2, phi=0)[1] < _ws(2, phi=1)[1]
+    # the attention workspace holds at least the INT8 codes of Q and K and fp16 V
+    assert _ws(2, B=1, H=40, N=75600)[1] >= 40 * 1182 * 64 * 128 * 4
+
+
+def _attn(q=FAKE, k=FAKE, v=FAKE, B=1, H=2, N=2048, d=128, block=64, keep=0.1, phi=1,
+          out=FAKE, out_dtype=1, out_lin=NULL, ws=FAKE, ws_bytes=0):
+    return lib().sla_attention_fwd(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype,
+                                   out_lin, ws, ws_bytes, NULL)
+
+
+def test_attention_rejects_bad_arguments_before_launch():
+    assert _attn(q=NULL) == INVALID
+    assert _attn(out=NULL) == INVALID
+    assert _attn(v=MISALIGNED) == INVALID
+    assert _attn(out_lin=MISALIGNED) == INVALID
+    assert _attn(d=96) == UNSUPPORTED
+    assert _attn(block=32) == UNSUPPORTED
+    assert _attn(N=-5) == INVALID
+    assert _attn(keep=-0.1) == INVALID
+    assert _attn(keep=float("nan")) == INVALID
+    assert _attn(keep=0.0, phi=0) == INVALID
+    assert _attn(phi=3) == INVALID
+    assert _attn(out_dtype=5) == INVALID
+    assert _attn(ws=NULL, ws_bytes=1 << 40) == WORKSPACE
+    assert _attn(ws_bytes=1024) == WORKSPACE
+    assert _attn(ws=MISALIGNED, ws_bytes=1 << 40) == WORKSPACE
+
+
+def test_quantize_and_select_reject_bad_arguments_before_launch():
+    L = lib()
+    args = [FAKE, FAKE, 1, 2, 2048, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, NULL]
+    assert L.sla_quantize_qk(*args) == WORKSPACE
+    bad = list(args)
+    bad[9] = NULL
+    assert L.sla_quantize_qk(*bad) == INVALID
+    bad = list(args)
+    bad[5] = 64
+    assert L.sla_quantize_qk(*bad) == UNSUPPORTED
+    sel = [FAKE, FAKE, 1, 2, 2048, 128, 64, 0.1, FAKE, NULL, FAKE, 0, NULL]
+    assert L.sla_block_select(*sel) == WORKSPACE
+    for keep in (0.0, -1.0, 1.01):
+        s2 = list(sel)
+        s2[7] = keep
+        assert L.sla_block_select(*s2) == INVALID
+    s2 = list(sel)
+    s2[8] = NULL
+    assert L.sla_block_select(*s2) == INVALID
+
+
+def test_debug_qk_rejects_bad_arguments():
+    L = lib()
+    assert L.sla_debug_qk_i32(FAKE, FAKE, 1, 1, 64, 128, 64, FAKE, -1, FAKE, NULL) == INVALID
+    assert L.sla_debug_qk_i32(NULL, FAKE, 1, 1, 64, 128, 64, FAKE, 1, FAKE, NULL) == INVALID
+    assert L.sla_debug_qk_i32(FAKE, FAKE, 1, 1, 64, 128, 64, FAKE, 0, FAKE, NULL) == OK
