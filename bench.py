@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--keep", type=float, default=None)
     ap.add_argument("--phi", default="elu1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times), to scale "
+                         "hardware byte counters against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the SageSLA forward is sharded by heads with no "
@@ -130,6 +133,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB 5 times")
+        return
 
     import sparse_linear_attention_sagesla_amd as sla
     from sparse_linear_attention_sagesla_amd import _lib

@@ -1,11 +1,12 @@
 // Block-sparse SageSLA attention kernel for gfx950 (CDNA4).
 //
 // One workgroup = one 64-row query block of one (b,h); four waves, each
-// owning 16 query rows.  The workgroup walks the query block's kept key
-// blocks (ascending).  Per kept block j, staged in LDS (double-buffered):
+// owning 16 query rows.  The workgroup walks a list of key blocks (tiles).
+// Per tile, staged in LDS by direct global->LDS 16-byte loads, double-buffered
+// so the next tile streams in while this one is computed:
 //   K8_j   int8 [64 keys][128]      (8 KB)   -> S^T = K8_j Q8_i^T     (INT8 MFMA)
-//   phiK_j fp16 [64 keys][128]      (16 KB)  -> G^T = phiK_j phiQ_i^T (fp16 MFMA)
 //   V_j    fp16 [128][64 perm keys] (16 KB)  -> O^T += V_j^T P^T, A^T += V_j^T G^T
+//   phiK_j fp16 [64 keys][128]      (16 KB)  -> G^T = phiK_j phiQ_i^T (fp16 MFMA)
 // Scores are computed transposed (keys x queries) so each lane ends up holding
 // one query's values for 16 keys; in that layout the exponentiated scores P and
 // the linear weights G are already the B operand of the next product and never
@@ -13,12 +14,18 @@
 //
 // Softmax branch (tutorial "TurboDiffusion技术架构解析：稀疏线性注意力应用实战"
 // §2.1 standard attention, on INT8 codes as in low-bit SageAttention): logits
-// acc * sq_i * sk_j / sqrt(128) taken in the log2 domain, online max/sum in
-// fp32, P rounded to fp16 with the normaliser summed from the rounded P.
+// acc * sq_i * sk_j / sqrt(128) in the log2 domain, online max/sum in fp32,
+// P rounded to fp16 with the normaliser summed from the rounded P.  The running
+// maximum is exact, so the largest weight of a row is exactly 1 in fp16 (no
+// rounding error on the dominant term of a peaked row); the accumulators are
+// rescaled only in tiles where some row's maximum rises.
 // Linear branch (same section, linear attention with phi = elu+1 / ReLU),
-// normalised, over the unselected blocks: numerator phi(Q)H - A and
-// denominator phi(Q)z - r, where H, z are the whole-head sums and A, r the
-// kept blocks' share accumulated in this loop.
+// normalised, over the unselected blocks, in one of two forms:
+//   subtraction: numerator phi(Q)H - A, denominator phi(Q)z - r, with H, z the
+//                whole-head sums and A, r the kept tiles' share (kept tiles
+//                carry both branches);
+//   direct:      A, r summed over the unselected tiles, walked after the kept
+//                ones (used when they are no more than the kept ones).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -32,91 +39,91 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+typedef __attribute__((address_space(3))) const half8 lds_half8;
 
 constexpr int kK8Bytes = kBlk * kD;          // 8 KB
 constexpr int kF16TileBytes = kBlk * kD * 2; // 16 KB
+constexpr int kVOff = kK8Bytes;                       // V tile offset in a stage
+constexpr int kFOff = kK8Bytes + kF16TileBytes;       // phi(K) tile offset in a stage
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 
-// LDS byte offsets of one 16-byte chunk, XOR-swizzled by row to spread banks.
-__device__ __forceinline__ int k8_off(int row, int ch) {      // 64 rows x 8 chunks
-  return (row * 8 + (ch ^ (row & 7))) * 16;
-}
-__device__ __forceinline__ int f16row_off(int row, int ch) {  // 64 rows x 16 chunks
-  return (row * 16 + (ch ^ (row & 7))) * 16;
-}
-__device__ __forceinline__ int vt_off(int row, int ch) {      // 128 rows x 8 chunks
-  return (row * 8 + (ch ^ (row & 7))) * 16;
-}
+enum Mode { kSoftOnly = 0, kSubtract = 1, kDirect = 2 };
 
 __device__ __forceinline__ float phi_apply(float x, int phi) {
   if (phi == kPhiElu1) return x > 0.0f ? x + 1.0f : __expf(x);
   return fmaxf(x, 0.0f);
 }
 
-struct TileRegs {
-  uint4 k8[2];
-  uint4 fk[4];
-  uint4 v[4];
+// LDS layout.  Tiles with 128-byte rows (K8, V) keep 16-byte chunk ch of row r
+// at chunk ch ^ ((r >> 1) & 7); the phi(K) tile (256-byte rows) at ch ^ (r & 15).
+// A 16-lane read group (16 consecutive rows, same chunk) then touches 16
+// distinct 4-bank groups of the 64-bank LDS.
+struct LaneOffsets {
+  int rd8;    // read byte offset of (row l16, chunk g) in a 128-byte-row tile; chunk g+4: ^64
+  int rdF;    // read byte offset of (row l16, chunk g) in the phi(K) tile; chunk g+4cc: ^(64cc)
+  int ld8;    // global byte offset (within the tile) this lane fetches for a 128-byte-row tile
+  int ldF;    // same for the phi(K) tile
 };
 
-// Global -> registers for one key block: INT8 codes (softmax tiles), fp16
-// phi(K)/16 (tiles that feed the linear branch) and fp16 V (always).
-__device__ __forceinline__ void load_tile(TileRegs& r, const int8_t* k8, const uint16_t* fk16,
-                                          const uint16_t* v16, size_t bh, int Np, int Nb, int j,
-                                          bool soft, bool lin, int t) {
-  if (soft) {
-    const uint4* ks = reinterpret_cast<const uint4*>(k8 + ((size_t)bh * Np + (size_t)j * kBlk) * kD);
-    r.k8[0] = ks[t];
-    r.k8[1] = ks[t + 256];
+__device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
+  LaneOffsets o;
+  const int l16 = lane & 15, g = lane >> 4;
+  o.rd8 = l16 * 128 + ((g ^ ((l16 >> 1) & 7)) << 4);
+  o.rdF = l16 * 256 + ((g ^ l16) << 4);
+  // LDS-direct loads: wave w, instruction m fills LDS chunks 256m + 64w + lane
+  {
+    const int row = 8 * wave + (lane >> 3);           // + 32m
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);
+    o.ld8 = row * 128 + ch * 16;                      // + 4096m
   }
-  const uint4* vs = reinterpret_cast<const uint4*>(v16 + ((size_t)bh * Nb + j) * kD * kBlk);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) r.v[m] = vs[t + 256 * m];
-  if (lin) {
-    const uint4* fs = reinterpret_cast<const uint4*>(fk16 + ((size_t)bh * Np + (size_t)j * kBlk) * kD);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) r.fk[m] = fs[t + 256 * m];
+  {
+    const int row = 4 * wave + (lane >> 4);           // + 16m
+    const int ch = (lane & 15) ^ (row & 15);
+    o.ldF = row * 256 + ch * 16;                      // + 4096m
   }
+  return o;
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& r, unsigned char* st, bool soft,
-                                           bool lin, int t) {
-  unsigned char* lk = st;
-  unsigned char* lv = st + kK8Bytes;
-  unsigned char* lf = st + kK8Bytes + kF16TileBytes;
-  if (soft) {
+__device__ __forceinline__ void lds_load16(const void* gsrc, lds_byte* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, (void __attribute__((address_space(3)))*)ldst, 16, 0, 0);
+}
+
+// Issues this wave's share of a tile's LDS-direct loads into `st`.
+template <bool kK8, bool kFK>
+__device__ __forceinline__ void issue_tile(lds_byte* st, const int8_t* k8, const uint16_t* v16,
+                                           const uint16_t* fk16, size_t bh, int Np, int Nb, int j,
+                                           int wave, const LaneOffsets& lo) {
+  const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(v16) +
+                              ((size_t)bh * Nb + j) * (size_t)kF16TileBytes + lo.ld8;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int gi = t + 256 * m;
-      *reinterpret_cast<uint4*>(lk + k8_off(gi >> 3, gi & 7)) = r.k8[m];
-    }
+  for (int m = 0; m < 4; ++m) lds_load16(vsrc + 4096 * m, st + kVOff + 4096 * m + 1024 * wave);
+  if (kK8) {
+    const unsigned char* ksrc = reinterpret_cast<const unsigned char*>(k8) +
+                                ((size_t)bh * Np + (size_t)j * kBlk) * kD + lo.ld8;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) lds_load16(ksrc + 4096 * m, st + 4096 * m + 1024 * wave);
   }
+  if (kFK) {
+    const unsigned char* fsrc = reinterpret_cast<const unsigned char*>(fk16) +
+                                ((size_t)bh * Np + (size_t)j * kBlk) * kD * 2 + lo.ldF;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int gi = t + 256 * m;
-    *reinterpret_cast<uint4*>(lv + vt_off(gi >> 3, gi & 7)) = r.v[m];
-  }
-  if (lin) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int gi = t + 256 * m;
-      *reinterpret_cast<uint4*>(lf + f16row_off(gi >> 4, gi & 15)) = r.fk[m];
-    }
+    for (int m = 0; m < 4; ++m) lds_load16(fsrc + 4096 * m, st + kFOff + 4096 * m + 1024 * wave);
   }
 }
 
 // S^T tile (64 keys x 16 queries of this wave) from the staged K8 tile.
 // s[kt][r] = sum_e K8[16kt+4g+r][e] * Q8[query l16][e]
-__device__ __forceinline__ void qk_tile(const unsigned char* lk, const v4i qf[2], int l16, int g,
-                                        v4i s[4]) {
+__device__ __forceinline__ void qk_tile(const lds_byte* st, const v4i qf[2], int rd8, v4i s[4]) {
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     s[kt] = v4i{0, 0, 0, 0};
-    const int row = 16 * kt + l16;
 #pragma unroll
     for (int dc = 0; dc < 2; ++dc) {
-      const v4i a = *reinterpret_cast<const v4i*>(lk + k8_off(row, 4 * dc + g));
+      const v4i a = *(lds_v4i*)(st + kt * 2048 + (rd8 ^ (64 * dc)));
       s[kt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qf[dc], s[kt], 0, 0, 0);
     }
   }
@@ -128,6 +135,8 @@ __device__ __forceinline__ void load_q8_frag(const int8_t* q8, size_t bh, int Np
   qf[0] = *reinterpret_cast<const v4i*>(p);
   qf[1] = *reinterpret_cast<const v4i*>(p + 64);
 }
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 struct SparseArgs {
   const uint16_t* q;
@@ -143,19 +152,146 @@ struct SparseArgs {
   const float* hscale;
   const float* z;
   int N, Nb, Np, k;
-  int phi;        // feature map for phi(Q) (0 = linear branch off)
-  int lin;        // linear branch has a non-empty complement
-  int direct;     // linear branch summed directly over the unselected blocks
+  int phi;        // feature map for phi(Q)
   void* out;
   int out_f32;
   float* out_linear;
 };
 
-// Tiles of a query block: p < k are its kept key blocks (softmax branch; in
-// the subtraction form they also give the kept share of the linear branch);
-// with the direct form, p >= k walk the unselected blocks (linear branch only).
+struct State {
+  v4f o[8];       // O^T accumulator (softmax numerator), d = 16dt + 4g + r
+  v4f al[8];      // A^T accumulator (linear branch, kept or unselected share)
+  float m_run;    // running log2-domain maximum (this lane's query)
+  float l_part;   // this lane's share of the softmax normaliser
+  float r_part;   // this lane's share of the linear denominator part
+};
+
+// One tile's computation from stage `st`.
+template <bool kSoft, bool kLin>
+__device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const v4i qf[2],
+                                             const half8 fq[4], const LaneOffsets& lo, float cs,
+                                             int kvalid, int g) {
+  half8 pf[2], gf[2];
+  const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  if (kSoft) {
+    v4i s[4];
+    qk_tile(st, qf, lo.rd8, s);
+    const bool tail = kvalid < kBlk;  // workgroup-uniform: only the ragged last block
+    if (tail) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kt + 4 * g + r >= kvalid) s[kt][r] = INT32_MIN;
+    }
+    int mi = s[0][0];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mi = max(mi, s[kt][r]);
+    mi = max(mi, __shfl_xor(mi, 16));
+    mi = max(mi, __shfl_xor(mi, 32));
+    const float mx = (float)mi * cs;  // cs >= 0, so this is the tile's largest logit
+    const bool up = mx > S.m_run;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float m_new = up ? mx : S.m_run;
+      const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) S.o[dt] *= alpha;
+      S.l_part *= alpha;
+      S.m_run = m_new;
+    }
+    const float nm = -S.m_run;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[kt][r], cs, nm));
+        if (tail && 16 * kt + 4 * g + r >= kvalid) p = 0.0f;
+        pf[kt >> 1][4 * (kt & 1) + r] = (_Float16)p;
+      }
+    }
+    float ls = S.l_part;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const half2v pr = {pf[c][2 * h], pf[c][2 * h + 1]};
+        ls = __builtin_amdgcn_fdot2(pr, ones, ls, false);
+      }
+    S.l_part = ls;
+  }
+  if (kLin) {
+    v4f gt[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      gt[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const half8 af = *(lds_half8*)(st + kFOff + kt * 4096 + (lo.rdF ^ (64 * cc)));
+        gt[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fq[cc], gt[kt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gf[kt >> 1][4 * (kt & 1) + r] = (_Float16)gt[kt][r];
+    float rs = S.r_part;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const half2v gr = {gf[c][2 * h], gf[c][2 * h + 1]};
+        rs = __builtin_amdgcn_fdot2(gr, ones, rs, false);
+      }
+    S.r_part = rs;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const half8 av = *(lds_half8*)(st + kVOff + dt * 2048 + (lo.rd8 ^ (64 * c)));
+      if (kSoft) S.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[c], S.o[dt], 0, 0, 0);
+      if (kLin) S.al[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, gf[c], S.al[dt], 0, 0, 0);
+    }
+  }
+}
+
+// Walks `n` tiles listed in `list` through the two LDS stages.
+template <bool kSoft, bool kLin>
+__device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_bytes,
+                                          const int32_t* list, int n, const SparseArgs& a,
+                                          size_t bh, const v4i qf[2], const half8 fq[4],
+                                          const LaneOffsets& lo, float qscale, int wave, int g) {
+  if (n <= 0) return;
+  auto block_of = [&](int p) { return min(max(list[p], 0), a.Nb - 1); };
+  issue_tile<kSoft, kLin>(smem, a.k8, a.v16, a.fk16, bh, a.Np, a.Nb, block_of(0), wave, lo);
+  for (int p = 0; p < n; p += 2) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int pp = p + half;
+      if (pp < n) {
+        lds_byte* cur = smem + half * stage_bytes;
+        lds_byte* nxt = smem + (1 - half) * stage_bytes;
+        const int j = block_of(pp);
+        wait_loads();
+        __syncthreads();  // tile pp is in LDS; every wave is done with tile pp-1
+        if (pp + 1 < n)
+          issue_tile<kSoft, kLin>(nxt, a.k8, a.v16, a.fk16, bh, a.Np, a.Nb, block_of(pp + 1), wave, lo);
+        const float cs = kSoft ? qscale * a.sk[bh * a.Nb + j] : 0.0f;
+        compute_tile<kSoft, kLin>(S, cur, qf, fq, lo, cs, a.N - j * kBlk, g);
+      }
+    }
+  }
+  __syncthreads();  // the stages may be refilled by a following walk
+}
+
+template <int kMode>
 __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_byte* smem = (lds_byte*)smem_raw;
+  constexpr bool kLinAny = kMode != kSoftOnly;
+  constexpr int stage_bytes = kK8Bytes + kF16TileBytes + (kLinAny ? kF16TileBytes : 0);
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -163,11 +299,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   const int l16 = lane & 15;
   const int i = blockIdx.x;
   const size_t bh = blockIdx.y;
-  const bool lin = a.phi != kPhiNone && a.lin;
-  const bool direct = lin && a.direct;
-  const int nu = direct ? a.Nb - a.k : 0;
-  const int ntiles = a.k + nu;
-  const int stage_bytes = kK8Bytes + kF16TileBytes + (lin ? kF16TileBytes : 0);
+  const LaneOffsets lo = lane_offsets(wave, lane);
 
   const int qrow = i * kBlk + 16 * wave + l16;  // this lane's query row
   const bool qvalid = qrow < a.N;
@@ -176,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   load_q8_frag(a.q8, bh, a.Np, qrow, g, qf);
 
   half8 fq[4];
-  if (lin) {
+  if (kLinAny) {
     const uint16_t* qp = a.q + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD + 8 * g;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -191,139 +323,45 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
     }
   }
 
-  v4f o[8], acc_l[8];
+  State S;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-    acc_l[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    S.o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    S.al[dt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  float m_run = -INFINITY, l_part = 0.0f, r_part = 0.0f;
+  S.m_run = -INFINITY;
+  S.l_part = 0.0f;
+  S.r_part = 0.0f;
   const float qscale = a.sq[bh * a.Nb + i] * (kInvSqrtD * kLog2e);
   const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
-  const int32_t* usel = direct ? a.uidx + (bh * a.Nb + i) * (size_t)nu : nullptr;
 
-  // key block of tile p, clamped so a malformed index list cannot read outside
-  // the staging buffers
-  auto tile_block = [&](int p) {
-    const int j = p < a.k ? sel[p] : usel[p - a.k];
-    return min(max(j, 0), a.Nb - 1);
-  };
-  auto tile_lin = [&](int p) { return lin && (direct ? p >= a.k : true); };
-
-  TileRegs regs;
-  if (ntiles > 0) {
-    load_tile(regs, a.k8, a.fk16, a.v16, bh, a.Np, a.Nb, tile_block(0), 0 < a.k, tile_lin(0), t);
-    store_tile(regs, smem, 0 < a.k, tile_lin(0), t);
-  }
-  __syncthreads();
-
-  for (int p = 0; p < ntiles; ++p) {
-    const int j = tile_block(p);
-    const bool soft = p < a.k;
-    const bool plin = tile_lin(p);
-    const bool more = p + 1 < ntiles;
-    if (more)
-      load_tile(regs, a.k8, a.fk16, a.v16, bh, a.Np, a.Nb, tile_block(p + 1), p + 1 < a.k,
-                tile_lin(p + 1), t);
-    const unsigned char* st = smem + (p & 1) * stage_bytes;
-    const unsigned char* lk = st;
-    const unsigned char* lv = st + kK8Bytes;
-    const unsigned char* lf = st + kK8Bytes + kF16TileBytes;
-
-    // ---- softmax branch scores of a kept block
-    half8 pf[2];
-    if (soft) {
-      v4i s[4];
-      qk_tile(lk, qf, l16, g, s);
-      const float cs = qscale * a.sk[bh * a.Nb + j];
-      const int kvalid = a.N - j * kBlk;  // keys >= kvalid are pad rows
-      float x[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * kt + 4 * g + r;
-          x[kt][r] = key < kvalid ? (float)s[kt][r] * cs : -INFINITY;
-          mx = fmaxf(mx, x[kt][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const _Float16 ph = (_Float16)exp2f(x[kt][r] - m_new);
-          pf[kt >> 1][4 * (kt & 1) + r] = ph;
-          psum += (float)ph;
-        }
-      l_part = l_part * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    }
-
-    // ---- linear-branch weights G^T = phiK phiQ^T of this block
-    half8 gf[2];
-    if (plin) {
-      v4f gt[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        gt[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-        const int row = 16 * kt + l16;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const half8 af = *reinterpret_cast<const half8*>(lf + f16row_off(row, 4 * cc + g));
-          gt[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fq[cc], gt[kt], 0, 0, 0);
-        }
-      }
-      float gsum = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const _Float16 gh = (_Float16)gt[kt][r];
-          gf[kt >> 1][4 * (kt & 1) + r] = gh;
-          gsum += (float)gh;
-        }
-      r_part += gsum;
-    }
-
-    // ---- O^T += V^T P^T and A^T += V^T G^T
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int row = 16 * dt + l16;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const half8 av = *reinterpret_cast<const half8*>(lv + vt_off(row, 4 * c + g));
-        if (soft) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[c], o[dt], 0, 0, 0);
-        if (plin) acc_l[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, gf[c], acc_l[dt], 0, 0, 0);
-      }
-    }
-
-    if (more) store_tile(regs, smem + ((p + 1) & 1) * stage_bytes, p + 1 < a.k, tile_lin(p + 1), t);
-    __syncthreads();
+  if (kMode == kSoftOnly) {
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, bh, qf, fq, lo, qscale, wave, g);
+  } else if (kMode == kSubtract) {
+    run_tiles<true, true>(S, smem, stage_bytes, sel, a.k, a, bh, qf, fq, lo, qscale, wave, g);
+  } else {
+    const int nu = a.Nb - a.k;
+    const int32_t* usel = a.uidx + (bh * a.Nb + i) * (size_t)nu;
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, a, bh, qf, fq, lo, qscale, wave, g);
   }
 
   // ---- epilogue: normalise, add the linear branch, store
-  float l = l_part + __shfl_xor(l_part, 16);
+  float l = S.l_part + __shfl_xor(S.l_part, 16);
   l += __shfl_xor(l, 32);
   const float inv_l = (a.k > 0 && l > 0.0f) ? 1.0f / l : 0.0f;
 
   v4f ol[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) ol[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (lin) {
-    float r = r_part + __shfl_xor(r_part, 16);
+  if (kLinAny) {
+    float r = S.r_part + __shfl_xor(S.r_part, 16);
     r += __shfl_xor(r, 32);
-    if (direct) {
+    if (kMode == kDirect) {
       // numerator and denominator summed over the unselected blocks
       const float inv_den = r > 0.0f ? 1.0f / r : 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) ol[dt] = acc_l[dt] * inv_den;
+      for (int dt = 0; dt < 8; ++dt) ol[dt] = S.al[dt] * inv_den;
     } else {
       const _Float16* ht = reinterpret_cast<const _Float16*>(a.h16t) + bh * kD * kD;
       const float hs = a.hscale[bh];
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
           const half8 ah = *reinterpret_cast<const half8*>(hrow + 32 * cc);
           num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fq[cc], num, 0, 0, 0);
         }
-        ol[dt] = (num * hs - acc_l[dt]) * inv_den;
+        ol[dt] = (num * hs - S.al[dt]) * inv_den;
       }
     }
   }
@@ -356,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
     const size_t orow = (bh * a.N + qrow) * kD;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const v4f res = o[dt] * inv_l + ol[dt];
+      const v4f res = S.o[dt] * inv_l + ol[dt];
       const int c0 = 16 * dt + 4 * g;
       if (a.out_f32) {
         *reinterpret_cast<v4f*>(reinterpret_cast<float*>(a.out) + orow + c0) = res;
@@ -383,7 +421,8 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
                                                        const int8_t* __restrict__ k8, int B, int H,
                                                        int Np, const int32_t* __restrict__ pairs,
                                                        int32_t* __restrict__ acc) {
-  __shared__ __align__(16) unsigned char lk[kK8Bytes];
+  __shared__ __align__(16) unsigned char lk_raw[kK8Bytes];
+  lds_byte* lk = (lds_byte*)lk_raw;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -394,22 +433,35 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
   if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Np / kBlk || j < 0 || j >= Np / kBlk)
     return;  // out-of-range pair: its acc tile is left untouched (uniform per workgroup)
   const size_t bh = (size_t)b * H + h;
-  const uint4* ks = reinterpret_cast<const uint4*>(k8 + (bh * Np + (size_t)j * kBlk) * kD);
+  const LaneOffsets lo = lane_offsets(wave, lane);
+  const unsigned char* ksrc = reinterpret_cast<const unsigned char*>(k8) +
+                              (bh * Np + (size_t)j * kBlk) * kD + lo.ld8;
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int gi = t + 256 * m;
-    *reinterpret_cast<uint4*>(lk + k8_off(gi >> 3, gi & 7)) = ks[gi];
-  }
+  for (int m = 0; m < 2; ++m) lds_load16(ksrc + 4096 * m, lk + 4096 * m + 1024 * wave);
+  wait_loads();
   __syncthreads();
   v4i qf[2];
   load_q8_frag(q8, bh, Np, i * kBlk + 16 * wave + l16, g, qf);
   v4i s[4];
-  qk_tile(lk, qf, l16, g, s);
+  qk_tile(lk, qf, lo.rd8, s);
   int32_t* dst = acc + (size_t)p * kBlk * kBlk + (size_t)(16 * wave + l16) * kBlk;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[16 * kt + 4 * g + r] = s[kt][r];
+}
+
+template <int kMode>
+hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
+  constexpr size_t stage = (size_t)kK8Bytes + kF16TileBytes + (kMode != kSoftOnly ? kF16TileBytes : 0);
+  static std::once_flag once;
+  std::call_once(once, [] {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
+  });
+  dim3 grid(sh.Nb, sh.BH);
+  sparse_fwd_kernel<kMode><<<grid, 256, 2 * stage, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -434,21 +486,13 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.Np = sh.Np;
   a.k = sh.k;
   a.phi = phi;
-  a.lin = (phi != kPhiNone && sh.k < sh.Nb) ? 1 : 0;
-  a.direct = linear_direct(sh) ? 1 : 0;
   a.out = out;
   a.out_f32 = out_f32;
   a.out_linear = out_linear;
-  const size_t stage = (size_t)kK8Bytes + kF16TileBytes + (phi != kPhiNone ? kF16TileBytes : 0);
-  const size_t lds = 2 * stage;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_fwd_kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * (kK8Bytes + 2 * kF16TileBytes));
-  });
-  dim3 grid(sh.Nb, sh.BH);
-  sparse_fwd_kernel<<<grid, 256, lds, s>>>(a);
-  return hipGetLastError();
+  const bool lin = phi != kPhiNone && sh.k < sh.Nb;
+  if (!lin) return launch_mode<kSoftOnly>(a, sh, s);
+  if (linear_direct(sh)) return launch_mode<kDirect>(a, sh, s);
+  return launch_mode<kSubtract>(a, sh, s);
 }
 
 hipError_t launch_debug_qk(const int8_t* q8, const int8_t* k8, const Shape& sh,
