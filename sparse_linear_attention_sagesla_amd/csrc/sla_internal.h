@@ -57,7 +57,7 @@ size_t topk_lds_bytes(int Nb, int* rows_per_group);
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* hpart,
                               float* zpart, hipStream_t s);
-hipError_t launch_linear_final(const float* hpart, const float* zpart, const Shape& sh,
+hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
                                uint16_t* h16t, float* hscale, float* z, hipStream_t s);
 // Linear-branch form: with few unselected blocks (Nb - k <= k) the branch is
 // summed directly over them; otherwise as whole-head sums minus the kept share.

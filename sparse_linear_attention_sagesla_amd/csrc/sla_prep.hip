@@ -84,13 +84,23 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
 }
 
 // K channel mean: blocks ascending, one fp64 division by N, rounded to fp32.
+// Loads are issued 32 at a time so the dependent additions do not wait on
+// one memory round trip each.
 __global__ __launch_bounds__(128) void key_mean_kernel(const double* __restrict__ ksum,
                                                        int N, int Nb, float* __restrict__ mu) {
   const int c = threadIdx.x;
   const int bh = blockIdx.x;
   const double* p = ksum + (size_t)bh * Nb * kD + c;
   double s = 0.0;
-  for (int i = 0; i < Nb; ++i) s += p[(size_t)i * kD];
+  int i = 0;
+  for (; i + 32 <= Nb; i += 32) {
+    double v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = p[(size_t)(i + u) * kD];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) s += v[u];
+  }
+  for (; i < Nb; ++i) s += p[(size_t)i * kD];
   mu[(size_t)bh * kD + c] = (float)(s / (double)N);
 }
 
@@ -168,25 +178,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 // Block scores and top-k.  A workgroup owns R query blocks of one (b,h).
 // Phase 1: lane j computes s_ij = sum_c qbar_ic kbar_jc for its key block j
 // and all R rows (fp64 fma, channels ascending; the fp32 x fp32 product is
-// exact in fp64 so each step rounds once) and stores an order-preserving
-// 64-bit key of s_ij in LDS.  Phase 2: one wave per row runs an MSB-first
-// radix select (8-bit digits) for the k-th largest key T, then keeps every
-// key > T plus the lowest-indexed keys == T, writing indices ascending.
+// exact in fp64 so each step rounds once) and keeps the scores in LDS.
+// Phase 2, one wave per row: the scores are spread over kBins buckets by the
+// monotone map floor((s - min) * kBins / (max - min)); one histogram and a
+// suffix scan find the bucket B holding the k-th largest score.  Scores in
+// buckets above B are kept; inside B the candidates are ranked exactly by
+// (score descending, index ascending) to find the last kept one (Ts, Tj).
+// Then j is kept iff s_j > Ts or (s_j == Ts and j <= Tj), written ascending.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t score_key(double s) {
-  if (s == 0.0) s = 0.0;  // -0 and +0 rank equal
-  const uint64_t u = (uint64_t)__double_as_longlong(s);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
+constexpr int kBins = 1024;
 
 template <int R>
 __global__ __launch_bounds__(256) void block_topk_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int Nb, int k,
     int32_t* __restrict__ idx, uint32_t* __restrict__ mask, int32_t* __restrict__ uidx) {
   extern __shared__ __align__(16) unsigned char smem[];
-  double* qs = reinterpret_cast<double*>(smem);                           // [R][128]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + R * kD * 8);        // [4][256]
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem + R * kD * 8 + 4096); // [R][Nb]
+  double* qs = reinterpret_cast<double*>(smem);                              // [R][128]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + R * kD * 8);           // [4][kBins]
+  double* cand_s = reinterpret_cast<double*>(smem + R * kD * 8 + 4 * kBins * 4);   // [4][64]
+  int* cand_j = reinterpret_cast<int*>(smem + R * kD * 8 + 4 * kBins * 4 + 4 * 64 * 8);  // [4][64]
+  double* sc = reinterpret_cast<double*>(smem + R * kD * 8 + 4 * kBins * 4 + 4 * 64 * 12);  // [R][Nb]
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -216,35 +227,52 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
       }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) keys[(size_t)r * Nb + j] = score_key(acc[r]);
+    for (int r = 0; r < R; ++r) sc[(size_t)r * Nb + j] = acc[r];
   }
   __syncthreads();
 
-  uint32_t* h = hist + wave * 256;
+  uint32_t* h = hist + wave * kBins;
+  double* cs = cand_s + wave * 64;
+  int* cj = cand_j + wave * 64;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = wave; r < R; r += 4) {
     const int i = i0 + r;
     if (i >= Nb) break;  // wave-uniform; no block barrier follows
-    const uint64_t* kr = keys + (size_t)r * Nb;
-    uint64_t prefix = 0, pmask = 0;
-    uint32_t kk = (uint32_t)k;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    const double* sr = sc + (size_t)r * Nb;
+    double mn = INFINITY, mx = -INFINITY;
+    for (int j = lane; j < Nb; j += 64) {
+      mn = fmin(mn, sr[j]);
+      mx = fmax(mx, sr[j]);
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[lane * 4 + q] = 0;
+    for (int off = 32; off >= 1; off >>= 1) {
+      mn = fmin(mn, __shfl_xor(mn, off));
+      mx = fmax(mx, __shfl_xor(mx, off));
+    }
+    double Ts;
+    int Tj;
+    if (!(mx > mn)) {
+      // every score equal: the k lowest indices
+      Ts = mx;
+      Tj = k - 1;
+    } else {
+      double scale = (double)kBins / (mx - mn);
+      if (!(scale < 1e300)) scale = 1e300;
+      auto bucket = [&](double v) { return (int)fmin((v - mn) * scale, (double)(kBins - 1)); };
+#pragma unroll
+      for (int q = 0; q < kBins / 64; ++q) h[lane * (kBins / 64) + q] = 0;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
-      for (int j = lane; j < Nb; j += 64) {
-        const uint64_t key = kr[j];
-        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
-      }
+      for (int j = lane; j < Nb; j += 64) atomicAdd(&h[bucket(sr[j])], 1u);
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       __builtin_amdgcn_wave_barrier();
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      uint32_t cnt[4];
+      // lane l owns buckets kBins-1-16l .. kBins-16-16l (descending)
+      constexpr int kPer = kBins / 64;
+      uint32_t cnt[kPer];
       uint32_t local = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        cnt[q] = h[255 - 4 * lane - q];
+      for (int q = 0; q < kPer; ++q) {
+        cnt[q] = h[kBins - 1 - kPer * lane - q];
         local += cnt[q];
       }
       uint32_t incl = local;
@@ -254,55 +282,103 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
         if (lane >= off) incl += v;
       }
       uint32_t before = incl - local;
-      int digit = -1;
-      uint32_t newkk = 0;
+      int B = -1;
+      uint32_t need = 0, nc = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (digit < 0 && before < kk && before + cnt[q] >= kk) {
-          digit = 255 - 4 * lane - q;
-          newkk = kk - before;
+      for (int q = 0; q < kPer; ++q) {
+        if (B < 0 && before < (uint32_t)k && before + cnt[q] >= (uint32_t)k) {
+          B = kBins - 1 - kPer * lane - q;
+          need = (uint32_t)k - before;
+          nc = cnt[q];
         }
         before += cnt[q];
       }
-      const uint64_t found = __ballot(digit >= 0);
+      const uint64_t found = __ballot(B >= 0);
       const int src = __ffsll((unsigned long long)found) - 1;
-      digit = __shfl(digit, src);
-      kk = __shfl(newkk, src);
-      prefix |= (uint64_t)digit << shift;
-      pmask |= 0xffull << shift;
-      __builtin_amdgcn_wave_barrier();
+      B = __shfl(B, src);
+      need = __shfl(need, src);
+      nc = __shfl(nc, src);
+      // the need-th best candidate of bucket B by (score desc, index asc)
+      Ts = 0.0;
+      Tj = 0;
+      if (nc <= 64) {
+        uint32_t base = 0;
+        for (int jb = 0; jb < Nb; jb += 64) {
+          const int j = jb + lane;
+          const bool in = j < Nb && bucket(sr[j]) == B;
+          const uint64_t bb = __ballot(in);
+          if (in) {
+            const uint32_t pos = base + (uint32_t)__popcll(bb & lt_mask);
+            cs[pos] = sr[j];
+            cj[pos] = j;
+          }
+          base += (uint32_t)__popcll(bb);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        bool mine = false;
+        double my_s = 0.0;
+        int my_j = 0;
+        if ((uint32_t)lane < nc) {
+          my_s = cs[lane];
+          my_j = cj[lane];
+          uint32_t rank = 0;
+          for (uint32_t c = 0; c < nc; ++c)
+            rank += (cs[c] > my_s || (cs[c] == my_s && cj[c] < my_j)) ? 1u : 0u;
+          mine = rank == need - 1;
+        }
+        const int who = __ffsll((unsigned long long)__ballot(mine)) - 1;
+        Ts = __shfl(my_s, who);
+        Tj = __shfl(my_j, who);
+      } else {
+        // large tie groups: rank every member of bucket B against all others
+        bool mine = false;
+        double my_s = 0.0;
+        int my_j = 0;
+        for (int jb = 0; jb < Nb; jb += 64) {
+          const int j = jb + lane;
+          if (j < Nb && bucket(sr[j]) == B) {
+            uint32_t rank = 0;
+            for (int u = 0; u < Nb; ++u) {
+              const double v = sr[u];
+              if (bucket(v) == B) rank += (v > sr[j] || (v == sr[j] && u < j)) ? 1u : 0u;
+            }
+            if (rank == need - 1) {
+              mine = true;
+              my_s = sr[j];
+              my_j = j;
+            }
+          }
+        }
+        const int who = __ffsll((unsigned long long)__ballot(mine)) - 1;
+        Ts = __shfl(my_s, who);
+        Tj = __shfl(my_j, who);
+      }
     }
-    const uint64_t T = prefix;
-    const uint32_t need_ties = kk;
     int32_t* out = idx + ((size_t)bh * Nb + i) * k;
     uint32_t* mrow = mask ? mask + ((size_t)bh * Nb + i) * ((Nb + 31) / 32) : nullptr;
     int32_t* urow = uidx ? uidx + ((size_t)bh * Nb + i) * (Nb - k) : nullptr;
-    uint32_t base = 0, ties = 0, ubase = 0;
+    uint32_t base = 0, ubase = 0;
     for (int jb = 0; jb < Nb; jb += 64) {
       const int j = jb + lane;
       const bool valid = j < Nb;
-      const uint64_t key = valid ? kr[j] : 0ull;
-      const bool gt = valid && key > T;
-      const bool eq = valid && key == T;
-      const uint64_t eqb = __ballot(eq);
-      const uint32_t eq_rank = ties + (uint32_t)__popcll(eqb & lt_mask);
-      const bool sel = gt || (eq && eq_rank < need_ties);
+      const double v = valid ? sr[j] : -INFINITY;
+      const bool sel = valid && (v > Ts || (v == Ts && j <= Tj));
       const uint64_t sb = __ballot(sel);
       const uint32_t pos = base + (uint32_t)__popcll(sb & lt_mask);
       if (sel && pos < (uint32_t)k) out[pos] = j;
+      if (mrow) {
+        const int w0 = jb >> 5;
+        if (lane == 0) mrow[w0] = (uint32_t)sb;
+        if (lane == 1 && w0 + 1 < (Nb + 31) / 32) mrow[w0 + 1] = (uint32_t)(sb >> 32);
+      }
       if (urow) {
         const uint64_t ub = __ballot(valid && !sel);
         const uint32_t upos = ubase + (uint32_t)__popcll(ub & lt_mask);
         if (valid && !sel && upos < (uint32_t)(Nb - k)) urow[upos] = j;
         ubase += (uint32_t)__popcll(ub);
       }
-      if (mrow) {
-        const int w0 = jb >> 5;
-        if (lane == 0) mrow[w0] = (uint32_t)sb;
-        if (lane == 1 && w0 + 1 < (Nb + 31) / 32) mrow[w0 + 1] = (uint32_t)(sb >> 32);
-      }
       base += (uint32_t)__popcll(sb);
-      ties += (uint32_t)__popcll(eqb);
     }
   }
 }
@@ -445,29 +521,52 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
   }
 }
 
-// Sum the chunk partials in order; store H^T as fp16 scaled by 2^-s so that
-// max|H| * 2^-s lies in [2^14, 2^15), plus 2^s and z.
-__global__ __launch_bounds__(256) void linear_final_kernel(
-    const float* __restrict__ hpart, const float* __restrict__ zpart,
-    uint16_t* __restrict__ h16t, float* __restrict__ hscale, float* __restrict__ z) {
+// Whole-head linear state, step 1: H (and z) as the chunk partials added in
+// chunk order.  Workgroup (bh, y) owns H elements [1024y, 1024y + 1024) and
+// writes the sum over chunk 0's slot (it alone reads and writes that range).
+__global__ __launch_bounds__(256) void linear_sum_kernel(float* __restrict__ hpart,
+                                                         const float* __restrict__ zpart,
+                                                         float* __restrict__ z) {
+  const int t = threadIdx.x;
+  const int bh = blockIdx.x;
+  float* hp = hpart + (size_t)bh * kLinChunks * kD * kD;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = blockIdx.y * 1024 + t + 256 * m;
+    float v[kLinChunks];
+#pragma unroll
+    for (int c = 0; c < kLinChunks; ++c) v[c] = hp[(size_t)c * kD * kD + e];
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kLinChunks; ++c) s += v[c];
+    hp[e] = s;
+  }
+  if (blockIdx.y == 0 && t < kD) {
+    float v[kLinChunks];
+#pragma unroll
+    for (int c = 0; c < kLinChunks; ++c) v[c] = zpart[((size_t)bh * kLinChunks + c) * kD + t];
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kLinChunks; ++c) s += v[c];
+    z[(size_t)bh * kD + t] = s;
+  }
+}
+
+// Step 2: store H^T as fp16 scaled by 2^-s so that max|H| * 2^-s lies in
+// [2^14, 2^15), plus 2^s.
+__global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict__ hpart,
+                                                         uint16_t* __restrict__ h16t,
+                                                         float* __restrict__ hscale) {
   __shared__ float red[4];
   const int t = threadIdx.x;
   const int bh = blockIdx.x;
-  const float* hp = hpart + (size_t)bh * kLinChunks * kD * kD;
+  const float* hs = hpart + (size_t)bh * kLinChunks * kD * kD;
   float hv[64];
   float mx = 0.0f;
 #pragma unroll
   for (int m = 0; m < 64; ++m) {
-    const int e = t + 256 * m;
-    float s = 0.0f;
-    for (int c = 0; c < kLinChunks; ++c) s += hp[(size_t)c * kD * kD + e];
-    hv[m] = s;
-    mx = fmaxf(mx, fabsf(s));
-  }
-  if (t < kD) {
-    float s = 0.0f;
-    for (int c = 0; c < kLinChunks; ++c) s += zpart[((size_t)bh * kLinChunks + c) * kD + t];
-    z[(size_t)bh * kD + t] = s;
+    hv[m] = hs[t + 256 * m];
+    mx = fmaxf(mx, fabsf(hv[m]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -510,10 +609,13 @@ hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu
 }
 
 size_t topk_lds_bytes(int Nb, int* rows_per_group) {
+  auto bytes = [&](int R) {
+    return (size_t)R * Nb * 8 + (size_t)R * kD * 8 + 4 * kBins * 4 + 4 * 64 * 12;
+  };
   int R = 8;
-  while (R > 1 && (size_t)R * Nb * 8 + (size_t)R * kD * 8 + 4096 > 64 * 1024) R >>= 1;
+  while (R > 1 && bytes(R) > 96 * 1024) R >>= 1;
   if (rows_per_group) *rows_per_group = R;
-  return (size_t)R * Nb * 8 + (size_t)R * kD * 8 + 4096;
+  return bytes(R);
 }
 
 hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
@@ -524,6 +626,12 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& 
   std::call_once(once, [] {
     const int big = 160 * 1024;
     hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<1>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
+    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<2>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
+    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<4>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
+    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<8>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, big);
   });
   dim3 grid((sh.Nb + R - 1) / R, sh.BH);
@@ -549,9 +657,12 @@ hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape&
   return hipGetLastError();
 }
 
-hipError_t launch_linear_final(const float* hpart, const float* zpart, const Shape& sh,
+hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
                                uint16_t* h16t, float* hscale, float* z, hipStream_t s) {
-  linear_final_kernel<<<sh.BH, 256, 0, s>>>(hpart, zpart, h16t, hscale, z);
+  linear_sum_kernel<<<dim3(sh.BH, kD * kD / 1024), 256, 0, s>>>(hpart, zpart, z);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  linear_cvt_kernel<<<sh.BH, 256, 0, s>>>(hpart, h16t, hscale);
   return hipGetLastError();
 }
 

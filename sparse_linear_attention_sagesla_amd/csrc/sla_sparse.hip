@@ -40,6 +40,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 typedef __attribute__((address_space(3))) const v4i lds_v4i;
 typedef __attribute__((address_space(3))) const half8 lds_half8;
@@ -88,30 +89,40 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
   return o;
 }
 
-__device__ __forceinline__ void lds_load16(const void* gsrc, lds_byte* ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (void __attribute__((address_space(3)))*)ldst, 16, 0, 0);
+// Buffer resource over one head's slice of a staging tensor (the per-head slice
+// is below 2^31 bytes, so tile offsets fit the 32-bit buffer offsets; reads
+// past `bytes` return zero instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+
+// 16 bytes per lane from rsrc[voff + soff] into LDS at ldst + 16 * lane.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                           lds_byte* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)ldst, 16,
+                                           voff, soff, 0, 0);
+}
+
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t k8, v16, fk16;  // this head's slices
+};
 
 // Issues this wave's share of a tile's LDS-direct loads into `st`.
 template <bool kK8, bool kFK>
-__device__ __forceinline__ void issue_tile(lds_byte* st, const int8_t* k8, const uint16_t* v16,
-                                           const uint16_t* fk16, size_t bh, int Np, int Nb, int j,
-                                           int wave, const LaneOffsets& lo) {
-  const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(v16) +
-                              ((size_t)bh * Nb + j) * (size_t)kF16TileBytes + lo.ld8;
+__device__ __forceinline__ void issue_tile(lds_byte* st, const TileSrc& src, int j, int wave,
+                                           const LaneOffsets& lo) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) lds_load16(vsrc + 4096 * m, st + kVOff + 4096 * m + 1024 * wave);
+  for (int m = 0; m < 4; ++m)
+    lds_load16(src.v16, lo.ld8, j * kF16TileBytes + 4096 * m, st + kVOff + 4096 * m + 1024 * wave);
   if (kK8) {
-    const unsigned char* ksrc = reinterpret_cast<const unsigned char*>(k8) +
-                                ((size_t)bh * Np + (size_t)j * kBlk) * kD + lo.ld8;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) lds_load16(ksrc + 4096 * m, st + 4096 * m + 1024 * wave);
+    for (int m = 0; m < 2; ++m)
+      lds_load16(src.k8, lo.ld8, j * kK8Bytes + 4096 * m, st + 4096 * m + 1024 * wave);
   }
   if (kFK) {
-    const unsigned char* fsrc = reinterpret_cast<const unsigned char*>(fk16) +
-                                ((size_t)bh * Np + (size_t)j * kBlk) * kD * 2 + lo.ldF;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) lds_load16(fsrc + 4096 * m, st + kFOff + 4096 * m + 1024 * wave);
+    for (int m = 0; m < 4; ++m)
+      lds_load16(src.fk16, lo.ldF, j * kF16TileBytes + 4096 * m, st + kFOff + 4096 * m + 1024 * wave);
   }
 }
 
@@ -166,8 +177,9 @@ struct State {
   float r_part;   // this lane's share of the linear denominator part
 };
 
-// One tile's computation from stage `st`.
-template <bool kSoft, bool kLin>
+// One tile's computation from stage `st`.  kMask: the tile is the ragged last
+// key block (keys >= kvalid are padding and get weight 0).
+template <bool kSoft, bool kLin, bool kMask>
 __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const v4i qf[2],
                                              const half8 fq[4], const LaneOffsets& lo, float cs,
                                              int kvalid, int g) {
@@ -176,8 +188,7 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
   if (kSoft) {
     v4i s[4];
     qk_tile(st, qf, lo.rd8, s);
-    const bool tail = kvalid < kBlk;  // workgroup-uniform: only the ragged last block
-    if (tail) {
+    if (kMask) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -193,7 +204,7 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
     mi = max(mi, __shfl_xor(mi, 32));
     const float mx = (float)mi * cs;  // cs >= 0, so this is the tile's largest logit
     const bool up = mx > S.m_run;
-    if (__builtin_amdgcn_ballot_w64(up)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(up) != 0, 0)) {
       const float m_new = up ? mx : S.m_run;
       const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_new);
 #pragma unroll
@@ -202,23 +213,24 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
       S.m_run = m_new;
     }
     const float nm = -S.m_run;
+    float ls = S.l_part;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[kt][r], cs, nm));
-        if (tail && 16 * kt + 4 * g + r >= kvalid) p = 0.0f;
-        pf[kt >> 1][4 * (kt & 1) + r] = (_Float16)p;
+      for (int r = 0; r < 4; r += 2) {
+        float2v p;
+        p.x = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[kt][r], cs, nm));
+        p.y = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[kt][r + 1], cs, nm));
+        if (kMask) {
+          if (16 * kt + 4 * g + r >= kvalid) p.x = 0.0f;
+          if (16 * kt + 4 * g + r + 1 >= kvalid) p.y = 0.0f;
+        }
+        const half2v ph = __builtin_convertvector(p, half2v);  // RNE
+        pf[kt >> 1][4 * (kt & 1) + r] = ph.x;
+        pf[kt >> 1][4 * (kt & 1) + r + 1] = ph.y;
+        ls = __builtin_amdgcn_fdot2(ph, ones, ls, false);
       }
     }
-    float ls = S.l_part;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const half2v pr = {pf[c][2 * h], pf[c][2 * h + 1]};
-        ls = __builtin_amdgcn_fdot2(pr, ones, ls, false);
-      }
     S.l_part = ls;
   }
   if (kLin) {
@@ -232,17 +244,16 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
         gt[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fq[cc], gt[kt], 0, 0, 0);
       }
     }
+    float rs = S.r_part;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gf[kt >> 1][4 * (kt & 1) + r] = (_Float16)gt[kt][r];
-    float rs = S.r_part;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const half2v gr = {gf[c][2 * h], gf[c][2 * h + 1]};
-        rs = __builtin_amdgcn_fdot2(gr, ones, rs, false);
+      for (int r = 0; r < 4; r += 2) {
+        const float2v gv = {gt[kt][r], gt[kt][r + 1]};
+        const half2v gh = __builtin_convertvector(gv, half2v);  // RNE
+        gf[kt >> 1][4 * (kt & 1) + r] = gh.x;
+        gf[kt >> 1][4 * (kt & 1) + r + 1] = gh.y;
+        rs = __builtin_amdgcn_fdot2(gh, ones, rs, false);
       }
     S.r_part = rs;
   }
@@ -261,11 +272,16 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
 template <bool kSoft, bool kLin>
 __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_bytes,
                                           const int32_t* list, int n, const SparseArgs& a,
-                                          size_t bh, const v4i qf[2], const half8 fq[4],
-                                          const LaneOffsets& lo, float qscale, int wave, int g) {
+                                          const TileSrc& src, size_t bh, const v4i qf[2],
+                                          const half8 fq[4], const LaneOffsets& lo, float qscale,
+                                          int wave, int g) {
   if (n <= 0) return;
-  auto block_of = [&](int p) { return min(max(list[p], 0), a.Nb - 1); };
-  issue_tile<kSoft, kLin>(smem, a.k8, a.v16, a.fk16, bh, a.Np, a.Nb, block_of(0), wave, lo);
+  // wave-uniform key block of tile p (kept in scalar registers), clamped so a
+  // malformed list cannot address outside the staging buffers
+  auto block_of = [&](int p) {
+    return __builtin_amdgcn_readfirstlane(min(max(list[p], 0), a.Nb - 1));
+  };
+  issue_tile<kSoft, kLin>(smem, src, block_of(0), wave, lo);
   for (int p = 0; p < n; p += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -277,9 +293,14 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
         wait_loads();
         __syncthreads();  // tile pp is in LDS; every wave is done with tile pp-1
         if (pp + 1 < n)
-          issue_tile<kSoft, kLin>(nxt, a.k8, a.v16, a.fk16, bh, a.Np, a.Nb, block_of(pp + 1), wave, lo);
+          issue_tile<kSoft, kLin>(nxt, src, block_of(pp + 1), wave, lo);
         const float cs = kSoft ? qscale * a.sk[bh * a.Nb + j] : 0.0f;
-        compute_tile<kSoft, kLin>(S, cur, qf, fq, lo, cs, a.N - j * kBlk, g);
+        const int kvalid = a.N - j * kBlk;
+        // lists are ascending, so only the last tile can be the ragged block
+        if (kSoft && kvalid < kBlk)
+          compute_tile<kSoft, kLin, true>(S, cur, qf, fq, lo, cs, kvalid, g);
+        else
+          compute_tile<kSoft, kLin, false>(S, cur, qf, fq, lo, cs, kvalid, g);
       }
     }
   }
@@ -334,16 +355,21 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   S.r_part = 0.0f;
   const float qscale = a.sq[bh * a.Nb + i] * (kInvSqrtD * kLog2e);
   const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
+  TileSrc src;
+  const size_t k8_head = (size_t)a.Np * kD, f16_head = (size_t)a.Np * kD * 2;
+  src.k8 = head_rsrc(a.k8 + bh * k8_head, k8_head);
+  src.v16 = head_rsrc(a.v16 + bh * (size_t)a.Np * kD, f16_head);
+  src.fk16 = head_rsrc(kLinAny ? a.fk16 + bh * (size_t)a.Np * kD : a.v16, f16_head);
 
   if (kMode == kSoftOnly) {
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
   } else if (kMode == kSubtract) {
-    run_tiles<true, true>(S, smem, stage_bytes, sel, a.k, a, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<true, true>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
   } else {
     const int nu = a.Nb - a.k;
     const int32_t* usel = a.uidx + (bh * a.Nb + i) * (size_t)nu;
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, bh, qf, fq, lo, qscale, wave, g);
-    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, a, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, a, src, bh, qf, fq, lo, qscale, wave, g);
   }
 
   // ---- epilogue: normalise, add the linear branch, store
@@ -434,10 +460,10 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
     return;  // out-of-range pair: its acc tile is left untouched (uniform per workgroup)
   const size_t bh = (size_t)b * H + h;
   const LaneOffsets lo = lane_offsets(wave, lane);
-  const unsigned char* ksrc = reinterpret_cast<const unsigned char*>(k8) +
-                              (bh * Np + (size_t)j * kBlk) * kD + lo.ld8;
+  const size_t k8_head = (size_t)Np * kD;
+  const __amdgpu_buffer_rsrc_t r = head_rsrc(k8 + bh * k8_head, k8_head);
 #pragma unroll
-  for (int m = 0; m < 2; ++m) lds_load16(ksrc + 4096 * m, lk + 4096 * m + 1024 * wave);
+  for (int m = 0; m < 2; ++m) lds_load16(r, lo.ld8, j * kK8Bytes + 4096 * m, lk + 4096 * m + 1024 * wave);
   wait_loads();
   __syncthreads();
   v4i qf[2];
