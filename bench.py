@@ -28,6 +28,8 @@ PEAK_I8_OPS = 5.0e15        # MI355X dense INT8 MFMA
 PEAK_F16_FLOPS = 2.5e15     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM = 8.0e12           # MI355X HBM3E bytes/s
 STAGES = ["stats", "kmean", "quantize", "topk", "linear_prep", "linear_final", "sparse"]
+SPARSE_SRC = os.path.join(ROOT, "sparse_linear_attention_sagesla_amd", "csrc", "sla_sparse.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sparse_fwd_kernel_wan14b720_counters.md")
 
 
 def log(*a):
@@ -64,6 +66,24 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def measured_traffic(workload: str, keep: float, phi: str):
+    """HBM bytes per sparse-kernel launch from the committed rocprofv3 counter
+    summary (calibrated FETCH_SIZE + WRITE_SIZE), or None when that summary was
+    taken on a different kernel source or workload."""
+    import hashlib
+    if (workload, keep, phi) != ("wan14b720", 0.1, "elu1") or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and not line.startswith((" ", "#", "-", "|")):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(SPARSE_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def work_counts(idx: np.ndarray, N: int, d: int, BH: int, keep_all: bool, linear: bool,
@@ -222,7 +242,7 @@ def main():
     achieved = f16_equiv / t_sparse / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_FLOPS / 1e12,
                 "unit": "TFLOP/s", "frac": round(achieved / (PEAK_F16_FLOPS / 1e12), 4),
-                "traffic": None, "kernel": "sparse_fwd_kernel",
+                "traffic": measured_traffic(wl.name, keep, phi), "kernel": "sparse_fwd_kernel",
                 "note": "fp16-equivalent: INT8 ops weighted 0.5 (INT8 peak is 2x the fp16 peak)"}
     bytes_io = {
         "stats": 2 * B * H * N * d * 2,
