@@ -21,6 +21,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+static_assert(SLA_MAX_TOKENS == sla::kMaxTokens, "token limit differs between the header and the kernels");
+
 sla_status check_shape(int B, int H, int N, int d, int block) {
   if (B < 1 || H < 1 || N < 1) return SLA_ERR_INVALID_ARG;
   if (d != SLA_HEAD_DIM || block != SLA_BLOCK) return SLA_ERR_UNSUPPORTED;
@@ -63,7 +65,10 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w)
     ws.sk = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
     ws.idx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.k > 0 ? s.k : 1) * sizeof(int32_t)));
     ws.v16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
-    if (phi != SLA_PHI_NONE && s.k < s.Nb && sla::linear_direct(s)) {
+    const bool direct = phi != SLA_PHI_NONE && s.k < s.Nb && sla::linear_direct(s);
+    if (!direct && s.k > 0)
+      ws.sched = reinterpret_cast<int32_t*>(take(BH * (size_t)((s.Nb + 1) / 2) * s.k * 2 * sizeof(int32_t)));
+    if (direct) {
       ws.uidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.Nb - s.k) * sizeof(int32_t)));
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
     } else if (phi != SLA_PHI_NONE && s.k < s.Nb) {

@@ -625,13 +625,13 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& 
   static std::once_flag once;
   std::call_once(once, [] {
     const int big = 160 * 1024;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<1>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<1>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<2>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<2>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<4>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<4>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<8>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<8>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, big);
   });
   dim3 grid((sh.Nb + R - 1) / R, sh.BH);

@@ -107,22 +107,24 @@ struct TileSrc {
   __amdgpu_buffer_rsrc_t k8, v16, fk16;  // this head's slices
 };
 
-// Issues this wave's share of a tile's LDS-direct loads into `st`.
-template <bool kK8, bool kFK>
+// Issues this wave's share of a tile's LDS-direct loads into `st` (kW waves
+// per workgroup; each instruction round of the workgroup moves kW KB).
+template <bool kK8, bool kFK, int kW = 4>
 __device__ __forceinline__ void issue_tile(lds_byte* st, const TileSrc& src, int j, int wave,
                                            const LaneOffsets& lo) {
+  constexpr int kRound = kW * 1024;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    lds_load16(src.v16, lo.ld8, j * kF16TileBytes + 4096 * m, st + kVOff + 4096 * m + 1024 * wave);
+  for (int m = 0; m < kF16TileBytes / kRound; ++m)
+    lds_load16(src.v16, lo.ld8, j * kF16TileBytes + kRound * m, st + kVOff + kRound * m + 1024 * wave);
   if (kK8) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      lds_load16(src.k8, lo.ld8, j * kK8Bytes + 4096 * m, st + 4096 * m + 1024 * wave);
+    for (int m = 0; m < kK8Bytes / kRound; ++m)
+      lds_load16(src.k8, lo.ld8, j * kK8Bytes + kRound * m, st + kRound * m + 1024 * wave);
   }
   if (kFK) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      lds_load16(src.fk16, lo.ldF, j * kF16TileBytes + 4096 * m, st + kFOff + 4096 * m + 1024 * wave);
+    for (int m = 0; m < kF16TileBytes / kRound; ++m)
+      lds_load16(src.fk16, lo.ldF, j * kF16TileBytes + kRound * m, st + kFOff + kRound * m + 1024 * wave);
   }
 }
 
@@ -149,6 +151,23 @@ __device__ __forceinline__ void load_q8_frag(const int8_t* q8, size_t bh, int Np
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for LDS hand-offs.  Unlike __syncthreads() it carries no
+// release fence, whose vmcnt(0) would also wait for the tile loads issued
+// ahead; each wave has already waited for its own share of the tile being
+// handed over, and its LDS reads are complete (lgkmcnt(0)) before it arrives.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Reads a value the kernel never writes through the constant address space, so
+// a wave-uniform address becomes a scalar load: it is counted by lgkmcnt and
+// waiting for it does not drain the tile loads in flight.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p, size_t i) {
+  typedef const __attribute__((address_space(4))) T cT;
+  return ((cT*)p)[i];
+}
+
 struct SparseArgs {
   const uint16_t* q;
   const int8_t* q8;
@@ -157,6 +176,7 @@ struct SparseArgs {
   const float* sk;
   const int32_t* idx;
   const int32_t* uidx;
+  int32_t* sched;
   const uint16_t* fk16;
   const uint16_t* v16;
   const uint16_t* h16t;
@@ -176,6 +196,16 @@ struct State {
   float l_part;   // this lane's share of the softmax normaliser
   float r_part;   // this lane's share of the linear denominator part
 };
+
+// Maximum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48).
+// Each permlane swap hands every lane its partner's value in one of the two
+// results, so max of the pair is the exchange-and-reduce step without LDS.
+__device__ __forceinline__ int rows_max(int x) {
+  const auto a = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  x = max((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)b[0], (int)b[1]);
+}
 
 // One tile's computation from stage `st`.  kMask: the tile is the ragged last
 // key block (keys >= kvalid are padding and get weight 0).
@@ -200,8 +230,7 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mi = max(mi, s[kt][r]);
-    mi = max(mi, __shfl_xor(mi, 16));
-    mi = max(mi, __shfl_xor(mi, 32));
+    mi = rows_max(mi);
     const float mx = (float)mi * cs;  // cs >= 0, so this is the tile's largest logit
     const bool up = mx > S.m_run;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(up) != 0, 0)) {
@@ -279,7 +308,7 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
   // wave-uniform key block of tile p (kept in scalar registers), clamped so a
   // malformed list cannot address outside the staging buffers
   auto block_of = [&](int p) {
-    return __builtin_amdgcn_readfirstlane(min(max(list[p], 0), a.Nb - 1));
+    return min(max(ld_uniform(list, p), 0), a.Nb - 1);
   };
   issue_tile<kSoft, kLin>(smem, src, block_of(0), wave, lo);
   for (int p = 0; p < n; p += 2) {
@@ -291,10 +320,10 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
         lds_byte* nxt = smem + (1 - half) * stage_bytes;
         const int j = block_of(pp);
         wait_loads();
-        __syncthreads();  // tile pp is in LDS; every wave is done with tile pp-1
+        lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
         if (pp + 1 < n)
           issue_tile<kSoft, kLin>(nxt, src, block_of(pp + 1), wave, lo);
-        const float cs = kSoft ? qscale * a.sk[bh * a.Nb + j] : 0.0f;
+        const float cs = kSoft ? qscale * ld_uniform(a.sk, bh * a.Nb + j) : 0.0f;
         const int kvalid = a.N - j * kBlk;
         // lists are ascending, so only the last tile can be the ragged block
         if (kSoft && kvalid < kBlk)
@@ -304,31 +333,15 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
       }
     }
   }
-  __syncthreads();  // the stages may be refilled by a following walk
+  lds_barrier();  // the stages may be refilled by a following walk
 }
 
-template <int kMode>
-__global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  lds_byte* smem = (lds_byte*)smem_raw;
-  constexpr bool kLinAny = kMode != kSoftOnly;
-  constexpr int stage_bytes = kK8Bytes + kF16TileBytes + (kLinAny ? kF16TileBytes : 0);
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int g = lane >> 4;
-  const int l16 = lane & 15;
-  const int i = blockIdx.x;
-  const size_t bh = blockIdx.y;
-  const LaneOffsets lo = lane_offsets(wave, lane);
-
-  const int qrow = i * kBlk + 16 * wave + l16;  // this lane's query row
-  const bool qvalid = qrow < a.N;
-
-  v4i qf[2];
+// Per-lane query state: INT8 codes (B operand of S^T), fp16 phi(Q)/16 (B
+// operand of G^T and of the phi(Q)H product), accumulators.
+template <bool kLinAny>
+__device__ __forceinline__ void init_query(const SparseArgs& a, size_t bh, int qrow, bool qvalid,
+                                           int g, v4i qf[2], half8 fq[4], State& S) {
   load_q8_frag(a.q8, bh, a.Np, qrow, g, qf);
-
-  half8 fq[4];
   if (kLinAny) {
     const uint16_t* qp = a.q + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD + 8 * g;
 #pragma unroll
@@ -343,8 +356,6 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
       }
     }
   }
-
-  State S;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     S.o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -353,26 +364,14 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   S.m_run = -INFINITY;
   S.l_part = 0.0f;
   S.r_part = 0.0f;
-  const float qscale = a.sq[bh * a.Nb + i] * (kInvSqrtD * kLog2e);
-  const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
-  TileSrc src;
-  const size_t k8_head = (size_t)a.Np * kD, f16_head = (size_t)a.Np * kD * 2;
-  src.k8 = head_rsrc(a.k8 + bh * k8_head, k8_head);
-  src.v16 = head_rsrc(a.v16 + bh * (size_t)a.Np * kD, f16_head);
-  src.fk16 = head_rsrc(kLinAny ? a.fk16 + bh * (size_t)a.Np * kD : a.v16, f16_head);
+}
 
-  if (kMode == kSoftOnly) {
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
-  } else if (kMode == kSubtract) {
-    run_tiles<true, true>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
-  } else {
-    const int nu = a.Nb - a.k;
-    const int32_t* usel = a.uidx + (bh * a.Nb + i) * (size_t)nu;
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
-    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, a, src, bh, qf, fq, lo, qscale, wave, g);
-  }
-
-  // ---- epilogue: normalise, add the linear branch, store
+// Normalise, add the linear branch, store this lane's query row.
+template <int kMode>
+__device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a, size_t bh,
+                                             int qrow, bool qvalid, int g, int l16,
+                                             const half8 fq[4]) {
+  constexpr bool kLinAny = kMode != kSoftOnly;
   float l = S.l_part + __shfl_xor(S.l_part, 16);
   l += __shfl_xor(l, 32);
   const float inv_l = (a.k > 0 && l > 0.0f) ? 1.0f / l : 0.0f;
@@ -441,6 +440,194 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   }
 }
 
+__device__ __forceinline__ TileSrc head_sources(const SparseArgs& a, size_t bh, bool lin) {
+  TileSrc src;
+  const size_t k8_head = (size_t)a.Np * kD, f16_head = (size_t)a.Np * kD * 2;
+  src.k8 = head_rsrc(a.k8 + bh * k8_head, k8_head);
+  src.v16 = head_rsrc(a.v16 + bh * (size_t)a.Np * kD, f16_head);
+  src.fk16 = head_rsrc(lin ? a.fk16 + bh * (size_t)a.Np * kD : a.v16, f16_head);
+  return src;
+}
+
+// One workgroup per query block (used for the direct form of the linear branch).
+template <int kMode>
+__global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_byte* smem = (lds_byte*)smem_raw;
+  constexpr bool kLinAny = kMode != kSoftOnly;
+  constexpr int stage_bytes = kK8Bytes + kF16TileBytes + (kLinAny ? kF16TileBytes : 0);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int i = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const LaneOffsets lo = lane_offsets(wave, lane);
+
+  const int qrow = i * kBlk + 16 * wave + l16;  // this lane's query row
+  const bool qvalid = qrow < a.N;
+  v4i qf[2];
+  half8 fq[4];
+  State S;
+  init_query<kLinAny>(a, bh, qrow, qvalid, g, qf, fq, S);
+  const float qscale = a.sq[bh * a.Nb + i] * (kInvSqrtD * kLog2e);
+  const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
+  const TileSrc src = head_sources(a, bh, kLinAny);
+
+  if (kMode == kSoftOnly) {
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
+  } else if (kMode == kSubtract) {
+    run_tiles<true, true>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
+  } else {
+    const int nu = a.Nb - a.k;
+    const int32_t* usel = a.uidx + (bh * a.Nb + i) * (size_t)nu;
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, a, src, bh, qf, fq, lo, qscale, wave, g);
+  }
+  finish_query<kMode>(S, a, bh, qrow, qvalid, g, l16, fq);
+}
+
+// ---------------------------------------------------------------------------
+// Query-block pairs.  Both blocks of a pair (2x, 2x+1) keep exactly k key
+// blocks; the key blocks kept by both ("common") and the remaining k-c private
+// ones of each side are paired into k steps: step s < c loads one tile that
+// both blocks use, a later step loads the s-th private tile of each side.
+// Every step is one tile for each query block, so no wave idles, and a tile
+// kept by both is loaded once.  The order of tiles does not change the result
+// beyond rounding (online softmax and the sums are order-free).
+// ---------------------------------------------------------------------------
+
+// One wave per pair: schedule[(bh, x, s)] = (key block for 2x, key block for
+// 2x+1, -1 when 2x+1 does not exist).  Lists are strictly ascending.
+__global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __restrict__ idx, int Nb,
+                                                           int k, int32_t* __restrict__ sched) {
+  __shared__ uint32_t bits[2][kMaxTokens / kBlk / 32];  // membership of each side's key blocks
+  const int lane = threadIdx.x;
+  const int x = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int npair = (Nb + 1) / 2;
+  const int32_t* la = idx + (bh * Nb + 2 * x) * (size_t)k;
+  const int32_t* lb = la + k;
+  int32_t* out = sched + (bh * npair + x) * (size_t)k * 2;
+  auto clampj = [&](int j) { return min(max(j, 0), Nb - 1); };
+  if (2 * x + 1 >= Nb) {
+    for (int t = lane; t < k; t += 64) {
+      out[2 * t] = clampj(la[t]);
+      out[2 * t + 1] = -1;
+    }
+    return;
+  }
+  const int words = (Nb + 31) >> 5;
+  for (int w = lane; w < words; w += 64) bits[0][w] = bits[1][w] = 0u;
+  __syncthreads();
+  for (int t = lane; t < k; t += 64) {
+    const int ja = clampj(la[t]), jb = clampj(lb[t]);
+    atomicOr(&bits[0][ja >> 5], 1u << (ja & 31));
+    atomicOr(&bits[1][jb >> 5], 1u << (jb & 31));
+  }
+  __syncthreads();
+  auto has = [&](int side, int j) { return (bits[side][j >> 5] >> (j & 31)) & 1u; };
+  auto below = [&](uint64_t m) {  // set bits of m under this lane
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  };
+  int nc = 0;
+  for (int base = 0; base < k; base += 64) {
+    const int t = base + lane;
+    nc += __popcll(__ballot(t < k && has(1, clampj(la[t]))));
+  }
+  int c = 0, pa = 0, pb = 0;
+  for (int base = 0; base < k; base += 64) {
+    const int t = base + lane;
+    const bool ok = t < k;
+    const int ja = ok ? clampj(la[t]) : 0, jb = ok ? clampj(lb[t]) : 0;
+    const bool common = ok && has(1, ja);
+    const bool priv_a = ok && !common;
+    const bool priv_b = ok && !has(0, jb);
+    const uint64_t mc = __ballot(common), ma = __ballot(priv_a), mb = __ballot(priv_b);
+    // positions stay below k for strictly ascending lists; the checks only
+    // keep a malformed list from writing outside this pair's schedule
+    const int sc = c + below(mc), sa = nc + pa + below(ma), sb = nc + pb + below(mb);
+    if (common && sc < k) {
+      out[2 * sc] = ja;
+      out[2 * sc + 1] = ja;
+    }
+    if (priv_a && sa < k) out[2 * sa] = ja;
+    if (priv_b && sb < k) out[2 * sb + 1] = jb;
+    c += __popcll(mc);
+    pa += __popcll(ma);
+    pb += __popcll(mb);
+  }
+}
+
+// Eight waves: waves 0-3 own 16-row slices of query block 2x, waves 4-7 of
+// block 2x+1.  Two LDS stages of two tile slots each; a step whose two tiles
+// are equal loads and reads slot 0 only.
+template <int kMode>
+__global__ __launch_bounds__(512, 1) void sparse_pair_kernel(SparseArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_byte* smem = (lds_byte*)smem_raw;
+  constexpr bool kLin = kMode == kSubtract;
+  constexpr int tile_bytes = kK8Bytes + kF16TileBytes + (kLin ? kF16TileBytes : 0);
+  constexpr int stage_bytes = 2 * tile_bytes;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int half = wave >> 2;  // which query block of the pair
+  const int wq = wave & 3;     // 16-row slice within it
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const size_t bh = blockIdx.y;
+  const int i = 2 * blockIdx.x + half;
+  const int ic = min(i, a.Nb - 1);
+  const LaneOffsets lo = lane_offsets(wave, lane);
+
+  const int qrow = ic * kBlk + 16 * wq + l16;
+  const bool qvalid = i < a.Nb && qrow < a.N;
+  v4i qf[2];
+  half8 fq[4];
+  State S;
+  init_query<kLin>(a, bh, qrow, qvalid, g, qf, fq, S);
+  const float qscale = a.sq[bh * a.Nb + ic] * (kInvSqrtD * kLog2e);
+  const TileSrc src = head_sources(a, bh, kLin);
+  const int npair = (a.Nb + 1) / 2;
+  const int32_t* sp = a.sched + (bh * npair + blockIdx.x) * (size_t)a.k * 2;
+  auto clampj = [&](int j) { return min(max(j, 0), a.Nb - 1); };
+  // issues the tiles of step `s` into stage `st`
+  auto issue_step = [&](int s, lds_byte* st) {
+    const int ja = ld_uniform(sp, 2 * (size_t)s), jb = ld_uniform(sp, 2 * (size_t)s + 1);
+    issue_tile<true, kLin, 8>(st, src, clampj(ja), wave, lo);
+    if (jb >= 0 && jb != ja) issue_tile<true, kLin, 8>(st + tile_bytes, src, clampj(jb), wave, lo);
+  };
+
+  if (a.k > 0) issue_step(0, smem);
+  for (int s0 = 0; s0 < a.k; s0 += 2) {
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      const int s = s0 + ph;
+      if (s < a.k) {
+        lds_byte* cur = smem + ph * stage_bytes;
+        wait_loads();
+        lds_barrier();  // step s is in LDS; every wave is done with step s-1
+        if (s + 1 < a.k) issue_step(s + 1, smem + (1 - ph) * stage_bytes);
+        const int ja = ld_uniform(sp, 2 * (size_t)s), jb = ld_uniform(sp, 2 * (size_t)s + 1);
+        const int j = half ? jb : ja;
+        if (j >= 0) {
+          const lds_byte* tile = cur + ((half && jb != ja) ? tile_bytes : 0);
+          const int jj = clampj(j);
+          const float cs = qscale * ld_uniform(a.sk, bh * a.Nb + jj);
+          const int kvalid = a.N - jj * kBlk;
+          if (kvalid < kBlk)
+            compute_tile<true, kLin, true>(S, tile, qf, fq, lo, cs, kvalid, g);
+          else
+            compute_tile<true, kLin, false>(S, tile, qf, fq, lo, cs, kvalid, g);
+        }
+      }
+    }
+  }
+  if (i < a.Nb) finish_query<kMode>(S, a, bh, qrow, qvalid, g, l16, fq);
+}
+
 // Integer S tiles for (b, h, i, j) pairs through the same staging and INT8
 // matrix-core path as the attention kernel.
 __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q8,
@@ -482,11 +669,29 @@ hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
   constexpr size_t stage = (size_t)kK8Bytes + kF16TileBytes + (kMode != kSoftOnly ? kF16TileBytes : 0);
   static std::once_flag once;
   std::call_once(once, [] {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
   });
   dim3 grid(sh.Nb, sh.BH);
   sparse_fwd_kernel<kMode><<<grid, 256, 2 * stage, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int kMode>
+hipError_t launch_pair(const SparseArgs& a, const Shape& sh, hipStream_t s) {
+  constexpr size_t stage = 2 * ((size_t)kK8Bytes + kF16TileBytes + (kMode == kSubtract ? kF16TileBytes : 0));
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_pair_kernel<kMode>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
+  });
+  const int npair = (sh.Nb + 1) / 2;
+  if (sh.k > 0) {
+    pair_schedule_kernel<<<dim3(npair, sh.BH), 64, 0, s>>>(a.idx, sh.Nb, sh.k, a.sched);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  sparse_pair_kernel<kMode><<<dim3(npair, sh.BH), 512, 2 * stage, s>>>(a);
   return hipGetLastError();
 }
 
@@ -502,6 +707,7 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.sk = ws.sk;
   a.idx = ws.idx;
   a.uidx = ws.uidx;
+  a.sched = ws.sched;
   a.fk16 = ws.fk16;
   a.v16 = ws.v16;
   a.h16t = ws.h16t;
@@ -516,9 +722,9 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.out_f32 = out_f32;
   a.out_linear = out_linear;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
-  if (!lin) return launch_mode<kSoftOnly>(a, sh, s);
-  if (linear_direct(sh)) return launch_mode<kDirect>(a, sh, s);
-  return launch_mode<kSubtract>(a, sh, s);
+  if (lin && linear_direct(sh)) return launch_mode<kDirect>(a, sh, s);
+  if (!lin) return launch_pair<kSoftOnly>(a, sh, s);
+  return launch_pair<kSubtract>(a, sh, s);
 }
 
 hipError_t launch_debug_qk(const int8_t* q8, const int8_t* k8, const Shape& sh,
