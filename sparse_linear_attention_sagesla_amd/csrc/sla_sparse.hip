@@ -300,7 +300,8 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
 // Walks `n` tiles listed in `list` through the two LDS stages.
 template <bool kSoft, bool kLin>
 __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_bytes,
-                                          const int32_t* list, int n, const SparseArgs& a,
+                                          const int32_t* list, int n, int stride,
+                                          const SparseArgs& a,
                                           const TileSrc& src, size_t bh, const v4i qf[2],
                                           const half8 fq[4], const LaneOffsets& lo, float qscale,
                                           int wave, int g) {
@@ -308,7 +309,7 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
   // wave-uniform key block of tile p (kept in scalar registers), clamped so a
   // malformed list cannot address outside the staging buffers
   auto block_of = [&](int p) {
-    return min(max(ld_uniform(list, p), 0), a.Nb - 1);
+    return min(max(ld_uniform(list, (size_t)p * stride), 0), a.Nb - 1);
   };
   issue_tile<kSoft, kLin>(smem, src, block_of(0), wave, lo);
   for (int p = 0; p < n; p += 2) {
@@ -325,7 +326,7 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
           issue_tile<kSoft, kLin>(nxt, src, block_of(pp + 1), wave, lo);
         const float cs = kSoft ? qscale * ld_uniform(a.sk, bh * a.Nb + j) : 0.0f;
         const int kvalid = a.N - j * kBlk;
-        // lists are ascending, so only the last tile can be the ragged block
+        // only the ragged last key block needs the masked variant
         if (kSoft && kvalid < kBlk)
           compute_tile<kSoft, kLin, true>(S, cur, qf, fq, lo, cs, kvalid, g);
         else
@@ -449,7 +450,8 @@ __device__ __forceinline__ TileSrc head_sources(const SparseArgs& a, size_t bh, 
   return src;
 }
 
-// One workgroup per query block (used for the direct form of the linear branch).
+// One workgroup per query block.  Workgroups x and x+8 of a head (same XCD,
+// dispatched together) take the query blocks of one pair.
 template <int kMode>
 __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -461,7 +463,10 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   const int wave = t >> 6;
   const int g = lane >> 4;
   const int l16 = lane & 15;
-  const int i = blockIdx.x;
+  const int x = blockIdx.x;
+  const int full = gridDim.x & ~15;
+  const int i = x < full ? (x & ~15) + 2 * (x & 7) + ((x >> 3) & 1) : x;
+  if (i >= a.Nb) return;  // the missing partner of an odd last block
   const size_t bh = blockIdx.y;
   const LaneOffsets lo = lane_offsets(wave, lane);
 
@@ -472,30 +477,30 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   State S;
   init_query<kLinAny>(a, bh, qrow, qvalid, g, qf, fq, S);
   const float qscale = a.sq[bh * a.Nb + i] * (kInvSqrtD * kLog2e);
-  const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
   const TileSrc src = head_sources(a, bh, kLinAny);
 
-  if (kMode == kSoftOnly) {
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
-  } else if (kMode == kSubtract) {
-    run_tiles<true, true>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
+  if (kMode != kDirect) {
+    // this block's side of its pair schedule
+    const int32_t* sel = a.sched + (bh * ((a.Nb + 1) / 2) + (i >> 1)) * (size_t)a.k * 2 + (i & 1);
+    run_tiles<true, kLinAny>(S, smem, stage_bytes, sel, a.k, 2, a, src, bh, qf, fq, lo, qscale, wave, g);
   } else {
     const int nu = a.Nb - a.k;
+    const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
     const int32_t* usel = a.uidx + (bh * a.Nb + i) * (size_t)nu;
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, a, src, bh, qf, fq, lo, qscale, wave, g);
-    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, a, src, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, 1, a, src, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, 1, a, src, bh, qf, fq, lo, qscale, wave, g);
   }
   finish_query<kMode>(S, a, bh, qrow, qvalid, g, l16, fq);
 }
 
 // ---------------------------------------------------------------------------
 // Query-block pairs.  Both blocks of a pair (2x, 2x+1) keep exactly k key
-// blocks; the key blocks kept by both ("common") and the remaining k-c private
-// ones of each side are paired into k steps: step s < c loads one tile that
-// both blocks use, a later step loads the s-th private tile of each side.
-// Every step is one tile for each query block, so no wave idles, and a tile
-// kept by both is loaded once.  The order of tiles does not change the result
-// beyond rounding (online softmax and the sums are order-free).
+// blocks.  Their walks are aligned: the c key blocks kept by both come first,
+// in the same steps on both sides, then each side's k-c private blocks.  The
+// two workgroups of a pair run side by side on one XCD, so a tile kept by
+// both is fetched from memory once and found in L2 by the other.  The order
+// of tiles changes the result only by rounding (online softmax and the sums
+// are order-free).
 // ---------------------------------------------------------------------------
 
 // One wave per pair: schedule[(bh, x, s)] = (key block for 2x, key block for
@@ -560,74 +565,6 @@ __global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __rest
   }
 }
 
-// Eight waves: waves 0-3 own 16-row slices of query block 2x, waves 4-7 of
-// block 2x+1.  Two LDS stages of two tile slots each; a step whose two tiles
-// are equal loads and reads slot 0 only.
-template <int kMode>
-__global__ __launch_bounds__(512, 1) void sparse_pair_kernel(SparseArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  lds_byte* smem = (lds_byte*)smem_raw;
-  constexpr bool kLin = kMode == kSubtract;
-  constexpr int tile_bytes = kK8Bytes + kF16TileBytes + (kLin ? kF16TileBytes : 0);
-  constexpr int stage_bytes = 2 * tile_bytes;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int half = wave >> 2;  // which query block of the pair
-  const int wq = wave & 3;     // 16-row slice within it
-  const int g = lane >> 4;
-  const int l16 = lane & 15;
-  const size_t bh = blockIdx.y;
-  const int i = 2 * blockIdx.x + half;
-  const int ic = min(i, a.Nb - 1);
-  const LaneOffsets lo = lane_offsets(wave, lane);
-
-  const int qrow = ic * kBlk + 16 * wq + l16;
-  const bool qvalid = i < a.Nb && qrow < a.N;
-  v4i qf[2];
-  half8 fq[4];
-  State S;
-  init_query<kLin>(a, bh, qrow, qvalid, g, qf, fq, S);
-  const float qscale = a.sq[bh * a.Nb + ic] * (kInvSqrtD * kLog2e);
-  const TileSrc src = head_sources(a, bh, kLin);
-  const int npair = (a.Nb + 1) / 2;
-  const int32_t* sp = a.sched + (bh * npair + blockIdx.x) * (size_t)a.k * 2;
-  auto clampj = [&](int j) { return min(max(j, 0), a.Nb - 1); };
-  // issues the tiles of step `s` into stage `st`
-  auto issue_step = [&](int s, lds_byte* st) {
-    const int ja = ld_uniform(sp, 2 * (size_t)s), jb = ld_uniform(sp, 2 * (size_t)s + 1);
-    issue_tile<true, kLin, 8>(st, src, clampj(ja), wave, lo);
-    if (jb >= 0 && jb != ja) issue_tile<true, kLin, 8>(st + tile_bytes, src, clampj(jb), wave, lo);
-  };
-
-  if (a.k > 0) issue_step(0, smem);
-  for (int s0 = 0; s0 < a.k; s0 += 2) {
-#pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {
-      const int s = s0 + ph;
-      if (s < a.k) {
-        lds_byte* cur = smem + ph * stage_bytes;
-        wait_loads();
-        lds_barrier();  // step s is in LDS; every wave is done with step s-1
-        if (s + 1 < a.k) issue_step(s + 1, smem + (1 - ph) * stage_bytes);
-        const int ja = ld_uniform(sp, 2 * (size_t)s), jb = ld_uniform(sp, 2 * (size_t)s + 1);
-        const int j = half ? jb : ja;
-        if (j >= 0) {
-          const lds_byte* tile = cur + ((half && jb != ja) ? tile_bytes : 0);
-          const int jj = clampj(j);
-          const float cs = qscale * ld_uniform(a.sk, bh * a.Nb + jj);
-          const int kvalid = a.N - jj * kBlk;
-          if (kvalid < kBlk)
-            compute_tile<true, kLin, true>(S, tile, qf, fq, lo, cs, kvalid, g);
-          else
-            compute_tile<true, kLin, false>(S, tile, qf, fq, lo, cs, kvalid, g);
-        }
-      }
-    }
-  }
-  if (i < a.Nb) finish_query<kMode>(S, a, bh, qrow, qvalid, g, l16, fq);
-}
-
 // Integer S tiles for (b, h, i, j) pairs through the same staging and INT8
 // matrix-core path as the attention kernel.
 __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q8,
@@ -672,26 +609,14 @@ hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
   });
-  dim3 grid(sh.Nb, sh.BH);
-  sparse_fwd_kernel<kMode><<<grid, 256, 2 * stage, s>>>(a);
-  return hipGetLastError();
-}
-
-template <int kMode>
-hipError_t launch_pair(const SparseArgs& a, const Shape& sh, hipStream_t s) {
-  constexpr size_t stage = 2 * ((size_t)kK8Bytes + kF16TileBytes + (kMode == kSubtract ? kF16TileBytes : 0));
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_pair_kernel<kMode>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
-  });
-  const int npair = (sh.Nb + 1) / 2;
-  if (sh.k > 0) {
-    pair_schedule_kernel<<<dim3(npair, sh.BH), 64, 0, s>>>(a.idx, sh.Nb, sh.k, a.sched);
+  // paired walks need both workgroups of every pair, so an odd block count is rounded up
+  const int slots = kMode == kDirect ? sh.Nb : 2 * ((sh.Nb + 1) / 2);
+  if (kMode != kDirect && sh.k > 0) {
+    pair_schedule_kernel<<<dim3((sh.Nb + 1) / 2, sh.BH), 64, 0, s>>>(a.idx, sh.Nb, sh.k, a.sched);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  sparse_pair_kernel<kMode><<<dim3(npair, sh.BH), 512, 2 * stage, s>>>(a);
+  sparse_fwd_kernel<kMode><<<dim3(slots, sh.BH), 256, 2 * stage, s>>>(a);
   return hipGetLastError();
 }
 
@@ -723,8 +648,8 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.out_linear = out_linear;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
   if (lin && linear_direct(sh)) return launch_mode<kDirect>(a, sh, s);
-  if (!lin) return launch_pair<kSoftOnly>(a, sh, s);
-  return launch_pair<kSubtract>(a, sh, s);
+  if (!lin) return launch_mode<kSoftOnly>(a, sh, s);
+  return launch_mode<kSubtract>(a, sh, s);
 }
 
 hipError_t launch_debug_qk(const int8_t* q8, const int8_t* k8, const Shape& sh,
