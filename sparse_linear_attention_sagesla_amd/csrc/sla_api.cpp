@@ -67,7 +67,8 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w)
     ws.v16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
     const bool direct = phi != SLA_PHI_NONE && s.k < s.Nb && sla::linear_direct(s);
     if (!direct && s.k > 0)
-      ws.sched = reinterpret_cast<int32_t*>(take(BH * (size_t)((s.Nb + 1) / 2) * s.k * 2 * sizeof(int32_t)));
+      ws.sched = reinterpret_cast<int32_t*>(
+          take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * s.k * sla::kGroup * sizeof(int32_t)));
     if (direct) {
       ws.uidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.Nb - s.k) * sizeof(int32_t)));
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));

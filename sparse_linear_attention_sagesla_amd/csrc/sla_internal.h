@@ -12,6 +12,7 @@ constexpr int kBlk = 64;        // tokens per query / key block
 constexpr int kD = 128;         // head dimension
 constexpr int kLinChunks = 32;  // key-block chunks per head in the linear-state reduction
 constexpr int kMaxTokens = 1 << 20;  // largest N the entry points accept
+constexpr int kGroup = 4;            // query blocks whose key-block walks are aligned
 constexpr float kPhiScale = 0.0625f;  // phi(Q), phi(K) are staged in fp16 as phi/16
 
 enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiRelu = 2 };
@@ -36,7 +37,7 @@ struct Workspace {
   float* sk = nullptr;        // [BH, Nb]
   int32_t* idx = nullptr;     // [BH, Nb, k]   kept key blocks, ascending
   int32_t* uidx = nullptr;    // [BH, Nb, Nb-k] the other key blocks (direct linear mode)
-  int32_t* sched = nullptr;   // [BH, (Nb+1)/2, k, 2] tile schedule of query-block pairs
+  int32_t* sched = nullptr;   // [BH, ceil(Nb/kGroup), k, kGroup] aligned walks of query-block groups
   uint16_t* fk16 = nullptr;   // [BH, Np, D]   fp16 phi(K)/16, row-major, pad rows 0
   uint16_t* v16 = nullptr;    // [BH, Nb, D, 64] fp16 V per block, [channel][permuted key]
   float* hpart = nullptr;     // [BH, kLinChunks, D, D] partial phi(K)^T V

@@ -28,6 +28,7 @@
 //                ones (used when they are no more than the kept ones).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 
@@ -450,8 +451,8 @@ __device__ __forceinline__ TileSrc head_sources(const SparseArgs& a, size_t bh, 
   return src;
 }
 
-// One workgroup per query block.  Workgroups x and x+8 of a head (same XCD,
-// dispatched together) take the query blocks of one pair.
+// One workgroup per query block.  Workgroups x, x+8, ..., x+8(kGroup-1) of a
+// head (same XCD, dispatched together) take the query blocks of one group.
 template <int kMode>
 __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -464,9 +465,10 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   const int g = lane >> 4;
   const int l16 = lane & 15;
   const int x = blockIdx.x;
-  const int full = gridDim.x & ~15;
-  const int i = x < full ? (x & ~15) + 2 * (x & 7) + ((x >> 3) & 1) : x;
-  if (i >= a.Nb) return;  // the missing partner of an odd last block
+  const int span = 8 * kGroup;
+  const int full = gridDim.x - gridDim.x % span;
+  const int i = x < full ? x - x % span + kGroup * (x & 7) + (x % span) / 8 : x;
+  if (i >= a.Nb) return;  // a missing member of the last group
   const size_t bh = blockIdx.y;
   const LaneOffsets lo = lane_offsets(wave, lane);
 
@@ -480,9 +482,11 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   const TileSrc src = head_sources(a, bh, kLinAny);
 
   if (kMode != kDirect) {
-    // this block's side of its pair schedule
-    const int32_t* sel = a.sched + (bh * ((a.Nb + 1) / 2) + (i >> 1)) * (size_t)a.k * 2 + (i & 1);
-    run_tiles<true, kLinAny>(S, smem, stage_bytes, sel, a.k, 2, a, src, bh, qf, fq, lo, qscale, wave, g);
+    // this block's column of its group schedule
+    const int ngroups = (a.Nb + kGroup - 1) / kGroup;
+    const int32_t* sel = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
+    run_tiles<true, kLinAny>(S, smem, stage_bytes, sel, a.k, kGroup, a, src, bh, qf, fq, lo, qscale,
+                             wave, g);
   } else {
     const int nu = a.Nb - a.k;
     const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
@@ -494,74 +498,125 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Query-block pairs.  Both blocks of a pair (2x, 2x+1) keep exactly k key
-// blocks.  Their walks are aligned: the c key blocks kept by both come first,
-// in the same steps on both sides, then each side's k-c private blocks.  The
-// two workgroups of a pair run side by side on one XCD, so a tile kept by
-// both is fetched from memory once and found in L2 by the other.  The order
-// of tiles changes the result only by rounding (online softmax and the sums
-// are order-free).
+// Query-block groups.  The kGroup consecutive query blocks of a group each
+// keep k key blocks.  Their walks are aligned so that a key block kept by
+// several of them is visited by all of those in the same step; the group's
+// workgroups run side by side on one XCD, so such a tile is fetched from
+// memory once and the other requests find it in L2.  The order of tiles
+// changes the result only by rounding (online softmax and the sums are
+// order-free).
+//
+// The schedule is built greedily, step by step: each step repeatedly takes the
+// remaining key block with the most owners among the group members still free
+// in that step (lowest index on ties), until every member has one.  When no
+// remaining block fits the free members, the lowest free member takes, alone,
+// its remaining block with the fewest owners (lowest index on ties); the block
+// stays pending for its other owners.  Every member gets exactly k blocks.
 // ---------------------------------------------------------------------------
 
-// One wave per pair: schedule[(bh, x, s)] = (key block for 2x, key block for
-// 2x+1, -1 when 2x+1 does not exist).  Lists are strictly ascending.
-__global__ __launch_bounds__(64) void pair_schedule_kernel(const int32_t* __restrict__ idx, int Nb,
-                                                           int k, int32_t* __restrict__ sched) {
-  __shared__ uint32_t bits[2][kMaxTokens / kBlk / 32];  // membership of each side's key blocks
+// Maximum over the 64 lanes of a wave (DPP within rows, permlane across rows).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, true));   // lane ^ 2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, true));  // 8-lane mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, true));  // 16-lane mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
+// LDS bytes of the schedule kernel: one owner byte per key block (rounded to
+// words) and the union of the group's kept blocks as (block << 8 | owners).
+inline size_t group_schedule_lds(int Nb, int k, int G) {
+  const size_t words = ((size_t)Nb + 3) / 4;
+  const size_t cap = std::min<size_t>((size_t)Nb, (size_t)G * k);
+  return 4 * (words + cap);
+}
+
+// One wave per group: sched[((bh, grp, s) * kG) + u] = key block of member u
+// (query block kG*grp + u) in step s.  Members past the last block get -1.
+template <int kG>
+__global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx, int Nb,
+                                                            int k, int32_t* __restrict__ sched) {
+  extern __shared__ uint32_t gsm[];
   const int lane = threadIdx.x;
-  const int x = blockIdx.x;
+  const int grp = blockIdx.x;
   const size_t bh = blockIdx.y;
-  const int npair = (Nb + 1) / 2;
-  const int32_t* la = idx + (bh * Nb + 2 * x) * (size_t)k;
-  const int32_t* lb = la + k;
-  int32_t* out = sched + (bh * npair + x) * (size_t)k * 2;
+  const int ngroups = (Nb + kG - 1) / kG;
+  const int first = grp * kG;
+  const int members = min(kG, Nb - first);
+  const uint32_t full = (1u << members) - 1u;
+  const int words = (Nb + 3) / 4;
+  uint32_t* own = gsm;          // owner byte of key block j: byte j&3 of word j>>2
+  uint32_t* uni = gsm + words;  // union, ascending key block
+  int32_t* out = sched + (bh * ngroups + grp) * (size_t)k * kG;
   auto clampj = [&](int j) { return min(max(j, 0), Nb - 1); };
-  if (2 * x + 1 >= Nb) {
+
+  for (int w = lane; w < words; w += 64) own[w] = 0u;
+  __syncthreads();
+  for (int u = 0; u < members; ++u) {
+    const int32_t* l = idx + (bh * Nb + first + u) * (size_t)k;
     for (int t = lane; t < k; t += 64) {
-      out[2 * t] = clampj(la[t]);
-      out[2 * t + 1] = -1;
+      const int j = clampj(l[t]);
+      atomicOr(&own[j >> 2], (1u << u) << (8 * (j & 3)));
     }
-    return;
-  }
-  const int words = (Nb + 31) >> 5;
-  for (int w = lane; w < words; w += 64) bits[0][w] = bits[1][w] = 0u;
-  __syncthreads();
-  for (int t = lane; t < k; t += 64) {
-    const int ja = clampj(la[t]), jb = clampj(lb[t]);
-    atomicOr(&bits[0][ja >> 5], 1u << (ja & 31));
-    atomicOr(&bits[1][jb >> 5], 1u << (jb & 31));
   }
   __syncthreads();
-  auto has = [&](int side, int j) { return (bits[side][j >> 5] >> (j & 31)) & 1u; };
-  auto below = [&](uint64_t m) {  // set bits of m under this lane
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-  };
-  int nc = 0;
-  for (int base = 0; base < k; base += 64) {
-    const int t = base + lane;
-    nc += __popcll(__ballot(t < k && has(1, clampj(la[t]))));
+  int n = 0;
+  for (int base = 0; base < Nb; base += 64) {
+    const int j = base + lane;
+    const uint32_t m = j < Nb ? (own[j >> 2] >> (8 * (j & 3))) & 0xffu : 0u;
+    const uint64_t bal = __ballot(m != 0u);
+    const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (m) uni[pos] = ((uint32_t)j << 8) | m;
+    n += __popcll(bal);
   }
-  int c = 0, pa = 0, pb = 0;
-  for (int base = 0; base < k; base += 64) {
-    const int t = base + lane;
-    const bool ok = t < k;
-    const int ja = ok ? clampj(la[t]) : 0, jb = ok ? clampj(lb[t]) : 0;
-    const bool common = ok && has(1, ja);
-    const bool priv_a = ok && !common;
-    const bool priv_b = ok && !has(0, jb);
-    const uint64_t mc = __ballot(common), ma = __ballot(priv_a), mb = __ballot(priv_b);
-    // positions stay below k for strictly ascending lists; the checks only
-    // keep a malformed list from writing outside this pair's schedule
-    const int sc = c + below(mc), sa = nc + pa + below(ma), sb = nc + pb + below(mb);
-    if (common && sc < k) {
-      out[2 * sc] = ja;
-      out[2 * sc + 1] = ja;
+  __syncthreads();
+  if (lane >= members && lane < kG)
+    for (int s = 0; s < k; ++s) out[(size_t)s * kG + lane] = -1;
+
+  for (int s = 0; s < k; ++s) {
+    uint32_t freem = full;
+    while (freem) {
+      // most owners among the free members, then lowest block (keys are unique)
+      uint32_t best = 0u;
+      for (int e = lane; e < n; e += 64) {
+        const uint32_t v = uni[e], m = v & 0xffu;
+        if (m && !(m & ~freem)) best = max(best, ((uint32_t)__popc(m) << 24) | (0xffffffu - (v >> 8)));
+      }
+      best = wave_max_u32(best);
+      uint32_t take = 0xffu;  // owners this pick may serve
+      if (!best) {
+        // the lowest free member alone, with its block of fewest owners
+        take = 1u << __builtin_ctz(freem);
+        for (int e = lane; e < n; e += 64) {
+          const uint32_t v = uni[e], m = v & 0xffu;
+          if (m & take) best = max(best, ((uint32_t)(kG + 1 - __popc(m)) << 24) | (0xffffffu - (v >> 8)));
+        }
+        best = wave_max_u32(best);
+        if (!best) {  // not reached for well-formed lists: the member has no block left
+          if (lane == 0) out[(size_t)s * kG + __builtin_ctz(freem)] = 0;
+          freem &= ~take;
+          continue;
+        }
+      }
+      const uint32_t j = 0xffffffu - (best & 0xffffffu);
+      // the lane holding block j removes the served owners; all lanes learn them
+      uint32_t m = 0u;
+      for (int e = lane; e < n; e += 64) {
+        const uint32_t v = uni[e];
+        if ((v >> 8) == j) {
+          m = v & take & 0xffu;
+          uni[e] = v & ~m;
+        }
+      }
+      m = wave_max_u32(m);
+      if (!m) m = take & freem & (0u - (take & freem));  // not reached; keeps the loop finite
+      if (lane < kG && ((m >> lane) & 1u)) out[(size_t)s * kG + lane] = (int32_t)j;
+      freem &= ~m;
     }
-    if (priv_a && sa < k) out[2 * sa] = ja;
-    if (priv_b && sb < k) out[2 * sb + 1] = jb;
-    c += __popcll(mc);
-    pa += __popcll(ma);
-    pb += __popcll(mb);
   }
 }
 
@@ -609,10 +664,17 @@ hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
   });
-  // paired walks need both workgroups of every pair, so an odd block count is rounded up
-  const int slots = kMode == kDirect ? sh.Nb : 2 * ((sh.Nb + 1) / 2);
+  // grouped walks need every member's workgroup, so the block count is rounded up
+  const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
+  const int slots = kMode == kDirect ? sh.Nb : kGroup * ngroups;
   if (kMode != kDirect && sh.k > 0) {
-    pair_schedule_kernel<<<dim3((sh.Nb + 1) / 2, sh.BH), 64, 0, s>>>(a.idx, sh.Nb, sh.k, a.sched);
+    static std::once_flag once_sched;
+    std::call_once(once_sched, [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(group_schedule_kernel<kGroup>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    });
+    group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, group_schedule_lds(sh.Nb, sh.k, kGroup), s>>>(
+        a.idx, sh.Nb, sh.k, a.sched);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
