@@ -67,8 +67,8 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w)
     ws.v16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
     const bool direct = phi != SLA_PHI_NONE && s.k < s.Nb && sla::linear_direct(s);
     if (!direct && s.k > 0)
-      ws.sched = reinterpret_cast<int32_t*>(
-          take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * s.k * sla::kGroup * sizeof(int32_t)));
+      ws.sched = reinterpret_cast<int2*>(
+          take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * s.k * sla::kGroup * sizeof(int2)));
     if (direct) {
       ws.uidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.Nb - s.k) * sizeof(int32_t)));
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
@@ -210,9 +210,6 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
     stage(SLA_STAGE_QUANTIZE,
           [&] { return sla::launch_quantize(qb, kb, w.mu, s, w.q8, w.k8, w.sq, w.sk, hs); });
-    stage(SLA_STAGE_TOPK, [&] {
-      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr, hs);
-    });
   }
   stage(SLA_STAGE_LINEAR_PREP, [&] {
     return sla::launch_linear_prep(kb, vb, s, phi_eff, !direct, w.fk16, w.v16, w.hpart, w.zpart, hs);
@@ -220,6 +217,14 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
   if (phi_eff != SLA_PHI_NONE && !direct)
     stage(SLA_STAGE_LINEAR_FINAL,
           [&] { return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs); });
+  // selection last, so the kept lists and walk schedule are still in the
+  // memory-side cache when the sparse kernel reads them
+  if (kk > 0)
+    stage(SLA_STAGE_TOPK, [&] {
+      hipError_t r = sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr, hs);
+      if (r == hipSuccess && !direct) r = sla::launch_group_schedule(w.idx, w.sk, s, w.sched, hs);
+      return r;
+    });
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
                                   out_linear, hs);

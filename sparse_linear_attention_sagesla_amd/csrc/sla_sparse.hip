@@ -177,7 +177,7 @@ struct SparseArgs {
   const float* sk;
   const int32_t* idx;
   const int32_t* uidx;
-  int32_t* sched;
+  const int2* sched;
   const uint16_t* fk16;
   const uint16_t* v16;
   const uint16_t* h16t;
@@ -338,6 +338,44 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
   lds_barrier();  // the stages may be refilled by a following walk
 }
 
+// Walks this block's column of its group schedule (entry of step s at
+// col[s * kGroup]: key block, bits of its INT8 scale) through the two LDS
+// stages.  Entries are read with scalar loads when they are needed; reading
+// them earlier (scalar loads a step ahead, or 64-step chunks in registers)
+// measured slower.
+template <bool kLin>
+__device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_bytes, const int2* col,
+                                          int n, const SparseArgs& a, const TileSrc& src,
+                                          const v4i qf[2], const half8 fq[4], const LaneOffsets& lo,
+                                          float qscale, int wave, int g) {
+  if (n <= 0) return;
+  const int* ent = reinterpret_cast<const int*>(col);
+  auto block_of = [&](int p) { return min(max(ld_uniform(ent, (size_t)p * 2 * kGroup), 0), a.Nb - 1); };
+  auto scale_of = [&](int p) { return __int_as_float(ld_uniform(ent, (size_t)p * 2 * kGroup + 1)); };
+  issue_tile<true, kLin>(smem, src, block_of(0), wave, lo);
+  for (int p = 0; p < n; p += 2) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int pp = p + half;
+      if (pp < n) {
+        lds_byte* cur = smem + half * stage_bytes;
+        lds_byte* nxt = smem + (1 - half) * stage_bytes;
+        const int j = block_of(pp);
+        wait_loads();
+        lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
+        if (pp + 1 < n) issue_tile<true, kLin>(nxt, src, block_of(pp + 1), wave, lo);
+        const float c = qscale * scale_of(pp);
+        const int kvalid = a.N - j * kBlk;
+        // only the ragged last key block needs the masked variant
+        if (kvalid < kBlk)
+          compute_tile<true, kLin, true>(S, cur, qf, fq, lo, c, kvalid, g);
+        else
+          compute_tile<true, kLin, false>(S, cur, qf, fq, lo, c, kvalid, g);
+      }
+    }
+  }
+}
+
 // Per-lane query state: INT8 codes (B operand of S^T), fp16 phi(Q)/16 (B
 // operand of G^T and of the phi(Q)H product), accumulators.
 template <bool kLinAny>
@@ -482,11 +520,9 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   const TileSrc src = head_sources(a, bh, kLinAny);
 
   if (kMode != kDirect) {
-    // this block's column of its group schedule
     const int ngroups = (a.Nb + kGroup - 1) / kGroup;
-    const int32_t* sel = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
-    run_tiles<true, kLinAny>(S, smem, stage_bytes, sel, a.k, kGroup, a, src, bh, qf, fq, lo, qscale,
-                             wave, g);
+    const int2* col = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
+    run_sched<kLinAny>(S, smem, stage_bytes, col, a.k, a, src, qf, fq, lo, qscale, wave, g);
   } else {
     const int nu = a.Nb - a.k;
     const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
@@ -531,14 +567,214 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 inline size_t group_schedule_lds(int Nb, int k, int G) {
   const size_t words = ((size_t)Nb + 3) / 4;
   const size_t cap = std::min<size_t>((size_t)Nb, (size_t)G * k);
-  return 4 * (words + cap);
+  return 4 * (words + 2 * cap);  // owner bytes, union, union sorted by owner set
+}
+
+// Schedule entries: (key block, bits of its INT8 scale), so the attention
+// kernel gets both with one vector load per 64 steps.  -1 marks no block.
+struct SchedOut {
+  int2* p;
+  const float* sk;  // this head's key-block scales
+  int Nb;
+  __device__ __forceinline__ void put(size_t i, int j) const {
+    p[i] = make_int2(j, j >= 0 ? __float_as_int(sk[min(j, Nb - 1)]) : 0);
+  }
+};
+
+// The union of a group's kept blocks, entry = block << 8 | remaining owners,
+// held by one wave in kSchedRegs registers per lane when it fits, else in LDS
+// (UnionLds: visit(f) calls f(entry) on every entry of this lane; f returns
+// true when it changed the entry).
+constexpr int kSchedRegs = 8;
+struct UnionLds {
+  uint32_t* e;
+  int n, lane;
+  template <typename F>
+  __device__ __forceinline__ void visit(F f) {
+    for (int i = lane; i < n; i += 64) {
+      uint32_t v = e[i];
+      if (f(v)) e[i] = v;
+    }
+  }
+};
+
+// The greedy steps over the union (see the group comment above); writes the
+// key block of every member and step to out[s * kG + u].
+template <int kG, typename Ent>
+__device__ __forceinline__ void greedy_steps(Ent& ent, int k, uint32_t full, int lane, const SchedOut& out) {
+  for (int s = 0; s < k; ++s) {
+    uint32_t freem = full;
+    while (freem) {
+      // most owners among the free members, then lowest block (keys are unique)
+      uint32_t best = 0u;
+      ent.visit([&](uint32_t& v) {
+        const uint32_t m = v & 0xffu;
+        if (m && !(m & ~freem)) best = max(best, ((uint32_t)__popc(m) << 24) | (0xffffffu - (v >> 8)));
+        return false;
+      });
+      best = wave_max_u32(best);
+      uint32_t take = 0xffu;  // owners this pick may serve
+      if (!best) {
+        // the lowest free member alone, with its block of fewest owners
+        take = 1u << __builtin_ctz(freem);
+        ent.visit([&](uint32_t& v) {
+          const uint32_t m = v & 0xffu;
+          if (m & take) best = max(best, ((uint32_t)(kG + 1 - __popc(m)) << 24) | (0xffffffu - (v >> 8)));
+          return false;
+        });
+        best = wave_max_u32(best);
+        if (!best) {  // not reached for well-formed lists: the member has no block left
+          if (lane == 0) out.put((size_t)s * kG + __builtin_ctz(freem), 0);
+          freem &= ~take;
+          continue;
+        }
+      }
+      const uint32_t j = 0xffffffu - (best & 0xffffffu);
+      // the lane holding block j removes the served owners; all lanes learn them
+      uint32_t m = 0u;
+      ent.visit([&](uint32_t& v) {
+        if (v && (v >> 8) == j) {
+          m = v & take & 0xffu;
+          v &= ~m;
+          return true;
+        }
+        return false;
+      });
+      m = wave_max_u32(m);
+      if (!m) m = take & freem & (0u - (take & freem));  // not reached; keeps the loop finite
+      if (lane < kG && ((m >> lane) & 1u)) out.put((size_t)s * kG + lane, (int32_t)j);
+      freem &= ~m;
+    }
+  }
+}
+
+// The same greedy with the union in registers: one pass over the entries
+// finds the pick and the lane holding it, which alone updates the entry.
+template <int kG, int kR>
+__device__ __forceinline__ void greedy_steps_regs(uint32_t (&u)[kR], int k, uint32_t full, int lane,
+                                                  const SchedOut& out) {
+  for (int s = 0; s < k; ++s) {
+    uint32_t freem = full;
+    while (freem) {
+      uint32_t best = 0u, take = 0xffu;
+      int slot = 0;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const uint32_t m = u[r] & 0xffu;
+        const uint32_t key =
+            (m && !(m & ~freem)) ? ((uint32_t)__popc(m) << 24) | (0xffffffu - (u[r] >> 8)) : 0u;
+        if (key > best) best = key, slot = r;
+      }
+      uint32_t top = wave_max_u32(best);
+      if (!top) {
+        // the lowest free member alone, with its block of fewest owners
+        take = 1u << __builtin_ctz(freem);
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const uint32_t m = u[r] & 0xffu;
+          const uint32_t key =
+              (m & take) ? ((uint32_t)(kG + 1 - __popc(m)) << 24) | (0xffffffu - (u[r] >> 8)) : 0u;
+          if (key > best) best = key, slot = r;
+        }
+        top = wave_max_u32(best);
+        if (!top) {  // not reached for well-formed lists: the member has no block left
+          if (lane == 0) out.put((size_t)s * kG + __builtin_ctz(freem), 0);
+          freem &= ~take;
+          continue;
+        }
+      }
+      const int holder = __builtin_ctzll(__ballot(best == top));  // keys are unique
+      uint32_t mine = 0u;
+      if (lane == holder) {
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+          if (r == slot) {
+            mine = u[r] & take & 0xffu;
+            u[r] &= ~mine;
+          }
+      }
+      uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)mine, holder);
+      if (!m) m = take & freem & (0u - (take & freem));  // not reached; keeps the loop finite
+      const uint32_t j = 0xffffffu - (top & 0xffffffu);
+      if (lane < kG && ((m >> lane) & 1u)) out.put((size_t)s * kG + lane, (int32_t)j);
+      freem &= ~m;
+    }
+  }
+}
+
+// Groups of four: the same greedy over per-owner-set queues.  The union is
+// sorted (stably, so by block within a set) into 15 queues, one per owner set;
+// lane L < 15 holds the head of queue L, so a pick is one wave-wide maximum
+// over the heads whose set is free.  Returns false, leaving the schedule to
+// the general greedy, when a step would need a block split between steps.
+__device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint32_t* q, int k,
+                                               uint32_t full, int lane, const SchedOut& out) {
+  constexpr uint32_t kSets[16] = {15, 7, 11, 13, 14, 3, 5, 6, 9, 10, 12, 1, 2, 4, 8, 0};
+  const uint64_t below = (1ull << lane) - 1ull;
+  // queue sizes and stable positions (all counts are wave-uniform)
+  int cnt[16];
+#pragma unroll
+  for (int t = 0; t < 15; ++t) cnt[t] = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int e = base + lane;
+    const uint32_t m = e < n ? uni[e] & 0xffu : 0u;
+#pragma unroll
+    for (int t = 0; t < 15; ++t) cnt[t] += __popcll(__ballot(m == kSets[t]));
+  }
+  int off[16], mine_head = 0, mine_end = 0;
+  int run = 0;
+#pragma unroll
+  for (int t = 0; t < 15; ++t) {
+    off[t] = run;
+    if (lane == t) mine_head = run, mine_end = run + cnt[t];
+    run += cnt[t];
+  }
+  for (int base = 0; base < n; base += 64) {
+    const int e = base + lane;
+    const uint32_t v = e < n ? uni[e] : 0u, m = v & 0xffu;
+#pragma unroll
+    for (int t = 0; t < 15; ++t) {
+      const uint64_t bal = __ballot(m == kSets[t]);
+      if (m == kSets[t]) q[off[t] + __popcll(bal & below)] = v >> 8;
+      off[t] += __popcll(bal);
+    }
+  }
+  __syncthreads();
+  uint32_t set = 0u;
+#pragma unroll
+  for (int t = 0; t < 15; ++t)
+    if (lane == t) set = kSets[t];
+  const uint32_t size = (uint32_t)__popc(set);
+  uint32_t hj = mine_head < mine_end ? q[mine_head] : 0xffffffu;
+
+  for (int s = 0; s < k; ++s) {
+    uint32_t freem = full;
+    while (freem) {
+      // most owners among the free members, then lowest block
+      const bool ok = set && !(set & ~freem) && mine_head < mine_end;
+      const uint32_t key = ok ? (size << 24) | (0xffffffu - hj) : 0u;
+      const uint32_t top = wave_max_u32(key);
+      if (!top) return false;
+      const int holder = __builtin_ctzll(__ballot(key == top));
+      const uint32_t bm = (uint32_t)__builtin_amdgcn_readlane((int)set, holder);
+      const int32_t bj = (int32_t)(0xffffffu - (top & 0xffffffu));
+      if (lane == holder) {
+        ++mine_head;
+        hj = mine_head < mine_end ? q[mine_head] : 0xffffffu;
+      }
+      if (lane < 4 && ((bm >> lane) & 1u)) out.put((size_t)s * 4 + lane, bj);
+      freem &= ~bm;
+    }
+  }
+  return true;
 }
 
 // One wave per group: sched[((bh, grp, s) * kG) + u] = key block of member u
 // (query block kG*grp + u) in step s.  Members past the last block get -1.
 template <int kG>
-__global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx, int Nb,
-                                                            int k, int32_t* __restrict__ sched) {
+__global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx,
+                                                            const float* __restrict__ sk, int Nb,
+                                                            int k, int2* __restrict__ sched) {
   extern __shared__ uint32_t gsm[];
   const int lane = threadIdx.x;
   const int grp = blockIdx.x;
@@ -550,7 +786,7 @@ __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __res
   const int words = (Nb + 3) / 4;
   uint32_t* own = gsm;          // owner byte of key block j: byte j&3 of word j>>2
   uint32_t* uni = gsm + words;  // union, ascending key block
-  int32_t* out = sched + (bh * ngroups + grp) * (size_t)k * kG;
+  const SchedOut out{sched + (bh * ngroups + grp) * (size_t)k * kG, sk + bh * Nb, Nb};
   auto clampj = [&](int j) { return min(max(j, 0), Nb - 1); };
 
   for (int w = lane; w < words; w += 64) own[w] = 0u;
@@ -575,48 +811,18 @@ __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __res
   }
   __syncthreads();
   if (lane >= members && lane < kG)
-    for (int s = 0; s < k; ++s) out[(size_t)s * kG + lane] = -1;
+    for (int s = 0; s < k; ++s) out.put((size_t)s * kG + lane, -1);
 
-  for (int s = 0; s < k; ++s) {
-    uint32_t freem = full;
-    while (freem) {
-      // most owners among the free members, then lowest block (keys are unique)
-      uint32_t best = 0u;
-      for (int e = lane; e < n; e += 64) {
-        const uint32_t v = uni[e], m = v & 0xffu;
-        if (m && !(m & ~freem)) best = max(best, ((uint32_t)__popc(m) << 24) | (0xffffffu - (v >> 8)));
-      }
-      best = wave_max_u32(best);
-      uint32_t take = 0xffu;  // owners this pick may serve
-      if (!best) {
-        // the lowest free member alone, with its block of fewest owners
-        take = 1u << __builtin_ctz(freem);
-        for (int e = lane; e < n; e += 64) {
-          const uint32_t v = uni[e], m = v & 0xffu;
-          if (m & take) best = max(best, ((uint32_t)(kG + 1 - __popc(m)) << 24) | (0xffffffu - (v >> 8)));
-        }
-        best = wave_max_u32(best);
-        if (!best) {  // not reached for well-formed lists: the member has no block left
-          if (lane == 0) out[(size_t)s * kG + __builtin_ctz(freem)] = 0;
-          freem &= ~take;
-          continue;
-        }
-      }
-      const uint32_t j = 0xffffffu - (best & 0xffffffu);
-      // the lane holding block j removes the served owners; all lanes learn them
-      uint32_t m = 0u;
-      for (int e = lane; e < n; e += 64) {
-        const uint32_t v = uni[e];
-        if ((v >> 8) == j) {
-          m = v & take & 0xffu;
-          uni[e] = v & ~m;
-        }
-      }
-      m = wave_max_u32(m);
-      if (!m) m = take & freem & (0u - (take & freem));  // not reached; keeps the loop finite
-      if (lane < kG && ((m >> lane) & 1u)) out[(size_t)s * kG + lane] = (int32_t)j;
-      freem &= ~m;
-    }
+  if (kG == 4 && greedy_queues4(uni, n, uni + n, k, full, lane, out)) return;
+  if (n <= 64 * kSchedRegs) {
+    // the union fits in registers: kSchedRegs entries per lane, 0 = empty
+    uint32_t u[kSchedRegs];
+#pragma unroll
+    for (int r = 0; r < kSchedRegs; ++r) u[r] = lane + 64 * r < n ? uni[lane + 64 * r] : 0u;
+    greedy_steps_regs<kG>(u, k, full, lane, out);
+  } else {
+    UnionLds ent{uni, n, lane};
+    greedy_steps<kG>(ent, k, full, lane, out);
   }
 }
 
@@ -665,19 +871,7 @@ hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
   });
   // grouped walks need every member's workgroup, so the block count is rounded up
-  const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
-  const int slots = kMode == kDirect ? sh.Nb : kGroup * ngroups;
-  if (kMode != kDirect && sh.k > 0) {
-    static std::once_flag once_sched;
-    std::call_once(once_sched, [] {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(group_schedule_kernel<kGroup>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    });
-    group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, group_schedule_lds(sh.Nb, sh.k, kGroup), s>>>(
-        a.idx, sh.Nb, sh.k, a.sched);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const int slots = kMode == kDirect ? sh.Nb : kGroup * ((sh.Nb + kGroup - 1) / kGroup);
   sparse_fwd_kernel<kMode><<<dim3(slots, sh.BH), 256, 2 * stage, s>>>(a);
   return hipGetLastError();
 }
@@ -712,6 +906,20 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   if (lin && linear_direct(sh)) return launch_mode<kDirect>(a, sh, s);
   if (!lin) return launch_mode<kSoftOnly>(a, sh, s);
   return launch_mode<kSubtract>(a, sh, s);
+}
+
+hipError_t launch_group_schedule(const int32_t* idx, const float* sk, const Shape& sh, int2* sched,
+                                 hipStream_t s) {
+  if (sh.k <= 0) return hipSuccess;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(group_schedule_kernel<kGroup>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
+  group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, group_schedule_lds(sh.Nb, sh.k, kGroup), s>>>(
+      idx, sk, sh.Nb, sh.k, sched);
+  return hipGetLastError();
 }
 
 hipError_t launch_debug_qk(const int8_t* q8, const int8_t* k8, const Shape& sh,
