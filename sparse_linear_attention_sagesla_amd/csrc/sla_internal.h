@@ -10,7 +10,7 @@ namespace sla {
 
 constexpr int kBlk = 64;        // tokens per query / key block
 constexpr int kD = 128;         // head dimension
-constexpr int kLinChunks = 32;  // key-block chunks per head in the linear-state reduction
+constexpr int kLinChunks = 24;  // key-block chunks per head in the linear-state reduction
 constexpr int kMaxTokens = 1 << 20;  // largest N the entry points accept
 constexpr int kGroup = 4;            // query blocks whose key-block walks are aligned
 constexpr float kPhiScale = 0.0625f;  // phi(Q), phi(K) are staged in fp16 as phi/16

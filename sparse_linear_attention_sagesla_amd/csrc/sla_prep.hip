@@ -402,14 +402,23 @@ __device__ __forceinline__ int perm_pos(int key) {
   return 32 * h + 8 * ((r & 15) >> 2) + (r & 3) + 4 * (r >> 4);
 }
 
+// LDS transpose tiles: row c (a channel) holds the 64 positions in 8 chunks of
+// 8 fp16, rows padded to 72 and chunk P stored at P ^ ((c >> 4) & 7).  Rows 8
+// apart (the transposed writes) and consecutive rows (the matrix-core and row
+// reads) then spread over the 64 banks.
+constexpr int kTRow = kBlk + 8;
+__device__ __forceinline__ int tpos(int c, int pos) {
+  return c * kTRow + ((((pos >> 3) ^ (c >> 4)) & 7) << 3) + (pos & 7);
+}
+
 template <int kMode>
 __global__ __launch_bounds__(256) void linear_prep_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int Nb, int phi,
     uint16_t* __restrict__ fk16, uint16_t* __restrict__ v16, float* __restrict__ hpart,
     float* __restrict__ zpart) {
-  // LDS: transposed tiles [128 channels][64 positions] fp16, 16 KB each
-  __shared__ __align__(16) _Float16 fkT[kD * kBlk];
-  __shared__ __align__(16) _Float16 vT[kD * kBlk];
+  // LDS: transposed tiles [128 channels][64 positions] fp16 (see tpos)
+  __shared__ __align__(16) _Float16 fkT[kD * kTRow];
+  __shared__ __align__(16) _Float16 vT[kD * kTRow];
   constexpr bool kLinear = kMode >= 1;
   constexpr bool kReduce = kMode >= 2;
   const int t = threadIdx.x;
@@ -466,19 +475,21 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
     for (int e = 0; e < 8; ++e) {
       const int c = cc * 8 + e;
       half4 hv = {vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
-      *reinterpret_cast<half4*>(&vT[c * kBlk + p0]) = hv;
+      *reinterpret_cast<half4*>(&vT[tpos(c, p0)]) = hv;
       if (kLinear) {
         half4 hf = {fv[0][e], fv[1][e], fv[2][e], fv[3][e]};
-        *reinterpret_cast<half4*>(&fkT[c * kBlk + p0]) = hf;
+        *reinterpret_cast<half4*>(&fkT[tpos(c, p0)]) = hf;
       }
     }
     __syncthreads();
-    // V staging copy-out: 16 KB contiguous per block
+    // V staging copy-out: 16 KB contiguous per block, 16-byte chunk q = 8c + P
     {
-      const uint4* srcv = reinterpret_cast<const uint4*>(vT);
       uint4* dstv = reinterpret_cast<uint4*>(v16 + ((size_t)bh * Nb + j) * kD * kBlk);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) dstv[t + 256 * m] = srcv[t + 256 * m];
+      for (int m = 0; m < 4; ++m) {
+        const int q = t + 256 * m;
+        dstv[q] = *reinterpret_cast<const uint4*>(&vT[tpos(q >> 3, 8 * (q & 7))]);
+      }
     }
     if (kReduce) {
       // H[c][e] += sum_pos fkT[c][pos] vT[e][pos]; wave owns c-tiles 2w, 2w+1
@@ -487,10 +498,10 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
         half8 af[2], bf[8];
 #pragma unroll
         for (int x = 0; x < 2; ++x)
-          af[x] = *reinterpret_cast<const half8*>(&fkT[(16 * (2 * wave + x) + l16) * kBlk + 32 * kc + 8 * g]);
+          af[x] = *reinterpret_cast<const half8*>(&fkT[tpos(16 * (2 * wave + x) + l16, 32 * kc + 8 * g)]);
 #pragma unroll
         for (int y = 0; y < 8; ++y)
-          bf[y] = *reinterpret_cast<const half8*>(&vT[(16 * y + l16) * kBlk + 32 * kc + 8 * g]);
+          bf[y] = *reinterpret_cast<const half8*>(&vT[tpos(16 * y + l16, 32 * kc + 8 * g)]);
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -498,9 +509,8 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
             acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[x], bf[y], acc[x][y], 0, 0, 0);
       }
       if (t < kD) {
-        const half8* row = reinterpret_cast<const half8*>(&fkT[t * kBlk]);
         for (int p = 0; p < kBlk / 8; ++p) {
-          const half8 hv = row[p];
+          const half8 hv = *reinterpret_cast<const half8*>(&fkT[tpos(t, 8 * p)]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) zacc += (float)hv[e];
         }
