@@ -27,6 +27,7 @@ METRIC = "SLA attn fwd ms/call + effective TOPS (% MFMA peak), Wan-14B-720p shap
 PEAK_I8_OPS = 5.0e15        # MI355X dense INT8 MFMA
 PEAK_F16_FLOPS = 2.5e15     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM = 8.0e12           # MI355X HBM3E bytes/s
+PEAK_F64_FLOPS = 78.6e12    # MI355X fp64 vector
 STAGES = ["stats", "kmean", "quantize", "topk", "linear_prep", "linear_final", "sparse"]
 SPARSE_SRC = os.path.join(ROOT, "sparse_linear_attention_sagesla_amd", "csrc", "sla_sparse.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sparse_fwd_kernel_wan14b720_counters.md")
@@ -250,6 +251,13 @@ def main():
         "linear_prep": 2 * B * H * N * d * 2 + (2 if linear else 1) * B * H * nb * 64 * d * 2,
     }
     bw = {n: round(bytes_io[n] / (stage_ms[n] * 1e-3) / 1e9, 1) for n in bytes_io if n in stage_ms}
+    hbm_frac = {n: round(g * 1e9 / PEAK_HBM, 3) for n, g in bw.items()}
+    # whole call against its ideal: sparse work at the MFMA peaks, streaming
+    # stages at the HBM peak, block scores at the fp64 vector peak
+    ideal_s = ops_i8 / PEAK_I8_OPS + ops_16 / PEAK_F16_FLOPS
+    ideal_s += sum(bytes_io[n] for n in bytes_io if n in stage_ms) / PEAK_HBM
+    if kk > 0:
+        ideal_s += 2.0 * B * H * nb * nb * d / PEAK_F64_FLOPS
     eff_tops = (ops_i8 + ops_16) / (ms_step * 1e-3) / 1e12
     dense_equiv = 4.0 * N * N * d * B * H / (ms_step * 1e-3) / 1e12
     rec = {
@@ -262,6 +270,8 @@ def main():
         "effective_tops": round(eff_tops, 2), "dense_equiv_tops": round(dense_equiv, 2),
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "stage_hbm_gbps": bw,
+        "stage_hbm_frac": hbm_frac,
+        "call_roofline_frac": round(ideal_s / (ms_step * 1e-3), 4),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -313,27 +313,36 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
     return min(max(ld_uniform(list, (size_t)p * stride), 0), a.Nb - 1);
   };
   issue_tile<kSoft, kLin>(smem, src, block_of(0), wave, lo);
-  for (int p = 0; p < n; p += 2) {
+  // lists are ascending, so only the last tile can be the ragged key block;
+  // it is peeled off so the loop carries one compute variant
+  const int nm = n - 1;
+  for (int p = 0; p < nm; p += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int pp = p + half;
-      if (pp < n) {
+      if (pp < nm) {
         lds_byte* cur = smem + half * stage_bytes;
         lds_byte* nxt = smem + (1 - half) * stage_bytes;
         const int j = block_of(pp);
         wait_loads();
         lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
-        if (pp + 1 < n)
-          issue_tile<kSoft, kLin>(nxt, src, block_of(pp + 1), wave, lo);
+        issue_tile<kSoft, kLin>(nxt, src, block_of(pp + 1), wave, lo);
         const float cs = kSoft ? qscale * ld_uniform(a.sk, bh * a.Nb + j) : 0.0f;
-        const int kvalid = a.N - j * kBlk;
-        // only the ragged last key block needs the masked variant
-        if (kSoft && kvalid < kBlk)
-          compute_tile<kSoft, kLin, true>(S, cur, qf, fq, lo, cs, kvalid, g);
-        else
-          compute_tile<kSoft, kLin, false>(S, cur, qf, fq, lo, cs, kvalid, g);
+        compute_tile<kSoft, kLin, false>(S, cur, qf, fq, lo, cs, kBlk, g);
       }
     }
+  }
+  {
+    const int j = block_of(nm);
+    const float cs = kSoft ? qscale * ld_uniform(a.sk, bh * a.Nb + j) : 0.0f;
+    const int kvalid = a.N - j * kBlk;
+    const lds_byte* cur = smem + (nm & 1) * stage_bytes;
+    wait_loads();
+    lds_barrier();
+    if (kSoft && kvalid < kBlk)
+      compute_tile<kSoft, kLin, true>(S, cur, qf, fq, lo, cs, kvalid, g);
+    else
+      compute_tile<kSoft, kLin, false>(S, cur, qf, fq, lo, cs, kvalid, g);
   }
   lds_barrier();  // the stages may be refilled by a following walk
 }
@@ -353,27 +362,33 @@ __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_by
   auto block_of = [&](int p) { return min(max(ld_uniform(ent, (size_t)p * 2 * kGroup), 0), a.Nb - 1); };
   auto scale_of = [&](int p) { return __int_as_float(ld_uniform(ent, (size_t)p * 2 * kGroup + 1)); };
   issue_tile<true, kLin>(smem, src, block_of(0), wave, lo);
-  for (int p = 0; p < n; p += 2) {
+  // the schedule puts a ragged key block only in the last step, which is
+  // peeled off so the loop carries one compute variant
+  const int nm = n - 1;
+  for (int p = 0; p < nm; p += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int pp = p + half;
-      if (pp < n) {
+      if (pp < nm) {
         lds_byte* cur = smem + half * stage_bytes;
         lds_byte* nxt = smem + (1 - half) * stage_bytes;
-        const int j = block_of(pp);
         wait_loads();
         lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
-        if (pp + 1 < n) issue_tile<true, kLin>(nxt, src, block_of(pp + 1), wave, lo);
-        const float c = qscale * scale_of(pp);
-        const int kvalid = a.N - j * kBlk;
-        // only the ragged last key block needs the masked variant
-        if (kvalid < kBlk)
-          compute_tile<true, kLin, true>(S, cur, qf, fq, lo, c, kvalid, g);
-        else
-          compute_tile<true, kLin, false>(S, cur, qf, fq, lo, c, kvalid, g);
+        issue_tile<true, kLin>(nxt, src, block_of(pp + 1), wave, lo);
+        compute_tile<true, kLin, false>(S, cur, qf, fq, lo, qscale * scale_of(pp), kBlk, g);
       }
     }
   }
+  const int j = block_of(nm);
+  const float c = qscale * scale_of(nm);
+  const int kvalid = a.N - j * kBlk;
+  const lds_byte* cur = smem + (nm & 1) * stage_bytes;
+  wait_loads();
+  lds_barrier();
+  if (kvalid < kBlk)
+    compute_tile<true, kLin, true>(S, cur, qf, fq, lo, c, kvalid, g);
+  else
+    compute_tile<true, kLin, false>(S, cur, qf, fq, lo, c, kvalid, g);
 }
 
 // Per-lane query state: INT8 codes (B operand of S^T), fp16 phi(Q)/16 (B
@@ -548,6 +563,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
 // remaining block fits the free members, the lowest free member takes, alone,
 // its remaining block with the fewest owners (lowest index on ties); the block
 // stays pending for its other owners.  Every member gets exactly k blocks.
+// A ragged last key block (N not a multiple of 64) is kept out of the greedy
+// and placed in the last step of every member that keeps it.
 // ---------------------------------------------------------------------------
 
 // Maximum over the 64 lanes of a wave (DPP within rows, permlane across rows).
@@ -601,9 +618,10 @@ struct UnionLds {
 // The greedy steps over the union (see the group comment above); writes the
 // key block of every member and step to out[s * kG + u].
 template <int kG, typename Ent>
-__device__ __forceinline__ void greedy_steps(Ent& ent, int k, uint32_t full, int lane, const SchedOut& out) {
+__device__ __forceinline__ void greedy_steps(Ent& ent, int k, uint32_t full, uint32_t last_busy, int lane,
+                                             const SchedOut& out) {
   for (int s = 0; s < k; ++s) {
-    uint32_t freem = full;
+    uint32_t freem = s == k - 1 ? full & ~last_busy : full;
     while (freem) {
       // most owners among the free members, then lowest block (keys are unique)
       uint32_t best = 0u;
@@ -651,10 +669,11 @@ __device__ __forceinline__ void greedy_steps(Ent& ent, int k, uint32_t full, int
 // The same greedy with the union in registers: one pass over the entries
 // finds the pick and the lane holding it, which alone updates the entry.
 template <int kG, int kR>
-__device__ __forceinline__ void greedy_steps_regs(uint32_t (&u)[kR], int k, uint32_t full, int lane,
+__device__ __forceinline__ void greedy_steps_regs(uint32_t (&u)[kR], int k, uint32_t full, uint32_t last_busy,
+                                                  int lane,
                                                   const SchedOut& out) {
   for (int s = 0; s < k; ++s) {
-    uint32_t freem = full;
+    uint32_t freem = s == k - 1 ? full & ~last_busy : full;
     while (freem) {
       uint32_t best = 0u, take = 0xffu;
       int slot = 0;
@@ -708,7 +727,8 @@ __device__ __forceinline__ void greedy_steps_regs(uint32_t (&u)[kR], int k, uint
 // over the heads whose set is free.  Returns false, leaving the schedule to
 // the general greedy, when a step would need a block split between steps.
 __device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint32_t* q, int k,
-                                               uint32_t full, int lane, const SchedOut& out) {
+                                               uint32_t full, uint32_t last_busy, int lane,
+                                               const SchedOut& out) {
   constexpr uint32_t kSets[16] = {15, 7, 11, 13, 14, 3, 5, 6, 9, 10, 12, 1, 2, 4, 8, 0};
   const uint64_t below = (1ull << lane) - 1ull;
   // queue sizes and stable positions (all counts are wave-uniform)
@@ -748,7 +768,7 @@ __device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint3
   uint32_t hj = mine_head < mine_end ? q[mine_head] : 0xffffffu;
 
   for (int s = 0; s < k; ++s) {
-    uint32_t freem = full;
+    uint32_t freem = s == k - 1 ? full & ~last_busy : full;
     while (freem) {
       // most owners among the free members, then lowest block
       const bool ok = set && !(set & ~freem) && mine_head < mine_end;
@@ -774,7 +794,8 @@ __device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint3
 template <int kG>
 __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx,
                                                             const float* __restrict__ sk, int Nb,
-                                                            int k, int2* __restrict__ sched) {
+                                                            int k, int ragged,
+                                                            int2* __restrict__ sched) {
   extern __shared__ uint32_t gsm[];
   const int lane = threadIdx.x;
   const int grp = blockIdx.x;
@@ -812,17 +833,30 @@ __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __res
   __syncthreads();
   if (lane >= members && lane < kG)
     for (int s = 0; s < k; ++s) out.put((size_t)s * kG + lane, -1);
+  // A ragged last key block goes to the last step of every member that keeps
+  // it, so the attention kernel masks padding only in its peeled last step.
+  uint32_t last_busy = 0u;
+  if (ragged && n > 0 && k > 0) {
+    const uint32_t v = uni[n - 1];  // the union is ascending
+    if ((int)(v >> 8) == Nb - 1) {
+      last_busy = v & 0xffu;
+      __syncthreads();
+      if (lane == 0) uni[n - 1] = v & ~0xffu;  // no owners left for the greedy
+      if (lane < kG && ((last_busy >> lane) & 1u)) out.put((size_t)(k - 1) * kG + lane, Nb - 1);
+      __syncthreads();
+    }
+  }
 
-  if (kG == 4 && greedy_queues4(uni, n, uni + n, k, full, lane, out)) return;
+  if (kG == 4 && greedy_queues4(uni, n, uni + n, k, full, last_busy, lane, out)) return;
   if (n <= 64 * kSchedRegs) {
     // the union fits in registers: kSchedRegs entries per lane, 0 = empty
     uint32_t u[kSchedRegs];
 #pragma unroll
     for (int r = 0; r < kSchedRegs; ++r) u[r] = lane + 64 * r < n ? uni[lane + 64 * r] : 0u;
-    greedy_steps_regs<kG>(u, k, full, lane, out);
+    greedy_steps_regs<kG>(u, k, full, last_busy, lane, out);
   } else {
     UnionLds ent{uni, n, lane};
-    greedy_steps<kG>(ent, k, full, lane, out);
+    greedy_steps<kG>(ent, k, full, last_busy, lane, out);
   }
 }
 
@@ -918,7 +952,7 @@ hipError_t launch_group_schedule(const int32_t* idx, const float* sk, const Shap
   });
   const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
   group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, group_schedule_lds(sh.Nb, sh.k, kGroup), s>>>(
-      idx, sk, sh.Nb, sh.k, sched);
+      idx, sk, sh.Nb, sh.k, sh.N != sh.Nb * kBlk ? 1 : 0, sched);
   return hipGetLastError();
 }
 
