@@ -72,8 +72,10 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w)
     if (direct) {
       ws.uidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.Nb - s.k) * sizeof(int32_t)));
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+      ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
     } else if (phi != SLA_PHI_NONE && s.k < s.Nb) {
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+      ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
       ws.hpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * D * sizeof(float)));
       ws.zpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * sizeof(float)));
       ws.h16t = reinterpret_cast<uint16_t*>(take(BH * D * D * sizeof(uint16_t)));
@@ -212,7 +214,7 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
           [&] { return sla::launch_quantize(qb, kb, w.mu, s, w.q8, w.k8, w.sq, w.sk, hs); });
   }
   stage(SLA_STAGE_LINEAR_PREP, [&] {
-    return sla::launch_linear_prep(kb, vb, s, phi_eff, !direct, w.fk16, w.v16, w.hpart, w.zpart, hs);
+    return sla::launch_linear_prep(kb, vb, s, phi_eff, !direct, w.fk16, w.v16, w.zb, w.hpart, w.zpart, hs);
   });
   if (phi_eff != SLA_PHI_NONE && !direct)
     stage(SLA_STAGE_LINEAR_FINAL,

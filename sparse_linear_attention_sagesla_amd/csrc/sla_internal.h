@@ -39,8 +39,9 @@ struct Workspace {
   int32_t* uidx = nullptr;    // [BH, Nb, Nb-k] the other key blocks (direct linear mode)
   int2* sched = nullptr;      // [BH, ceil(Nb/kGroup), k, kGroup] aligned walks of query-block
                               // groups: (key block, bits of its INT8 scale)
-  uint16_t* fk16 = nullptr;   // [BH, Np, D]   fp16 phi(K)/16, row-major, pad rows 0
+  uint16_t* fk16 = nullptr;   // [BH, Nb, D, 64] fp16 phi(K)/16 per block, [channel][permuted key]
   uint16_t* v16 = nullptr;    // [BH, Nb, D, 64] fp16 V per block, [channel][permuted key]
+  float* zb = nullptr;        // [BH, Nb, D]   fp32 per-block sum of phi(K)/16 over the keys
   float* hpart = nullptr;     // [BH, kLinChunks, D, D] partial phi(K)^T V
   float* zpart = nullptr;     // [BH, kLinChunks, D]    partial sum phi(K)
   uint16_t* h16t = nullptr;   // [BH, D(out), D(in)] fp16 H^T * 2^-s
@@ -59,7 +60,7 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& 
                              int32_t* idx, uint32_t* mask, int32_t* uidx, hipStream_t s);
 size_t topk_lds_bytes(int Nb, int* rows_per_group);
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
-                              bool reduce, uint16_t* fk16, uint16_t* v16, float* hpart,
+                              bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
                               float* zpart, hipStream_t s);
 hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
                                uint16_t* h16t, float* hscale, float* z, hipStream_t s);

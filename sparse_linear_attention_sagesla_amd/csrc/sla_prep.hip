@@ -386,16 +386,17 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 // ---------------------------------------------------------------------------
 // Linear-branch staging.  A workgroup walks a contiguous chunk of key blocks
 // of one (b,h).  For every block it
-//   * writes phi(K)/16 as fp16, row-major [key][channel] (pad rows 0),
-//   * writes V as fp16 in the per-block layout [channel][permuted key] that
-//     the attention kernel reads as a matrix-core operand (pad keys 0),
+//   * writes V and phi(K)/16 as fp16 in the per-block layout
+//     [channel][permuted key] that the attention kernel reads as matrix-core
+//     operands (pad keys 0),
+//   * writes the block's sum of phi(K)/16 over its keys (fp32, per channel),
 //   * accumulates H = sum phi(K)^T V and z = sum phi(K) for the chunk
 //     (fp16 operands, fp32 accumulation, blocks in ascending order).
 // Permuted key order inside each 32-key half: position 8g+s holds key
 // 4g+s (s<4) or 16+4g+(s-4) (s>=4), matching the transposed score tiles
 // that feed the P.V product.
-// kMode: 0 = V staging only, 1 = V and phi(K) staging, 2 = staging plus the
-// H, z partial sums.
+// kMode: 0 = V staging only, 1 = V and phi(K) staging and block sums, 2 =
+// staging plus the H, z partial sums.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int perm_pos(int key) {
   const int h = key >> 5, r = key & 31;
@@ -414,8 +415,8 @@ __device__ __forceinline__ int tpos(int c, int pos) {
 template <int kMode>
 __global__ __launch_bounds__(256) void linear_prep_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int Nb, int phi,
-    uint16_t* __restrict__ fk16, uint16_t* __restrict__ v16, float* __restrict__ hpart,
-    float* __restrict__ zpart) {
+    uint16_t* __restrict__ fk16, uint16_t* __restrict__ v16, float* __restrict__ zb,
+    float* __restrict__ hpart, float* __restrict__ zpart) {
   // LDS: transposed tiles [128 channels][64 positions] fp16 (see tpos)
   __shared__ __align__(16) _Float16 fkT[kD * kTRow];
   __shared__ __align__(16) _Float16 vT[kD * kTRow];
@@ -462,12 +463,6 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
         vv[m][e] = (_Float16)xv[e];
         if (kLinear) fv[m][e] = (r < rows) ? (_Float16)(phi_apply(xk[e], phi) * kPhiScale) : (_Float16)0.0f;
       }
-      if (kLinear) {
-        half8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fv[m][e];
-        *reinterpret_cast<half8*>(fk16 + (((size_t)bh * Nb + j) * kBlk + r) * kD + cc * 8) = o;
-      }
     }
     // transposed LDS writes: 4 consecutive keys -> 4 consecutive positions
     const int p0 = perm_pos(4 * a);
@@ -482,14 +477,29 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
       }
     }
     __syncthreads();
-    // V staging copy-out: 16 KB contiguous per block, 16-byte chunk q = 8c + P
+    // V (and phi(K)) staging copy-out: 16 KB contiguous per block, 16-byte
+    // chunk q = 8c + P
     {
-      uint4* dstv = reinterpret_cast<uint4*>(v16 + ((size_t)bh * Nb + j) * kD * kBlk);
+      const size_t blk = ((size_t)bh * Nb + j) * kD * kBlk;
+      uint4* dstv = reinterpret_cast<uint4*>(v16 + blk);
+      uint4* dstf = reinterpret_cast<uint4*>(fk16 + blk);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int q = t + 256 * m;
         dstv[q] = *reinterpret_cast<const uint4*>(&vT[tpos(q >> 3, 8 * (q & 7))]);
+        if (kLinear) dstf[q] = *reinterpret_cast<const uint4*>(&fkT[tpos(q >> 3, 8 * (q & 7))]);
       }
+    }
+    // per-block sum of phi(K)/16 over the keys, channel t
+    if (kLinear && t < kD) {
+      float zj = 0.0f;
+      for (int p = 0; p < kBlk / 8; ++p) {
+        const half8 hv = *reinterpret_cast<const half8*>(&fkT[tpos(t, 8 * p)]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zj += (float)hv[e];
+      }
+      zb[((size_t)bh * Nb + j) * kD + t] = zj;
+      if (kReduce) zacc += zj;
     }
     if (kReduce) {
       // H[c][e] += sum_pos fkT[c][pos] vT[e][pos]; wave owns c-tiles 2w, 2w+1
@@ -507,13 +517,6 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
 #pragma unroll
           for (int y = 0; y < 8; ++y)
             acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[x], bf[y], acc[x][y], 0, 0, 0);
-      }
-      if (t < kD) {
-        for (int p = 0; p < kBlk / 8; ++p) {
-          const half8 hv = *reinterpret_cast<const half8*>(&fkT[tpos(t, 8 * p)]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) zacc += (float)hv[e];
-        }
       }
     }
     __syncthreads();
@@ -655,15 +658,15 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& 
 }
 
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
-                              bool reduce, uint16_t* fk16, uint16_t* v16, float* hpart,
+                              bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
                               float* zpart, hipStream_t s) {
   dim3 grid(kLinChunks, sh.BH);
   if (phi == kPhiNone)
-    linear_prep_kernel<0><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, hpart, zpart);
+    linear_prep_kernel<0><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart);
   else if (!reduce)
-    linear_prep_kernel<1><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, hpart, zpart);
+    linear_prep_kernel<1><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart);
   else
-    linear_prep_kernel<2><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, hpart, zpart);
+    linear_prep_kernel<2><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart);
   return hipGetLastError();
 }
 

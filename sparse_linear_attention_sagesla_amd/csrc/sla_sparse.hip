@@ -5,12 +5,14 @@
 // Per tile, staged in LDS by direct global->LDS 16-byte loads, double-buffered
 // so the next tile streams in while this one is computed:
 //   K8_j   int8 [64 keys][128]      (8 KB)   -> S^T = K8_j Q8_i^T     (INT8 MFMA)
-//   V_j    fp16 [128][64 perm keys] (16 KB)  -> O^T += V_j^T P^T, A^T += V_j^T G^T
-//   phiK_j fp16 [64 keys][128]      (16 KB)  -> G^T = phiK_j phiQ_i^T (fp16 MFMA)
+//   V_j    fp16 [128][64 perm keys] (16 KB)  -> O^T += V_j^T P^T      (fp16 MFMA)
+//   phiK_j fp16 [128][64 perm keys] (16 KB)  -> M^T += V_j^T phiK_j   (fp16 MFMA)
 // Scores are computed transposed (keys x queries) so each lane ends up holding
-// one query's values for 16 keys; in that layout the exponentiated scores P and
-// the linear weights G are already the B operand of the next product and never
-// leave registers, and the online-softmax statistics are per lane.
+// one query's values for 16 keys; in that layout the exponentiated scores P are
+// already the B operand of the P.V product and never leave registers, and the
+// online-softmax statistics are per lane.  The V fragments read for P.V are
+// also the A operand of the linear branch's M^T = sum V_j^T phiK_j, of which
+// each wave owns 32 phi channels.
 //
 // Softmax branch (tutorial "TurboDiffusion技术架构解析：稀疏线性注意力应用实战"
 // §2.1 standard attention, on INT8 codes as in low-bit SageAttention): logits
@@ -21,11 +23,15 @@
 // rescaled only in tiles where some row's maximum rises.
 // Linear branch (same section, linear attention with phi = elu+1 / ReLU),
 // normalised, over the unselected blocks, in one of two forms:
-//   subtraction: numerator phi(Q)H - A, denominator phi(Q)z - r, with H, z the
-//                whole-head sums and A, r the kept tiles' share (kept tiles
-//                carry both branches);
-//   direct:      A, r summed over the unselected tiles, walked after the kept
-//                ones (used when they are no more than the kept ones).
+//   subtraction: numerator phi(Q)(H - M), denominator phi(Q)(z - z_M), with
+//                H, z the whole-head sums and M = sum phi(K_j)^T V_j,
+//                z_M = sum of the block sums of phi(K_j) over the kept tiles
+//                (kept tiles carry both branches);
+//   direct:      M, z_M summed over the unselected tiles, walked after the
+//                kept ones (used when they are no more than the kept ones);
+//                numerator phi(Q)M, denominator phi(Q)z_M.
+// M is the query block's, shared by its four waves: at the end it is stored
+// once in LDS (fp16, power-of-two scaled) and multiplied by each wave's phi(Q).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -60,33 +66,29 @@ __device__ __forceinline__ float phi_apply(float x, int phi) {
   return fmaxf(x, 0.0f);
 }
 
-// LDS layout.  Tiles with 128-byte rows (K8, V) keep 16-byte chunk ch of row r
-// at chunk ch ^ ((r >> 1) & 7); the phi(K) tile (256-byte rows) at ch ^ (r & 15).
-// A 16-lane read group (16 consecutive rows, same chunk) then touches 16
-// distinct 4-bank groups of the 64-bank LDS.
+// LDS layout.  The staged tiles have 128-byte rows and keep 16-byte chunk ch
+// of row r at chunk ch ^ ((r >> 1) & 7); the final M^T (256-byte rows) keeps
+// chunk ch of row r at ch ^ (r & 15).  A 16-lane read group (16 consecutive
+// rows, same chunk) then touches 16 distinct 4-bank groups of the 64-bank LDS.
 struct LaneOffsets {
-  int rd8;    // read byte offset of (row l16, chunk g) in a 128-byte-row tile; chunk g+4: ^64
-  int rdF;    // read byte offset of (row l16, chunk g) in the phi(K) tile; chunk g+4cc: ^(64cc)
-  int ld8;    // global byte offset (within the tile) this lane fetches for a 128-byte-row tile
-  int ldF;    // same for the phi(K) tile
+  int rd8;    // read byte offset of (row l16, chunk g) in a staged tile; chunk g+4: ^64
+  int rdK;    // rd8 in rows 32w.. of the stage's phi(K) tile (w = this wave)
+  int rdM;    // read byte offset of (row l16, chunk g) in M^T; chunk g+4cc: ^(64cc)
+  int ld8;    // global byte offset (within the tile) this lane fetches
+  int zo;     // byte offset of this lane's phi channel 32w + (lane & 31) in a block sum
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
   LaneOffsets o;
   const int l16 = lane & 15, g = lane >> 4;
   o.rd8 = l16 * 128 + ((g ^ ((l16 >> 1) & 7)) << 4);
-  o.rdF = l16 * 256 + ((g ^ l16) << 4);
+  o.rdK = kFOff + 4096 * wave + o.rd8;  // bit 6 of the base is 0, so ^64 still picks chunk g+4
+  o.rdM = l16 * 256 + ((g ^ l16) << 4);
   // LDS-direct loads: wave w, instruction m fills LDS chunks 256m + 64w + lane
-  {
-    const int row = 8 * wave + (lane >> 3);           // + 32m
-    const int ch = (lane & 7) ^ ((row >> 1) & 7);
-    o.ld8 = row * 128 + ch * 16;                      // + 4096m
-  }
-  {
-    const int row = 4 * wave + (lane >> 4);           // + 16m
-    const int ch = (lane & 15) ^ (row & 15);
-    o.ldF = row * 256 + ch * 16;                      // + 4096m
-  }
+  const int row = 8 * wave + (lane >> 3);             // + 32m
+  const int ch = (lane & 7) ^ ((row >> 1) & 7);
+  o.ld8 = row * 128 + ch * 16;                        // + 4096m
+  o.zo = 4 * (32 * wave + (lane & 31));
   return o;
 }
 
@@ -105,7 +107,7 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int voff, i
 }
 
 struct TileSrc {
-  __amdgpu_buffer_rsrc_t k8, v16, fk16;  // this head's slices
+  __amdgpu_buffer_rsrc_t k8, v16, fk16, zb;  // this head's slices
 };
 
 // Issues this wave's share of a tile's LDS-direct loads into `st` (kW waves
@@ -125,8 +127,13 @@ __device__ __forceinline__ void issue_tile(lds_byte* st, const TileSrc& src, int
   if (kFK) {
 #pragma unroll
     for (int m = 0; m < kF16TileBytes / kRound; ++m)
-      lds_load16(src.fk16, lo.ldF, j * kF16TileBytes + kRound * m, st + kFOff + kRound * m + 1024 * wave);
+      lds_load16(src.fk16, lo.ld8, j * kF16TileBytes + kRound * m, st + kFOff + kRound * m + 1024 * wave);
   }
+}
+
+// This lane's channel of key block j's phi(K) block sum.
+__device__ __forceinline__ float load_zb(const TileSrc& src, int j, const LaneOffsets& lo) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.zb, lo.zo, j * (kD * 4), 0));
 }
 
 // S^T tile (64 keys x 16 queries of this wave) from the staged K8 tile.
@@ -180,6 +187,7 @@ struct SparseArgs {
   const int2* sched;
   const uint16_t* fk16;
   const uint16_t* v16;
+  const float* zb;
   const uint16_t* h16t;
   const float* hscale;
   const float* z;
@@ -192,10 +200,11 @@ struct SparseArgs {
 
 struct State {
   v4f o[8];       // O^T accumulator (softmax numerator), d = 16dt + 4g + r
-  v4f al[8];      // A^T accumulator (linear branch, kept or unselected share)
+  v4f mk[8][2];   // M^T accumulator (linear branch, kept or unselected share):
+                  // row d = 16dt + 4g + r, phi channel 32w + 16x + l16
   float m_run;    // running log2-domain maximum (this lane's query)
   float l_part;   // this lane's share of the softmax normaliser
-  float r_part;   // this lane's share of the linear denominator part
+  float zk;       // z_M, phi channel 32w + (lane & 31)
 };
 
 // Maximum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48).
@@ -212,9 +221,9 @@ __device__ __forceinline__ int rows_max(int x) {
 // key block (keys >= kvalid are padding and get weight 0).
 template <bool kSoft, bool kLin, bool kMask>
 __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const v4i qf[2],
-                                             const half8 fq[4], const LaneOffsets& lo, float cs,
+                                             const LaneOffsets& lo, float cs, float zj,
                                              int kvalid, int g) {
-  half8 pf[2], gf[2];
+  half8 pf[2], fk[2][2];
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
   if (kSoft) {
     v4i s[4];
@@ -264,28 +273,12 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
     S.l_part = ls;
   }
   if (kLin) {
-    v4f gt[4];
+    // B operands phiK[key][channel] for this wave's channels 32w + 16x + l16
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      gt[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const half8 af = *(lds_half8*)(st + kFOff + kt * 4096 + (lo.rdF ^ (64 * cc)));
-        gt[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fq[cc], gt[kt], 0, 0, 0);
-      }
-    }
-    float rs = S.r_part;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const float2v gv = {gt[kt][r], gt[kt][r + 1]};
-        const half2v gh = __builtin_convertvector(gv, half2v);  // RNE
-        gf[kt >> 1][4 * (kt & 1) + r] = gh.x;
-        gf[kt >> 1][4 * (kt & 1) + r + 1] = gh.y;
-        rs = __builtin_amdgcn_fdot2(gh, ones, rs, false);
-      }
-    S.r_part = rs;
+      for (int c = 0; c < 2; ++c) fk[x][c] = *(lds_half8*)(st + 2048 * x + (lo.rdK ^ (64 * c)));
+    S.zk += zj;
   }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
@@ -293,7 +286,11 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
     for (int c = 0; c < 2; ++c) {
       const half8 av = *(lds_half8*)(st + kVOff + dt * 2048 + (lo.rd8 ^ (64 * c)));
       if (kSoft) S.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[c], S.o[dt], 0, 0, 0);
-      if (kLin) S.al[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, gf[c], S.al[dt], 0, 0, 0);
+      if (kLin) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          S.mk[dt][x] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, fk[x][c], S.mk[dt][x], 0, 0, 0);
+      }
     }
   }
 }
@@ -304,15 +301,16 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
                                           const int32_t* list, int n, int stride,
                                           const SparseArgs& a,
                                           const TileSrc& src, size_t bh, const v4i qf[2],
-                                          const half8 fq[4], const LaneOffsets& lo, float qscale,
-                                          int wave, int g) {
+                                          const LaneOffsets& lo, float qscale, int wave, int g) {
   if (n <= 0) return;
   // wave-uniform key block of tile p (kept in scalar registers), clamped so a
   // malformed list cannot address outside the staging buffers
   auto block_of = [&](int p) {
     return min(max(ld_uniform(list, (size_t)p * stride), 0), a.Nb - 1);
   };
-  issue_tile<kSoft, kLin>(smem, src, block_of(0), wave, lo);
+  int j = block_of(0);
+  issue_tile<kSoft, kLin>(smem, src, j, wave, lo);
+  float zc = kLin ? load_zb(src, j, lo) : 0.0f;
   // lists are ascending, so only the last tile can be the ragged key block;
   // it is peeled off so the loop carries one compute variant
   const int nm = n - 1;
@@ -323,26 +321,28 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
       if (pp < nm) {
         lds_byte* cur = smem + half * stage_bytes;
         lds_byte* nxt = smem + (1 - half) * stage_bytes;
-        const int j = block_of(pp);
+        const int jn = block_of(pp + 1);
         wait_loads();
         lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
-        issue_tile<kSoft, kLin>(nxt, src, block_of(pp + 1), wave, lo);
+        issue_tile<kSoft, kLin>(nxt, src, jn, wave, lo);
+        const float zn = kLin ? load_zb(src, jn, lo) : 0.0f;
         const float cs = kSoft ? qscale * ld_uniform(a.sk, bh * a.Nb + j) : 0.0f;
-        compute_tile<kSoft, kLin, false>(S, cur, qf, fq, lo, cs, kBlk, g);
+        compute_tile<kSoft, kLin, false>(S, cur, qf, lo, cs, zc, kBlk, g);
+        j = jn;
+        zc = zn;
       }
     }
   }
   {
-    const int j = block_of(nm);
     const float cs = kSoft ? qscale * ld_uniform(a.sk, bh * a.Nb + j) : 0.0f;
     const int kvalid = a.N - j * kBlk;
     const lds_byte* cur = smem + (nm & 1) * stage_bytes;
     wait_loads();
     lds_barrier();
     if (kSoft && kvalid < kBlk)
-      compute_tile<kSoft, kLin, true>(S, cur, qf, fq, lo, cs, kvalid, g);
+      compute_tile<kSoft, kLin, true>(S, cur, qf, lo, cs, zc, kvalid, g);
     else
-      compute_tile<kSoft, kLin, false>(S, cur, qf, fq, lo, cs, kvalid, g);
+      compute_tile<kSoft, kLin, false>(S, cur, qf, lo, cs, zc, kvalid, g);
   }
   lds_barrier();  // the stages may be refilled by a following walk
 }
@@ -355,13 +355,15 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
 template <bool kLin>
 __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_bytes, const int2* col,
                                           int n, const SparseArgs& a, const TileSrc& src,
-                                          const v4i qf[2], const half8 fq[4], const LaneOffsets& lo,
+                                          const v4i qf[2], const LaneOffsets& lo,
                                           float qscale, int wave, int g) {
   if (n <= 0) return;
   const int* ent = reinterpret_cast<const int*>(col);
   auto block_of = [&](int p) { return min(max(ld_uniform(ent, (size_t)p * 2 * kGroup), 0), a.Nb - 1); };
   auto scale_of = [&](int p) { return __int_as_float(ld_uniform(ent, (size_t)p * 2 * kGroup + 1)); };
-  issue_tile<true, kLin>(smem, src, block_of(0), wave, lo);
+  int j = block_of(0);
+  issue_tile<true, kLin>(smem, src, j, wave, lo);
+  float zc = kLin ? load_zb(src, j, lo) : 0.0f;
   // the schedule puts a ragged key block only in the last step, which is
   // peeled off so the loop carries one compute variant
   const int nm = n - 1;
@@ -374,59 +376,140 @@ __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_by
         lds_byte* nxt = smem + (1 - half) * stage_bytes;
         wait_loads();
         lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
-        issue_tile<true, kLin>(nxt, src, block_of(pp + 1), wave, lo);
-        compute_tile<true, kLin, false>(S, cur, qf, fq, lo, qscale * scale_of(pp), kBlk, g);
+        const int jn = block_of(pp + 1);
+        issue_tile<true, kLin>(nxt, src, jn, wave, lo);
+        const float zn = kLin ? load_zb(src, jn, lo) : 0.0f;
+        compute_tile<true, kLin, false>(S, cur, qf, lo, qscale * scale_of(pp), zc, kBlk, g);
+        j = jn;
+        zc = zn;
       }
     }
   }
-  const int j = block_of(nm);
   const float c = qscale * scale_of(nm);
   const int kvalid = a.N - j * kBlk;
   const lds_byte* cur = smem + (nm & 1) * stage_bytes;
   wait_loads();
   lds_barrier();
   if (kvalid < kBlk)
-    compute_tile<true, kLin, true>(S, cur, qf, fq, lo, c, kvalid, g);
+    compute_tile<true, kLin, true>(S, cur, qf, lo, c, zc, kvalid, g);
   else
-    compute_tile<true, kLin, false>(S, cur, qf, fq, lo, c, kvalid, g);
+    compute_tile<true, kLin, false>(S, cur, qf, lo, c, zc, kvalid, g);
 }
 
-// Per-lane query state: INT8 codes (B operand of S^T), fp16 phi(Q)/16 (B
-// operand of G^T and of the phi(Q)H product), accumulators.
-template <bool kLinAny>
-__device__ __forceinline__ void init_query(const SparseArgs& a, size_t bh, int qrow, bool qvalid,
-                                           int g, v4i qf[2], half8 fq[4], State& S) {
-  load_q8_frag(a.q8, bh, a.Np, qrow, g, qf);
-  if (kLinAny) {
-    const uint16_t* qp = a.q + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD + 8 * g;
+// fp16 phi(Q)/16 of this lane's query, channels 32cc + 8g + e (B operand of
+// the phi(Q)H and phi(Q)M products).
+__device__ __forceinline__ void load_phi_q(const SparseArgs& a, size_t bh, int qrow, bool qvalid,
+                                           int g, half8 fq[4]) {
+  const uint16_t* qp = a.q + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD + 8 * g;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qp + 32 * cc);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int cc = 0; cc < 4; ++cc) {
+    const uint4 u = *reinterpret_cast<const uint4*>(qp + 32 * cc);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
-        const float x = __uint_as_float(bits);
-        fq[cc][e] = qvalid ? (_Float16)(phi_apply(x, a.phi) * kPhiScale) : (_Float16)0.0f;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+      const float x = __uint_as_float(bits);
+      fq[cc][e] = qvalid ? (_Float16)(phi_apply(x, a.phi) * kPhiScale) : (_Float16)0.0f;
     }
   }
+}
+
+// Per-lane query state: INT8 codes (B operand of S^T), accumulators.
+__device__ __forceinline__ void init_query(const SparseArgs& a, size_t bh, int qrow, int g,
+                                           v4i qf[2], State& S) {
+  load_q8_frag(a.q8, bh, a.Np, qrow, g, qf);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     S.o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-    S.al[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    S.mk[dt][0] = v4f{0.f, 0.f, 0.f, 0.f};
+    S.mk[dt][1] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   S.m_run = -INFINITY;
   S.l_part = 0.0f;
-  S.r_part = 0.0f;
+  S.zk = 0.0f;
+}
+
+// Maximum over the 64 lanes of a wave (DPP within rows, permlane across rows).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, true));   // lane ^ 2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, true));  // 8-lane mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, true));  // 16-lane mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
+// The linear branch's share phi(Q) M for this lane's query (O^T layout, d =
+// 16dt + 4g + r) and phi(Q) z_M.  The workgroup's four waves hold M^T by
+// channel slices; M^T goes through LDS once as fp16 scaled by 2^-s so that
+// max|M| 2^-s lies in [2^14, 2^15), and comes back as A operands.
+__device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, const half8 fq[4],
+                                             const LaneOffsets& lo, int wave, int lane,
+                                             v4f num[8], float& den) {
+  constexpr int kZOff = kD * kD * 2;             // z_M, fp32 [128]
+  constexpr int kRedOff = kZOff + kD * 4;        // per-wave maxima
+  const int g = lane >> 4, l16 = lane & 15;
+  float mx = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S.mk[dt][x][r]));
+  const uint32_t wm = wave_max_u32(__float_as_uint(mx));  // non-negative floats order as integers
+  lds_barrier();  // every wave is done with the tile stages
+  if (lane == 0) *(__attribute__((address_space(3))) uint32_t*)(smem + kRedOff + 4 * wave) = wm;
+  if (lane < 32) *(__attribute__((address_space(3))) float*)(smem + kZOff + 4 * (32 * wave + lane)) = S.zk;
+  lds_barrier();
+  uint32_t m4 = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    m4 = max(m4, *(__attribute__((address_space(3))) const uint32_t*)(smem + kRedOff + 4 * w));
+  const float mall = __uint_as_float(m4);
+  const int sh = mall > 0.0f ? ilogbf(mall) - 14 : 0;
+  const float down = ldexpf(1.0f, -sh);
+  typedef __attribute__((address_space(3))) _Float16 lds_h;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * dt + 4 * g + r;
+        const int ch = (4 * wave + 2 * x + (l16 >> 3)) ^ (row & 15);
+        *(lds_h*)(smem + row * 256 + ch * 16 + 2 * (l16 & 7)) = (_Float16)(S.mk[dt][x][r] * down);
+      }
+  lds_barrier();
+  const float up = ldexpf(1.0f, sh);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const half8 am = *(lds_half8*)(smem + 4096 * dt + (lo.rdM ^ (64 * cc)));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, fq[cc], acc, 0, 0, 0);
+    }
+    num[dt] = acc * up;
+  }
+  float d = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      d += (float)fq[cc][e] * *(__attribute__((address_space(3))) const float*)(smem + kZOff + 4 * (32 * cc + 8 * g + e));
+  d += __shfl_xor(d, 16);
+  den = d + __shfl_xor(d, 32);
 }
 
 // Normalise, add the linear branch, store this lane's query row.
 template <int kMode>
 __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a, size_t bh,
-                                             int qrow, bool qvalid, int g, int l16,
-                                             const half8 fq[4]) {
+                                             int qrow, bool qvalid, lds_byte* smem,
+                                             const LaneOffsets& lo, int wave, int lane) {
   constexpr bool kLinAny = kMode != kSoftOnly;
+  const int g = lane >> 4, l16 = lane & 15;
   float l = S.l_part + __shfl_xor(S.l_part, 16);
   l += __shfl_xor(l, 32);
   const float inv_l = (a.k > 0 && l > 0.0f) ? 1.0f / l : 0.0f;
@@ -435,13 +518,16 @@ __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) ol[dt] = v4f{0.f, 0.f, 0.f, 0.f};
   if (kLinAny) {
-    float r = S.r_part + __shfl_xor(S.r_part, 16);
-    r += __shfl_xor(r, 32);
+    half8 fq[4];
+    load_phi_q(a, bh, qrow, qvalid, g, fq);
+    v4f nm[8];
+    float dm;
+    linear_share(S, smem, fq, lo, wave, lane, nm, dm);
     if (kMode == kDirect) {
       // numerator and denominator summed over the unselected blocks
-      const float inv_den = r > 0.0f ? 1.0f / r : 0.0f;
+      const float inv_den = dm > 0.0f ? 1.0f / dm : 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) ol[dt] = S.al[dt] * inv_den;
+      for (int dt = 0; dt < 8; ++dt) ol[dt] = nm[dt] * inv_den;
     } else {
       const _Float16* ht = reinterpret_cast<const _Float16*>(a.h16t) + bh * kD * kD;
       const float hs = a.hscale[bh];
@@ -454,7 +540,7 @@ __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a
       dz += __shfl_xor(dz, 16);
       dz += __shfl_xor(dz, 32);
       // whole head minus the kept share; a denominator lost in rounding counts as 0
-      const float den = dz - r;
+      const float den = dz - dm;
       const float inv_den = den > 1e-6f * dz ? 1.0f / den : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -465,7 +551,7 @@ __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a
           const half8 ah = *reinterpret_cast<const half8*>(hrow + 32 * cc);
           num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fq[cc], num, 0, 0, 0);
         }
-        ol[dt] = (num * hs - S.al[dt]) * inv_den;
+        ol[dt] = (num * hs - nm[dt]) * inv_den;
       }
     }
   }
@@ -501,6 +587,8 @@ __device__ __forceinline__ TileSrc head_sources(const SparseArgs& a, size_t bh, 
   src.k8 = head_rsrc(a.k8 + bh * k8_head, k8_head);
   src.v16 = head_rsrc(a.v16 + bh * (size_t)a.Np * kD, f16_head);
   src.fk16 = head_rsrc(lin ? a.fk16 + bh * (size_t)a.Np * kD : a.v16, f16_head);
+  src.zb = head_rsrc(lin ? a.zb + bh * (size_t)a.Nb * kD : reinterpret_cast<const float*>(a.v16),
+                     (size_t)a.Nb * kD * 4);
   return src;
 }
 
@@ -528,24 +616,23 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   const int qrow = i * kBlk + 16 * wave + l16;  // this lane's query row
   const bool qvalid = qrow < a.N;
   v4i qf[2];
-  half8 fq[4];
   State S;
-  init_query<kLinAny>(a, bh, qrow, qvalid, g, qf, fq, S);
+  init_query(a, bh, qrow, g, qf, S);
   const float qscale = a.sq[bh * a.Nb + i] * (kInvSqrtD * kLog2e);
   const TileSrc src = head_sources(a, bh, kLinAny);
 
   if (kMode != kDirect) {
     const int ngroups = (a.Nb + kGroup - 1) / kGroup;
     const int2* col = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
-    run_sched<kLinAny>(S, smem, stage_bytes, col, a.k, a, src, qf, fq, lo, qscale, wave, g);
+    run_sched<kLinAny>(S, smem, stage_bytes, col, a.k, a, src, qf, lo, qscale, wave, g);
   } else {
     const int nu = a.Nb - a.k;
     const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
     const int32_t* usel = a.uidx + (bh * a.Nb + i) * (size_t)nu;
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, 1, a, src, bh, qf, fq, lo, qscale, wave, g);
-    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, 1, a, src, bh, qf, fq, lo, qscale, wave, g);
+    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, 1, a, src, bh, qf, lo, qscale, wave, g);
+    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, 1, a, src, bh, qf, lo, qscale, wave, g);
   }
-  finish_query<kMode>(S, a, bh, qrow, qvalid, g, l16, fq);
+  finish_query<kMode>(S, a, bh, qrow, qvalid, smem, lo, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -567,17 +654,6 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
 // and placed in the last step of every member that keeps it.
 // ---------------------------------------------------------------------------
 
-// Maximum over the 64 lanes of a wave (DPP within rows, permlane across rows).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, true));   // lane ^ 1
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, true));   // lane ^ 2
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, true));  // 8-lane mirror
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, true));  // 16-lane mirror
-  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  x = max((uint32_t)a[0], (uint32_t)a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return max((uint32_t)b[0], (uint32_t)b[1]);
-}
 
 // LDS bytes of the schedule kernel: one owner byte per key block (rounded to
 // words) and the union of the group's kept blocks as (block << 8 | owners).
@@ -925,6 +1001,7 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.sched = ws.sched;
   a.fk16 = ws.fk16;
   a.v16 = ws.v16;
+  a.zb = ws.zb;
   a.h16t = ws.h16t;
   a.hscale = ws.hscale;
   a.z = ws.z;
