@@ -29,7 +29,7 @@ struct Shape {
 struct Workspace {
   double* ksum = nullptr;     // [BH, Nb, D]   fp64 K block sums (for the K mean)
   float* qbar = nullptr;      // [BH, Nb, D]   fp32 Q block means
-  float* kbar = nullptr;      // [BH, Nb, D]   fp32 K block means
+  float* kbar = nullptr;      // [BH, D, Nb]   fp32 K block means, channel-major
   float* mu = nullptr;        // [BH, D]       K channel mean
   int8_t* q8 = nullptr;       // [BH, Np, D]   INT8 codes
   int8_t* k8 = nullptr;       // [BH, Np, D]

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
     if (tensor == 0) {
       qbar[o + e] = mean;
     } else {
-      kbar[o + e] = mean;
+      // channel-major, so the scoring pass reads consecutive key blocks
+      kbar[((size_t)bh * kD + cg * 8 + e) * Nb + blk] = mean;
       ksum[o + e] = acc[e];
     }
   }
@@ -176,9 +177,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 
 // ---------------------------------------------------------------------------
 // Block scores and top-k.  A workgroup owns R query blocks of one (b,h).
-// Phase 1: lane j computes s_ij = sum_c qbar_ic kbar_jc for its key block j
-// and all R rows (fp64 fma, channels ascending; the fp32 x fp32 product is
-// exact in fp64 so each step rounds once) and keeps the scores in LDS.
+// Phase 1: lane t computes s_ij = sum_c qbar_ic kbar_jc for the key blocks
+// j = t + 256u of a pass and all R rows (fp64 fma, channels ascending; the
+// fp32 x fp32 product is exact in fp64 so each step rounds once) and keeps the
+// scores in LDS.  kbar is channel-major, so a wave's loads of one channel are
+// contiguous; qbar goes through LDS as fp64 [channel][row] and is read a
+// chunk of channels at a time into registers.
 // Phase 2, one wave per row: the scores are spread over kBins buckets by the
 // monotone map floor((s - min) * kBins / (max - min)); one histogram and a
 // suffix scan find the bucket B holding the k-th largest score.  Scores in
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int Nb, int k,
     int32_t* __restrict__ idx, uint32_t* __restrict__ mask, int32_t* __restrict__ uidx) {
   extern __shared__ __align__(16) unsigned char smem[];
-  double* qs = reinterpret_cast<double*>(smem);                              // [R][128]
+  double* qs = reinterpret_cast<double*>(smem);                              // [128][R]
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + R * kD * 8);           // [4][kBins]
   double* cand_s = reinterpret_cast<double*>(smem + R * kD * 8 + 4 * kBins * 4);   // [4][64]
   int* cand_j = reinterpret_cast<int*>(smem + R * kD * 8 + 4 * kBins * 4 + 4 * 64 * 8);  // [4][64]
@@ -203,31 +207,59 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   const int wave = t >> 6;
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
-  const float* kb = kbar + (size_t)bh * Nb * kD;
+  const float* kb = kbar + (size_t)bh * kD * Nb;  // [128][Nb]
 
   for (int e = t; e < R * kD; e += 256) {
-    const int r = e / kD;
+    const int r = e % R, c = e / R;
     const int i = min(i0 + r, Nb - 1);
-    qs[e] = (double)qbar[((size_t)bh * Nb + i) * kD + (e % kD)];
+    qs[e] = (double)qbar[((size_t)bh * Nb + i) * kD + c];
   }
   __syncthreads();
 
-  for (int j = t; j < Nb; j += 256) {
-    double acc[R];
+  constexpr int kSlots = 5;       // key blocks per lane and pass
+  constexpr int kCh = R >= 8 ? 4 : 8;  // channels per register chunk of qbar
+  // this head's kbar slice (below 2^31 bytes); reads past it return 0
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(kb), 0, (int)((size_t)kD * Nb * 4), 0x00020000);
+  for (int base = 0; base < Nb; base += 256 * kSlots) {
+    double acc[kSlots][R];
+    int voff[kSlots];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * kD);
-    for (int c4 = 0; c4 < kD / 4; ++c4) {
-      const float4 kv = kr[c4];
-      const double kd[4] = {(double)kv.x, (double)kv.y, (double)kv.z, (double)kv.w};
+    for (int u = 0; u < kSlots; ++u) {
+      voff[u] = 4 * min(base + 256 * u + t, Nb - 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int r = 0; r < R; ++r) acc[u][r] = 0.0;
+    }
+    for (int c0 = 0; c0 < kD; c0 += kCh) {
+      // all loads of the chunk first, so they are in flight together
+      float kv[kSlots][kCh];
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * kD + 4 * c4 + e], kd[e], acc[r]);
-      }
+      for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+        for (int e = 0; e < kCh; ++e)
+          kv[u][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kr, voff[u], 4 * (c0 + e) * Nb, 0));
+      double qd[kCh][R];
+#pragma unroll
+      for (int e = 0; e < kCh; ++e)
+#pragma unroll
+        for (int r = 0; r < R; ++r) qd[e][r] = qs[(c0 + e) * R + r];
+#pragma unroll
+      for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+        for (int e = 0; e < kCh; ++e) {
+          const double kd = (double)kv[u][e];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[u][r] = fma(qd[e][r], kd, acc[u][r]);
+        }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) sc[(size_t)r * Nb + j] = acc[r];
+    for (int u = 0; u < kSlots; ++u) {
+      const int j = base + 256 * u + t;
+      if (j < Nb) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[(size_t)r * Nb + j] = acc[u][r];
+      }
+    }
   }
   __syncthreads();
 
