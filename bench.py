@@ -220,9 +220,9 @@ def main():
     kk = sla.topk_count(nb, keep)
     linear = phi != "none" and kk < nb
     direct = linear and (nb - kk) <= kk
-    skipped = set()
+    skipped = {2}  # the INT8 coding runs inside the statistics and staging passes
     if kk == 0:
-        skipped |= {0, 1, 2, 3}
+        skipped |= {0, 1, 3}
     if not linear or direct:
         skipped.add(5)
     stage_ms = {}
@@ -245,10 +245,11 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / (PEAK_F16_FLOPS / 1e12), 4),
                 "traffic": measured_traffic(wl.name, keep, phi), "kernel": "sparse_fwd_kernel",
                 "note": "fp16-equivalent: INT8 ops weighted 0.5 (INT8 peak is 2x the fp16 peak)"}
+    codes = B * H * nb * 64 * d  # INT8 codes of one of Q, K
     bytes_io = {
-        "stats": 2 * B * H * N * d * 2,
-        "quantize": 2 * B * H * N * d * 2 + 2 * B * H * nb * 64 * d,
-        "linear_prep": 2 * B * H * N * d * 2 + (2 if linear else 1) * B * H * nb * 64 * d * 2,
+        "stats": 2 * B * H * N * d * 2 + codes,
+        "linear_prep": 2 * B * H * N * d * 2 + (2 if linear else 1) * B * H * nb * 64 * d * 2
+        + (codes if kk > 0 else 0),
     }
     bw = {n: round(bytes_io[n] / (stage_ms[n] * 1e-3) / 1e9, 1) for n in bytes_io if n in stage_ms}
     hbm_frac = {n: round(g * 1e9 / PEAK_HBM, 3) for n, g in bw.items()}

@@ -145,14 +145,18 @@ sla_status sla_attention_fwd(const void *q, const void *k, const void *v,
                              void *stream);
 
 /* Stages of sla_attention_fwd (see sla_attention_fwd_timed); they are launched
- * in the order STATS, KMEAN, QUANTIZE, LINEAR_PREP, LINEAR_FINAL, TOPK, SPARSE. */
+ * in the order STATS, KMEAN, LINEAR_PREP, LINEAR_FINAL, TOPK, SPARSE.  The
+ * INT8 coding is folded into STATS (Q) and LINEAR_PREP (K), so QUANTIZE, the
+ * coding as a pass of its own (sla_quantize_qk), records nothing here. */
 typedef enum sla_stage {
-  SLA_STAGE_STATS = 0,        /* fp64 block sums, pooled block means of Q and K   */
+  SLA_STAGE_STATS = 0,        /* fp64 block sums, pooled block means of Q and K,  */
+                              /* INT8 codes and scales of Q                       */
   SLA_STAGE_KMEAN = 1,        /* K channel mean                                   */
-  SLA_STAGE_QUANTIZE = 2,     /* INT8 codes and scales of Q and smoothed K        */
+  SLA_STAGE_QUANTIZE = 2,     /* INT8 coding on its own: not run by this call     */
   SLA_STAGE_TOPK = 3,         /* block scores, top-k key-block selection and the  */
                               /* aligned key-block walks of query-block groups    */
-  SLA_STAGE_LINEAR_PREP = 4,  /* fp16 staging of V and phi(K), partial phi(K)^T V */
+  SLA_STAGE_LINEAR_PREP = 4,  /* fp16 staging of V and phi(K), partial phi(K)^T V,*/
+                              /* INT8 codes and scales of smoothed K              */
   SLA_STAGE_LINEAR_FINAL = 5, /* whole-head phi(K)^T V and sum phi(K)             */
   SLA_STAGE_SPARSE = 6,       /* block-sparse attention + linear branch + combine */
   SLA_N_STAGES = 7

@@ -136,9 +136,10 @@ sla_status sla_quantize_qk(const void* q, const void* k, int B, int H, int N, in
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
-  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, hs);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, q_i8, q_scale, hs);
   if (e == hipSuccess) e = sla::launch_key_mean(w.ksum, s, k_mean, hs);
-  if (e == hipSuccess) e = sla::launch_quantize(qb, kb, k_mean, s, q_i8, k_i8, q_scale, k_scale, hs);
+  if (e == hipSuccess)
+    e = sla::launch_quantize(qb, kb, k_mean, s, q_i8, k_i8, q_scale, k_scale, true, hs);
   return device_status(e);
 }
 
@@ -161,7 +162,7 @@ sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, i
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
-  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, hs);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, nullptr, nullptr, hs);
   if (e == hipSuccess)
     e = sla::launch_block_topk(w.qbar, w.kbar, s, kblock_idx, kblock_mask, nullptr, hs);
   return device_status(e);
@@ -208,13 +209,16 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
       e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + 1]), hs);
   };
   if (kk > 0) {
-    stage(SLA_STAGE_STATS, [&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, hs); });
+    stage(SLA_STAGE_STATS, [&] {
+      return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs);
+    });
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
-    stage(SLA_STAGE_QUANTIZE,
-          [&] { return sla::launch_quantize(qb, kb, w.mu, s, w.q8, w.k8, w.sq, w.sk, hs); });
   }
+  // Q is coded by the statistics pass and K by the staging pass (one read of
+  // each), so the QUANTIZE stage does not run here
   stage(SLA_STAGE_LINEAR_PREP, [&] {
-    return sla::launch_linear_prep(kb, vb, s, phi_eff, !direct, w.fk16, w.v16, w.zb, w.hpart, w.zpart, hs);
+    return sla::launch_linear_prep(kb, vb, s, phi_eff, !direct, w.fk16, w.v16, w.zb, w.hpart,
+                                   w.zpart, w.mu, kk > 0 ? w.k8 : nullptr, w.sk, hs);
   });
   if (phi_eff != SLA_PHI_NONE && !direct)
     stage(SLA_STAGE_LINEAR_FINAL,

@@ -50,18 +50,20 @@ struct Workspace {
 };
 
 // Stage launchers (all enqueue on `s`, return the launch status).
+// Block means and K block sums; also Q's INT8 codes and scales when q8 is set.
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
-                              double* ksum, float* qbar, float* kbar, hipStream_t s);
+                              double* ksum, float* qbar, float* kbar, int8_t* q8, float* sq,
+                              hipStream_t s);
 hipError_t launch_key_mean(const double* ksum, const Shape& sh, float* mu, hipStream_t s);
 hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu,
                            const Shape& sh, int8_t* q8, int8_t* k8, float* sq, float* sk,
-                           hipStream_t s);
+                           bool k_only, hipStream_t s);
 hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
                              int32_t* idx, uint32_t* mask, int32_t* uidx, hipStream_t s);
 size_t topk_lds_bytes(int Nb, int* rows_per_group);
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
-                              float* zpart, hipStream_t s);
+                              float* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s);
 hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
                                uint16_t* h16t, float* hscale, float* z, hipStream_t s);
 // Linear-branch form: with few unselected blocks (Nb - k <= k) the branch is

@@ -40,48 +40,115 @@ __device__ __forceinline__ float phi_apply(float x, int phi) {
   return fmaxf(x, 0.0f);
 }
 
+// INT8 coding of a block with a = max|x| over its valid rows: scale = a/127
+// and inv = 127/a (IEEE fp32 divisions), or 0 and 0 for an all-zero block.
+// Returns whether the block has codes (a > 0).
+__device__ __forceinline__ bool code_scale(float a, float& scale, float& inv) {
+  scale = 0.0f;
+  inv = 0.0f;
+  if (a > 0.0f) {
+    scale = a / 127.0f;
+    inv = 127.0f / a;
+  }
+  return a > 0.0f;
+}
+
+// Codes of 8 consecutive channels of one row: clamp(rint(x * inv), +-127),
+// little-endian bytes; 0 unless `live` (a valid row of a block with a > 0).
+// The one coding routine of the statistics pass (Q), the quantiser and the
+// staging pass (K).
+__device__ __forceinline__ uint2 code_row8(const float* x, float inv, bool live) {
+  uint32_t w[2] = {0u, 0u};
+  if (live) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float y = rintf(x[e] * inv);
+      y = fminf(fmaxf(y, -127.0f), 127.0f);
+      const uint32_t b = (uint32_t)(int32_t)y & 0xffu;
+      w[e >> 2] |= b << (8 * (e & 3));
+    }
+  }
+  return make_uint2(w[0], w[1]);
+}
+
 // ---------------------------------------------------------------------------
-// Block statistics.  One workgroup covers 8 consecutive blocks of one (b,h);
-// 16 lanes per (block, tensor) each own 8 channels and add the valid rows in
-// ascending order in fp64.  Outputs: Q/K block means rounded to fp32 and the
-// fp64 K block sums (for the K channel mean).
+// Block statistics, and the Q quantiser.  One workgroup per (block, b*h):
+// lane t loads rows t/16 + 16m (m < 4), channels 8*(t%16).. of Q and K (one
+// read of each), then
+//   * Q's INT8 codes and scale (the quantiser's arithmetic, code_row8), when
+//     q8 is set;
+//   * through LDS, lane c < 128 adds Q channel c and lane 128 + c K channel c
+//     over the valid rows in ascending order in fp64.
+// Outputs: Q/K block means rounded to fp32 (K channel-major, for the block
+// scores) and the fp64 K block sums (for the K channel mean).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void block_stats_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int N, int Nb,
-    double* __restrict__ ksum, float* __restrict__ qbar, float* __restrict__ kbar) {
+    double* __restrict__ ksum, float* __restrict__ qbar, float* __restrict__ kbar,
+    int8_t* __restrict__ q8, float* __restrict__ sq) {
+  __shared__ __align__(16) uint16_t tile[2][kBlk][kD];  // bf16 Q, K rows of the block
+  __shared__ float red[4];
   const int t = threadIdx.x;
-  const int blk = blockIdx.x * 8 + (t >> 5);
-  const int tensor = (t >> 4) & 1;
-  const int cg = t & 15;
+  const int blk = blockIdx.x;
   const int bh = blockIdx.y;
-  if (blk >= Nb) return;
+  const int cc = t & 15;
+  const int rr = t >> 4;
   const int rows = min(kBlk, N - blk * kBlk);
-  const uint16_t* src = (tensor == 0 ? q : k) +
-                        ((size_t)bh * N + (size_t)blk * kBlk) * kD + cg * 8;
-  double acc[8];
+  const size_t row0 = (size_t)bh * N + (size_t)blk * kBlk;
+  uint4 uq[4], uk[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-#pragma unroll 4
-  for (int r = 0; r < rows; ++r) {
-    const uint4 u = *reinterpret_cast<const uint4*>(src + (size_t)r * kD);
-    float x[8];
-    unpack_bf16x8(u, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += (double)x[e];
-  }
-  const size_t o = ((size_t)bh * Nb + blk) * kD + cg * 8;
-  const double n = (double)rows;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float mean = (float)(acc[e] / n);
-    if (tensor == 0) {
-      qbar[o + e] = mean;
-    } else {
-      // channel-major, so the scoring pass reads consecutive key blocks
-      kbar[((size_t)bh * kD + cg * 8 + e) * Nb + blk] = mean;
-      ksum[o + e] = acc[e];
+  for (int m = 0; m < 4; ++m) {
+    const int r = rr + 16 * m;
+    uq[m] = uk[m] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows) {
+      uq[m] = *reinterpret_cast<const uint4*>(q + (row0 + r) * kD + cc * 8);
+      uk[m] = *reinterpret_cast<const uint4*>(k + (row0 + r) * kD + cc * 8);
     }
   }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = rr + 16 * m;
+    *reinterpret_cast<uint4*>(&tile[0][r][cc * 8]) = uq[m];
+    *reinterpret_cast<uint4*>(&tile[1][r][cc * 8]) = uk[m];
+  }
+  float amax = 0.0f;
+  float x[4][8];
+  if (q8) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      unpack_bf16x8(uq[m], x[m]);  // pad rows are 0
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[m][e]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((t & 63) == 0) red[t >> 6] = amax;
+  }
+  __syncthreads();
+  {
+    // sums in ascending row order
+    const int tensor = t >> 7, c = t & 127;
+    double acc = 0.0;
+    for (int r = 0; r < rows; ++r) acc += (double)bf16_to_f32(tile[tensor][r][c]);
+    const float mean = (float)(acc / (double)rows);
+    if (tensor == 0) {
+      qbar[((size_t)bh * Nb + blk) * kD + c] = mean;
+    } else {
+      // channel-major, so the scoring pass reads consecutive key blocks
+      kbar[((size_t)bh * kD + c) * Nb + blk] = mean;
+      ksum[((size_t)bh * Nb + blk) * kD + c] = acc;
+    }
+  }
+  if (!q8) return;
+  float scale, inv;
+  const bool any = code_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), scale, inv);
+  int8_t* dst = q8 + ((size_t)bh * Nb * kBlk + (size_t)blk * kBlk) * kD + cc * 8;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = rr + 16 * m;
+    *reinterpret_cast<uint2*>(dst + (size_t)r * kD) = code_row8(x[m], inv, any && r < rows);
+  }
+  if (t == 0) sq[(size_t)bh * Nb + blk] = scale;
 }
 
 // K channel mean: blocks ascending, one fp64 division by N, rounded to fp32.
@@ -106,7 +173,8 @@ __global__ __launch_bounds__(128) void key_mean_kernel(const double* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// INT8 quantiser.  One workgroup per (block, b*h, tensor).  Lane t owns
+// INT8 quantiser.  One workgroup per (block, b*h, tensor) (tensor 0 = Q,
+// 1 = K - mu; `first` skips Q when the statistics pass has coded it).  Lane t owns
 // channels 8*(t%16).. of rows t/16 + 16m.  a = max|x| over valid rows;
 // scale = a/127, inv = 127/a (IEEE fp32 division); code = rint(x*inv)
 // clamped to [-127,127]; pad rows are written as 0.
@@ -114,12 +182,12 @@ __global__ __launch_bounds__(128) void key_mean_kernel(const double* __restrict_
 __global__ __launch_bounds__(256) void quantize_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float* __restrict__ mu, int N, int Nb, int8_t* __restrict__ q8,
-    int8_t* __restrict__ k8, float* __restrict__ sq, float* __restrict__ sk) {
+    int8_t* __restrict__ k8, float* __restrict__ sq, float* __restrict__ sk, int first) {
   __shared__ float red[4];
   const int t = threadIdx.x;
   const int blk = blockIdx.x;
   const int bh = blockIdx.y;
-  const bool isk = blockIdx.z == 1;
+  const bool isk = blockIdx.z + first == 1;
   const int cc = t & 15;
   const int rr = t >> 4;
   const int rows = min(kBlk, N - blk * kBlk);
@@ -150,27 +218,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
-  const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float scale = 0.0f, inv = 0.0f;
-  if (a > 0.0f) {
-    scale = a / 127.0f;
-    inv = 127.0f / a;
-  }
+  float scale, inv;
+  const bool any = code_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), scale, inv);
   int8_t* dst = (isk ? k8 : q8) + ((size_t)bh * Nb * kBlk + (size_t)blk * kBlk) * kD + cc * 8;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int r = rr + 16 * m;
-    uint32_t w[2] = {0u, 0u};
-    if (r < rows && a > 0.0f) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y = rintf(x[m][e] * inv);
-        y = fminf(fmaxf(y, -127.0f), 127.0f);
-        const uint32_t b = (uint32_t)(int32_t)y & 0xffu;
-        w[e >> 2] |= b << (8 * (e & 3));
-      }
-    }
-    *reinterpret_cast<uint2*>(dst + (size_t)r * kD) = make_uint2(w[0], w[1]);
+    *reinterpret_cast<uint2*>(dst + (size_t)r * kD) = code_row8(x[m], inv, any && r < rows);
   }
   if (t == 0) (isk ? sk : sq)[(size_t)bh * Nb + blk] = scale;
 }
@@ -423,7 +477,9 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 //     operands (pad keys 0),
 //   * writes the block's sum of phi(K)/16 over its keys (fp32, per channel),
 //   * accumulates H = sum phi(K)^T V and z = sum phi(K) for the chunk
-//     (fp16 operands, fp32 accumulation, blocks in ascending order).
+//     (fp16 operands, fp32 accumulation, blocks in ascending order),
+//   * when k8 is set, writes the INT8 codes and scale of the smoothed block
+//     K - mu (the quantiser's arithmetic, code_row8).
 // Permuted key order inside each 32-key half: position 8g+s holds key
 // 4g+s (s<4) or 16+4g+(s-4) (s>=4), matching the transposed score tiles
 // that feed the P.V product.
@@ -448,10 +504,12 @@ template <int kMode>
 __global__ __launch_bounds__(256) void linear_prep_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int Nb, int phi,
     uint16_t* __restrict__ fk16, uint16_t* __restrict__ v16, float* __restrict__ zb,
-    float* __restrict__ hpart, float* __restrict__ zpart) {
+    float* __restrict__ hpart, float* __restrict__ zpart, const float* __restrict__ mu,
+    int8_t* __restrict__ k8, float* __restrict__ sk) {
   // LDS: transposed tiles [128 channels][64 positions] fp16 (see tpos)
   __shared__ __align__(16) _Float16 fkT[kD * kTRow];
   __shared__ __align__(16) _Float16 vT[kD * kTRow];
+  __shared__ float red[4];
   constexpr bool kLinear = kMode >= 1;
   constexpr bool kReduce = kMode >= 2;
   const int t = threadIdx.x;
@@ -473,28 +531,49 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
 #pragma unroll
     for (int y = 0; y < 8; ++y) acc[x][y] = float4v{0.f, 0.f, 0.f, 0.f};
   float zacc = 0.0f;
+  const bool quant = k8 != nullptr;  // workgroup-uniform
+  const bool needk = kLinear || quant;
+  float m8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m8[e] = quant ? mu[(size_t)bh * kD + cc * 8 + e] : 0.0f;
 
-  for (int j = j0; j < j1; ++j) {
+  // raw bf16 rows 4a+m, channels 8cc.. of block j (pad rows 0)
+  auto load_raw = [&](int j, uint4* rv, uint4* rk) {
     const int rows = min(kBlk, N - j * kBlk);
     const size_t row0 = (size_t)bh * N + (size_t)j * kBlk;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = 4 * a + m;
+      rv[m] = rk[m] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rows) {
+        rv[m] = *reinterpret_cast<const uint4*>(v + (row0 + r) * kD + cc * 8);
+        if (needk) rk[m] = *reinterpret_cast<const uint4*>(k + (row0 + r) * kD + cc * 8);
+      }
+    }
+  };
+  for (int j = j0; j < j1; ++j) {
+    const int rows = min(kBlk, N - j * kBlk);
+    uint4 rv[4], rk[4];
+    load_raw(j, rv, rk);
     _Float16 fv[4][8], vv[4][8];
+    float amax = 0.0f;  // max |K - mu| over this lane's valid rows
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int r = 4 * a + m;
       float xv[8], xk[8];
-      if (r < rows) {
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(v + (row0 + r) * kD + cc * 8), xv);
-        if (kLinear)
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(k + (row0 + r) * kD + cc * 8), xk);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = xk[e] = 0.0f;
-      }
+      unpack_bf16x8(rv[m], xv);
+      unpack_bf16x8(rk[m], xk);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         vv[m][e] = (_Float16)xv[e];
         if (kLinear) fv[m][e] = (r < rows) ? (_Float16)(phi_apply(xk[e], phi) * kPhiScale) : (_Float16)0.0f;
+        if (quant && r < rows) amax = fmaxf(amax, fabsf(xk[e] - m8[e]));
       }
+    }
+    if (quant) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      if (lane == 0) red[wave] = amax;
     }
     // transposed LDS writes: 4 consecutive keys -> 4 consecutive positions
     const int p0 = perm_pos(4 * a);
@@ -509,6 +588,21 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
       }
     }
     __syncthreads();
+    if (quant) {
+      float scale, inv;
+      const bool any = code_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), scale, inv);
+      int8_t* dst = k8 + ((size_t)bh * Nb + j) * kBlk * kD + cc * 8;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = 4 * a + m;
+        float xq[8];  // K - mu, recomputed from the raw row still in registers
+        unpack_bf16x8(rk[m], xq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xq[e] = xq[e] - m8[e];
+        *reinterpret_cast<uint2*>(dst + (size_t)r * kD) = code_row8(xq, inv, any && r < rows);
+      }
+      if (t == 0) sk[(size_t)bh * Nb + j] = scale;
+    }
     // V (and phi(K)) staging copy-out: 16 KB contiguous per block, 16-byte
     // chunk q = 8c + P
     {
@@ -634,9 +728,10 @@ __global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict
 }  // namespace
 
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
-                              double* ksum, float* qbar, float* kbar, hipStream_t s) {
-  dim3 grid((sh.Nb + 7) / 8, sh.BH);
-  block_stats_kernel<<<grid, 256, 0, s>>>(q, k, sh.N, sh.Nb, ksum, qbar, kbar);
+                              double* ksum, float* qbar, float* kbar, int8_t* q8, float* sq,
+                              hipStream_t s) {
+  dim3 grid(sh.Nb, sh.BH);
+  block_stats_kernel<<<grid, 256, 0, s>>>(q, k, sh.N, sh.Nb, ksum, qbar, kbar, q8, sq);
   return hipGetLastError();
 }
 
@@ -647,9 +742,9 @@ hipError_t launch_key_mean(const double* ksum, const Shape& sh, float* mu, hipSt
 
 hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu,
                            const Shape& sh, int8_t* q8, int8_t* k8, float* sq, float* sk,
-                           hipStream_t s) {
-  dim3 grid(sh.Nb, sh.BH, 2);
-  quantize_kernel<<<grid, 256, 0, s>>>(q, k, mu, sh.N, sh.Nb, q8, k8, sq, sk);
+                           bool k_only, hipStream_t s) {
+  dim3 grid(sh.Nb, sh.BH, k_only ? 1 : 2);
+  quantize_kernel<<<grid, 256, 0, s>>>(q, k, mu, sh.N, sh.Nb, q8, k8, sq, sk, k_only ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -691,14 +786,14 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& 
 
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
-                              float* zpart, hipStream_t s) {
+                              float* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s) {
   dim3 grid(kLinChunks, sh.BH);
   if (phi == kPhiNone)
-    linear_prep_kernel<0><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart);
+    linear_prep_kernel<0><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart, mu, k8, sk);
   else if (!reduce)
-    linear_prep_kernel<1><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart);
+    linear_prep_kernel<1><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart, mu, k8, sk);
   else
-    linear_prep_kernel<2><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart);
+    linear_prep_kernel<2><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart, mu, k8, sk);
   return hipGetLastError();
 }
 
