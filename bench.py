@@ -28,7 +28,7 @@ PEAK_I8_OPS = 5.0e15        # MI355X dense INT8 MFMA
 PEAK_F16_FLOPS = 2.5e15     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM = 8.0e12           # MI355X HBM3E bytes/s
 PEAK_F64_FLOPS = 78.6e12    # MI355X fp64 vector
-STAGES = ["stats", "kmean", "quantize", "topk", "linear_prep", "linear_final", "sparse"]
+STAGES = ["stats", "kmean", "quantize", "topk", "linear_prep", "linear_final", "sparse", "schedule"]
 SPARSE_SRC = os.path.join(ROOT, "sparse_linear_attention_sagesla_amd", "csrc", "sla_sparse.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sparse_fwd_kernel_wan14b720_counters.md")
 
@@ -222,7 +222,9 @@ def main():
     direct = linear and (nb - kk) <= kk
     skipped = {2}  # the INT8 coding runs inside the statistics and staging passes
     if kk == 0:
-        skipped |= {0, 1, 3}
+        skipped |= {0, 1, 3, 7}
+    if direct:
+        skipped.add(7)
     if not linear or direct:
         skipped.add(5)
     stage_ms = {}

@@ -137,38 +137,50 @@ sla_status sla_block_select(const void *q, const void *k, int B, int H, int N,
  *   out         [B,H,N,128], bf16 or fp32 per out_dtype                 (out)
  *   out_linear  fp32 [B,H,N,128] linear branch alone; may be NULL       (out)
  * Workspace: SLA_OP_ATTENTION (holds codes, selection, fp16 staging and the
- * linear state, about 3 bytes/element of Q). */
+ * linear state, about 3 bytes/element of Q).
+ * Streams: work is enqueued on `stream`, except the block scores (TOPK), which
+ * run on a side stream the library creates on first use for the current
+ * device (non-blocking, default priority, kept until exit), forked after the
+ * statistics pass and joined before the walk schedule by event edges.  When
+ * `stream` has completed, so has the whole call; the call stays capturable.
+ * Calls on several streams of one device share the side stream. */
 sla_status sla_attention_fwd(const void *q, const void *k, const void *v,
                              int B, int H, int N, int d, int block, double keep,
                              int phi, void *out, int out_dtype,
                              float *out_linear, void *ws, size_t ws_bytes,
                              void *stream);
 
-/* Stages of sla_attention_fwd (see sla_attention_fwd_timed); they are launched
- * in the order STATS, KMEAN, LINEAR_PREP, LINEAR_FINAL, TOPK, SPARSE.  The
- * INT8 coding is folded into STATS (Q) and LINEAR_PREP (K), so QUANTIZE, the
- * coding as a pass of its own (sla_quantize_qk), records nothing here. */
+/* Stages of sla_attention_fwd (see sla_attention_fwd_timed).  On the caller's
+ * stream they run in the order STATS, KMEAN, LINEAR_PREP, LINEAR_FINAL,
+ * SCHEDULE, SPARSE; TOPK runs on a library-owned side stream of the device,
+ * after STATS and before SCHEDULE (event edges), overlapping the linear
+ * staging, so its events are recorded on that stream.  The INT8 coding is
+ * folded into STATS (Q) and LINEAR_PREP (K), so QUANTIZE, the coding as a pass
+ * of its own (sla_quantize_qk), records nothing here. */
 typedef enum sla_stage {
   SLA_STAGE_STATS = 0,        /* fp64 block sums, pooled block means of Q and K,  */
                               /* INT8 codes and scales of Q                       */
   SLA_STAGE_KMEAN = 1,        /* K channel mean                                   */
   SLA_STAGE_QUANTIZE = 2,     /* INT8 coding on its own: not run by this call     */
-  SLA_STAGE_TOPK = 3,         /* block scores, top-k key-block selection and the  */
-                              /* aligned key-block walks of query-block groups    */
+  SLA_STAGE_TOPK = 3,         /* block scores and top-k key-block selection       */
   SLA_STAGE_LINEAR_PREP = 4,  /* fp16 staging of V and phi(K), partial phi(K)^T V,*/
                               /* INT8 codes and scales of smoothed K              */
   SLA_STAGE_LINEAR_FINAL = 5, /* whole-head phi(K)^T V and sum phi(K)             */
   SLA_STAGE_SPARSE = 6,       /* block-sparse attention + linear branch + combine */
-  SLA_N_STAGES = 7
+  SLA_STAGE_SCHEDULE = 7,     /* aligned key-block walks of query-block groups    */
+  SLA_N_STAGES = 8
 } sla_stage;
 
 /* sla_attention_fwd that also records caller-created HIP events (hipEvent_t,
- * same device) on `stream`: stage_events[2*s] just before stage s is
- * enqueued and stage_events[2*s+1] just after.  stage_events may be NULL and
- * any entry may be NULL; stages that a call skips (selection when keep == 0,
- * linear stages when phi == NONE) record nothing.  Same arguments, ownership
- * and errors as sla_attention_fwd; a failed hipEventRecord gives
- * SLA_ERR_DEVICE. */
+ * same device) around its stages: stage_events[2*s] just before stage s is
+ * enqueued and stage_events[2*s+1] just after, on the stream the stage runs
+ * on (`stream`, or the side stream for TOPK).  stage_events is NULL or holds
+ * 2 * SLA_N_STAGES entries (SLA_N_STAGES grew from 7 to 8 in version 1.1.0),
+ * any of which may be NULL; stages that a call skips (selection and schedule
+ * when keep == 0, the schedule when the linear branch takes the direct form,
+ * linear stages when phi == NONE, QUANTIZE always) record nothing.  Same
+ * arguments, ownership and errors as sla_attention_fwd; a failed
+ * hipEventRecord gives SLA_ERR_DEVICE. */
 sla_status sla_attention_fwd_timed(const void *q, const void *k, const void *v,
                                    int B, int H, int N, int d, int block,
                                    double keep, int phi, void *out,

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sla.h"
 #include "sla_internal.h"
@@ -87,6 +88,35 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w)
 }
 
 sla_status device_status(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_DEVICE; }
+
+// A side stream per device (non-blocking, default priority) on which the block
+// scores run while the caller's stream stages the linear branch: the fork and
+// the join are event edges, so the call stays asynchronous and capturable.
+// The fork/join sequence of a call is enqueued under the lock, so concurrent
+// calls never interleave their uses of the two events.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -199,19 +229,32 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
   const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
   const bool direct = phi_eff != SLA_PHI_NONE && sla::linear_direct(s);
   hipError_t e = hipSuccess;
-  // runs one stage between its two optional events
-  auto stage = [&](int id, auto&& launch) {
+  // runs one stage between its two optional events, on stream `on`
+  auto stage_on = [&](hipStream_t on, int id, auto&& launch) {
     if (e != hipSuccess) return;
     if (stage_events && stage_events[2 * id])
-      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id]), hs);
+      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id]), on);
     if (e == hipSuccess) e = launch();
     if (e == hipSuccess && stage_events && stage_events[2 * id + 1])
-      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + 1]), hs);
+      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + 1]), on);
   };
+  auto stage = [&](int id, auto&& launch) { stage_on(hs, id, launch); };
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
   if (kk > 0) {
     stage(SLA_STAGE_STATS, [&] {
       return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs);
     });
+    // fork: the block scores and top-k need only the block means
+    side_lock.lock();
+    if (e == hipSuccess) e = side_stream(&side);
+    if (e == hipSuccess) e = hipEventRecord(side->fork, hs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+    stage_on(side ? side->stream : hs, SLA_STAGE_TOPK, [&] {
+      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr,
+                                    side->stream);
+    });
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
   // Q is coded by the statistics pass and K by the staging pass (one read of
@@ -223,14 +266,13 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
   if (phi_eff != SLA_PHI_NONE && !direct)
     stage(SLA_STAGE_LINEAR_FINAL,
           [&] { return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs); });
-  // selection last, so the kept lists and walk schedule are still in the
-  // memory-side cache when the sparse kernel reads them
-  if (kk > 0)
-    stage(SLA_STAGE_TOPK, [&] {
-      hipError_t r = sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr, hs);
-      if (r == hipSuccess && !direct) r = sla::launch_group_schedule(w.idx, w.sk, s, w.sched, hs);
-      return r;
-    });
+  if (kk > 0) {
+    // join, then the walk schedule (it needs the K block scales of the staging pass)
+    if (e == hipSuccess) e = hipStreamWaitEvent(hs, side->join, 0);
+    side_lock.unlock();
+    if (!direct)
+      stage(SLA_STAGE_SCHEDULE, [&] { return sla::launch_group_schedule(w.idx, w.sk, s, w.sched, hs); });
+  }
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
                                   out_linear, hs);
@@ -269,6 +311,6 @@ const char* sla_status_string(int status) {
   }
 }
 
-int sla_version(void) { return 100; }
+int sla_version(void) { return 10100; }
 
 }  // extern "C"
