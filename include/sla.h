@@ -138,10 +138,11 @@ sla_status sla_block_select(const void *q, const void *k, int B, int H, int N,
  *   out_linear  fp32 [B,H,N,128] linear branch alone; may be NULL       (out)
  * Workspace: SLA_OP_ATTENTION (holds codes, selection, fp16 staging and the
  * linear state, about 3 bytes/element of Q).
- * Streams: work is enqueued on `stream`, except the block scores (TOPK), which
- * run on a side stream the library creates on first use for the current
- * device (non-blocking, default priority, kept until exit), forked after the
- * statistics pass and joined before the walk schedule by event edges.  When
+ * Streams: work is enqueued on `stream`, except the block scores (TOPK) and
+ * the walk schedule (SCHEDULE), which run on a side stream the library
+ * creates on first use for the current device (non-blocking, default
+ * priority, kept until exit), forked after the statistics pass and joined
+ * before the attention kernel by event edges.  When
  * `stream` has completed, so has the whole call; the call stays capturable.
  * Calls on several streams of one device share the side stream. */
 sla_status sla_attention_fwd(const void *q, const void *k, const void *v,
@@ -152,9 +153,9 @@ sla_status sla_attention_fwd(const void *q, const void *k, const void *v,
 
 /* Stages of sla_attention_fwd (see sla_attention_fwd_timed).  On the caller's
  * stream they run in the order STATS, KMEAN, LINEAR_PREP, LINEAR_FINAL,
- * SCHEDULE, SPARSE; TOPK runs on a library-owned side stream of the device,
- * after STATS and before SCHEDULE (event edges), overlapping the linear
- * staging, so its events are recorded on that stream.  The INT8 coding is
+ * SPARSE; TOPK and then SCHEDULE run on a library-owned side stream of the
+ * device, after STATS and before SPARSE (event edges), overlapping the linear
+ * staging, so their events are recorded on that stream.  The INT8 coding is
  * folded into STATS (Q) and LINEAR_PREP (K), so QUANTIZE, the coding as a pass
  * of its own (sla_quantize_qk), records nothing here. */
 typedef enum sla_stage {
@@ -174,7 +175,7 @@ typedef enum sla_stage {
 /* sla_attention_fwd that also records caller-created HIP events (hipEvent_t,
  * same device) around its stages: stage_events[2*s] just before stage s is
  * enqueued and stage_events[2*s+1] just after, on the stream the stage runs
- * on (`stream`, or the side stream for TOPK).  stage_events is NULL or holds
+ * on (`stream`, or the side stream for TOPK and SCHEDULE).  stage_events is NULL or holds
  * 2 * SLA_N_STAGES entries (SLA_N_STAGES grew from 7 to 8 in version 1.1.0),
  * any of which may be NULL; stages that a call skips (selection and schedule
  * when keep == 0, the schedule when the linear branch takes the direct form,

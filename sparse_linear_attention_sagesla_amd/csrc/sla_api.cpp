@@ -68,8 +68,8 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w)
     ws.v16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
     const bool direct = phi != SLA_PHI_NONE && s.k < s.Nb && sla::linear_direct(s);
     if (!direct && s.k > 0)
-      ws.sched = reinterpret_cast<int2*>(
-          take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * s.k * sla::kGroup * sizeof(int2)));
+      ws.sched = reinterpret_cast<int32_t*>(
+          take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * s.k * sla::kGroup * sizeof(int32_t)));
     if (direct) {
       ws.uidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.Nb - s.k) * sizeof(int32_t)));
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
@@ -254,6 +254,11 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
       return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr,
                                     side->stream);
     });
+    // then the walk schedule, which needs only the kept lists
+    if (!direct)
+      stage_on(side ? side->stream : hs, SLA_STAGE_SCHEDULE, [&] {
+        return sla::launch_group_schedule(w.idx, s, w.sched, side->stream);
+      });
     if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
@@ -267,11 +272,9 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
     stage(SLA_STAGE_LINEAR_FINAL,
           [&] { return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs); });
   if (kk > 0) {
-    // join, then the walk schedule (it needs the K block scales of the staging pass)
+    // join before the attention kernel
     if (e == hipSuccess) e = hipStreamWaitEvent(hs, side->join, 0);
     side_lock.unlock();
-    if (!direct)
-      stage(SLA_STAGE_SCHEDULE, [&] { return sla::launch_group_schedule(w.idx, w.sk, s, w.sched, hs); });
   }
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,

@@ -37,8 +37,8 @@ struct Workspace {
   float* sk = nullptr;        // [BH, Nb]
   int32_t* idx = nullptr;     // [BH, Nb, k]   kept key blocks, ascending
   int32_t* uidx = nullptr;    // [BH, Nb, Nb-k] the other key blocks (direct linear mode)
-  int2* sched = nullptr;      // [BH, ceil(Nb/kGroup), k, kGroup] aligned walks of query-block
-                              // groups: (key block, bits of its INT8 scale)
+  int32_t* sched = nullptr;   // [BH, ceil(Nb/kGroup), k, kGroup] aligned walks of query-block
+                              // groups: key block, -1 for none
   uint16_t* fk16 = nullptr;   // [BH, Nb, D, 64] fp16 phi(K)/16 per block, [channel][permuted key]
   uint16_t* v16 = nullptr;    // [BH, Nb, D, 64] fp16 V per block, [channel][permuted key]
   float* zb = nullptr;        // [BH, Nb, D]   fp32 per-block sum of phi(K)/16 over the keys
@@ -71,7 +71,7 @@ hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh
 inline bool linear_direct(const Shape& sh) { return sh.Nb - sh.k <= sh.k; }
 // Aligned walks of the query-block groups from the kept lists (ws.sched);
 // needed by launch_sparse_fwd unless the linear branch takes the direct form.
-hipError_t launch_group_schedule(const int32_t* idx, const float* sk, const Shape& sh, int2* sched,
+hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
                                  hipStream_t s);
 hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
                              void* out, int out_f32, float* out_linear, hipStream_t s);

@@ -184,7 +184,7 @@ struct SparseArgs {
   const float* sk;
   const int32_t* idx;
   const int32_t* uidx;
-  const int2* sched;
+  const int32_t* sched;
   const uint16_t* fk16;
   const uint16_t* v16;
   const float* zb;
@@ -347,23 +347,23 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
   lds_barrier();  // the stages may be refilled by a following walk
 }
 
-// Walks this block's column of its group schedule (entry of step s at
-// col[s * kGroup]: key block, bits of its INT8 scale) through the two LDS
-// stages.  Entries are read with scalar loads when they are needed; reading
-// them earlier (scalar loads a step ahead, or 64-step chunks in registers)
-// measured slower.
+// Walks this block's column of its group schedule (key block of step s at
+// col[s * kGroup]) through the two LDS stages.  A step's entry, and then the
+// INT8 scale of its key block, are read with scalar loads when its tile is
+// issued, a tile ahead of their use; reading entries earlier (a step further
+// ahead, or 64-step chunks in registers) measured slower.
 template <bool kLin>
-__device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_bytes, const int2* col,
-                                          int n, const SparseArgs& a, const TileSrc& src,
-                                          const v4i qf[2], const LaneOffsets& lo,
-                                          float qscale, int wave, int g) {
+__device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_bytes,
+                                          const int32_t* col, int n, const SparseArgs& a,
+                                          const TileSrc& src, size_t bh, const v4i qf[2],
+                                          const LaneOffsets& lo, float qscale, int wave, int g) {
   if (n <= 0) return;
-  const int* ent = reinterpret_cast<const int*>(col);
-  auto block_of = [&](int p) { return min(max(ld_uniform(ent, (size_t)p * 2 * kGroup), 0), a.Nb - 1); };
-  auto scale_of = [&](int p) { return __int_as_float(ld_uniform(ent, (size_t)p * 2 * kGroup + 1)); };
+  auto block_of = [&](int p) { return min(max(ld_uniform(col, (size_t)p * kGroup), 0), a.Nb - 1); };
+  auto scale_of = [&](int j) { return ld_uniform(a.sk, bh * a.Nb + j); };
   int j = block_of(0);
   issue_tile<true, kLin>(smem, src, j, wave, lo);
   float zc = kLin ? load_zb(src, j, lo) : 0.0f;
+  float sc = scale_of(j);
   // the schedule puts a ragged key block only in the last step, which is
   // peeled off so the loop carries one compute variant
   const int nm = n - 1;
@@ -379,13 +379,15 @@ __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_by
         const int jn = block_of(pp + 1);
         issue_tile<true, kLin>(nxt, src, jn, wave, lo);
         const float zn = kLin ? load_zb(src, jn, lo) : 0.0f;
-        compute_tile<true, kLin, false>(S, cur, qf, lo, qscale * scale_of(pp), zc, kBlk, g);
+        const float sn = scale_of(jn);
+        compute_tile<true, kLin, false>(S, cur, qf, lo, qscale * sc, zc, kBlk, g);
         j = jn;
         zc = zn;
+        sc = sn;
       }
     }
   }
-  const float c = qscale * scale_of(nm);
+  const float c = qscale * sc;
   const int kvalid = a.N - j * kBlk;
   const lds_byte* cur = smem + (nm & 1) * stage_bytes;
   wait_loads();
@@ -623,8 +625,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
 
   if (kMode != kDirect) {
     const int ngroups = (a.Nb + kGroup - 1) / kGroup;
-    const int2* col = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
-    run_sched<kLinAny>(S, smem, stage_bytes, col, a.k, a, src, qf, lo, qscale, wave, g);
+    const int32_t* col = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
+    run_sched<kLinAny>(S, smem, stage_bytes, col, a.k, a, src, bh, qf, lo, qscale, wave, g);
   } else {
     const int nu = a.Nb - a.k;
     const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
@@ -663,15 +665,11 @@ inline size_t group_schedule_lds(int Nb, int k, int G) {
   return 4 * (words + 2 * cap);  // owner bytes, union, union sorted by owner set
 }
 
-// Schedule entries: (key block, bits of its INT8 scale), so the attention
-// kernel gets both with one vector load per 64 steps.  -1 marks no block.
+// Schedule entries: the key block, -1 for none.  The schedule depends only on
+// the kept lists, so it is built as soon as the selection is done.
 struct SchedOut {
-  int2* p;
-  const float* sk;  // this head's key-block scales
-  int Nb;
-  __device__ __forceinline__ void put(size_t i, int j) const {
-    p[i] = make_int2(j, j >= 0 ? __float_as_int(sk[min(j, Nb - 1)]) : 0);
-  }
+  int32_t* p;
+  __device__ __forceinline__ void put(size_t i, int j) const { p[i] = j; }
 };
 
 // The union of a group's kept blocks, entry = block << 8 | remaining owners,
@@ -869,9 +867,8 @@ __device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint3
 // (query block kG*grp + u) in step s.  Members past the last block get -1.
 template <int kG>
 __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx,
-                                                            const float* __restrict__ sk, int Nb,
-                                                            int k, int ragged,
-                                                            int2* __restrict__ sched) {
+                                                            int Nb, int k, int ragged,
+                                                            int32_t* __restrict__ sched) {
   extern __shared__ uint32_t gsm[];
   const int lane = threadIdx.x;
   const int grp = blockIdx.x;
@@ -883,7 +880,7 @@ __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __res
   const int words = (Nb + 3) / 4;
   uint32_t* own = gsm;          // owner byte of key block j: byte j&3 of word j>>2
   uint32_t* uni = gsm + words;  // union, ascending key block
-  const SchedOut out{sched + (bh * ngroups + grp) * (size_t)k * kG, sk + bh * Nb, Nb};
+  const SchedOut out{sched + (bh * ngroups + grp) * (size_t)k * kG};
   auto clampj = [&](int j) { return min(max(j, 0), Nb - 1); };
 
   for (int w = lane; w < words; w += 64) own[w] = 0u;
@@ -1019,7 +1016,7 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   return launch_mode<kSubtract>(a, sh, s);
 }
 
-hipError_t launch_group_schedule(const int32_t* idx, const float* sk, const Shape& sh, int2* sched,
+hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
                                  hipStream_t s) {
   if (sh.k <= 0) return hipSuccess;
   static std::once_flag once;
@@ -1029,7 +1026,7 @@ hipError_t launch_group_schedule(const int32_t* idx, const float* sk, const Shap
   });
   const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
   group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, group_schedule_lds(sh.Nb, sh.k, kGroup), s>>>(
-      idx, sk, sh.Nb, sh.k, sh.N != sh.Nb * kBlk ? 1 : 0, sched);
+      idx, sh.Nb, sh.k, sh.N != sh.Nb * kBlk ? 1 : 0, sched);
   return hipGetLastError();
 }
 
