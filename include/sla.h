@@ -23,9 +23,10 @@
  *  - Blocks: Nb = ceil(N / 64); the last block may be ragged; rows past N
  *    ("pad rows") never take part in any sum, maximum or softmax.
  *  - The caller allocates and owns every buffer, including the workspace
- *    (size from sla_workspace_size).  The library allocates nothing and keeps
- *    no mutable global state; calls on different streams are independent as
- *    long as their workspaces differ.
+ *    (size from sla_workspace_size).  The library allocates no device memory.
+ *    Its only global state is, per device, one side stream and two events
+ *    that sla_attention_fwd creates on first use and keeps until exit; calls
+ *    on different streams are independent as long as their workspaces differ.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
  *    the call returns without synchronising.  Arguments are validated before
  *    anything is enqueued: on any error status nothing has been enqueued.
