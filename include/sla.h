@@ -156,7 +156,7 @@ sla_status sla_attention_fwd(const void *q, const void *k, const void *v,
  * stream they run in the order STATS, KMEAN, LINEAR_PREP, LINEAR_FINAL,
  * SPARSE; TOPK and then SCHEDULE run on a library-owned side stream of the
  * device, after STATS and before SPARSE (event edges), overlapping the linear
- * staging, so their events are recorded on that stream.  The INT8 coding is
+ * staging.  The INT8 coding is
  * folded into STATS (Q) and LINEAR_PREP (K), so QUANTIZE, the coding as a pass
  * of its own (sla_quantize_qk), records nothing here. */
 typedef enum sla_stage {
@@ -175,8 +175,10 @@ typedef enum sla_stage {
 
 /* sla_attention_fwd that also records caller-created HIP events (hipEvent_t,
  * same device) around its stages: stage_events[2*s] just before stage s is
- * enqueued and stage_events[2*s+1] just after, on the stream the stage runs
- * on (`stream`, or the side stream for TOPK and SCHEDULE).  stage_events is NULL or holds
+ * enqueued and stage_events[2*s+1] just after.  With stage_events set, every
+ * stage runs on `stream` in the order STATS, TOPK, SCHEDULE, KMEAN,
+ * LINEAR_PREP, LINEAR_FINAL, SPARSE (no side stream), so that each is timed
+ * alone; with NULL it is exactly sla_attention_fwd.  stage_events is NULL or holds
  * 2 * SLA_N_STAGES entries (SLA_N_STAGES grew from 7 to 8 in version 1.1.0),
  * any of which may be NULL; stages that a call skips (selection and schedule
  * when keep == 0, the schedule when the linear branch takes the direct form,

@@ -241,25 +241,30 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
   auto stage = [&](int id, auto&& launch) { stage_on(hs, id, launch); };
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
+  // with stage events every stage runs on the caller's stream, one after
+  // another, so that each is timed alone
+  const bool fork = stage_events == nullptr;
   if (kk > 0) {
     stage(SLA_STAGE_STATS, [&] {
       return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs);
     });
     // fork: the block scores and top-k need only the block means
-    side_lock.lock();
-    if (e == hipSuccess) e = side_stream(&side);
-    if (e == hipSuccess) e = hipEventRecord(side->fork, hs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-    stage_on(side ? side->stream : hs, SLA_STAGE_TOPK, [&] {
-      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr,
-                                    side->stream);
+    hipStream_t sel = hs;
+    if (fork) {
+      side_lock.lock();
+      if (e == hipSuccess) e = side_stream(&side);
+      if (e == hipSuccess) e = hipEventRecord(side->fork, hs);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+      if (e == hipSuccess) sel = side->stream;
+    }
+    stage_on(sel, SLA_STAGE_TOPK, [&] {
+      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr, sel);
     });
     // then the walk schedule, which needs only the kept lists
     if (!direct)
-      stage_on(side ? side->stream : hs, SLA_STAGE_SCHEDULE, [&] {
-        return sla::launch_group_schedule(w.idx, s, w.sched, side->stream);
-      });
-    if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+      stage_on(sel, SLA_STAGE_SCHEDULE,
+               [&] { return sla::launch_group_schedule(w.idx, s, w.sched, sel); });
+    if (fork && e == hipSuccess) e = hipEventRecord(side->join, side->stream);
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
   // Q is coded by the statistics pass and K by the staging pass (one read of
@@ -271,7 +276,7 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
   if (phi_eff != SLA_PHI_NONE && !direct)
     stage(SLA_STAGE_LINEAR_FINAL,
           [&] { return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs); });
-  if (kk > 0) {
+  if (kk > 0 && fork) {
     // join before the attention kernel
     if (e == hipSuccess) e = hipStreamWaitEvent(hs, side->join, 0);
     side_lock.unlock();
