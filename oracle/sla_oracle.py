@@ -18,7 +18,11 @@ Sources (web pages on TurboDiffusion; citations name the page and section):
          90% of attention connections, keeps about 10%, and is built on top
          of SageAttention.
 * [DIG]  "TurboDiffusion" tool digest, section "使用方式与安装": SageSLA is the
-         SageAttention-based fast SLA forward pass.
+         SageAttention-based fast SLA forward pass; section "训练": SLA is
+         trained white-box, aligned to the full-attention model.
+* [NEWS] TurboDiffusion news summary (jiqiren.org.cn), section "方法论": full
+         attention is replaced by SLA and the pretrained model is fine-tuned
+         to the sparsity.
 
 What the oracle computes, per (batch, head), with blocks of ``block`` tokens
 (Nb = ceil(N / block), the last block may be ragged; only valid rows count):
@@ -39,6 +43,9 @@ What the oracle computes, per (batch, head), with blocks of ``block`` tokens
     z_U = sum_u phi(k_u); zero when U is empty or the denominator is zero
     [TUT §2.1 linear attention, normalised].
  7. Output = softmax branch + linear branch.
+ 8. Backward (``sla_backward_head``): dQ, dK, dV of that output for a given
+    output gradient, the selection held fixed, the INT8 rounding passed
+    straight through [NEWS 方法论: SLA is fine-tuned into the model].
 
 The pages print the SLA formula as phi(Q)(T_k[phi(K)]^T V), which has no
 softmax part; read together with the description of SLA as low-rank
@@ -257,28 +264,36 @@ def _rows_of(blocks, N: int, block: int) -> np.ndarray:
     return np.concatenate([np.arange(j * block, min(N, (j + 1) * block)) for j in blocks])
 
 
+def block_logits(i, sel, q8, k8, sq, sk, N, block, d, q64=None, k64=None):
+    """Logits of query block i against the valid keys of blocks ``sel``.
+
+    acc * sq_i * sk_j / sqrt(d), acc the exact integer dot product of the INT8
+    codes (an fp64 matrix product: every partial sum is an integer below 2^53,
+    so it is exact in any order); with ``q64``/``k64`` given, QK^T/sqrt(d) of
+    those fp64 matrices instead.  Returns (logits, acc or None).
+    """
+    qrows = np.arange(i * block, min(N, (i + 1) * block))
+    krows = _rows_of(sel, N, block)
+    if q64 is None:
+        acc = q8[qrows].astype(np.float64) @ k8[krows].astype(np.float64).T
+        kscale = np.repeat(sk[np.asarray(sel)].astype(np.float64),
+                           [min(N, (j + 1) * block) - j * block for j in sel])
+        return acc * float(sq[i]) * kscale[None, :] / math.sqrt(d), acc
+    return (q64[qrows] @ k64[krows].T) / math.sqrt(d), None
+
+
 def softmax_branch_block(i, sel, q8, k8, sq, sk, v64, N, block, d,
                          q64=None, k64=None):
     """Softmax attention of query block i over the valid keys of blocks ``sel``.
 
-    logits = acc * sq_i * sk_j / sqrt(d), acc the exact integer dot product of
-    the INT8 codes (computed as an fp64 matrix product: every partial sum is
-    an integer below 2^53, so it is exact in any order).  With ``q64``/``k64``
-    given, the logits are QK^T/sqrt(d) of those fp64 matrices instead
-    (quantisation bypassed).  Returns (out [rows, d], acc or None).
+    Logits from ``block_logits`` (INT8, or exact with ``q64``/``k64``).
+    Returns (out [rows, d], acc or None).
     """
     qrows = np.arange(i * block, min(N, (i + 1) * block))
     krows = _rows_of(sel, N, block)
     if krows.size == 0:
         return np.zeros((qrows.size, v64.shape[1])), None
-    if q64 is None:
-        acc = q8[qrows].astype(np.float64) @ k8[krows].astype(np.float64).T
-        kscale = np.repeat(sk[np.asarray(sel)].astype(np.float64),
-                           [min(N, (j + 1) * block) - j * block for j in sel])
-        logits = acc * float(sq[i]) * kscale[None, :] / math.sqrt(d)
-    else:
-        acc = None
-        logits = (q64[qrows] @ k64[krows].T) / math.sqrt(d)
+    logits, acc = block_logits(i, sel, q8, k8, sq, sk, N, block, d, q64, k64)
     m = logits.max(axis=1, keepdims=True)
     p = np.exp(logits - m)
     return (p @ v64[krows]) / p.sum(axis=1, keepdims=True), acc
@@ -359,3 +374,142 @@ def qk_accumulator(q8, k8, i: int, j: int, block: int) -> np.ndarray:
     a = q8[i * block:(i + 1) * block].astype(np.int64)
     b = k8[j * block:(j + 1) * block].astype(np.int64)
     return a @ b.T
+
+
+# --------------------------------------------------------------------------
+# 8: backward (trainable SLA)
+# --------------------------------------------------------------------------
+def phi_grad(x: np.ndarray, kind) -> np.ndarray:
+    """Derivative of the feature map: elu+1 -> 1 (x > 0) or exp(x); ReLU -> 1 (x > 0) or 0.
+
+    At x = 0 both take the left-hand value (exp(0) = 1 for elu+1, 0 for ReLU).
+    """
+    kind = phi_code(kind)
+    x = np.asarray(x, dtype=np.float64)
+    if kind == PHI_ELU1:
+        return np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))
+    if kind == PHI_RELU:
+        return np.where(x > 0.0, 1.0, 0.0)
+    raise ValueError("phi 'none' has no feature map")
+
+
+def softmax_branch_grad_block(i, sel, q64, k64, v64, do64, N, block, logits):
+    """Gradients of the softmax branch of query block i (fp64).
+
+    ``logits`` [rows_i, keys of sel] are the forward's logits.  With P the row
+    softmax, O_s = P V and the loss gradient dO:
+        dP = dO V^T,  D = rowsum(dO * O_s),  dL = P * (dP - D)
+        dQ_i += dL K / sqrt(d),  dK += dL^T Q_i / sqrt(d),  dV += P^T dO.
+    The logits are differentiated as QK^T/sqrt(d) of the real-valued inputs:
+    the INT8 rounding passes the gradient straight through, and the K mean
+    subtracted before coding adds the same amount to every logit of a row,
+    which the softmax cancels.  Returns (qrows, krows, dq_i, dk_rows, dv_rows).
+    """
+    d = q64.shape[1]
+    qrows = np.arange(i * block, min(N, (i + 1) * block))
+    krows = _rows_of(sel, N, block)
+    if krows.size == 0:
+        z = np.zeros((0, d))
+        return qrows, krows, np.zeros((qrows.size, d)), z, z
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    g = do64[qrows]
+    o_s = p @ v64[krows]
+    dp = g @ v64[krows].T
+    dl = p * (dp - (g * o_s).sum(axis=1, keepdims=True))
+    s = 1.0 / math.sqrt(d)
+    return qrows, krows, (dl @ k64[krows]) * s, (dl.T @ q64[qrows]) * s, p.T @ g
+
+
+def linear_branch_grad_block(i, sel, q64, k64, v64, do64, N, block, phi_kind):
+    """Gradients of the linear branch of query block i (fp64).
+
+    Forward: O_l = num / den, num = phi(Q_i) H_U, den = phi(Q_i) z_U over the
+    unselected rows U.  With g = dO:
+        dnum = g / den,  dden = -(g . O_l) / den
+        dphi(Q_i) = dnum H_U^T + dden z_U^T
+        dH_U = phi(Q_i)^T dnum,  dz_U = phi(Q_i)^T dden
+        dphi(K_u) = V_u dH_U^T + dz_U,  dV_u = phi(K_u) dH_U
+    and dX = dphi(X) * phi'(X).  Rows whose forward output is 0 (U empty or a
+    zero denominator) pass no gradient.  Returns (qrows, urows, dq_i, dk_u, dv_u).
+    """
+    d = q64.shape[1]
+    nb = n_blocks(N, block)
+    qrows = np.arange(i * block, min(N, (i + 1) * block))
+    unsel = np.setdiff1d(np.arange(nb), np.asarray(sel, dtype=np.int64))
+    urows = _rows_of(unsel, N, block)
+    dq = np.zeros((qrows.size, d))
+    if urows.size == 0:
+        z = np.zeros((0, d))
+        return qrows, urows, dq, z, z
+    fk = phi(k64[urows], phi_kind)
+    H = fk.T @ v64[urows]
+    z = fk.sum(axis=0)
+    fq = phi(q64[qrows], phi_kind)
+    num = fq @ H
+    den = fq @ z
+    ok = den != 0.0
+    g = np.where(ok[:, None], do64[qrows], 0.0)
+    safe = np.where(ok, den, 1.0)
+    o_l = num / safe[:, None]
+    dnum = g / safe[:, None]
+    dden = -(g * o_l).sum(axis=1) / safe
+    dfq = dnum @ H.T + np.outer(dden, z)
+    dq = dfq * phi_grad(q64[qrows], phi_kind)
+    dH = fq.T @ dnum
+    dz = fq.T @ dden
+    dfk = v64[urows] @ dH.T + dz[None, :]
+    dk = dfk * phi_grad(k64[urows], phi_kind)
+    dv = fk @ dH
+    return qrows, urows, dq, dk, dv
+
+
+def sla_backward_head(q_bits, k_bits, v_bits, do_bits, block: int = 64, keep: float = 0.1,
+                      phi_kind="elu1", quantize: bool = True, smooth: bool = True, idx=None,
+                      query_blocks=None):
+    """Gradients (dQ, dK, dV) of the SageSLA forward of one (batch, head).
+
+    SLA is trained: full attention is swapped for it and the model fine-tuned
+    [NEWS 方法论], with white-box alignment to full attention [DIG 训练],
+    so the forward has a gradient.  The selection is a fixed mask (top-k has
+    none); the softmax branch uses the forward's logits (INT8 or, with
+    ``quantize=False``, exact) and differentiates them as exact QK^T/sqrt(d);
+    the linear branch is differentiated exactly.  Inputs are bf16 bits [N, d];
+    ``do_bits`` is the loss gradient of the output.  ``query_blocks``
+    restricts the sum to those query blocks' contributions (their dQ rows are
+    then complete; dK and dV hold only their share).  Returns a dict with
+    dq, dk, dv (fp64 [N, d]) and idx.
+    """
+    phi_kind = phi_code(phi_kind)
+    q_bits = np.asarray(q_bits)
+    N, d = q_bits.shape
+    nb = n_blocks(N, block)
+    k = topk_count(nb, keep)
+    if k == 0 and phi_kind == PHI_NONE:
+        raise ValueError("keep = 0 with phi = none computes nothing")
+    if idx is None:
+        idx, _ = select_head(q_bits, k_bits, block, keep)
+    q8, k8, sq, sk, _ = quantize_qk(q_bits, k_bits, block, smooth=smooth)
+    q64, k64, v64 = bf16_to_f64(q_bits), bf16_to_f64(k_bits), bf16_to_f64(v_bits)
+    do64 = bf16_to_f64(do_bits)
+    dq = np.zeros((N, d))
+    dk = np.zeros((N, d))
+    dv = np.zeros((N, d))
+    for i in (range(nb) if query_blocks is None else query_blocks):
+        sel = np.asarray(idx[i])
+        if sel.size:
+            logits, _ = block_logits(i, sel, q8, k8, sq, sk, N, block, d,
+                                     None if quantize else q64, None if quantize else k64)
+            qr, kr, a, b, c = softmax_branch_grad_block(i, sel, q64, k64, v64, do64, N, block,
+                                                        logits)
+            dq[qr] += a
+            dk[kr] += b
+            dv[kr] += c
+        if phi_kind != PHI_NONE:
+            qr, ur, a, b, c = linear_branch_grad_block(i, sel, q64, k64, v64, do64, N, block,
+                                                       phi_kind)
+            dq[qr] += a
+            dk[ur] += b
+            dv[ur] += c
+    return {"dq": dq, "dk": dk, "dv": dv, "idx": idx}

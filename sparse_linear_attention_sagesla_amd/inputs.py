@@ -155,6 +155,23 @@ def make_inputs(wl: Workload | str, heads=None, threads: int | None = None):
     return Q, K, V
 
 
+def make_dout(wl: Workload | str, heads=None) -> np.ndarray:
+    """Output gradient dO for the backward, N(0,1) bf16 bits [B, H', N, d].
+
+    Drawn from its own stream per (batch, head), so adding it changes none of
+    Q, K, V.
+    """
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    heads = list(range(wl.H)) if heads is None else list(heads)
+    out = np.empty((wl.B, len(heads), wl.N, wl.d), np.uint16)
+    for b in range(wl.B):
+        for hi, h in enumerate(heads):
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 9])))
+            out[b, hi] = f32_to_bf16_bits(rng.standard_normal((wl.N, wl.d), dtype=np.float32))
+    return out
+
+
 def random_bf16(shape, seed: int, scale: float = 1.0, offset: float = 0.0) -> np.ndarray:
     """Plain N(offset, scale^2) bf16 bits, for edge-case tests."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77])))
