@@ -73,7 +73,8 @@ typedef enum sla_out_dtype {
 typedef enum sla_op {
   SLA_OP_QUANTIZE = 0,
   SLA_OP_SELECT = 1,
-  SLA_OP_ATTENTION = 2
+  SLA_OP_ATTENTION = 2,
+  SLA_OP_ATTENTION_BWD = 3
 } sla_op;
 
 /* Number of key blocks every query block keeps: 0 if keep <= 0, n_blocks if
@@ -191,6 +192,37 @@ sla_status sla_attention_fwd_timed(const void *q, const void *k, const void *v,
                                    int out_dtype, float *out_linear, void *ws,
                                    size_t ws_bytes, void *stream,
                                    void *const *stage_events);
+
+/* Gradients of sla_attention_fwd (same q, k, v, keep, phi) for the output
+ * gradient dout.  SLA is fine-tuned into the model it accelerates (news
+ * summary, section "方法论"; tool digest, section "训练"), so the forward is
+ * differentiated:
+ *   - the kept lists are those of the forward and are held fixed;
+ *   - softmax branch: P are the forward's weights (INT8 logits, fp16 P,
+ *     1/l from the fp16 sum) and the logits are differentiated as
+ *     QK^T/sqrt(128) of the real Q and K (the INT8 rounding passes the
+ *     gradient straight through; the K mean shifts a row's logits equally
+ *     and has no gradient):  dP = dout V^T, D = rowsum(dout * O_softmax),
+ *     dS = P (dP - D);  dQ += dS K / sqrt(128), dK += dS^T Q / sqrt(128),
+ *     dV += P^T dout;
+ *   - linear branch: exact, with phi'(x) = 1 for x > 0, else exp(x) (elu+1)
+ *     or 0 (ReLU); rows whose forward linear output is zero pass nothing.
+ * The selection, codes and linear state are recomputed (nothing is carried
+ * over from a forward call).  The linear branch is taken in the subtraction
+ * form for every keep < 1.
+ *   q, k, v, dout bf16 [B,H,N,128]                                     (in)
+ *   dq, dk, dv    [B,H,N,128], bf16 or fp32 per grad_dtype (sla_out_dtype)
+ *                 (out; every element written)
+ * Arithmetic: INT8 matrix cores for the logits, bf16 matrix cores with fp32
+ * accumulation for every other product (P and dS rounded to bf16), fp32
+ * elsewhere.  Workspace: SLA_OP_ATTENTION_BWD (about 14 bytes per element of
+ * Q at keep 0.1).  All work runs on `stream`.  Errors as sla_attention_fwd;
+ * dout and the three outputs must be 16-byte aligned. */
+sla_status sla_attention_bwd(const void *q, const void *k, const void *v,
+                             const void *dout, int B, int H, int N, int d,
+                             int block, double keep, int phi, void *dq,
+                             void *dk, void *dv, int grad_dtype, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /* Integer Q.K^T tiles from the attention kernel's INT8 matrix-core path, for
  * checking accumulators bit for bit.  pairs: int32 [n_pairs,4] device array

@@ -1,6 +1,6 @@
 """ctypes binding of libsla.so (argument marshalling only).
 
-Every step of the SageSLA forward runs in the HIP kernels behind the C ABI
+Every step of the SageSLA forward and backward runs in the HIP kernels behind the C ABI
 declared in include/sla.h; this module only checks tensors, allocates outputs
 and workspaces through torch, and passes raw device pointers and the current
 HIP stream.  If the library is missing the calls raise: there is no fallback.
@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 
 SLA_OK, SLA_ERR_INVALID_ARG, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_DEVICE = range(5)
 PHI = {"none": 0, "elu1": 1, "relu": 2}
-OP_QUANTIZE, OP_SELECT, OP_ATTENTION = 0, 1, 2
+OP_QUANTIZE, OP_SELECT, OP_ATTENTION, OP_ATTENTION_BWD = 0, 1, 2, 3
 BLOCK = 64
 HEAD_DIM = 128
 
@@ -51,6 +51,8 @@ def load() -> ctypes.CDLL:
     lib.sla_attention_fwd.restype = c_int
     lib.sla_attention_fwd_timed.argtypes = lib.sla_attention_fwd.argtypes + [c_void_p]
     lib.sla_attention_fwd_timed.restype = c_int
+    lib.sla_attention_bwd.argtypes = [c_void_p] * 4 + [c_int] * 5 + [c_double, c_int] + [c_void_p] * 3 + [c_int, c_void_p, c_size_t, c_void_p]
+    lib.sla_attention_bwd.restype = c_int
     lib.sla_debug_qk_i32.argtypes = [c_void_p, c_void_p] + [c_int] * 5 + [c_void_p, c_int, c_void_p, c_void_p]
     lib.sla_debug_qk_i32.restype = c_int
     lib.sla_status_string.argtypes = [c_int]
@@ -168,6 +170,27 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0
                                     _ptr(out), 1 if out_dtype == torch.float32 else 0, _ptr(lin),
                                     _ptr(ws), ws.numel(), _stream(dev)), "sla_attention_fwd")
     return (out, lin) if return_linear else out
+
+
+def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                  keep: float = 0.1, phi: str = "elu1", grad_dtype=torch.bfloat16, workspace=None):
+    """Gradients (dq, dk, dv) of the SageSLA forward for the output gradient dout."""
+    q, k, v, dout = _bhnd(q, "q"), _bhnd(k, "k"), _bhnd(v, "v"), _bhnd(dout, "dout")
+    if k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout must have the same shape")
+    if grad_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("grad_dtype must be bfloat16 or float32")
+    B, H, N, d = q.shape
+    dev = q.device
+    dq, dk, dv = (torch.empty(B, H, N, d, dtype=grad_dtype, device=dev) for _ in range(3))
+    ph = PHI[phi] if isinstance(phi, str) else int(phi)
+    nbytes = workspace_size(OP_ATTENTION_BWD, B, H, N, keep, ph)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(load().sla_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, BLOCK,
+                                    float(keep), ph, _ptr(dq), _ptr(dk), _ptr(dv),
+                                    1 if grad_dtype == torch.float32 else 0, _ptr(ws), ws.numel(),
+                                    _stream(dev)), "sla_attention_bwd")
+    return dq, dk, dv
 
 
 def debug_qk_i32(q8: torch.Tensor, k8: torch.Tensor, N: int, pairs: torch.Tensor):

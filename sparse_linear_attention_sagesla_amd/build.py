@@ -33,6 +33,7 @@ SOURCES = {
     # statistics / quantiser / selection must follow a fixed rounding order
     "sla_prep.hip": ["-ffp-contract=off"],
     "sla_sparse.hip": [],
+    "sla_bwd_prep.hip": [],
     "sla_api.cpp": ["-x", "hip", "-ffp-contract=off"],
 }
 

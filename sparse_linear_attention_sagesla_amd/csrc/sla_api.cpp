@@ -45,7 +45,9 @@ Shape make_shape(int B, int H, int N, int k) {
 }
 
 // Carves the workspace for `op`; with base == nullptr only the size is computed.
-size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w) {
+// The backward's extra buffers go to `bw`.
+size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
+             sla::BwdWorkspace* bw = nullptr) {
   size_t off = 0;
   auto take = [&](size_t bytes) -> unsigned char* {
     unsigned char* p = base ? base + off : nullptr;
@@ -58,6 +60,46 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w)
   ws.ksum = reinterpret_cast<double*>(take(BH * Nb * D * sizeof(double)));
   ws.qbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
   ws.kbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+  if (op == SLA_OP_ATTENTION_BWD) {
+    // the forward's buffers in the subtraction form, then the backward's
+    const bool lin = phi != SLA_PHI_NONE && s.k < s.Nb;
+    ws.mu = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
+    ws.q8 = reinterpret_cast<int8_t*>(take(BH * Np * D));
+    ws.k8 = reinterpret_cast<int8_t*>(take(BH * Np * D));
+    ws.sq = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
+    ws.sk = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
+    ws.idx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.k > 0 ? s.k : 1) * sizeof(int32_t)));
+    ws.v16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+    if (s.k > 0)
+      ws.sched = reinterpret_cast<int32_t*>(
+          take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * s.k * sla::kGroup * sizeof(int32_t)));
+    sla::BwdWorkspace tb;
+    sla::BwdWorkspace& b = bw ? *bw : tb;
+    if (lin) {
+      ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+      ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+      ws.hpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * D * sizeof(float)));
+      ws.zpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * sizeof(float)));
+      ws.h16t = reinterpret_cast<uint16_t*>(take(BH * D * D * sizeof(uint16_t)));
+      ws.hscale = reinterpret_cast<float*>(take(BH * sizeof(float)));
+      ws.z = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
+      b.hb = reinterpret_cast<uint16_t*>(take(BH * D * D * sizeof(uint16_t)));
+      b.fqs = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+      b.gpart = reinterpret_cast<float*>(take(BH * sla::kGradChunks * D * D * sizeof(float)));
+      b.gzpart = reinterpret_cast<float*>(take(BH * sla::kGradChunks * D * sizeof(float)));
+      b.G = reinterpret_cast<float*>(take(BH * D * D * sizeof(float)));
+      b.gz = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
+    }
+    b.kt = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+    b.qt = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+    b.dot = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
+    b.stats = reinterpret_cast<float*>(take(BH * Nb * 256 * sizeof(float)));
+    if (s.k > 0) {
+      b.maskT = reinterpret_cast<uint32_t*>(take(BH * Nb * (size_t)((s.Nb + 31) / 32) * sizeof(uint32_t)));
+      b.coff = reinterpret_cast<int32_t*>(take(BH * (Nb + 1) * sizeof(int32_t)));
+      b.cidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)s.k * sizeof(int32_t)));
+    }
+  }
   if (op == SLA_OP_ATTENTION) {
     ws.mu = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
     ws.q8 = reinterpret_cast<int8_t*>(take(BH * Np * D));
@@ -139,9 +181,9 @@ sla_status sla_workspace_size(int op, int B, int H, int N, int d, int block, dou
   *bytes = 0;
   const sla_status st = check_shape(B, H, N, d, block);
   if (st != SLA_OK) return st;
-  if (op < SLA_OP_QUANTIZE || op > SLA_OP_ATTENTION) return SLA_ERR_INVALID_ARG;
+  if (op < SLA_OP_QUANTIZE || op > SLA_OP_ATTENTION_BWD) return SLA_ERR_INVALID_ARG;
   int k = 0;
-  if (op == SLA_OP_ATTENTION) {
+  if (op == SLA_OP_ATTENTION || op == SLA_OP_ATTENTION_BWD) {
     if (std::isnan(keep) || keep < 0.0 || keep > 1.0) return SLA_ERR_INVALID_ARG;
     if (phi < SLA_PHI_NONE || phi > SLA_PHI_RELU) return SLA_ERR_INVALID_ARG;
     k = sla_topk_count((N + SLA_BLOCK - 1) / SLA_BLOCK, keep);
@@ -295,6 +337,66 @@ sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B,
                                  ws, ws_bytes, stream, nullptr);
 }
 
+sla_status sla_attention_bwd(const void* q, const void* k, const void* v, const void* dout,
+                             int B, int H, int N, int d, int block, double keep, int phi,
+                             void* dq, void* dk, void* dv, int grad_dtype, void* ws,
+                             size_t ws_bytes, void* stream) {
+  sla_status st = check_shape(B, H, N, d, block);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return SLA_ERR_INVALID_ARG;
+  if (std::isnan(keep) || keep < 0.0 || keep > 1.0) return SLA_ERR_INVALID_ARG;
+  if (phi < SLA_PHI_NONE || phi > SLA_PHI_RELU) return SLA_ERR_INVALID_ARG;
+  if (grad_dtype != SLA_OUT_BF16 && grad_dtype != SLA_OUT_F32) return SLA_ERR_INVALID_ARG;
+  const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
+  const int kk = sla_topk_count(Nb, keep);
+  if (kk == 0 && phi == SLA_PHI_NONE) return SLA_ERR_INVALID_ARG;
+  int R = 1;
+  if (kk > 0 && sla::topk_lds_bytes(Nb, &R) > 160 * 1024) return SLA_ERR_UNSUPPORTED;
+  const Shape s = make_shape(B, H, N, kk);
+  const size_t need = carve(SLA_OP_ATTENTION_BWD, s, phi, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  Workspace w;
+  sla::BwdWorkspace bw;
+  carve(SLA_OP_ATTENTION_BWD, s, phi, static_cast<unsigned char*>(ws), &w, &bw);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  const auto* vb = static_cast<const uint16_t*>(v);
+  const auto* gb = static_cast<const uint16_t*>(dout);
+  const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
+  const int f32 = grad_dtype == SLA_OUT_F32 ? 1 : 0;
+  hipError_t e = hipSuccess;
+  auto run = [&](auto&& launch) {
+    if (e == hipSuccess) e = launch();
+  };
+  // the forward's staging: codes, selection, walk schedule, linear state
+  if (kk > 0) {
+    run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs); });
+    run([&] { return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, nullptr, hs); });
+    run([&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
+    run([&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
+  }
+  run([&] {
+    return sla::launch_linear_prep(kb, vb, s, phi_eff, true, w.fk16, w.v16, w.zb, w.hpart, w.zpart,
+                                   w.mu, kk > 0 ? w.k8 : nullptr, w.sk, hs);
+  });
+  if (phi_eff != SLA_PHI_NONE)
+    run([&] {
+      return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs, bw.hb);
+    });
+  // the backward's own staging
+  run([&] { return sla::launch_transpose_blocks(kk > 0 ? kb : nullptr, kk > 0 ? qb : nullptr, gb, s,
+                                                bw.kt, bw.qt, bw.dot, hs); });
+  if (kk > 0) run([&] { return sla::launch_column_lists(w.idx, s, bw.maskT, bw.coff, bw.cidx, hs); });
+  run([&] { return sla::launch_bwd_q(qb, vb, gb, w, bw, s, phi_eff, dq, f32, hs); });
+  if (phi_eff != SLA_PHI_NONE) run([&] { return sla::launch_grad_h(bw, s, hs); });
+  run([&] { return sla::launch_bwd_kv(kb, vb, gb, w, bw, s, phi_eff, dk, dv, f32, hs); });
+  return device_status(e);
+}
+
 sla_status sla_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
                             int block, const int32_t* pairs, int n_pairs, int32_t* acc,
                             void* stream) {
@@ -319,6 +421,6 @@ const char* sla_status_string(int status) {
   }
 }
 
-int sla_version(void) { return 10100; }
+int sla_version(void) { return 10200; }
 
 }  // extern "C"

@@ -49,6 +49,24 @@ struct Workspace {
   float* z = nullptr;         // [BH, D] fp32 sum phi(K)/16
 };
 
+// Extra device buffers of the backward (null when unused).
+struct BwdWorkspace {
+  uint16_t* hb = nullptr;     // [BH, D, D]     bf16 H row-major (staged scale, phi/16)
+  uint16_t* kt = nullptr;     // [BH, Nb, D, 64] bf16 K^T per block, [channel][permuted key]
+  uint16_t* qt = nullptr;     // [BH, Nb, D, 64] bf16 Q^T per block
+  uint16_t* dot = nullptr;    // [BH, Nb, D, 64] bf16 dO^T per block
+  uint16_t* fqs = nullptr;    // [BH, Nb, D, 64] bf16 (phi(Q)/den)^T per block
+  float* stats = nullptr;     // [BH, Nb, 4, 64] per row: log2 max, 1/l, D, u (permuted)
+  uint32_t* maskT = nullptr;  // [BH, Nb, ceil(Nb/32)] query blocks keeping each key block
+  int32_t* coff = nullptr;    // [BH, Nb + 1] column starts in cidx (per head)
+  int32_t* cidx = nullptr;    // [BH, Nb * k] query blocks per key block, ascending
+  float* gpart = nullptr;     // [BH, kGradChunks, D, D] partial G
+  float* gzpart = nullptr;    // [BH, kGradChunks, D]    partial g_z
+  float* G = nullptr;         // [BH, D, D] sum of (phi(Q)/den)^T dO over all rows
+  float* gz = nullptr;        // [BH, D]    sum of (phi(Q)/den)^T u
+};
+constexpr int kGradChunks = 16;  // query-block chunks per head in the G reduction
+
 // Stage launchers (all enqueue on `s`, return the launch status).
 // Block means and K block sums; also Q's INT8 codes and scales when q8 is set.
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
@@ -65,7 +83,8 @@ hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape&
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
                               float* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s);
 hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
-                               uint16_t* h16t, float* hscale, float* z, hipStream_t s);
+                               uint16_t* h16t, float* hscale, float* z, hipStream_t s,
+                               uint16_t* hb = nullptr);
 // Linear-branch form: with few unselected blocks (Nb - k <= k) the branch is
 // summed directly over them; otherwise as whole-head sums minus the kept share.
 inline bool linear_direct(const Shape& sh) { return sh.Nb - sh.k <= sh.k; }
@@ -75,6 +94,22 @@ hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* s
                                  hipStream_t s);
 hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
                              void* out, int out_f32, float* out_linear, hipStream_t s);
+// Backward launchers.
+// Per block: K^T, Q^T, dO^T as bf16 [channel][permuted row] (any may be null).
+hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* q, const uint16_t* dout,
+                                   const Shape& sh, uint16_t* kt, uint16_t* qt, uint16_t* dot,
+                                   hipStream_t s);
+// Column lists: for every key block, the query blocks whose kept list holds it.
+hipError_t launch_column_lists(const int32_t* idx, const Shape& sh, uint32_t* maskT,
+                               int32_t* coff, int32_t* cidx, hipStream_t s);
+hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* dout,
+                        const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
+                        void* dq, int grad_f32, hipStream_t s);
+// G = sum over all rows of (phi(Q)/den)^T dO and g_z (from bwd_q's outputs).
+hipError_t launch_grad_h(const BwdWorkspace& bw, const Shape& sh, hipStream_t s);
+hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                         const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
+                         void* dk, void* dv, int grad_f32, hipStream_t s);
 hipError_t launch_debug_qk(const int8_t* q8, const int8_t* k8, const Shape& sh,
                            const int32_t* pairs, int n_pairs, int32_t* acc, hipStream_t s);
 

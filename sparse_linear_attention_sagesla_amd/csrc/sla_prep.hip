@@ -692,10 +692,12 @@ __global__ __launch_bounds__(256) void linear_sum_kernel(float* __restrict__ hpa
 }
 
 // Step 2: store H^T as fp16 scaled by 2^-s so that max|H| * 2^-s lies in
-// [2^14, 2^15), plus 2^s.
+// [2^14, 2^15), plus 2^s; with hb set, also H itself (row-major, unscaled)
+// as bf16 for the backward.
 __global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict__ hpart,
                                                          uint16_t* __restrict__ h16t,
-                                                         float* __restrict__ hscale) {
+                                                         float* __restrict__ hscale,
+                                                         uint16_t* __restrict__ hb) {
   __shared__ float red[4];
   const int t = threadIdx.x;
   const int bh = blockIdx.x;
@@ -722,6 +724,11 @@ __global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict
     const int e = t + 256 * m;       // H[c][o] with c = e / 128, o = e % 128
     const int c = e >> 7, o = e & 127;
     out[(size_t)o * kD + c] = (_Float16)(hv[m] * down);
+  }
+  if (hb) {
+    __bf16* ob = reinterpret_cast<__bf16*>(hb) + (size_t)bh * kD * kD;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) ob[t + 256 * m] = (__bf16)hv[m];
   }
 }
 
@@ -798,11 +805,12 @@ hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape&
 }
 
 hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
-                               uint16_t* h16t, float* hscale, float* z, hipStream_t s) {
+                               uint16_t* h16t, float* hscale, float* z, hipStream_t s,
+                               uint16_t* hb) {
   linear_sum_kernel<<<dim3(sh.BH, kD * kD / 1024), 256, 0, s>>>(hpart, zpart, z);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  linear_cvt_kernel<<<sh.BH, 256, 0, s>>>(hpart, h16t, hscale);
+  linear_cvt_kernel<<<sh.BH, 256, 0, s>>>(hpart, h16t, hscale, hb);
   return hipGetLastError();
 }
 

@@ -505,6 +505,40 @@ __device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, con
   den = d + __shfl_xor(d, 32);
 }
 
+// Linear output in the subtraction form, from the kept share (nm, dm) that
+// linear_share returns: (phi(Q)H - phi(Q)M) / (phi(Q)z - phi(Q)z_M).  Returns
+// 1/den, 0 when the denominator is lost in rounding; den is in the staged
+// scale (phi/16 on both sides: 1/256 of the true denominator).
+__device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t bh, int g, int l16,
+                                                     const half8 fq[4], const v4f nm[8], float dm,
+                                                     v4f ol[8]) {
+  const _Float16* ht = reinterpret_cast<const _Float16*>(a.h16t) + bh * kD * kD;
+  const float hs = a.hscale[bh];
+  const float* zz = a.z + bh * kD;
+  float dz = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dz += (float)fq[cc][e] * zz[32 * cc + 8 * g + e];
+  dz += __shfl_xor(dz, 16);
+  dz += __shfl_xor(dz, 32);
+  // whole head minus the kept share; a denominator lost in rounding counts as 0
+  const float den = dz - dm;
+  const float inv_den = den > 1e-6f * dz ? 1.0f / den : 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    v4f num = v4f{0.f, 0.f, 0.f, 0.f};
+    const _Float16* hrow = ht + (size_t)(16 * dt + l16) * kD + 8 * g;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const half8 ah = *reinterpret_cast<const half8*>(hrow + 32 * cc);
+      num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fq[cc], num, 0, 0, 0);
+    }
+    ol[dt] = (num * hs - nm[dt]) * inv_den;
+  }
+  return inv_den;
+}
+
 // Normalise, add the linear branch, store this lane's query row.
 template <int kMode>
 __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a, size_t bh,
@@ -531,30 +565,7 @@ __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) ol[dt] = nm[dt] * inv_den;
     } else {
-      const _Float16* ht = reinterpret_cast<const _Float16*>(a.h16t) + bh * kD * kD;
-      const float hs = a.hscale[bh];
-      const float* zz = a.z + bh * kD;
-      float dz = 0.0f;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dz += (float)fq[cc][e] * zz[32 * cc + 8 * g + e];
-      dz += __shfl_xor(dz, 16);
-      dz += __shfl_xor(dz, 32);
-      // whole head minus the kept share; a denominator lost in rounding counts as 0
-      const float den = dz - dm;
-      const float inv_den = den > 1e-6f * dz ? 1.0f / den : 0.0f;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        v4f num = v4f{0.f, 0.f, 0.f, 0.f};
-        const _Float16* hrow = ht + (size_t)(16 * dt + l16) * kD + 8 * g;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const half8 ah = *reinterpret_cast<const half8*>(hrow + 32 * cc);
-          num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fq[cc], num, 0, 0, 0);
-        }
-        ol[dt] = (num * hs - nm[dt]) * inv_den;
-      }
+      linear_subtract_out(a, bh, g, l16, fq, nm, dm, ol);
     }
   }
 
@@ -969,6 +980,647 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
     for (int r = 0; r < 4; ++r) dst[16 * kt + 4 * g + r] = s[kt][r];
 }
 
+// ---------------------------------------------------------------------------
+// Backward.  Gradient of the forward above for a given dO, with the kept lists
+// held fixed (top-k has no gradient) and the INT8 rounding of the logits
+// passed straight through: the logits are differentiated as QK^T/sqrt(d) of
+// the real Q and K, while the weights P are the forward's own.  With O_s the
+// softmax output and O_l = num/den the linear one:
+//   dP = dO V^T,  D = rowsum(dO * O_s),  dS = P * (dP - D)
+//   dQ += dS K / sqrt(d),  dK += dS^T Q / sqrt(d),  dV += P^T dO
+//   u = -rowsum(dO * O_l),  dphi(Q) = (dO (H - M)^T + u (z - z_M)) / den
+//   dphi(K_u) = (dH_U) V_u + dz_U,  dV_u += phi(K_u)^T-side: phi(K_u) dH_U
+// over the unselected keys u, where dH_U and dz_U of a key block are the sums,
+// over the query blocks that leave it out, of phi(Q)^T dO / den and
+// phi(Q)^T u / den.  Those are formed as the whole-head sums G, g_z minus the
+// sums W_j, w_j over the query blocks that keep block j.
+//
+// Query side: one workgroup per query block, in the forward's grouped walks.
+// Sweep 1 is the forward (statistics, O_s, M); then D, u and dphi(Q); sweep 2
+// re-walks the kept tiles (INT8 K codes, V rows, K^T) for dQ += dS K.  It
+// leaves, per query row, the log2 maximum, 1/l, D and u, and phi(Q)/den
+// transposed per block, for the key side.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) const v4f lds_v4f;
+
+constexpr int kBwdVOff = kK8Bytes;                        // V rows [64 keys][128] bf16
+constexpr int kBwdKtOff = kK8Bytes + kF16TileBytes;       // K^T [128][64 perm keys] bf16
+constexpr int kBwdStage = kK8Bytes + 2 * kF16TileBytes;   // 40 KB
+constexpr int kMRowOff = 33 * 1024;                       // M row-major, after linear_share's area
+constexpr int kZOffShared = kD * kD * 2;                  // z_M as linear_share leaves it (fp32 [128])
+
+// Position of row t of a block in the permuted order of the transposed tiles
+// (inside each 32-row half: rows 4g..4g+3 at 8g.., rows 16+4g.. at 8g+4..).
+__device__ __forceinline__ int perm_row(int t) {
+  const int r = t & 31;
+  return 32 * (t >> 5) + 8 * ((r & 15) >> 2) + (r & 3) + 4 * (r >> 4);
+}
+constexpr float kSqrtD = 11.313708498984761f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float phi_slope(float x, int phi) {
+  if (phi == kPhiElu1) return x > 0.0f ? 1.0f : __expf(x);
+  return x > 0.0f ? 1.0f : 0.0f;
+}
+
+// 16 bytes of a 256-byte row, read as 8 bf16 at 16-byte chunk `chunk`, from a
+// tile whose row r keeps chunk ch at ch ^ (r & 15).
+__device__ __forceinline__ bf16x8 lds_row_frag(const lds_byte* base, int row, int chunk) {
+  return *(lds_bf16x8*)(base + row * 256 + ((chunk ^ (row & 15)) << 4));
+}
+
+// Byte offset a lane fetches when a wave moves rounds of 1 KB of a tile with
+// 256-byte rows into LDS so that row r keeps chunk ch at ch ^ (r & 15).
+__device__ __forceinline__ int row256_ld(int wave, int lane) {
+  const int r = 4 * wave + (lane >> 4);
+  return r * 256 + ((((lane & 15) ^ r) & 15) << 4);
+}
+
+// Stores 4 consecutive channels of one row (bf16 with round to nearest even,
+// or fp32).
+__device__ __forceinline__ void store_row4(void* base, size_t off, v4f x, int f32) {
+  if (f32) {
+    *reinterpret_cast<v4f*>(reinterpret_cast<float*>(base) + off) = x;
+  } else {
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t b0 = __float_as_uint(x[2 * h]);
+      const uint32_t b1 = __float_as_uint(x[2 * h + 1]);
+      const uint32_t r0 = (b0 + 0x7fffu + ((b0 >> 16) & 1u)) >> 16;
+      const uint32_t r1 = (b1 + 0x7fffu + ((b1 >> 16) & 1u)) >> 16;
+      w[h] = r0 | (r1 << 16);
+    }
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = make_uint2(w[0], w[1]);
+  }
+}
+
+__device__ __forceinline__ void store_one(void* base, size_t off, float x, int f32) {
+  if (f32) {
+    reinterpret_cast<float*>(base)[off] = x;
+  } else {
+    const uint32_t b = __float_as_uint(x);
+    reinterpret_cast<uint16_t*>(base)[off] = (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+  }
+}
+
+struct BwdQArgs {
+  SparseArgs f;           // forward inputs: raw Q, codes, schedule, linear staging
+  const uint16_t* v;      // V bf16 [BH, N, D]
+  const uint16_t* kt;     // K^T bf16 per block [BH, Nb, D, 64 permuted keys]
+  const uint16_t* dout;   // dO bf16 [BH, N, D]
+  const uint16_t* hb;     // H bf16 row-major [BH, D(phi), D(v)], staged scale (phi/16)
+  float* stats;           // [BH, Nb, 4, 64]: log2 max, 1/l, D (row order), u (permuted)
+  uint16_t* fqs;          // (phi(Q)/den)^T bf16 per block [BH, Nb, D, 64 permuted rows]
+  void* dq;
+  int grad_f32;
+};
+
+struct BwdQSrc {
+  __amdgpu_buffer_rsrc_t k8, v, kt;
+};
+
+__device__ __forceinline__ void issue_bwd_q_tile(lds_byte* st, const BwdQSrc& src, int j, int wave,
+                                                 const LaneOffsets& lo, int vld) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    lds_load16(src.v, vld, j * kF16TileBytes + 4096 * m, st + kBwdVOff + 4096 * m + 1024 * wave);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    lds_load16(src.k8, lo.ld8, j * kK8Bytes + 4096 * m, st + 4096 * m + 1024 * wave);
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    lds_load16(src.kt, lo.ld8, j * kF16TileBytes + 4096 * m, st + kBwdKtOff + 4096 * m + 1024 * wave);
+}
+
+// One kept tile of sweep 2: S^T from the codes, the forward's fp16 weights,
+// dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
+template <bool kMask>
+__device__ __forceinline__ void bwd_q_tile(const lds_byte* st, const v4i qf[2], const bf16x8 gf[4],
+                                           const LaneOffsets& lo, float cs, float m_fin,
+                                           float inv_l, float Dt, int kvalid, int g, int l16,
+                                           v4f dqa[8]) {
+  v4i s[4];
+  qk_tile(st, qf, lo.rd8, s);
+  v4f dp[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    dp[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      dp[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row_frag(st + kBwdVOff, 16 * kt + l16, 4 * ks + g),
+                                                       gf[ks], dp[kt], 0, 0, 0);
+  }
+  bf16x8 dsf[2];
+  const float nm = -m_fin;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float p = (float)(_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf((float)s[kt][r], cs, nm));
+      if (kMask && 16 * kt + 4 * g + r >= kvalid) p = 0.0f;
+      dsf[kt >> 1][4 * (kt & 1) + r] = (__bf16)(p * inv_l * (dp[kt][r] - Dt));
+    }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 ak = *(lds_bf16x8*)(st + kBwdKtOff + ct * 2048 + (lo.rd8 ^ (64 * c)));
+      dqa[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, dsf[c], dqa[ct], 0, 0, 0);
+    }
+}
+
+template <bool kLin>
+__global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_byte* smem = (lds_byte*)smem_raw;
+  const SparseArgs& a = b.f;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int x = blockIdx.x;
+  const int span = 8 * kGroup;
+  const int full = gridDim.x - gridDim.x % span;
+  const int i = x < full ? x - x % span + kGroup * (x & 7) + (x % span) / 8 : x;
+  if (i >= a.Nb) return;  // a missing member of the last group
+  const size_t bh = blockIdx.y;
+  const LaneOffsets lo = lane_offsets(wave, lane);
+  const int qrow = i * kBlk + 16 * wave + l16;
+  const bool qvalid = qrow < a.N;
+  v4i qf[2];
+  State S;
+  init_query(a, bh, qrow, g, qf, S);
+  const float qscale = a.sq[bh * a.Nb + i] * (kInvSqrtD * kLog2e);
+  const int ngroups = (a.Nb + kGroup - 1) / kGroup;
+  const int32_t* col =
+      a.k > 0 ? a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup : nullptr;
+  run_sched<kLin>(S, smem, kBwdStage, col, a.k, a, head_sources(a, bh, kLin), bh, qf, lo, qscale,
+                  wave, g);
+
+  // softmax statistics of this lane's query and D = dO . O_s
+  float l = S.l_part + __shfl_xor(S.l_part, 16);
+  l += __shfl_xor(l, 32);
+  const float inv_l = (a.k > 0 && l > 0.0f && qvalid) ? 1.0f / l : 0.0f;
+  const float m_fin = inv_l > 0.0f ? S.m_run : INFINITY;  // rows without weights get P = 0
+  const uint16_t* dorow = b.dout + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD;
+  v4f go[8];  // dO in the O^T layout, channel 16dt + 4g + r
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const uint2 w = *reinterpret_cast<const uint2*>(dorow + 16 * dt + 4 * g);
+    go[dt] = qvalid ? v4f{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)}
+                    : v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  float dpart = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dpart += go[dt][r] * S.o[dt][r];
+  dpart += __shfl_xor(dpart, 16);
+  dpart += __shfl_xor(dpart, 32);
+  const float Dt = dpart * inv_l;
+
+  // dO of this lane's query as B operands (channels 32ks + 8g + e)
+  bf16x8 gf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 w = *reinterpret_cast<const uint4*>(dorow + 32 * ks + 8 * g);
+    gf[ks] = qvalid ? __builtin_bit_cast(bf16x8, w) : bf16x8{};
+  }
+
+  v4f dqa[8];  // dQ^T, channel 16ct + 4g + r, in units of 1/sqrt(d)
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) dqa[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  float u = 0.0f;
+  const int tl = 16 * wave + l16;  // row within the block
+  if (kLin) {
+    half8 fq[4];
+    load_phi_q(a, bh, qrow, qvalid, g, fq);
+    v4f nm[8];
+    float dm;
+    linear_share(S, smem, fq, lo, wave, lane, nm, dm);
+    v4f ol[8];
+    const float inv_den = linear_subtract_out(a, bh, g, l16, fq, nm, dm, ol);
+    float up = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) up += go[dt][r] * ol[dt][r];
+    up += __shfl_xor(up, 16);
+    up += __shfl_xor(up, 32);
+    u = qvalid ? -up : 0.0f;
+    // M (kept share, staged scale) row-major as bf16: row c = 32w + 16x + l16
+    // holds M[c][16dt + 4g + r]
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int xx = 0; xx < 2; ++xx) {
+        const int c = 32 * wave + 16 * xx + l16;
+        bf16x8 w4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w4[r] = (__bf16)S.mk[dt][xx][r];
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 h4 = {w4[0], w4[1], w4[2], w4[3]};
+        *(__attribute__((address_space(3))) bf16x4*)(smem + kMRowOff + c * 256 +
+                                                     (((2 * dt + (g >> 1)) ^ l16) << 4) + 8 * (g & 1)) = h4;
+      }
+    lds_barrier();
+    // dphi(Q)^T[c][t] = ((H - M) dO^T)[c][t] + u (z - z_M)[c], in the staged
+    // scale: the true value is that times inv_den / 16
+    const __bf16* hrow = reinterpret_cast<const __bf16*>(b.hb) + bh * kD * kD;
+    const float* zz = a.z + bh * kD;
+    const uint16_t* qrowp = a.q + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD;
+    const float fscale = inv_den * (1.0f / 256.0f);  // phi(Q) -> phi(Q)/den (true scale)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      v4f ah = v4f{0.f, 0.f, 0.f, 0.f}, am = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 hv = *reinterpret_cast<const bf16x8*>(hrow + (16 * ct + l16) * kD + 32 * ks + 8 * g);
+        ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, gf[ks], ah, 0, 0, 0);
+        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row_frag(smem + kMRowOff, 16 * ct + l16, 4 * ks + g),
+                                                     gf[ks], am, 0, 0, 0);
+      }
+      const uint2 qw = *reinterpret_cast<const uint2*>(qrowp + 16 * ct + 4 * g);
+      const float qv[4] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * ct + 4 * g + r;
+        const float zi = zz[c] - *(__attribute__((address_space(3))) const float*)(smem + kZOffShared + 4 * c);
+        const float dphi = (ah[r] - am[r] + u * zi) * (inv_den * 0.0625f);
+        dqa[ct][r] = qvalid ? dphi * phi_slope(qv[r], a.phi) * kSqrtD : 0.0f;
+        // phi(Q)/den, transposed into [c][permuted row] (region of M^T, now free)
+        const float fv = qvalid ? phi_apply(qv[r], a.phi) * fscale : 0.0f;
+        *(__attribute__((address_space(3))) __bf16*)(smem + c * 128 + 2 * perm_row(tl)) = (__bf16)fv;
+      }
+    }
+    lds_barrier();
+    // the block's (phi(Q)/den)^T: 16 KB, 16 bytes per thread per step
+    uint16_t* dst = b.fqs + ((size_t)bh * a.Nb + i) * (kD * kBlk);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int off = 16 * (t + 256 * m);
+      *reinterpret_cast<v4i*>(reinterpret_cast<unsigned char*>(dst) + off) = *(lds_v4i*)(smem + off);
+    }
+  }
+  if (lane < 16) {
+    float* st4 = b.stats + ((size_t)bh * a.Nb + i) * 256;
+    st4[tl] = m_fin;
+    st4[64 + tl] = inv_l;
+    st4[128 + tl] = Dt;
+    st4[192 + perm_row(tl)] = u;
+  }
+
+  // sweep 2: dQ += dS K over the kept tiles
+  if (a.k > 0) {
+    lds_barrier();  // LDS is reused for the tile stages
+    BwdQSrc src;
+    const size_t k8_head = (size_t)a.Np * kD;
+    src.k8 = head_rsrc(a.k8 + bh * k8_head, k8_head);
+    src.v = head_rsrc(b.v + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
+    src.kt = head_rsrc(b.kt + bh * (size_t)a.Np * kD, (size_t)a.Np * kD * 2);
+    const int vld = row256_ld(wave, lane);
+    auto block_of = [&](int p) { return min(max(ld_uniform(col, (size_t)p * kGroup), 0), a.Nb - 1); };
+    auto scale_of = [&](int j) { return ld_uniform(a.sk, bh * a.Nb + j); };
+    int j = block_of(0);
+    issue_bwd_q_tile(smem, src, j, wave, lo, vld);
+    float sc = scale_of(j);
+    const int nm1 = a.k - 1;
+    for (int p = 0; p < nm1; p += 2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int pp = p + half;
+        if (pp < nm1) {
+          lds_byte* cur = smem + half * kBwdStage;
+          lds_byte* nxt = smem + (1 - half) * kBwdStage;
+          wait_loads();
+          lds_barrier();
+          const int jn = block_of(pp + 1);
+          issue_bwd_q_tile(nxt, src, jn, wave, lo, vld);
+          const float sn = scale_of(jn);
+          bwd_q_tile<false>(cur, qf, gf, lo, qscale * sc, m_fin, inv_l, Dt, kBlk, g, l16, dqa);
+          j = jn;
+          sc = sn;
+        }
+      }
+    }
+    const int kvalid = a.N - j * kBlk;
+    const lds_byte* cur = smem + (nm1 & 1) * kBwdStage;
+    wait_loads();
+    lds_barrier();
+    if (kvalid < kBlk)
+      bwd_q_tile<true>(cur, qf, gf, lo, qscale * sc, m_fin, inv_l, Dt, kvalid, g, l16, dqa);
+    else
+      bwd_q_tile<false>(cur, qf, gf, lo, qscale * sc, m_fin, inv_l, Dt, kBlk, g, l16, dqa);
+  }
+  if (qvalid) {
+    const size_t orow = (bh * a.N + qrow) * kD;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) store_row4(b.dq, orow + 16 * ct + 4 * g, dqa[ct] * kInvSqrtD, b.grad_f32);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side: one workgroup per key block j (four waves, 16 keys each), walking
+// the query blocks that keep j (ascending).  Per query block i it stages the
+// INT8 Q codes, dO rows, dO^T, Q^T, (phi(Q)/den)^T and the row statistics:
+//   S, P (the forward's weights), dP = dO V^T, dS
+//   dV += P^T dO,  dK += dS^T Q,  W += (phi(Q)/den)^T dO,  w += (phi(Q)/den)^T u
+// then the linear gradient through G - W and g_z - w.
+// ---------------------------------------------------------------------------
+constexpr int kKvDoOff = kK8Bytes;                        // dO rows [64][128] bf16
+constexpr int kKvDotOff = kK8Bytes + kF16TileBytes;       // dO^T [128][64 perm] bf16
+constexpr int kKvQtOff = kK8Bytes + 2 * kF16TileBytes;    // Q^T
+constexpr int kKvFqOff = kK8Bytes + 3 * kF16TileBytes;    // (phi(Q)/den)^T
+constexpr int kKvStOff = kK8Bytes + 4 * kF16TileBytes;    // 4 x 64 fp32 statistics
+constexpr int kKvStage = kKvStOff + 1024;                  // 73 KB
+
+struct BwdKvArgs {
+  const int8_t* q8;
+  const int8_t* k8;
+  const float* sq;
+  const float* sk;
+  const uint16_t* kin;    // K bf16 [BH, N, D]
+  const uint16_t* v;      // V bf16 [BH, N, D]
+  const uint16_t* dout;   // dO bf16 [BH, N, D]
+  const uint16_t* qt;     // Q^T bf16 per block
+  const uint16_t* dot;    // dO^T bf16 per block
+  const uint16_t* fqs;    // (phi(Q)/den)^T bf16 per block
+  const float* stats;     // [BH, Nb, 4, 64]
+  const int32_t* coff;    // [BH, Nb + 1] column starts within the head's list
+  const int32_t* cidx;    // [BH, Nb * k] query blocks keeping each key block, ascending
+  const float* G;         // [BH, D, D] sum over all query blocks of (phi(Q)/den)^T dO
+  const float* gz;        // [BH, D]    sum of (phi(Q)/den)^T u
+  int N, Nb, Np, k, phi;
+  void* dk;
+  void* dv;
+  int grad_f32;
+};
+
+struct BwdKvSrc {
+  __amdgpu_buffer_rsrc_t q8, dout, dot, qt, fqs, stats;
+};
+
+template <bool kLin>
+__device__ __forceinline__ void issue_kv_tile(lds_byte* st, const BwdKvSrc& src, int i, int wave,
+                                              const LaneOffsets& lo, int vld, int lane) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    lds_load16(src.dout, vld, i * kF16TileBytes + 4096 * m, st + kKvDoOff + 4096 * m + 1024 * wave);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    lds_load16(src.q8, lo.ld8, i * kK8Bytes + 4096 * m, st + 4096 * m + 1024 * wave);
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    lds_load16(src.dot, lo.ld8, i * kF16TileBytes + 4096 * m, st + kKvDotOff + 4096 * m + 1024 * wave);
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    lds_load16(src.qt, lo.ld8, i * kF16TileBytes + 4096 * m, st + kKvQtOff + 4096 * m + 1024 * wave);
+  if (kLin) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      lds_load16(src.fqs, lo.ld8, i * kF16TileBytes + 4096 * m, st + kKvFqOff + 4096 * m + 1024 * wave);
+  }
+  if (wave == 0) lds_load16(src.stats, 16 * lane, i * 1024, st + kKvStOff);
+}
+
+struct KvAcc {
+  v4f dv[8];     // dV[key 4g + r][e 16et + l16]
+  v4f dk[8];     // dK[key 4g + r][c 16ct + l16] (units of 1/sqrt(d))
+  v4f w[2][8];   // W[c = 32w + 16mt + 4g + r][e = 16et + l16]
+  v4f wz[2];     // w[c] in the lanes with l16 == 0
+};
+
+template <bool kLin>
+__device__ __forceinline__ void kv_tile(const lds_byte* st, const v4i kf[2], const bf16x8 vf[4],
+                                        const LaneOffsets& lo, float cs, int wave, int g, int l16,
+                                        KvAcc& A) {
+  v4i s[4];
+  qk_tile(st, kf, lo.rd8, s);  // s[tt][r] = S[row 16tt + 4g + r][key l16]
+  v4f dp[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    dp[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row_frag(st + kKvDoOff, 16 * tt + l16, 4 * ks + g),
+                                                       vf[ks], dp[tt], 0, 0, 0);
+  }
+  bf16x8 pa[2], dsa[2];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const v4f mr = *(lds_v4f*)(st + kKvStOff + 4 * (16 * tt + 4 * g));
+    const v4f il = *(lds_v4f*)(st + kKvStOff + 256 + 4 * (16 * tt + 4 * g));
+    const v4f dd = *(lds_v4f*)(st + kKvStOff + 512 + 4 * (16 * tt + 4 * g));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p =
+          (float)(_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf((float)s[tt][r], cs, -mr[r])) * il[r];
+      pa[tt >> 1][4 * (tt & 1) + r] = (__bf16)p;
+      dsa[tt >> 1][4 * (tt & 1) + r] = (__bf16)(p * (dp[tt][r] - dd[r]));
+    }
+  }
+  bf16x8 af[2][2], ub[2];
+  if (kLin) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        af[mt][c] = *(lds_bf16x8*)(st + kKvFqOff + (2 * wave + mt) * 2048 + (lo.rd8 ^ (64 * c)));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const v4f u0 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g));
+      const v4f u1 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g + 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ub[c][e] = l16 == 0 ? (__bf16)u0[e] : (__bf16)0.0f;
+        ub[c][4 + e] = l16 == 0 ? (__bf16)u1[e] : (__bf16)0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int et = 0; et < 8; ++et) {
+      const bf16x8 bo = *(lds_bf16x8*)(st + kKvDotOff + et * 2048 + (lo.rd8 ^ (64 * c)));
+      A.dv[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[c], bo, A.dv[et], 0, 0, 0);
+      if (kLin) {
+        A.w[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], bo, A.w[0][et], 0, 0, 0);
+        A.w[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], bo, A.w[1][et], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const bf16x8 bq = *(lds_bf16x8*)(st + kKvQtOff + ct * 2048 + (lo.rd8 ^ (64 * c)));
+      A.dk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], bq, A.dk[ct], 0, 0, 0);
+    }
+    if (kLin) {
+      A.wz[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], ub[c], A.wz[0], 0, 0, 0);
+      A.wz[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], ub[c], A.wz[1], 0, 0, 0);
+    }
+  }
+}
+
+template <bool kLin>
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_byte* smem = (lds_byte*)smem_raw;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int j = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const LaneOffsets lo = lane_offsets(wave, lane);
+  const int krow = j * kBlk + 16 * wave + l16;  // this lane's key as a B/A operand row
+  const bool kvalid = krow < a.N;
+  v4i kf[2];
+  load_q8_frag(a.k8, bh, a.Np, krow, g, kf);
+  const uint16_t* vrow = a.v + ((size_t)bh * a.N + (kvalid ? krow : 0)) * kD;
+  bf16x8 vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 w = *reinterpret_cast<const uint4*>(vrow + 32 * ks + 8 * g);
+    vf[ks] = kvalid ? __builtin_bit_cast(bf16x8, w) : bf16x8{};
+  }
+  KvAcc A;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    A.dv[e] = v4f{0.f, 0.f, 0.f, 0.f};
+    A.dk[e] = v4f{0.f, 0.f, 0.f, 0.f};
+    A.w[0][e] = v4f{0.f, 0.f, 0.f, 0.f};
+    A.w[1][e] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  A.wz[0] = A.wz[1] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // this key block's column, clamped to the head's list
+  const int c0 = a.coff ? min(max(a.coff[bh * (a.Nb + 1) + j], 0), a.Nb * a.k) : 0;
+  const int n = a.coff ? min(a.coff[bh * (a.Nb + 1) + j + 1], a.Nb * a.k) - c0 : 0;
+  if (n > 0) {
+    const int32_t* list = a.cidx + bh * (size_t)a.Nb * a.k + c0;
+    BwdKvSrc src;
+    const size_t f16_head = (size_t)a.Np * kD * 2;
+    src.q8 = head_rsrc(a.q8 + bh * (size_t)a.Np * kD, (size_t)a.Np * kD);
+    src.dout = head_rsrc(a.dout + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
+    src.dot = head_rsrc(a.dot + bh * (size_t)a.Np * kD, f16_head);
+    src.qt = head_rsrc(a.qt + bh * (size_t)a.Np * kD, f16_head);
+    src.fqs = head_rsrc(kLin ? a.fqs + bh * (size_t)a.Np * kD : a.qt, f16_head);
+    src.stats = head_rsrc(a.stats + bh * (size_t)a.Nb * 256, (size_t)a.Nb * 1024);
+    const int vld = row256_ld(wave, lane);
+    const float ks = a.sk[bh * a.Nb + j] * (kInvSqrtD * kLog2e);
+    auto block_of = [&](int p) { return min(max(ld_uniform(list, (size_t)p), 0), a.Nb - 1); };
+    int i = block_of(0);
+    issue_kv_tile<kLin>(smem, src, i, wave, lo, vld, lane);
+    float si = ld_uniform(a.sq, bh * a.Nb + i);
+    for (int p = 0; p < n; p += 2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int pp = p + half;
+        if (pp < n) {
+          lds_byte* cur = smem + half * kKvStage;
+          lds_byte* nxt = smem + (1 - half) * kKvStage;
+          wait_loads();
+          lds_barrier();  // block pp is in LDS; every wave is done with block pp-1
+          int in = i;
+          float sn = si;
+          if (pp + 1 < n) {
+            in = block_of(pp + 1);
+            issue_kv_tile<kLin>(nxt, src, in, wave, lo, vld, lane);
+            sn = ld_uniform(a.sq, bh * a.Nb + in);
+          }
+          kv_tile<kLin>(cur, kf, vf, lo, si * ks, wave, g, l16, A);
+          i = in;
+          si = sn;
+        }
+      }
+    }
+  }
+
+  // linear gradient through G - W and g_z - w
+  v4f dfk[8], dvl[8];
+  constexpr int kGaOff = 0, kGbOff = 32 * 1024, kGzOff = 64 * 1024;
+  if (kLin) {
+    lds_barrier();  // every wave is done with the stages
+    const float* Gh = a.G + bh * kD * kD;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int et = 0; et < 8; ++et)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 32 * wave + 16 * mt + 4 * g + r;
+          const int e = 16 * et + l16;
+          const __bf16 gv = (__bf16)(Gh[c * kD + e] - A.w[mt][et][r]);
+          *(__attribute__((address_space(3))) __bf16*)(smem + kGaOff + c * 256 +
+                                                      ((((e >> 3) ^ (c & 15)) & 15) << 4) + 2 * (e & 7)) = gv;
+          *(__attribute__((address_space(3))) __bf16*)(smem + kGbOff + e * 256 +
+                                                      ((((c >> 3) ^ (e & 15)) & 15) << 4) + 2 * (c & 7)) = gv;
+        }
+    if (l16 == 0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 32 * wave + 16 * mt + 4 * g + r;
+          *(__attribute__((address_space(3))) float*)(smem + kGzOff + 4 * c) = a.gz[bh * kD + c] - A.wz[mt][r];
+        }
+    }
+    lds_barrier();
+    // phi(K) of this lane's key as A operands (channels 32ks + 8g + e)
+    const uint16_t* krp = a.kin + ((size_t)bh * a.N + (kvalid ? krow : 0)) * kD;
+    bf16x8 fk[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 w = *reinterpret_cast<const uint4*>(krp + 32 * ks + 8 * g);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xv = (e & 1) ? bf16_hi(ww[e >> 1]) : bf16_lo(ww[e >> 1]);
+        fk[ks][e] = kvalid ? (__bf16)phi_apply(xv, a.phi) : (__bf16)0.0f;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      dfk[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+      dvl[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        dfk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ks], lds_row_frag(smem + kGaOff, 16 * ct + l16, 4 * ks + g),
+                                                          dfk[ct], 0, 0, 0);
+        dvl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[ks], lds_row_frag(smem + kGbOff, 16 * ct + l16, 4 * ks + g),
+                                                          dvl[ct], 0, 0, 0);
+      }
+    }
+  }
+  // outputs: lane holds keys 16w + 4g + r, channel 16ct + l16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int kr = j * kBlk + 16 * wave + 4 * g + r;
+    if (kr >= a.N) continue;
+    const size_t orow = (bh * a.N + kr) * kD;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const int c = 16 * ct + l16;
+      float dkv = A.dk[ct][r] * kInvSqrtD;
+      float dvv = A.dv[ct][r];
+      if (kLin) {
+        const uint16_t kb = a.kin[orow + c];
+        const float gzh = *(__attribute__((address_space(3))) const float*)(smem + kGzOff + 4 * c);
+        dkv += (dfk[ct][r] + gzh) * phi_slope(bf16_lo(kb), a.phi);
+        dvv += dvl[ct][r];
+      }
+      store_one(a.dk, orow + c, dkv, a.grad_f32);
+      store_one(a.dv, orow + c, dvv, a.grad_f32);
+    }
+  }
+}
+
 template <int kMode>
 hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
   constexpr size_t stage = (size_t)kK8Bytes + kF16TileBytes + (kMode != kSoftOnly ? kF16TileBytes : 0);
@@ -1014,6 +1666,95 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   if (lin && linear_direct(sh)) return launch_mode<kDirect>(a, sh, s);
   if (!lin) return launch_mode<kSoftOnly>(a, sh, s);
   return launch_mode<kSubtract>(a, sh, s);
+}
+
+hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* dout,
+                        const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
+                        void* dq, int grad_f32, hipStream_t s) {
+  BwdQArgs b;
+  SparseArgs& a = b.f;
+  a = SparseArgs{};
+  a.q = q;
+  a.q8 = ws.q8;
+  a.k8 = ws.k8;
+  a.sq = ws.sq;
+  a.sk = ws.sk;
+  a.sched = ws.sched;
+  a.fk16 = ws.fk16;
+  a.v16 = ws.v16;
+  a.zb = ws.zb;
+  a.h16t = ws.h16t;
+  a.hscale = ws.hscale;
+  a.z = ws.z;
+  a.N = sh.N;
+  a.Nb = sh.Nb;
+  a.Np = sh.Np;
+  a.k = sh.k;
+  a.phi = phi;
+  b.v = v;
+  b.kt = bw.kt;
+  b.dout = dout;
+  b.hb = bw.hb;
+  b.stats = bw.stats;
+  b.fqs = bw.fqs;
+  b.dq = dq;
+  b.grad_f32 = grad_f32;
+  const bool lin = phi != kPhiNone && sh.k < sh.Nb;
+  const int slots = kGroup * ((sh.Nb + kGroup - 1) / kGroup);
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kBwdStage);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kBwdStage);
+  });
+  if (lin)
+    bwd_q_kernel<true><<<dim3(slots, sh.BH), 256, 2 * kBwdStage, s>>>(b);
+  else
+    bwd_q_kernel<false><<<dim3(slots, sh.BH), 256, 2 * kBwdStage, s>>>(b);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                         const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
+                         void* dk, void* dv, int grad_f32, hipStream_t s) {
+  BwdKvArgs a;
+  a.q8 = ws.q8;
+  a.k8 = ws.k8;
+  a.sq = ws.sq;
+  a.sk = ws.sk;
+  a.kin = k;
+  a.v = v;
+  a.dout = dout;
+  a.qt = bw.qt;
+  a.dot = bw.dot;
+  a.fqs = bw.fqs;
+  a.stats = bw.stats;
+  a.coff = sh.k > 0 ? bw.coff : nullptr;
+  a.cidx = bw.cidx;
+  a.G = bw.G;
+  a.gz = bw.gz;
+  a.N = sh.N;
+  a.Nb = sh.Nb;
+  a.Np = sh.Np;
+  a.k = sh.k;
+  a.phi = phi;
+  a.dk = dk;
+  a.dv = dv;
+  a.grad_f32 = grad_f32;
+  const bool lin = phi != kPhiNone && sh.k < sh.Nb;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_kv_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kKvStage);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_kv_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kKvStage);
+  });
+  if (lin)
+    bwd_kv_kernel<true><<<dim3(sh.Nb, sh.BH), 256, 2 * kKvStage, s>>>(a);
+  else
+    bwd_kv_kernel<false><<<dim3(sh.Nb, sh.BH), 256, 2 * kKvStage, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,

@@ -1,0 +1,94 @@
+"""Parity of the backward (sla_attention_bwd, through the C ABI) against the
+fp64 oracle's sla_backward_head, on seeded inputs spanning several tiles with
+a ragged last block.
+
+Tolerance, from the arithmetic: every product on the GPU side has bf16
+operands (the inputs are bf16 already; P, dS, phi(Q)/den, phi(K) and G - W
+are rounded once, unit roundoff u = 2^-9) and fp32 accumulation; P also
+carries the forward's fp16 rounding (2^-11).  A gradient entry is a sum of
+such products, so its error is about u times the sum of the absolute values
+of its terms (one rounding dominates: the bf16 P or dS); softmax-gradient
+rows sum to zero, so those sums can exceed the entry itself.  The bound used
+is rel-L2 <= 4u = 7.8e-3 (per tensor) and max-abs <= 8u times the tensor's
+largest entry, plus an absolute floor of 1e-5 for tensors that vanish
+exactly (one token: its softmax gradient cancels to zero in exact arithmetic,
+to ~1e-7 in fp32).  Measured: rel-L2 1.3e-3 to 3.1e-3, max-abs at most 2.1u
+of the largest entry.
+"""
+import numpy as np
+import pytest
+
+from oracle import sla_oracle as O
+from sparse_linear_attention_sagesla_amd.inputs import make_dout, make_inputs, random_bf16
+
+from gpu_util import errors, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+sla = pytest.importorskip("sparse_linear_attention_sagesla_amd")
+
+U_BF16 = 2.0 ** -9
+REL = 4 * U_BF16
+MAXREL = 8 * U_BF16
+
+
+ATOL_FLOOR = 1e-5
+
+
+def _check(name, got, want):
+    max_abs, rel = errors(got, want)
+    scale = float(np.abs(want).max())
+    print(f"[bwd] {name}: max-abs {max_abs:.3e} (max |ref| {scale:.3e}) rel-L2 {rel:.3e}", flush=True)
+    bound = MAXREL * scale + ATOL_FLOOR
+    assert max_abs <= bound, f"{name}: max-abs {max_abs:.3e} > {bound:.3e}"
+    if scale > ATOL_FLOOR:
+        assert rel <= REL, f"{name}: rel-L2 {rel:.3e} > {REL:.3e}"
+
+
+def _run(Q, K, V, G, keep, phi, grad_dtype=torch.float32):
+    print(f"[case] bwd shape={tuple(Q.shape)} keep={keep} phi={phi}", flush=True)
+    q, k, v, g = (to_dev(x) for x in (Q, K, V, G))
+    dq, dk, dv = sla.attention_bwd(q, k, v, g, keep=keep, phi=phi, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return [x.float().cpu().numpy() for x in (dq, dk, dv)]
+
+
+def _compare(Q, K, V, G, keep, phi, tag):
+    got = _run(Q, K, V, G, keep, phi)
+    for h in range(Q.shape[1]):
+        r = O.sla_backward_head(Q[0, h], K[0, h], V[0, h], G[0, h], block=64, keep=keep,
+                                phi_kind=phi)
+        for i, name in enumerate(("dq", "dk", "dv")):
+            _check(f"{tag} h{h} {name}", got[i][0, h], r[name])
+
+
+@pytest.mark.parametrize("keep,phi", [(0.3, "elu1"), (0.3, "relu"), (0.3, "none"),
+                                      (0.0, "elu1"), (1.0, "elu1"), (0.6, "elu1")])
+def test_backward_parity_ragged(keep, phi):
+    N = 64 * 9 - 23  # nine blocks, the last with 41 rows
+    Q, K, V, G = (random_bf16((1, 2, N, 128), s) for s in (101, 102, 103, 104))
+    _compare(Q, K, V, G, keep, phi, f"ragged keep={keep} {phi}")
+
+
+def test_backward_parity_tiny_workload():
+    Q, K, V = make_inputs("tiny")
+    G = make_dout("tiny")
+    _compare(Q, K, V, G, 0.1, "elu1", "tiny")
+
+
+@pytest.mark.parametrize("N", [1, 64, 130])
+def test_backward_small_shapes(N):
+    Q, K, V, G = (random_bf16((1, 1, N, 128), s) for s in (111, 112, 113, 114))
+    _compare(Q, K, V, G, 0.5, "elu1", f"N={N}")
+
+
+def test_backward_bf16_grads_round_the_fp32_ones():
+    N = 64 * 5 - 7
+    Q, K, V, G = (random_bf16((1, 2, N, 128), s) for s in (121, 122, 123, 124))
+    f32 = _run(Q, K, V, G, 0.4, "elu1", torch.float32)
+    b16 = _run(Q, K, V, G, 0.4, "elu1", torch.bfloat16)
+    for a, b in zip(f32, b16):
+        # bf16 output is the round-to-nearest-even of the same fp32 value
+        r = torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(r, b)
