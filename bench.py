@@ -135,6 +135,41 @@ def cpu_baseline(Q, K, V, wl, keep, phi, n_blocks_sample=160):
                        f"query blocks; {t2 - t0:.1f} s of CPU work")}
 
 
+def backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, fwd_ms, steps, stream, dev):
+    """sla_attention_bwd on the same inputs and a seeded dO: ms per call (one
+    warmup call, then `steps` timed calls back to back, bf16 gradients)."""
+    import torch
+    from sparse_linear_attention_sagesla_amd.inputs import make_dout
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    g = torch.from_numpy(make_dout(wl).view(np.int16)).view(torch.bfloat16).to(dev)
+    ph = _lib.PHI[phi]
+    nbytes = sla.workspace_size(sla.OP_ATTENTION_BWD, B, H, N, keep, ph)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    grads = [torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+
+    def call():
+        rc = lib.sla_attention_bwd(_lib._ptr(q), _lib._ptr(k), _lib._ptr(v), _lib._ptr(g), B, H, N,
+                                   d, 64, float(keep), ph, *[_lib._ptr(x) for x in grads], 0,
+                                   _lib._ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(lib.sla_status_string(rc).decode())
+
+    call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    log(f"[bench] backward: {ms:.3f} ms/call over {steps} calls")
+    return {"ms_per_call": round(ms, 4), "steps": steps, "ratio_to_forward": round(ms / fwd_ms, 3),
+            "grad_dtype": "bf16", "workspace_bytes": int(nbytes),
+            "note": "sla_attention_bwd: selection, codes and linear state recomputed, then "
+                    "dQ (query side), G, dK/dV (key side)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +179,8 @@ def main():
     ap.add_argument("--keep", type=float, default=None)
     ap.add_argument("--phi", default="elu1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=3,
+                    help="also time this many sla_attention_bwd calls (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale "
                          "hardware byte counters against a kernel of known traffic")
@@ -283,6 +320,9 @@ def main():
         "call_roofline_frac": round(ideal_s / (ms_step * 1e-3), 4),
         "roofline": roofline,
     }
+    if args.backward_steps > 0:
+        rec["backward"] = backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, ms_step,
+                                       args.backward_steps, stream, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(Q, K, V, wl, keep, phi)

@@ -123,7 +123,13 @@ __global__ __launch_bounds__(1024) void column_offsets_kernel(const uint32_t* __
   if (t == 1023) co[Nb] = part[1023];
 }
 
-// The column lists, ascending: one wave per key block.
+// The column lists: one wave per key block.  The key side runs the kGroup
+// consecutive key blocks of a group side by side on one XCD, so a column is
+// ordered to meet its group mates: first the query blocks that all of the
+// group keep, then those kept by three of them, two, and this one alone,
+// ascending within each class.  The shared prefix is then walked in step by
+// every member and each staged query block is fetched once for all of them.
+static_assert(kGroup == 4, "the owner count below is a 4-input bit-sliced adder");
 __global__ __launch_bounds__(256) void column_fill_kernel(const uint32_t* __restrict__ maskT,
                                                           const int32_t* __restrict__ coff, int Nb,
                                                           int W, int k,
@@ -132,25 +138,46 @@ __global__ __launch_bounds__(256) void column_fill_kernel(const uint32_t* __rest
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const size_t bh = blockIdx.y;
   if (j >= Nb) return;
+  const int j0 = j - j % kGroup;
   const uint32_t* row = maskT + (bh * Nb + j) * (size_t)W;
   int32_t* out = cidx + bh * (size_t)Nb * k + coff[bh * (size_t)(Nb + 1) + j];
   int base = 0;
-  for (int w0 = 0; w0 < W; w0 += 64) {
-    uint32_t word = w0 + lane < W ? row[w0 + lane] : 0u;
-    const int c = __popc(word);
-    int incl = c;  // inclusive scan over the wave
+  for (int cls = kGroup; cls >= 1; --cls) {
+    for (int w0 = 0; w0 < W; w0 += 64) {
+      uint32_t word = 0u;
+      if (w0 + lane < W) {
+        // owners per query block among the group's members, as a bit-sliced count
+        uint32_t m[4];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
+        for (int u = 0; u < 4; ++u)
+          m[u] = j0 + u < Nb ? maskT[(bh * Nb + j0 + u) * (size_t)W + w0 + lane] : 0u;
+        const uint32_t s0 = m[0] ^ m[1], c0 = m[0] & m[1];
+        const uint32_t s1 = m[2] ^ m[3], c1 = m[2] & m[3];
+        const uint32_t b0 = s0 ^ s1, cr = s0 & s1;
+        const uint32_t b1 = c0 ^ c1 ^ cr;
+        const uint32_t b2 = (c0 & c1) | ((c0 ^ c1) & cr);
+        const uint32_t n4 = b2;
+        const uint32_t n3 = ~b2 & b1 & b0;
+        const uint32_t n2 = ~b2 & b1 & ~b0;
+        const uint32_t n1 = ~b2 & ~b1 & b0;
+        const uint32_t sel = cls == 4 ? n4 : cls == 3 ? n3 : cls == 2 ? n2 : n1;
+        word = row[w0 + lane] & sel;
+      }
+      const int c = __popc(word);
+      int incl = c;  // inclusive scan over the wave
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      int pos = base + incl - c;
+      while (word) {
+        const int b = __ffs(word) - 1;
+        out[pos++] = 32 * (w0 + lane) + b;
+        word &= word - 1;
+      }
+      base += __shfl(incl, 63);
     }
-    int pos = base + incl - c;
-    while (word) {
-      const int b = __ffs(word) - 1;
-      out[pos++] = 32 * (w0 + lane) + b;
-      word &= word - 1;
-    }
-    base += __shfl(incl, 63);
   }
 }
 

@@ -59,7 +59,7 @@ struct BwdWorkspace {
   float* stats = nullptr;     // [BH, Nb, 4, 64] per row: log2 max, 1/l, D, u (permuted)
   uint32_t* maskT = nullptr;  // [BH, Nb, ceil(Nb/32)] query blocks keeping each key block
   int32_t* coff = nullptr;    // [BH, Nb + 1] column starts in cidx (per head)
-  int32_t* cidx = nullptr;    // [BH, Nb * k] query blocks per key block, ascending
+  int32_t* cidx = nullptr;    // [BH, Nb * k] query blocks per key block (group order)
   float* gpart = nullptr;     // [BH, kGradChunks, D, D] partial G
   float* gzpart = nullptr;    // [BH, kGradChunks, D]    partial g_z
   float* G = nullptr;         // [BH, D, D] sum of (phi(Q)/den)^T dO over all rows

@@ -1327,7 +1327,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
 
 // ---------------------------------------------------------------------------
 // Key side: one workgroup per key block j (four waves, 16 keys each), walking
-// the query blocks that keep j (ascending).  Per query block i it stages the
+// the query blocks that keep j (shared with the group's other key blocks first).  Per query block i it stages the
 // INT8 Q codes, dO rows, dO^T, Q^T, (phi(Q)/den)^T and the row statistics:
 //   S, P (the forward's weights), dP = dO V^T, dS
 //   dV += P^T dO,  dK += dS^T Q,  W += (phi(Q)/den)^T dO,  w += (phi(Q)/den)^T u
@@ -1353,7 +1353,7 @@ struct BwdKvArgs {
   const uint16_t* fqs;    // (phi(Q)/den)^T bf16 per block
   const float* stats;     // [BH, Nb, 4, 64]
   const int32_t* coff;    // [BH, Nb + 1] column starts within the head's list
-  const int32_t* cidx;    // [BH, Nb * k] query blocks keeping each key block, ascending
+  const int32_t* cidx;    // [BH, Nb * k] query blocks keeping each key block
   const float* G;         // [BH, D, D] sum over all query blocks of (phi(Q)/den)^T dO
   const float* gz;        // [BH, D]    sum of (phi(Q)/den)^T u
   int N, Nb, Np, k, phi;
@@ -1475,7 +1475,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
   const int wave = t >> 6;
   const int g = lane >> 4;
   const int l16 = lane & 15;
-  const int j = blockIdx.x;
+  // workgroups x, x+8, x+16, x+24 (one XCD, dispatched together) take four
+  // consecutive key blocks, whose columns overlap, so their staged query
+  // blocks meet in that XCD's L2
+  const int x = blockIdx.x;
+  const int span = 8 * kGroup;
+  const int full = gridDim.x - gridDim.x % span;
+  const int j = x < full ? x - x % span + kGroup * (x & 7) + (x % span) / 8 : x;
   const size_t bh = blockIdx.y;
   const LaneOffsets lo = lane_offsets(wave, lane);
   const int krow = j * kBlk + 16 * wave + l16;  // this lane's key as a B/A operand row

@@ -125,3 +125,34 @@ def test_debug_qk_rejects_bad_arguments():
     assert L.sla_debug_qk_i32(FAKE, FAKE, 1, 1, 64, 128, 64, FAKE, -1, FAKE, NULL) == INVALID
     assert L.sla_debug_qk_i32(NULL, FAKE, 1, 1, 64, 128, 64, FAKE, 1, FAKE, NULL) == INVALID
     assert L.sla_debug_qk_i32(FAKE, FAKE, 1, 1, 64, 128, 64, FAKE, 0, FAKE, NULL) == OK
+
+
+def _bwd(q=FAKE, k=FAKE, v=FAKE, g=FAKE, B=1, H=2, N=2048, d=128, block=64, keep=0.1, phi=1,
+         dq=FAKE, dk=FAKE, dv=FAKE, grad_dtype=1, ws=FAKE, ws_bytes=0):
+    return lib().sla_attention_bwd(q, k, v, g, B, H, N, d, block, keep, phi, dq, dk, dv,
+                                   grad_dtype, ws, ws_bytes, NULL)
+
+
+def test_backward_workspace_size():
+    st, nb = _ws(3)
+    assert st == OK and nb > _ws(2)[1]
+    assert _ws(3, phi=0)[1] < nb
+    assert _ws(3, keep=0.0, phi=1)[0] == OK
+    # holds at least the INT8 codes, fp16 V, the three bf16 transposes and the statistics
+    assert _ws(3, B=1, H=40, N=75600)[1] >= 40 * 1182 * 64 * 128 * (2 + 2 + 6) + 40 * 1182 * 1024
+
+
+def test_backward_rejects_bad_arguments_before_launch():
+    assert _bwd(g=NULL) == INVALID
+    assert _bwd(dk=NULL) == INVALID
+    assert _bwd(dv=MISALIGNED) == INVALID
+    assert _bwd(g=MISALIGNED) == INVALID
+    assert _bwd(d=96) == UNSUPPORTED
+    assert _bwd(block=32) == UNSUPPORTED
+    assert _bwd(keep=float("nan")) == INVALID
+    assert _bwd(keep=1.5) == INVALID
+    assert _bwd(keep=0.0, phi=0) == INVALID
+    assert _bwd(phi=5) == INVALID
+    assert _bwd(grad_dtype=2) == INVALID
+    assert _bwd(ws_bytes=4096) == WORKSPACE
+    assert _bwd(ws=NULL, ws_bytes=1 << 40) == WORKSPACE
