@@ -92,3 +92,63 @@ def test_backward_bf16_grads_round_the_fp32_ones():
         # bf16 output is the round-to-nearest-even of the same fp32 value
         r = torch.from_numpy(a).to(torch.bfloat16).float().numpy()
         assert np.array_equal(r, b)
+
+
+def test_backward_parity_many_blocks():
+    """150 query blocks (ragged last block), one head, every gradient entry."""
+    from sparse_linear_attention_sagesla_amd.inputs import Workload, make_head
+    wl = Workload("mid", 1, 1, 64 * 150 - 37, None, 7001)
+    Q, K, V = (x[None, None] for x in make_head(wl, 0, 0))
+    G = random_bf16(Q.shape, 131)
+    _compare(Q, K, V, G, 0.1, "elu1", "mid")
+
+
+@pytest.fixture(scope="module")
+def wan720():
+    from sparse_linear_attention_sagesla_amd.inputs import WORKLOADS
+    wl = WORKLOADS["wan14b720"]
+    Q, K, V = make_inputs(wl)
+    G = make_dout(wl)
+    print(f"[case] bwd wan14b720 shape={tuple(Q.shape)}", flush=True)
+    q, k, v, g = (to_dev(x) for x in (Q, K, V, G))
+    dq, dk, dv = sla.attention_bwd(q, k, v, g, keep=0.1, phi="elu1", grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return Q, K, V, G, (q, k, v, g), (dq, dk, dv)
+
+
+def test_backward_wan720_sampled_dq(wan720):
+    """Full Wan-14B-720p shape: dQ of sampled query blocks (the last one ragged)
+    against the oracle, which needs only those blocks for their dQ rows."""
+    Q, K, V, G, _, (dq, _, _) = wan720
+    nb = O.n_blocks(Q.shape[2], 64)
+    for h in (0, 23):
+        blocks = [0, 517, nb - 1]
+        r = O.sla_backward_head(Q[0, h], K[0, h], V[0, h], G[0, h], block=64, keep=0.1,
+                                phi_kind="elu1", query_blocks=blocks)
+        rows = np.concatenate([np.arange(i * 64, min(Q.shape[2], (i + 1) * 64)) for i in blocks])
+        _check(f"wan720 h{h} dq rows of {blocks}", dq[0, h, rows].cpu().numpy(), r["dq"][rows])
+
+
+def test_backward_wan720_dv_rows_sum_to_twice_dout(wan720):
+    """Every row's softmax weights and linear weights each sum to one, so the
+    dV rows of a head sum to twice the dO rows (no row of this shape has an
+    empty or vanishing linear branch).  The per-channel sums of N = 75600
+    fp32 gradient rows carry independent, unbiased (round-to-nearest)
+    errors of a few u times the entries, so the bound is 8u * rms(dV) *
+    sqrt(N) * 4 (four standard deviations of such a sum)."""
+    Q, K, V, G, _, (_, _, dv) = wan720
+    dvs = dv.double().sum(dim=2).cpu().numpy()           # [B, H, d]
+    want = 2.0 * O.bf16_to_f64(G).sum(axis=2)            # [B, H, d]
+    rms = float(dv.double().pow(2).mean().sqrt())
+    bound = 8 * U_BF16 * rms * np.sqrt(Q.shape[2]) * 4
+    err = float(np.abs(dvs - want).max())
+    print(f"[bwd] wan720 dv row sums: max err {err:.3e} bound {bound:.3e}", flush=True)
+    assert err <= bound
+
+
+def test_backward_is_deterministic(wan720):
+    _, _, _, _, (q, k, v, g), (dq, dk, dv) = wan720
+    dq2, dk2, dv2 = sla.attention_bwd(q, k, v, g, keep=0.1, phi="elu1", grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a, b)
