@@ -29,6 +29,7 @@ PEAK_F16_FLOPS = 2.5e15     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM = 8.0e12           # MI355X HBM3E bytes/s
 PEAK_F64_FLOPS = 78.6e12    # MI355X fp64 vector
 STAGES = ["stats", "kmean", "quantize", "topk", "linear_prep", "linear_final", "sparse", "schedule"]
+BWD_STAGES = ["fwd_staging", "transpose", "columns", "query", "grad_h", "key"]
 SPARSE_SRC = os.path.join(ROOT, "sparse_linear_attention_sagesla_amd", "csrc", "sla_sparse.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sparse_fwd_kernel_wan14b720_counters.md")
 
@@ -147,10 +148,12 @@ def backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, fwd_ms, steps, stream, 
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     grads = [torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev) for _ in range(3)]
 
-    def call():
-        rc = lib.sla_attention_bwd(_lib._ptr(q), _lib._ptr(k), _lib._ptr(v), _lib._ptr(g), B, H, N,
-                                   d, 64, float(keep), ph, *[_lib._ptr(x) for x in grads], 0,
-                                   _lib._ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+    def call(events=None):
+        ev = (ctypes.c_void_p * len(events))(*events) if events else None
+        rc = lib.sla_attention_bwd_timed(_lib._ptr(q), _lib._ptr(k), _lib._ptr(v), _lib._ptr(g), B,
+                                         H, N, d, 64, float(keep), ph,
+                                         *[_lib._ptr(x) for x in grads], 0, _lib._ptr(ws),
+                                         ws.numel(), ctypes.c_void_p(stream.cuda_stream), ev)
         if rc != 0:
             raise RuntimeError(lib.sla_status_string(rc).decode())
 
@@ -164,10 +167,50 @@ def backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, fwd_ms, steps, stream, 
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     log(f"[bench] backward: {ms:.3f} ms/call over {steps} calls")
-    return {"ms_per_call": round(ms, 4), "steps": steps, "ratio_to_forward": round(ms / fwd_ms, 3),
-            "grad_dtype": "bf16", "workspace_bytes": int(nbytes),
-            "note": "sla_attention_bwd: selection, codes and linear state recomputed, then "
-                    "dQ (query side), G, dK/dV (key side)"}
+    # stage times from further calls with stage events
+    hip = HipEvents()
+    evs = [hip.create(2 * len(BWD_STAGES)) for _ in range(steps)]
+    for e in evs:
+        call(e)
+    torch.cuda.synchronize()
+    nb = sla.n_blocks(N)
+    kk = sla.topk_count(nb, keep)
+    linear = phi != "none" and kk < nb
+    stage_ms = {}
+    for si, name in enumerate(BWD_STAGES):
+        if (name == "columns" and kk == 0) or (name == "grad_h" and not linear):
+            continue
+        stage_ms[name] = float(np.mean([hip.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]))
+    for e in evs:
+        hip.destroy(e)
+    rec = {"ms_per_call": round(ms, 4), "steps": steps, "ratio_to_forward": round(ms / fwd_ms, 3),
+           "grad_dtype": "bf16", "workspace_bytes": int(nbytes),
+           "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+           "note": "sla_attention_bwd: selection, codes and linear state recomputed, then "
+                   "dQ (query side), G, dK/dV (key side)"}
+    if kk > 0:
+        # matrix-core work of the two attention kernels on valid rows, fp16-equivalent
+        idx = sla.block_select(q, k, keep).cpu().numpy()
+        nbk = idx.shape[2]
+        rows = np.full(nbk, 64, dtype=np.int64)
+        rows[-1] = N - 64 * (nbk - 1)
+        kept_rows = rows[idx.reshape(-1, idx.shape[-1])].sum(axis=1)
+        P = float((np.tile(rows, idx.shape[0] * idx.shape[1]) * kept_rows).sum())
+        lin = 1.0 if linear else 0.0
+        work = {  # (INT8 ops, fp16/bf16 flops)
+            "query": (2 * 2 * d * P, 2 * d * P + lin * 4 * d * P + 4 * d * P
+                      + lin * 3 * 2 * d * d * N * B * H),
+            "key": (2 * d * P, 6 * d * P + lin * 4 * d * P + lin * 2 * 2 * d * d * N * B * H),
+        }
+        rl = {}
+        for name, (i8, f16) in work.items():
+            t_s = stage_ms[name] * 1e-3
+            ach = (0.5 * i8 + f16) / t_s / 1e12
+            rl[name] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_FLOPS / 1e12,
+                        "unit": "TFLOP/s", "frac": round(ach / (PEAK_F16_FLOPS / 1e12), 4),
+                        "kernel": "bwd_q_kernel" if name == "query" else "bwd_kv_kernel"}
+        rec["roofline"] = rl
+    return rec
 
 
 def main():

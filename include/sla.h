@@ -224,6 +224,32 @@ sla_status sla_attention_bwd(const void *q, const void *k, const void *v,
                              void *dk, void *dv, int grad_dtype, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* Stages of sla_attention_bwd, all on the caller's stream in this order. */
+typedef enum sla_bwd_stage {
+  SLA_BWD_STAGE_FWD_STAGING = 0, /* the forward's statistics, selection, walk
+                                    schedule, K mean and linear staging           */
+  SLA_BWD_STAGE_TRANSPOSE = 1,   /* K^T, Q^T, dO^T per block                      */
+  SLA_BWD_STAGE_COLUMNS = 2,     /* per key block, the query blocks keeping it    */
+  SLA_BWD_STAGE_QUERY = 3,       /* query side: dQ, row statistics                */
+  SLA_BWD_STAGE_GRAD_H = 4,      /* whole-head linear-gradient sums               */
+  SLA_BWD_STAGE_KEY = 5,         /* key side: dK, dV                              */
+  SLA_BWD_N_STAGES = 6
+} sla_bwd_stage;
+
+/* sla_attention_bwd that also records caller-created HIP events (hipEvent_t,
+ * same device) on `stream` around its stages: stage_events[2*s] just before
+ * stage s and stage_events[2*s+1] just after.  stage_events is NULL or holds
+ * 2 * SLA_BWD_N_STAGES entries, any of which may be NULL; stages a call skips
+ * (COLUMNS when keep == 0, GRAD_H without the linear branch) record nothing.
+ * Same arguments, ownership and errors as sla_attention_bwd; a failed
+ * hipEventRecord gives SLA_ERR_DEVICE. */
+sla_status sla_attention_bwd_timed(const void *q, const void *k, const void *v,
+                                   const void *dout, int B, int H, int N, int d,
+                                   int block, double keep, int phi, void *dq,
+                                   void *dk, void *dv, int grad_dtype, void *ws,
+                                   size_t ws_bytes, void *stream,
+                                   void *const *stage_events);
+
 /* Integer Q.K^T tiles from the attention kernel's INT8 matrix-core path, for
  * checking accumulators bit for bit.  pairs: int32 [n_pairs,4] device array
  * of (b, h, query block i, key block j); acc: int32 [n_pairs,64,64],

@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.sla_attention_fwd_timed.restype = c_int
     lib.sla_attention_bwd.argtypes = [c_void_p] * 4 + [c_int] * 5 + [c_double, c_int] + [c_void_p] * 3 + [c_int, c_void_p, c_size_t, c_void_p]
     lib.sla_attention_bwd.restype = c_int
+    lib.sla_attention_bwd_timed.argtypes = lib.sla_attention_bwd.argtypes + [c_void_p]
+    lib.sla_attention_bwd_timed.restype = c_int
     lib.sla_debug_qk_i32.argtypes = [c_void_p, c_void_p] + [c_int] * 5 + [c_void_p, c_int, c_void_p, c_void_p]
     lib.sla_debug_qk_i32.restype = c_int
     lib.sla_status_string.argtypes = [c_int]

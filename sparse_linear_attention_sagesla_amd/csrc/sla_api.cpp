@@ -337,10 +337,10 @@ sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B,
                                  ws, ws_bytes, stream, nullptr);
 }
 
-sla_status sla_attention_bwd(const void* q, const void* k, const void* v, const void* dout,
-                             int B, int H, int N, int d, int block, double keep, int phi,
-                             void* dq, void* dk, void* dv, int grad_dtype, void* ws,
-                             size_t ws_bytes, void* stream) {
+sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, const void* dout,
+                                   int B, int H, int N, int d, int block, double keep, int phi,
+                                   void* dq, void* dk, void* dv, int grad_dtype, void* ws,
+                                   size_t ws_bytes, void* stream, void* const* stage_events) {
   sla_status st = check_shape(B, H, N, d, block);
   if (st != SLA_OK) return st;
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return SLA_ERR_INVALID_ARG;
@@ -372,7 +372,12 @@ sla_status sla_attention_bwd(const void* q, const void* k, const void* v, const 
   auto run = [&](auto&& launch) {
     if (e == hipSuccess) e = launch();
   };
+  auto mark = [&](int id, int end) {
+    if (e == hipSuccess && stage_events && stage_events[2 * id + end])
+      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + end]), hs);
+  };
   // the forward's staging: codes, selection, walk schedule, linear state
+  mark(SLA_BWD_STAGE_FWD_STAGING, 0);
   if (kk > 0) {
     run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs); });
     run([&] { return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, nullptr, hs); });
@@ -387,14 +392,37 @@ sla_status sla_attention_bwd(const void* q, const void* k, const void* v, const 
     run([&] {
       return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs, bw.hb);
     });
+  mark(SLA_BWD_STAGE_FWD_STAGING, 1);
   // the backward's own staging
+  mark(SLA_BWD_STAGE_TRANSPOSE, 0);
   run([&] { return sla::launch_transpose_blocks(kk > 0 ? kb : nullptr, kk > 0 ? qb : nullptr, gb, s,
                                                 bw.kt, bw.qt, bw.dot, hs); });
-  if (kk > 0) run([&] { return sla::launch_column_lists(w.idx, s, bw.maskT, bw.coff, bw.cidx, hs); });
+  mark(SLA_BWD_STAGE_TRANSPOSE, 1);
+  if (kk > 0) {
+    mark(SLA_BWD_STAGE_COLUMNS, 0);
+    run([&] { return sla::launch_column_lists(w.idx, s, bw.maskT, bw.coff, bw.cidx, hs); });
+    mark(SLA_BWD_STAGE_COLUMNS, 1);
+  }
+  mark(SLA_BWD_STAGE_QUERY, 0);
   run([&] { return sla::launch_bwd_q(qb, vb, gb, w, bw, s, phi_eff, dq, f32, hs); });
-  if (phi_eff != SLA_PHI_NONE) run([&] { return sla::launch_grad_h(bw, s, hs); });
+  mark(SLA_BWD_STAGE_QUERY, 1);
+  if (phi_eff != SLA_PHI_NONE) {
+    mark(SLA_BWD_STAGE_GRAD_H, 0);
+    run([&] { return sla::launch_grad_h(bw, s, hs); });
+    mark(SLA_BWD_STAGE_GRAD_H, 1);
+  }
+  mark(SLA_BWD_STAGE_KEY, 0);
   run([&] { return sla::launch_bwd_kv(kb, vb, gb, w, bw, s, phi_eff, dk, dv, f32, hs); });
+  mark(SLA_BWD_STAGE_KEY, 1);
   return device_status(e);
+}
+
+sla_status sla_attention_bwd(const void* q, const void* k, const void* v, const void* dout,
+                             int B, int H, int N, int d, int block, double keep, int phi,
+                             void* dq, void* dk, void* dv, int grad_dtype, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return sla_attention_bwd_timed(q, k, v, dout, B, H, N, d, block, keep, phi, dq, dk, dv,
+                                 grad_dtype, ws, ws_bytes, stream, nullptr);
 }
 
 sla_status sla_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
