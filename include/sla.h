@@ -250,6 +250,51 @@ sla_status sla_attention_bwd_timed(const void *q, const void *k, const void *v,
                                    size_t ws_bytes, void *stream,
                                    void *const *stage_events);
 
+/* ---- W8A8 INT8 linear layers and FusedNorm ----------------------------------
+ * Weights and activations of the linear layers quantised to 8 bits for the
+ * INT8 units (news summary, opening component list; commentary, section
+ * "步数蒸馏与W8A8量化"), with a fused normalisation in front of them (blog,
+ * section "1. 计算资源优化：CPU Offload与混合精度计算").  The quantiser is the one
+ * of sla_quantize_qk applied per row: a = max|x| over the row, scale =
+ * fp32(a/127), code = clamp(rint_half_even(fp32(x * fp32(127/a))), +-127),
+ * a == 0 giving scale 0 and zero codes.  Row lengths K: multiples of 64,
+ * 64 <= K <= 16384.  All pointers are device pointers, 16-byte aligned; work
+ * is enqueued on `stream`; no workspace. */
+
+/* Per-row INT8 codes of a bf16 [rows, K] matrix: a weight matrix [N, K] per
+ * output channel, or activations [M, K] per token.
+ *   x      bf16 [rows, K]                                            (in)
+ *   codes  int8 [rows, K]; scale fp32 [rows]                         (out) */
+sla_status sla_rowquant_i8(const void *x, int rows, int K, int8_t *codes,
+                           float *scale, void *stream);
+
+/* FusedNorm: LayerNorm of every row of x, an optional per-channel affine
+ * (which also expresses adaptive-norm modulation: gamma = 1 + scale, beta =
+ * shift), then the per-row INT8 codes of the result, in one pass.
+ *   mu = fp32(sum(x)/K) with the sum in fp64; var = sum((x - mu)^2)/K in fp64;
+ *   rstd = fp32(1/sqrt(var + eps)); then in fp32, in this order:
+ *   y = x - mu; y = y * rstd; y = y * gamma[k]; y = y + beta[k].
+ *   x            bf16 [rows, K]                                      (in)
+ *   gamma, beta  fp32 [K] each, or NULL (omitted step)               (in)
+ *   eps          > 0 (Wan's LayerNorm uses 1e-6)
+ *   codes int8 [rows, K], scale fp32 [rows]                          (out)
+ *   mean, rstd   fp32 [rows] each, or NULL                           (out) */
+sla_status sla_fused_norm_i8(const void *x, int rows, int K, const float *gamma,
+                             const float *beta, float eps, int8_t *codes,
+                             float *scale, float *mean, float *rstd,
+                             void *stream);
+
+/* W8A8 linear layer: y[m][n] = (sum_k x8[m][k] * w8[n][k]) * x_scale[m] *
+ * w_scale[n] + bias[n], the integer sum exact (int32), the rest fp32.
+ *   x8 int8 [M, K], x_scale fp32 [M]; w8 int8 [N, K], w_scale fp32 [N] (in)
+ *   bias fp32 [N] or NULL                                             (in)
+ *   y [M, N], bf16 (round to nearest even) or fp32 per out_dtype       (out)
+ * N must be a multiple of 4; M * K and N * K below 2^31. */
+sla_status sla_w8a8_linear(const int8_t *x8, const float *x_scale,
+                           const int8_t *w8, const float *w_scale,
+                           const float *bias, int M, int N, int K, void *y,
+                           int out_dtype, void *stream);
+
 /* Integer Q.K^T tiles from the attention kernel's INT8 matrix-core path, for
  * checking accumulators bit for bit.  pairs: int32 [n_pairs,4] device array
  * of (b, h, query block i, key block j); acc: int32 [n_pairs,64,64],

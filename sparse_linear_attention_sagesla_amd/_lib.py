@@ -55,6 +55,13 @@ def load() -> ctypes.CDLL:
     lib.sla_attention_bwd.restype = c_int
     lib.sla_attention_bwd_timed.argtypes = lib.sla_attention_bwd.argtypes + [c_void_p]
     lib.sla_attention_bwd_timed.restype = c_int
+    lib.sla_rowquant_i8.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
+    lib.sla_rowquant_i8.restype = c_int
+    lib.sla_fused_norm_i8.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, ctypes.c_float,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.sla_fused_norm_i8.restype = c_int
+    lib.sla_w8a8_linear.argtypes = [c_void_p] * 5 + [c_int] * 3 + [c_void_p, c_int, c_void_p]
+    lib.sla_w8a8_linear.restype = c_int
     lib.sla_debug_qk_i32.argtypes = [c_void_p, c_void_p] + [c_int] * 5 + [c_void_p, c_int, c_void_p, c_void_p]
     lib.sla_debug_qk_i32.restype = c_int
     lib.sla_status_string.argtypes = [c_int]
@@ -193,6 +200,67 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch
                                     1 if grad_dtype == torch.float32 else 0, _ptr(ws), ws.numel(),
                                     _stream(dev)), "sla_attention_bwd")
     return dq, dk, dv
+
+
+def _rows2d(x: torch.Tensor, name: str, dtype=torch.bfloat16):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or not x.is_cuda or x.dtype != dtype:
+        raise ValueError(f"{name} must be a 2-D {dtype} GPU tensor")
+    return x.contiguous()
+
+
+def _vec(x, n: int, name: str):
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.numel() != n or not x.is_cuda:
+        raise ValueError(f"{name} must be a float32 GPU tensor of {n} elements")
+    return x.contiguous()
+
+
+def rowquant_i8(x: torch.Tensor):
+    """Per-row INT8 codes and scales of a bf16 [rows, K] matrix: (codes, scale)."""
+    x = _rows2d(x, "x")
+    rows, K = x.shape
+    codes = torch.empty(rows, K, dtype=torch.int8, device=x.device)
+    scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(load().sla_rowquant_i8(_ptr(x), rows, K, _ptr(codes), _ptr(scale), _stream(x.device)),
+           "sla_rowquant_i8")
+    return codes, scale
+
+
+def fused_norm_i8(x: torch.Tensor, gamma=None, beta=None, eps: float = 1e-6):
+    """FusedNorm: LayerNorm (+ per-channel affine) then per-row INT8:
+    (codes, scale, mean, rstd)."""
+    x = _rows2d(x, "x")
+    rows, K = x.shape
+    gamma, beta = _vec(gamma, K, "gamma"), _vec(beta, K, "beta")
+    dev = x.device
+    codes = torch.empty(rows, K, dtype=torch.int8, device=dev)
+    scale, mean, rstd = (torch.empty(rows, dtype=torch.float32, device=dev) for _ in range(3))
+    _check(load().sla_fused_norm_i8(_ptr(x), rows, K, _ptr(gamma), _ptr(beta), float(eps),
+                                    _ptr(codes), _ptr(scale), _ptr(mean), _ptr(rstd),
+                                    _stream(dev)), "sla_fused_norm_i8")
+    return codes, scale, mean, rstd
+
+
+def w8a8_linear(x8: torch.Tensor, x_scale: torch.Tensor, w8: torch.Tensor, w_scale: torch.Tensor,
+                bias=None, out_dtype=torch.bfloat16, out=None):
+    """y = (x8 w8^T) * x_scale[:, None] * w_scale[None, :] + bias, [M, N]."""
+    x8, w8 = _rows2d(x8, "x8", torch.int8), _rows2d(w8, "w8", torch.int8)
+    M, K = x8.shape
+    N, K2 = w8.shape
+    if K2 != K:
+        raise ValueError("x8 and w8 must have the same K")
+    x_scale, w_scale, bias = _vec(x_scale, M, "x_scale"), _vec(w_scale, N, "w_scale"), _vec(bias, N, "bias")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=x8.device)
+    elif out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor of out_dtype")
+    _check(load().sla_w8a8_linear(_ptr(x8), _ptr(x_scale), _ptr(w8), _ptr(w_scale), _ptr(bias), M, N,
+                                  K, _ptr(out), 1 if out_dtype == torch.float32 else 0,
+                                  _stream(x8.device)), "sla_w8a8_linear")
+    return out
 
 
 def debug_qk_i32(q8: torch.Tensor, k8: torch.Tensor, N: int, pairs: torch.Tensor):

@@ -425,6 +425,43 @@ sla_status sla_attention_bwd(const void* q, const void* k, const void* v, const 
                                  grad_dtype, ws, ws_bytes, stream, nullptr);
 }
 
+sla_status sla_rowquant_i8(const void* x, int rows, int K, int8_t* codes, float* scale,
+                           void* stream) {
+  if (!x || !codes || !scale || rows < 1) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes)) return SLA_ERR_INVALID_ARG;
+  if (K < 64 || K > sla::kMaxRowK || K % 64 != 0) return SLA_ERR_UNSUPPORTED;
+  return device_status(sla::launch_rowquant(static_cast<const uint16_t*>(x), rows, K, false, nullptr,
+                                            nullptr, 0.0f, codes, scale, nullptr, nullptr,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+sla_status sla_fused_norm_i8(const void* x, int rows, int K, const float* gamma, const float* beta,
+                             float eps, int8_t* codes, float* scale, float* mean, float* rstd,
+                             void* stream) {
+  if (!x || !codes || !scale || rows < 1) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes)) return SLA_ERR_INVALID_ARG;
+  if (!(eps > 0.0f) || std::isinf(eps)) return SLA_ERR_INVALID_ARG;
+  if (K < 64 || K > sla::kMaxRowK || K % 64 != 0) return SLA_ERR_UNSUPPORTED;
+  return device_status(sla::launch_rowquant(static_cast<const uint16_t*>(x), rows, K, true, gamma,
+                                            beta, eps, codes, scale, mean, rstd,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+sla_status sla_w8a8_linear(const int8_t* x8, const float* x_scale, const int8_t* w8,
+                           const float* w_scale, const float* bias, int M, int N, int K, void* y,
+                           int out_dtype, void* stream) {
+  if (!x8 || !x_scale || !w8 || !w_scale || !y || M < 1 || N < 1) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(x8) || !aligned16(w8) || !aligned16(w_scale) || !aligned16(y) ||
+      (bias && !aligned16(bias)))
+    return SLA_ERR_INVALID_ARG;
+  if (out_dtype != SLA_OUT_BF16 && out_dtype != SLA_OUT_F32) return SLA_ERR_INVALID_ARG;
+  if (K < 64 || K > sla::kMaxRowK || K % 64 != 0 || N % 4 != 0) return SLA_ERR_UNSUPPORTED;
+  if ((long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return SLA_ERR_UNSUPPORTED;
+  return device_status(sla::launch_w8a8_gemm(x8, x_scale, w8, w_scale, bias, M, N, K, y,
+                                             out_dtype == SLA_OUT_F32 ? 1 : 0,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 sla_status sla_debug_qk_i32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
                             int block, const int32_t* pairs, int n_pairs, int32_t* acc,
                             void* stream) {
@@ -449,6 +486,6 @@ const char* sla_status_string(int status) {
   }
 }
 
-int sla_version(void) { return 10200; }
+int sla_version(void) { return 10300; }
 
 }  // extern "C"

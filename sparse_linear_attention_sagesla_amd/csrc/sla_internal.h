@@ -14,6 +14,7 @@ constexpr int kLinChunks = 24;  // key-block chunks per head in the linear-state
 constexpr int kMaxTokens = 1 << 20;  // largest N the entry points accept
 constexpr int kGroup = 4;            // query blocks whose key-block walks are aligned
 constexpr float kPhiScale = 0.0625f;  // phi(Q), phi(K) are staged in fp16 as phi/16
+constexpr int kMaxRowK = 16384;       // longest row of the W8A8 quantisers
 
 enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiRelu = 2 };
 
@@ -110,6 +111,14 @@ hipError_t launch_grad_h(const BwdWorkspace& bw, const Shape& sh, hipStream_t s)
 hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                          const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
                          void* dk, void* dv, int grad_f32, hipStream_t s);
+// W8A8: per-row INT8 codes of a bf16 [rows, K] matrix, LayerNorm-ed first
+// (and scaled/shifted per channel) when norm is set; and the INT8 GEMM.
+hipError_t launch_rowquant(const uint16_t* x, int rows, int K, bool norm, const float* gamma,
+                           const float* beta, float eps, int8_t* codes, float* scale, float* mu,
+                           float* rstd, hipStream_t s);
+hipError_t launch_w8a8_gemm(const int8_t* x8, const float* sx, const int8_t* w8, const float* sw,
+                            const float* bias, int M, int N, int K, void* y, int out_f32,
+                            hipStream_t s);
 hipError_t launch_debug_qk(const int8_t* q8, const int8_t* k8, const Shape& sh,
                            const int32_t* pairs, int n_pairs, int32_t* acc, hipStream_t s);
 

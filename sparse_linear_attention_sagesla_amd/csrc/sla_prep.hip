@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "sla_internal.h"
+#include "sla_quant.h"
 
 namespace sla {
 namespace {
@@ -19,56 +20,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
-
-// 8 consecutive bf16 values packed in a uint4 -> 8 floats.
-__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* x) {
-  x[0] = __uint_as_float(u.x << 16);
-  x[1] = __uint_as_float(u.x & 0xffff0000u);
-  x[2] = __uint_as_float(u.y << 16);
-  x[3] = __uint_as_float(u.y & 0xffff0000u);
-  x[4] = __uint_as_float(u.z << 16);
-  x[5] = __uint_as_float(u.z & 0xffff0000u);
-  x[6] = __uint_as_float(u.w << 16);
-  x[7] = __uint_as_float(u.w & 0xffff0000u);
-}
-
 __device__ __forceinline__ float phi_apply(float x, int phi) {
   if (phi == kPhiElu1) return x > 0.0f ? x + 1.0f : __expf(x);
   return fmaxf(x, 0.0f);
-}
-
-// INT8 coding of a block with a = max|x| over its valid rows: scale = a/127
-// and inv = 127/a (IEEE fp32 divisions), or 0 and 0 for an all-zero block.
-// Returns whether the block has codes (a > 0).
-__device__ __forceinline__ bool code_scale(float a, float& scale, float& inv) {
-  scale = 0.0f;
-  inv = 0.0f;
-  if (a > 0.0f) {
-    scale = a / 127.0f;
-    inv = 127.0f / a;
-  }
-  return a > 0.0f;
-}
-
-// Codes of 8 consecutive channels of one row: clamp(rint(x * inv), +-127),
-// little-endian bytes; 0 unless `live` (a valid row of a block with a > 0).
-// The one coding routine of the statistics pass (Q), the quantiser and the
-// staging pass (K).
-__device__ __forceinline__ uint2 code_row8(const float* x, float inv, bool live) {
-  uint32_t w[2] = {0u, 0u};
-  if (live) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float y = rintf(x[e] * inv);
-      y = fminf(fmaxf(y, -127.0f), 127.0f);
-      const uint32_t b = (uint32_t)(int32_t)y & 0xffu;
-      w[e >> 2] |= b << (8 * (e & 3));
-    }
-  }
-  return make_uint2(w[0], w[1]);
 }
 
 // ---------------------------------------------------------------------------

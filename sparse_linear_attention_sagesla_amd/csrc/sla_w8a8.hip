@@ -1,0 +1,346 @@
+// W8A8 INT8 linear layers and FusedNorm for gfx950 (CDNA4).
+//
+// Weights and activations are quantised to 8 bits to run the linear layers on
+// the INT8 units (news summary, opening component list; commentary, section
+// "步数蒸馏与W8A8量化"), with a fused normalisation operator in front
+// (blog, section "1. 计算资源优化：CPU Offload与混合精度计算").
+//
+//   rowquant_kernel<norm>  one workgroup per row: per-row INT8 codes and scale of
+//                          a bf16 matrix (weights per output channel, or plain
+//                          activations per token); with `norm`, the row is first
+//                          LayerNorm-ed (fp64 mean and variance, fp32 steps as
+//                          fixed below) and optionally scaled and shifted per
+//                          channel (the FusedNorm).
+//   w8a8_gemm_kernel       y[m][n] = (sum_k x8[m][k] w8[n][k]) * sx[m] * sw[n] + b[n]:
+//                          256 x 256 output tile per workgroup (four waves of
+//                          128 x 128), K in steps of 64 through three LDS stages
+//                          filled by direct global->LDS loads, 32x32x32 INT8
+//                          MFMA with int32 accumulation, XCD-grouped tile order.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+
+#include "sla_internal.h"
+#include "sla_quant.h"
+
+namespace sla {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+
+constexpr int kRowThreads = 256;
+constexpr int kRowChunks = kMaxRowK / (8 * kRowThreads);  // 8-value chunks per thread
+
+// ---------------------------------------------------------------------------
+// Per-row quantiser / FusedNorm.  Thread t holds the 8-value chunks
+// 8 (t + 256 c) .. + 7 of the row (c < kRowChunks).
+// LayerNorm: mu = fp32(sum_k x / K) with the sum in fp64; var = (sum_k
+// (x - mu)^2) / K in fp64 (x - mu exact in fp64); rstd = fp32(1 / sqrt(var +
+// eps)) in fp64; then, in fp32 and in this order, t = x - mu, t = t * rstd,
+// t = t * gamma, t = t + beta (gamma, beta optional).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int t = threadIdx.x;
+  __syncthreads();
+  if ((t & 63) == 0) red[t >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <bool kNorm>
+__global__ __launch_bounds__(kRowThreads) void rowquant_kernel(
+    const uint16_t* __restrict__ x, int K, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float eps, int8_t* __restrict__ codes,
+    float* __restrict__ scale, float* __restrict__ mu_out, float* __restrict__ rstd_out) {
+  __shared__ double red[4];
+  __shared__ float redf[4];
+  const int t = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const uint16_t* xr = x + row * (size_t)K;
+  float v[kRowChunks][8];
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int k0 = 8 * (t + kRowThreads * c);
+    if (k0 < K) {
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(xr + k0), v[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
+    }
+  }
+  if (kNorm) {
+    double s = 0.0;
+#pragma unroll
+    for (int c = 0; c < kRowChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += (double)v[c][e];
+    const float mu = (float)(block_sum_f64(s, red) / (double)K);
+    double q = 0.0;
+#pragma unroll
+    for (int c = 0; c < kRowChunks; ++c) {
+      if (8 * (t + kRowThreads * c) < K) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double d = (double)v[c][e] - (double)mu;
+          q += d * d;
+        }
+      }
+    }
+    const double var = block_sum_f64(q, red) / (double)K;
+    const float rstd = (float)(1.0 / sqrt(var + (double)eps));
+#pragma unroll
+    for (int c = 0; c < kRowChunks; ++c) {
+      const int k0 = 8 * (t + kRowThreads * c);
+      if (k0 < K) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float y = v[c][e] - mu;
+          y = y * rstd;
+          if (gamma) y = y * gamma[k0 + e];
+          if (beta) y = y + beta[k0 + e];
+          v[c][e] = y;
+        }
+      }
+    }
+    if (t == 0) {
+      if (mu_out) mu_out[row] = mu;
+      if (rstd_out) rstd_out[row] = rstd;
+    }
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[c][e]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  if ((t & 63) == 0) redf[t >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+  float sc, inv;
+  const bool live = code_scale(a, sc, inv);
+  int8_t* cr = codes + row * (size_t)K;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int k0 = 8 * (t + kRowThreads * c);
+    if (k0 < K) *reinterpret_cast<uint2*>(cr + k0) = code_row8(v[c], inv, live);
+  }
+  if (t == 0) scale[row] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// INT8 GEMM.  C tile [n][m] = W8 rows (A operand) x X8 rows (B operand): the
+// 32x32 accumulator of a lane holds column m = lane & 31 and rows
+// n = 8j + 4 (lane >> 5) + i (j, i < 4), i.e. four consecutive output
+// channels of one token, stored as one 8- or 16-byte write.
+// LDS stage: A rows (256 x 64 bytes), then B rows; 16-byte chunk c of row r
+// kept at c ^ ((r >> 2) & 3), so the 16 rows a quarter-wave reads at one chunk
+// cover all 64 banks.
+// ---------------------------------------------------------------------------
+constexpr int kGT = 256;                 // output tile edge (n and m)
+constexpr int kGK = 64;                  // K per stage
+constexpr int kGStageHalf = kGT * kGK;   // 16 KB: one operand's stage
+constexpr int kGStage = 2 * kGStageHalf; // 32 KB
+constexpr int kGStages = 3;
+constexpr int kGLoads = 8;               // LDS-direct loads per wave per stage
+constexpr int kGroupM = 8;               // m tiles per group of the tile order
+
+struct GemmArgs {
+  const int8_t* x8;   // [M, K]
+  const float* sx;    // [M]
+  const int8_t* w8;   // [N, K]
+  const float* sw;    // [N]
+  const float* bias;  // [N] or null
+  void* y;            // [M, N] bf16 or fp32
+  int M, N, K;
+  int Mt, Nt;         // tile counts
+  int per_xcd;        // tiles per XCD slot range
+  int out_f32;
+};
+
+__device__ __forceinline__ void gemm_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, lds_byte* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)dst, 16, voff,
+                                           soff, 0, 0);
+}
+
+__device__ __forceinline__ void gemm_wait_older() {
+  // at most kGLoads loads of this wave in flight: the stage before the last
+  // issued one has landed (vmcnt in bits 3:0; expcnt, lgkmcnt at maxima)
+  __builtin_amdgcn_s_waitcnt(kGLoads | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void gemm_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_byte* smem = (lds_byte*)smem_raw;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  // XCD-grouped tile order: workgroup x runs on XCD x % 8; each XCD takes a
+  // contiguous range of the grouped order (kGroupM m tiles x all n tiles,
+  // m fastest), so the tiles it runs together share operand rows in its L2
+  const int x = blockIdx.x;
+  const int tid = (x & 7) * a.per_xcd + (x >> 3);
+  if (tid >= a.Mt * a.Nt) return;
+  const int group = tid / (kGroupM * a.Nt);
+  const int first_m = group * kGroupM;
+  const int gsize = min(a.Mt - first_m, kGroupM);
+  const int in_group = tid % (kGroupM * a.Nt);
+  const int mt = first_m + in_group % gsize;
+  const int nt = in_group / gsize;
+  const int m0 = mt * kGT, n0 = nt * kGT;
+
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(a.w8 + (size_t)n0 * a.K), 0, (int)min((size_t)(a.N - n0) * a.K, (size_t)0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(a.x8 + (size_t)m0 * a.K), 0, (int)min((size_t)(a.M - m0) * a.K, (size_t)0x7fffffff), 0x00020000);
+  // this lane's load offsets: instruction i of wave w fills rows 16(4w + i) +
+  // lane/4, stored chunk lane % 4, fetched chunk (lane % 4) ^ ((lane >> 4) & 3)
+  const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (16 * (4 * wave + i) + (lane >> 2)) * a.K + 16 * chunk;
+  auto issue = [&](lds_byte* st, int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gemm_load(rw, voff[i], k0, st + 1024 * (4 * wave + i));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gemm_load(rx, voff[i], k0, st + kGStageHalf + 1024 * (4 * wave + i));
+  };
+
+  // wave w: output rows n in [128 (w & 1), +128), columns m in [128 (w >> 1), +128)
+  const int wn = 128 * (wave & 1), wm = 128 * (wave >> 1);
+  const int r32 = lane & 31, khalf = lane >> 5;
+  v16i acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+
+  auto compute = [&](const lds_byte* st) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = khalf + 2 * kk;
+      v4i af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rn = wn + 32 * i + r32;
+        af[i] = *(lds_v4i*)(st + rn * kGK + ((c ^ ((rn >> 2) & 3)) << 4));
+        const int rm = wm + 32 * i + r32;
+        bf[i] = *(lds_v4i*)(st + kGStageHalf + rm * kGK + ((c ^ ((rm >> 2) & 3)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int steps = a.K / kGK;
+  issue(smem, 0);
+  if (steps > 1) issue(smem + kGStage, kGK);
+  // unrolled by the stage count so every stage address is a constant offset
+  for (int p0 = 0; p0 < steps; p0 += kGStages) {
+#pragma unroll
+    for (int ph = 0; ph < kGStages; ++ph) {
+      const int p = p0 + ph;
+      if (p < steps) {
+        if (p + 1 < steps)
+          gemm_wait_older();
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        gemm_barrier();  // stage p is in; every wave is done with stage p-1
+        if (p + 2 < steps) issue(smem + ((ph + 2) % kGStages) * kGStage, (p + 2) * kGK);
+        compute(smem + ph * kGStage);
+      }
+    }
+  }
+
+  // epilogue: y = acc * sx[m] * sw[n] + bias[n]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm + 32 * j + r32;
+    if (m >= a.M) continue;
+    const float sxm = a.sx[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn + 32 * i + 8 * q + 4 * khalf;
+        if (n >= a.N) continue;
+        const v4f swv = *reinterpret_cast<const v4f*>(a.sw + n);
+        v4f yv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yv[e] = (float)acc[i][j][4 * q + e] * sxm * swv[e];
+        if (a.bias) yv += *reinterpret_cast<const v4f*>(a.bias + n);
+        const size_t off = (size_t)m * a.N + n;
+        if (a.out_f32) {
+          *reinterpret_cast<v4f*>(reinterpret_cast<float*>(a.y) + off) = yv;
+        } else {
+          uint32_t w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t b0 = __float_as_uint(yv[2 * h]);
+            const uint32_t b1 = __float_as_uint(yv[2 * h + 1]);
+            const uint32_t r0 = (b0 + 0x7fffu + ((b0 >> 16) & 1u)) >> 16;
+            const uint32_t r1 = (b1 + 0x7fffu + ((b1 >> 16) & 1u)) >> 16;
+            w[h] = r0 | (r1 << 16);
+          }
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + off) = make_uint2(w[0], w[1]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rowquant(const uint16_t* x, int rows, int K, bool norm, const float* gamma,
+                           const float* beta, float eps, int8_t* codes, float* scale, float* mu,
+                           float* rstd, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (norm)
+    rowquant_kernel<true><<<rows, kRowThreads, 0, s>>>(x, K, gamma, beta, eps, codes, scale, mu, rstd);
+  else
+    rowquant_kernel<false><<<rows, kRowThreads, 0, s>>>(x, K, nullptr, nullptr, 0.0f, codes, scale,
+                                                          nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_w8a8_gemm(const int8_t* x8, const float* sx, const int8_t* w8, const float* sw,
+                            const float* bias, int M, int N, int K, void* y, int out_f32,
+                            hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  GemmArgs a;
+  a.x8 = x8;
+  a.sx = sx;
+  a.w8 = w8;
+  a.sw = sw;
+  a.bias = bias;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.Mt = (M + kGT - 1) / kGT;
+  a.Nt = (N + kGT - 1) / kGT;
+  const int tiles = a.Mt * a.Nt;
+  a.per_xcd = (tiles + 7) / 8;
+  a.out_f32 = out_f32;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(w8a8_gemm_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGStages * kGStage);
+  });
+  w8a8_gemm_kernel<<<8 * a.per_xcd, 256, kGStages * kGStage, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sla
