@@ -213,6 +213,49 @@ def backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, fwd_ms, steps, stream, 
     return rec
 
 
+def w8a8_leg(sla, wl, steps, stream, dev):
+    """FusedNorm + W8A8 GEMM of the Wan-14B FFN up-projection at this
+    workload's token count: x [N, 5120] bf16 N(0,1), W [13824, 5120] bf16
+    N(0, 0.02^2) quantised per output channel once (untimed), then `steps`
+    timed FusedNorm calls and `steps` timed GEMM calls (bf16 output)."""
+    import torch
+    M, K, Nf = wl.N, 5120, 13824
+    g = torch.Generator(device=dev).manual_seed(11)
+    x = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(Nf, K, device=dev, generator=g)).to(torch.bfloat16)
+    w8, sw = sla.rowquant_i8(w)
+    x8, sx, _, _ = sla.fused_norm_i8(x)
+    y = torch.empty(M, Nf, dtype=torch.bfloat16, device=dev)
+    sla.w8a8_linear(x8, sx, w8, sw, out=y)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    norm_ms = timed(lambda: sla.fused_norm_i8(x))
+    gemm_ms = timed(lambda: sla.w8a8_linear(x8, sx, w8, sw, out=y))
+    ops = 2.0 * M * Nf * K
+    tops = ops / (gemm_ms * 1e-3) / 1e12
+    norm_bytes = M * K * 2 + M * K + M * 12
+    gbps = norm_bytes / (norm_ms * 1e-3) / 1e9
+    log(f"[bench] w8a8: FusedNorm {norm_ms:.3f} ms, GEMM {gemm_ms:.3f} ms ({tops:.0f} TOPS)")
+    return {"config": {"M": M, "K": K, "N": Nf, "layer": "Wan-14B FFN up-projection"},
+            "fused_norm_ms": round(norm_ms, 4), "gemm_ms": round(gemm_ms, 4),
+            "gemm_roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_I8_OPS / 1e12,
+                              "unit": "TOP/s", "frac": round(tops / (PEAK_I8_OPS / 1e12), 4),
+                              "kernel": "w8a8_gemm_kernel"},
+            "fused_norm_roofline": {"bound": "hbm", "achieved": round(gbps, 1),
+                                    "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                    "frac": round(gbps * 1e9 / PEAK_HBM, 4),
+                                    "kernel": "rowquant_kernel<true>"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +267,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3,
                     help="also time this many sla_attention_bwd calls (0: skip)")
+    ap.add_argument("--w8a8-steps", type=int, default=5,
+                    help="also time this many FusedNorm + W8A8 GEMM calls at the Wan-14B "
+                         "FFN shape (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale "
                          "hardware byte counters against a kernel of known traffic")
@@ -366,6 +412,8 @@ def main():
     if args.backward_steps > 0:
         rec["backward"] = backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, ms_step,
                                        args.backward_steps, stream, dev)
+    if args.w8a8_steps > 0:
+        rec["w8a8"] = w8a8_leg(sla, wl, args.w8a8_steps, stream, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(Q, K, V, wl, keep, phi)

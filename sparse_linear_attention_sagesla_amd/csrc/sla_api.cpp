@@ -439,7 +439,8 @@ sla_status sla_fused_norm_i8(const void* x, int rows, int K, const float* gamma,
                              float eps, int8_t* codes, float* scale, float* mean, float* rstd,
                              void* stream) {
   if (!x || !codes || !scale || rows < 1) return SLA_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(codes)) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
+    return SLA_ERR_INVALID_ARG;
   if (!(eps > 0.0f) || std::isinf(eps)) return SLA_ERR_INVALID_ARG;
   if (K < 64 || K > sla::kMaxRowK || K % 64 != 0) return SLA_ERR_UNSUPPORTED;
   return device_status(sla::launch_rowquant(static_cast<const uint16_t*>(x), rows, K, true, gamma,

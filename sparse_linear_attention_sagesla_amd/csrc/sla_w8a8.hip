@@ -5,15 +5,15 @@
 // "步数蒸馏与W8A8量化"), with a fused normalisation operator in front
 // (blog, section "1. 计算资源优化：CPU Offload与混合精度计算").
 //
-//   rowquant_kernel<norm>  one workgroup per row: per-row INT8 codes and scale of
+//   rowquant_kernel<norm>  one wave per row: per-row INT8 codes and scale of
 //                          a bf16 matrix (weights per output channel, or plain
 //                          activations per token); with `norm`, the row is first
 //                          LayerNorm-ed (fp64 mean and variance, fp32 steps as
 //                          fixed below) and optionally scaled and shifted per
 //                          channel (the FusedNorm).
 //   w8a8_gemm_kernel       y[m][n] = (sum_k x8[m][k] w8[n][k]) * sx[m] * sw[n] + b[n]:
-//                          256 x 256 output tile per workgroup (four waves of
-//                          128 x 128), K in steps of 64 through three LDS stages
+//                          256 x 256 output tile per workgroup (eight waves of
+//                          128 x 64, two per SIMD), K in steps of 64 through three LDS stages
 //                          filled by direct global->LDS loads, 32x32x32 INT8
 //                          MFMA with int32 accumulation, XCD-grouped tile order.
 #include <hip/hip_runtime.h>
@@ -33,106 +33,132 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 typedef __attribute__((address_space(3))) const v4i lds_v4i;
 
-constexpr int kRowThreads = 256;
-constexpr int kRowChunks = kMaxRowK / (8 * kRowThreads);  // 8-value chunks per thread
+constexpr int kRowWaves = 4;                   // rows per workgroup (one wave each)
+constexpr int kRowChunks = kMaxRowK / (8 * 64); // 8-value chunks per lane
 
 // ---------------------------------------------------------------------------
-// Per-row quantiser / FusedNorm.  Thread t holds the 8-value chunks
-// 8 (t + 256 c) .. + 7 of the row (c < kRowChunks).
+// Per-row quantiser / FusedNorm: one wave per row.  Lane l holds the 8-value
+// chunks 8 (l + 64 c) .. + 7 of the row as packed bf16 (c < K / 512) and
+// unpacks them in each pass: the sums, the normalised maximum, the codes.
 // LayerNorm: mu = fp32(sum_k x / K) with the sum in fp64; var = (sum_k
 // (x - mu)^2) / K in fp64 (x - mu exact in fp64); rstd = fp32(1 / sqrt(var +
 // eps)) in fp64; then, in fp32 and in this order, t = x - mu, t = t * rstd,
 // t = t * gamma, t = t + beta (gamma, beta optional).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+__device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  const int t = threadIdx.x;
-  __syncthreads();
-  if ((t & 63) == 0) red[t >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  return v;
 }
 
 template <bool kNorm>
-__global__ __launch_bounds__(kRowThreads) void rowquant_kernel(
-    const uint16_t* __restrict__ x, int K, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float eps, int8_t* __restrict__ codes,
-    float* __restrict__ scale, float* __restrict__ mu_out, float* __restrict__ rstd_out) {
-  __shared__ double red[4];
-  __shared__ float redf[4];
-  const int t = threadIdx.x;
-  const size_t row = blockIdx.x;
-  const uint16_t* xr = x + row * (size_t)K;
-  float v[kRowChunks][8];
+__device__ __forceinline__ void norm_chunk(const uint4& u, int k0, float mu, float rstd,
+                                           const float* __restrict__ gamma,
+                                           const float* __restrict__ beta, float* y) {
+  unpack_bf16x8(u, y);
+  if (kNorm) {
+    float g[8], b[8];
+    if (gamma) {
+      *reinterpret_cast<float4*>(g) = *reinterpret_cast<const float4*>(gamma + k0);
+      *reinterpret_cast<float4*>(g + 4) = *reinterpret_cast<const float4*>(gamma + k0 + 4);
+    }
+    if (beta) {
+      *reinterpret_cast<float4*>(b) = *reinterpret_cast<const float4*>(beta + k0);
+      *reinterpret_cast<float4*>(b + 4) = *reinterpret_cast<const float4*>(beta + k0 + 4);
+    }
 #pragma unroll
-  for (int c = 0; c < kRowChunks; ++c) {
-    const int k0 = 8 * (t + kRowThreads * c);
-    if (k0 < K) {
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(xr + k0), v[c]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) {
+      float t = y[e] - mu;
+      t = t * rstd;
+      if (gamma) t = t * g[e];
+      if (beta) t = t + b[e];
+      y[e] = t;
     }
   }
+}
+
+// Tells the compiler the packed row may have changed, so that each pass
+// unpacks it again instead of keeping every converted value alive across
+// passes (which does not fit in registers).
+__device__ __forceinline__ void launder(uint4 (&u)[kRowChunks]) {
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) asm volatile("" : "+v"(u[c].x), "+v"(u[c].y), "+v"(u[c].z), "+v"(u[c].w));
+}
+
+template <bool kNorm>
+__global__ __launch_bounds__(64 * kRowWaves) void rowquant_kernel(
+    const uint16_t* __restrict__ x, int rows, int K, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float eps, int8_t* __restrict__ codes,
+    float* __restrict__ scale, float* __restrict__ mu_out, float* __restrict__ rstd_out) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (row >= (size_t)rows) return;
+  const uint16_t* xr = x + row * (size_t)K;
+  uint4 u[kRowChunks];
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int k0 = 8 * (lane + 64 * c);
+    u[c] = k0 < K ? *reinterpret_cast<const uint4*>(xr + k0) : make_uint4(0, 0, 0, 0);
+  }
+  float mu = 0.0f, rstd = 1.0f;
   if (kNorm) {
     double s = 0.0;
 #pragma unroll
-    for (int c = 0; c < kRowChunks; ++c)
+    for (int c = 0; c < kRowChunks; ++c) {
+      float v[8];
+      unpack_bf16x8(u[c], v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += (double)v[c][e];
-    const float mu = (float)(block_sum_f64(s, red) / (double)K);
+      for (int e = 0; e < 8; ++e) s += (double)v[e];
+    }
+    mu = (float)(wave_sum_f64(s) / (double)K);
+    launder(u);
     double q = 0.0;
 #pragma unroll
     for (int c = 0; c < kRowChunks; ++c) {
-      if (8 * (t + kRowThreads * c) < K) {
+      if (8 * (lane + 64 * c) < K) {
+        float v[8];
+        unpack_bf16x8(u[c], v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const double d = (double)v[c][e] - (double)mu;
+          const double d = (double)v[e] - (double)mu;
           q += d * d;
         }
       }
     }
-    const double var = block_sum_f64(q, red) / (double)K;
-    const float rstd = (float)(1.0 / sqrt(var + (double)eps));
-#pragma unroll
-    for (int c = 0; c < kRowChunks; ++c) {
-      const int k0 = 8 * (t + kRowThreads * c);
-      if (k0 < K) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float y = v[c][e] - mu;
-          y = y * rstd;
-          if (gamma) y = y * gamma[k0 + e];
-          if (beta) y = y + beta[k0 + e];
-          v[c][e] = y;
-        }
-      }
-    }
-    if (t == 0) {
+    rstd = (float)(1.0 / sqrt(wave_sum_f64(q) / (double)K + (double)eps));
+    launder(u);
+    if (lane == 0) {
       if (mu_out) mu_out[row] = mu;
       if (rstd_out) rstd_out[row] = rstd;
     }
   }
   float a = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kRowChunks; ++c)
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int k0 = 8 * (lane + 64 * c);
+    if (k0 < K) {
+      float y[8];
+      norm_chunk<kNorm>(u[c], k0, mu, rstd, gamma, beta, y);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[c][e]));
+      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(y[e]));
+    }
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-  if ((t & 63) == 0) redf[t >> 6] = a;
-  __syncthreads();
-  a = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
   float sc, inv;
   const bool live = code_scale(a, sc, inv);
+  launder(u);
   int8_t* cr = codes + row * (size_t)K;
 #pragma unroll
   for (int c = 0; c < kRowChunks; ++c) {
-    const int k0 = 8 * (t + kRowThreads * c);
-    if (k0 < K) *reinterpret_cast<uint2*>(cr + k0) = code_row8(v[c], inv, live);
+    const int k0 = 8 * (lane + 64 * c);
+    if (k0 < K) {
+      float y[8];
+      norm_chunk<kNorm>(u[c], k0, mu, rstd, gamma, beta, y);
+      *reinterpret_cast<uint2*>(cr + k0) = code_row8(y, inv, live);
+    }
   }
-  if (t == 0) scale[row] = sc;
+  if (lane == 0) scale[row] = sc;
 }
 
 // ---------------------------------------------------------------------------
@@ -149,7 +175,8 @@ constexpr int kGK = 64;                  // K per stage
 constexpr int kGStageHalf = kGT * kGK;   // 16 KB: one operand's stage
 constexpr int kGStage = 2 * kGStageHalf; // 32 KB
 constexpr int kGStages = 3;
-constexpr int kGLoads = 8;               // LDS-direct loads per wave per stage
+constexpr int kGWaves = 8;               // two per SIMD
+constexpr int kGLoads = 4;               // LDS-direct loads per wave per stage
 constexpr int kGroupM = 8;               // m tiles per group of the tile order
 
 struct GemmArgs {
@@ -178,7 +205,7 @@ __device__ __forceinline__ void gemm_wait_older() {
 
 __device__ __forceinline__ void gemm_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   lds_byte* smem = (lds_byte*)smem_raw;
   const int t = threadIdx.x;
@@ -202,44 +229,47 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs a) {
       const_cast<int8_t*>(a.w8 + (size_t)n0 * a.K), 0, (int)min((size_t)(a.N - n0) * a.K, (size_t)0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(a.x8 + (size_t)m0 * a.K), 0, (int)min((size_t)(a.M - m0) * a.K, (size_t)0x7fffffff), 0x00020000);
-  // this lane's load offsets: instruction i of wave w fills rows 16(4w + i) +
+  // this lane's load offsets: instruction i of wave w fills rows 16(2w + i) +
   // lane/4, stored chunk lane % 4, fetched chunk (lane % 4) ^ ((lane >> 4) & 3)
   const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  int voff[4];
+  int voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = (16 * (4 * wave + i) + (lane >> 2)) * a.K + 16 * chunk;
+  for (int i = 0; i < 2; ++i) voff[i] = (16 * (2 * wave + i) + (lane >> 2)) * a.K + 16 * chunk;
   auto issue = [&](lds_byte* st, int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gemm_load(rw, voff[i], k0, st + 1024 * (4 * wave + i));
+    for (int i = 0; i < 2; ++i) gemm_load(rw, voff[i], k0, st + 1024 * (2 * wave + i));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gemm_load(rx, voff[i], k0, st + kGStageHalf + 1024 * (4 * wave + i));
+    for (int i = 0; i < 2; ++i) gemm_load(rx, voff[i], k0, st + kGStageHalf + 1024 * (2 * wave + i));
   };
 
-  // wave w: output rows n in [128 (w & 1), +128), columns m in [128 (w >> 1), +128)
-  const int wn = 128 * (wave & 1), wm = 128 * (wave >> 1);
+  // wave w: output rows n in [128 (w & 1), +128), columns m in [64 (w >> 1), +64)
+  const int wn = 128 * (wave & 1), wm = 64 * (wave >> 1);
   const int r32 = lane & 31, khalf = lane >> 5;
-  v16i acc[4][4];
+  v16i acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
 
   auto compute = [&](const lds_byte* st) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c = khalf + 2 * kk;
-      v4i af[4], bf[4];
+      v4i af[4], bf[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rn = wn + 32 * i + r32;
         af[i] = *(lds_v4i*)(st + rn * kGK + ((c ^ ((rn >> 2) & 3)) << 4));
-        const int rm = wm + 32 * i + r32;
-        bf[i] = *(lds_v4i*)(st + kGStageHalf + rm * kGK + ((c ^ ((rm >> 2) & 3)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rm = wm + 32 * j + r32;
+        bf[j] = *(lds_v4i*)(st + kGStageHalf + rm * kGK + ((c ^ ((rm >> 2) & 3)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   };
@@ -266,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(GemmArgs a) {
 
   // epilogue: y = acc * sx[m] * sw[n] + bias[n]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int m = m0 + wm + 32 * j + r32;
     if (m >= a.M) continue;
     const float sxm = a.sx[m];
@@ -307,11 +337,13 @@ hipError_t launch_rowquant(const uint16_t* x, int rows, int K, bool norm, const 
                            const float* beta, float eps, int8_t* codes, float* scale, float* mu,
                            float* rstd, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  const int blocks = (rows + kRowWaves - 1) / kRowWaves;
   if (norm)
-    rowquant_kernel<true><<<rows, kRowThreads, 0, s>>>(x, K, gamma, beta, eps, codes, scale, mu, rstd);
+    rowquant_kernel<true><<<blocks, 64 * kRowWaves, 0, s>>>(x, rows, K, gamma, beta, eps, codes, scale,
+                                                             mu, rstd);
   else
-    rowquant_kernel<false><<<rows, kRowThreads, 0, s>>>(x, K, nullptr, nullptr, 0.0f, codes, scale,
-                                                          nullptr, nullptr);
+    rowquant_kernel<false><<<blocks, 64 * kRowWaves, 0, s>>>(x, rows, K, nullptr, nullptr, 0.0f, codes,
+                                                              scale, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -339,7 +371,7 @@ hipError_t launch_w8a8_gemm(const int8_t* x8, const float* sx, const int8_t* w8,
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(w8a8_gemm_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kGStages * kGStage);
   });
-  w8a8_gemm_kernel<<<8 * a.per_xcd, 256, kGStages * kGStage, s>>>(a);
+  w8a8_gemm_kernel<<<8 * a.per_xcd, 64 * kGWaves, kGStages * kGStage, s>>>(a);
   return hipGetLastError();
 }
 

@@ -156,3 +156,29 @@ def test_backward_rejects_bad_arguments_before_launch():
     assert _bwd(grad_dtype=2) == INVALID
     assert _bwd(ws_bytes=4096) == WORKSPACE
     assert _bwd(ws=NULL, ws_bytes=1 << 40) == WORKSPACE
+
+
+def test_w8a8_entry_points_reject_bad_arguments():
+    L = lib()
+    assert L.sla_rowquant_i8(NULL, 4, 128, FAKE, FAKE, NULL) == INVALID
+    assert L.sla_rowquant_i8(FAKE, 0, 128, FAKE, FAKE, NULL) == INVALID
+    assert L.sla_rowquant_i8(MISALIGNED, 4, 128, FAKE, FAKE, NULL) == INVALID
+    for K in (0, 96, 16384 + 64):
+        assert L.sla_rowquant_i8(FAKE, 4, K, FAKE, FAKE, NULL) == UNSUPPORTED
+    assert L.sla_fused_norm_i8(FAKE, 4, 128, NULL, NULL, 0.0, FAKE, FAKE, NULL, NULL, NULL) == INVALID
+    assert L.sla_fused_norm_i8(FAKE, 4, 128, NULL, NULL, float("nan"), FAKE, FAKE, NULL, NULL, NULL) == INVALID
+    assert L.sla_fused_norm_i8(FAKE, 4, 100, NULL, NULL, 1e-6, FAKE, FAKE, NULL, NULL, NULL) == UNSUPPORTED
+    assert L.sla_fused_norm_i8(FAKE, 4, 128, NULL, NULL, 1e-6, NULL, FAKE, NULL, NULL, NULL) == INVALID
+    args = [FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 128, FAKE, 0, NULL]
+    bad = list(args); bad[0] = NULL
+    assert L.sla_w8a8_linear(*bad) == INVALID
+    bad = list(args); bad[6] = 6                      # N not a multiple of 4
+    assert L.sla_w8a8_linear(*bad) == UNSUPPORTED
+    bad = list(args); bad[7] = 100                    # K not a multiple of 64
+    assert L.sla_w8a8_linear(*bad) == UNSUPPORTED
+    bad = list(args); bad[9] = 3
+    assert L.sla_w8a8_linear(*bad) == INVALID
+    bad = list(args); bad[4] = MISALIGNED
+    assert L.sla_w8a8_linear(*bad) == INVALID
+    bad = list(args); bad[5] = 1 << 20; bad[7] = 4096  # M * K >= 2^31
+    assert L.sla_w8a8_linear(*bad) == UNSUPPORTED
