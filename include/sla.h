@@ -289,7 +289,8 @@ sla_status sla_fused_norm_i8(const void *x, int rows, int K, const float *gamma,
  *   x8 int8 [M, K], x_scale fp32 [M]; w8 int8 [N, K], w_scale fp32 [N] (in)
  *   bias fp32 [N] or NULL                                             (in)
  *   y [M, N], bf16 (round to nearest even) or fp32 per out_dtype       (out)
- * N must be a multiple of 4; M * K and N * K below 2^31. */
+ * K must be a multiple of 128 (128 <= K <= 16384) and N of 4; M * K and
+ * N * K below 2^31. */
 sla_status sla_w8a8_linear(const int8_t *x8, const float *x_scale,
                            const int8_t *w8, const float *w_scale,
                            const float *bias, int M, int N, int K, void *y,

@@ -456,7 +456,7 @@ sla_status sla_w8a8_linear(const int8_t* x8, const float* x_scale, const int8_t*
       (bias && !aligned16(bias)))
     return SLA_ERR_INVALID_ARG;
   if (out_dtype != SLA_OUT_BF16 && out_dtype != SLA_OUT_F32) return SLA_ERR_INVALID_ARG;
-  if (K < 64 || K > sla::kMaxRowK || K % 64 != 0 || N % 4 != 0) return SLA_ERR_UNSUPPORTED;
+  if (K < 128 || K > sla::kMaxRowK || K % 128 != 0 || N % 4 != 0) return SLA_ERR_UNSUPPORTED;
   if ((long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return SLA_ERR_UNSUPPORTED;
   return device_status(sla::launch_w8a8_gemm(x8, x_scale, w8, w_scale, bias, M, N, K, y,
                                              out_dtype == SLA_OUT_F32 ? 1 : 0,

@@ -13,7 +13,7 @@
 //                          channel (the FusedNorm).
 //   w8a8_gemm_kernel       y[m][n] = (sum_k x8[m][k] w8[n][k]) * sx[m] * sw[n] + b[n]:
 //                          256 x 256 output tile per workgroup (eight waves of
-//                          128 x 64, two per SIMD), K in steps of 64 through three LDS stages
+//                          128 x 64, two per SIMD), K in steps of 128 through two LDS stages
 //                          filled by direct global->LDS loads, 32x32x32 INT8
 //                          MFMA with int32 accumulation, XCD-grouped tile order.
 #include <hip/hip_runtime.h>
@@ -166,17 +166,16 @@ __global__ __launch_bounds__(64 * kRowWaves) void rowquant_kernel(
 // 32x32 accumulator of a lane holds column m = lane & 31 and rows
 // n = 8j + 4 (lane >> 5) + i (j, i < 4), i.e. four consecutive output
 // channels of one token, stored as one 8- or 16-byte write.
-// LDS stage: A rows (256 x 64 bytes), then B rows; 16-byte chunk c of row r
-// kept at c ^ ((r >> 2) & 3), so the 16 rows a quarter-wave reads at one chunk
+// LDS stage: A rows (256 x 128 bytes), then B rows; 16-byte chunk c of row r
+// kept at c ^ ((r >> 1) & 7), so the 16 rows a quarter-wave reads at one chunk
 // cover all 64 banks.
 // ---------------------------------------------------------------------------
 constexpr int kGT = 256;                 // output tile edge (n and m)
-constexpr int kGK = 64;                  // K per stage
-constexpr int kGStageHalf = kGT * kGK;   // 16 KB: one operand's stage
-constexpr int kGStage = 2 * kGStageHalf; // 32 KB
-constexpr int kGStages = 3;
+constexpr int kGK = 128;                 // K per stage
+constexpr int kGStageHalf = kGT * kGK;   // 32 KB: one operand's stage
+constexpr int kGStage = 2 * kGStageHalf; // 64 KB
+constexpr int kGStages = 2;
 constexpr int kGWaves = 8;               // two per SIMD
-constexpr int kGLoads = 4;               // LDS-direct loads per wave per stage
 constexpr int kGroupM = 8;               // m tiles per group of the tile order
 
 struct GemmArgs {
@@ -195,12 +194,6 @@ struct GemmArgs {
 __device__ __forceinline__ void gemm_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, lds_byte* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)dst, 16, voff,
                                            soff, 0, 0);
-}
-
-__device__ __forceinline__ void gemm_wait_older() {
-  // at most kGLoads loads of this wave in flight: the stage before the last
-  // issued one has landed (vmcnt in bits 3:0; expcnt, lgkmcnt at maxima)
-  __builtin_amdgcn_s_waitcnt(kGLoads | (0x7 << 4) | (0xF << 8));
 }
 
 __device__ __forceinline__ void gemm_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -229,17 +222,19 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
       const_cast<int8_t*>(a.w8 + (size_t)n0 * a.K), 0, (int)min((size_t)(a.N - n0) * a.K, (size_t)0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(a.x8 + (size_t)m0 * a.K), 0, (int)min((size_t)(a.M - m0) * a.K, (size_t)0x7fffffff), 0x00020000);
-  // this lane's load offsets: instruction i of wave w fills rows 16(2w + i) +
-  // lane/4, stored chunk lane % 4, fetched chunk (lane % 4) ^ ((lane >> 4) & 3)
-  const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  int voff[2];
+  // this lane's load offsets: instruction i of wave w fills rows 8(4w + i) +
+  // lane/8 (1 KB), stored chunk lane % 8, fetched chunk (lane % 8) ^ ((row >> 1) & 7)
+  int voff[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) voff[i] = (16 * (2 * wave + i) + (lane >> 2)) * a.K + 16 * chunk;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * wave + i) + (lane >> 3);
+    voff[i] = row * a.K + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+  }
   auto issue = [&](lds_byte* st, int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) gemm_load(rw, voff[i], k0, st + 1024 * (2 * wave + i));
+    for (int i = 0; i < 4; ++i) gemm_load(rw, voff[i], k0, st + 1024 * (4 * wave + i));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) gemm_load(rx, voff[i], k0, st + kGStageHalf + 1024 * (2 * wave + i));
+    for (int i = 0; i < 4; ++i) gemm_load(rx, voff[i], k0, st + kGStageHalf + 1024 * (4 * wave + i));
   };
 
   // wave w: output rows n in [128 (w & 1), +128), columns m in [64 (w >> 1), +64)
@@ -253,18 +248,18 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
 
   auto compute = [&](const lds_byte* st) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kGK / 32; ++kk) {
       const int c = khalf + 2 * kk;
       v4i af[4], bf[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rn = wn + 32 * i + r32;
-        af[i] = *(lds_v4i*)(st + rn * kGK + ((c ^ ((rn >> 2) & 3)) << 4));
+        af[i] = *(lds_v4i*)(st + rn * kGK + ((c ^ ((rn >> 1) & 7)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rm = wm + 32 * j + r32;
-        bf[j] = *(lds_v4i*)(st + kGStageHalf + rm * kGK + ((c ^ ((rm >> 2) & 3)) << 4));
+        bf[j] = *(lds_v4i*)(st + kGStageHalf + rm * kGK + ((c ^ ((rm >> 1) & 7)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -274,21 +269,17 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
     }
   };
 
-  const int steps = a.K / kGK;
+  const int steps = a.K / kGK;  // K is a multiple of 128
   issue(smem, 0);
-  if (steps > 1) issue(smem + kGStage, kGK);
   // unrolled by the stage count so every stage address is a constant offset
   for (int p0 = 0; p0 < steps; p0 += kGStages) {
 #pragma unroll
     for (int ph = 0; ph < kGStages; ++ph) {
       const int p = p0 + ph;
       if (p < steps) {
-        if (p + 1 < steps)
-          gemm_wait_older();
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         gemm_barrier();  // stage p is in; every wave is done with stage p-1
-        if (p + 2 < steps) issue(smem + ((ph + 2) % kGStages) * kGStage, (p + 2) * kGK);
+        if (p + 1 < steps) issue(smem + ((ph + 1) % kGStages) * kGStage, (p + 1) * kGK);
         compute(smem + ph * kGStage);
       }
     }

@@ -174,7 +174,7 @@ def test_w8a8_entry_points_reject_bad_arguments():
     assert L.sla_w8a8_linear(*bad) == INVALID
     bad = list(args); bad[6] = 6                      # N not a multiple of 4
     assert L.sla_w8a8_linear(*bad) == UNSUPPORTED
-    bad = list(args); bad[7] = 100                    # K not a multiple of 64
+    bad = list(args); bad[7] = 192                    # K not a multiple of 128
     assert L.sla_w8a8_linear(*bad) == UNSUPPORTED
     bad = list(args); bad[9] = 3
     assert L.sla_w8a8_linear(*bad) == INVALID

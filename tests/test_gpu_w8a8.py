@@ -76,9 +76,9 @@ def _run_gemm(x8, sx, w8, sw, bv, dtype):
     return y
 
 
-@pytest.mark.parametrize("M,N,K,bias", [(300, 260, 64, True), (256, 256, 192, False),
-                                        (513, 516, 5120, True), (1, 4, 64, False),
-                                        (700, 1024, 1536, True)])
+@pytest.mark.parametrize("M,N,K,bias", [(300, 260, 128, True), (256, 256, 384, False),
+                                        (513, 516, 5120, True), (1, 4, 128, False),
+                                        (700, 1024, 1536, True), (129, 64, 13824, False)])
 def test_gemm_parity(M, N, K, bias):
     print(f"[case] gemm M={M} N={N} K={K} bias={bias}", flush=True)
     x8, sx, w8, sw, bv = _gemm_case(M, N, K, bias, M + N + K)
