@@ -176,6 +176,9 @@ constexpr int kGStageHalf = kGT * kGK;   // 32 KB: one operand's stage
 constexpr int kGStage = 2 * kGStageHalf; // 64 KB
 constexpr int kGStages = 2;
 constexpr int kGWaves = 8;               // two per SIMD
+constexpr int kGOutRow = 2 * 128 + 16;   // LDS row of a wave's bf16 output (padded)
+constexpr int kGOutWave = 64 * kGOutRow; // a wave's 64 x 128 output in LDS
+constexpr int kGLds = kGStages * kGStage > kGWaves * kGOutWave ? kGStages * kGStage : kGWaves * kGOutWave;
 constexpr int kGroupM = 8;               // m tiles per group of the tile order
 
 struct GemmArgs {
@@ -285,26 +288,31 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
     }
   }
 
-  // epilogue: y = acc * sx[m] * sw[n] + bias[n]
+  // epilogue: y = acc * sx[m] * sw[n] + bias[n].  bf16 output goes through
+  // LDS (each wave's 64 tokens x 128 channels as rows) so that the stores are
+  // whole 256-byte row segments; fp32 output is stored from the registers.
+  gemm_barrier();  // every wave is done with the stages
+  lds_byte* my = smem + wave * kGOutWave;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = m0 + wm + 32 * j + r32;
-    if (m >= a.M) continue;
-    const float sxm = a.sx[m];
+    const float sxm = m < a.M ? a.sx[m] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn + 32 * i + 8 * q + 4 * khalf;
-        if (n >= a.N) continue;
-        const v4f swv = *reinterpret_cast<const v4f*>(a.sw + n);
-        v4f yv;
+        const int nl = 32 * i + 8 * q + 4 * khalf;  // channel within the wave's 128
+        const int n = n0 + wn + nl;
+        v4f yv = v4f{0.f, 0.f, 0.f, 0.f};
+        if (n < a.N) {
+          const v4f swv = *reinterpret_cast<const v4f*>(a.sw + n);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) yv[e] = (float)acc[i][j][4 * q + e] * sxm * swv[e];
-        if (a.bias) yv += *reinterpret_cast<const v4f*>(a.bias + n);
-        const size_t off = (size_t)m * a.N + n;
+          for (int e = 0; e < 4; ++e) yv[e] = (float)acc[i][j][4 * q + e] * sxm * swv[e];
+          if (a.bias) yv += *reinterpret_cast<const v4f*>(a.bias + n);
+        }
         if (a.out_f32) {
-          *reinterpret_cast<v4f*>(reinterpret_cast<float*>(a.y) + off) = yv;
+          if (m < a.M && n < a.N)
+            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(a.y) + (size_t)m * a.N + n) = yv;
         } else {
           uint32_t w[2];
 #pragma unroll
@@ -315,8 +323,30 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
             const uint32_t r1 = (b1 + 0x7fffu + ((b1 >> 16) & 1u)) >> 16;
             w[h] = r0 | (r1 << 16);
           }
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + off) = make_uint2(w[0], w[1]);
+          typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+          *(__attribute__((address_space(3))) v2u*)(my + (32 * j + r32) * kGOutRow + 2 * nl) =
+              v2u{w[0], w[1]};
         }
+      }
+    }
+  }
+  if (!a.out_f32) {
+    // this wave's rows back out: 16 lanes x 16 bytes per row, four rows per step
+    // (the wave reads only what it wrote, so no workgroup barrier is needed)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int cl = lane & 15;
+    const int n = n0 + wn + 8 * cl;
+#pragma unroll
+    for (int s4 = 0; s4 < 16; ++s4) {
+      const int r = 4 * s4 + (lane >> 4);
+      const int m = m0 + wm + r;
+      const v4i v = *(lds_v4i*)(my + r * kGOutRow + 16 * cl);
+      if (m < a.M) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.y) + (size_t)m * a.N + n;
+        if (n + 8 <= a.N)
+          *reinterpret_cast<v4i*>(dst) = v;
+        else if (n < a.N)
+          *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
       }
     }
   }
@@ -360,9 +390,9 @@ hipError_t launch_w8a8_gemm(const int8_t* x8, const float* sx, const int8_t* w8,
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(w8a8_gemm_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGStages * kGStage);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
   });
-  w8a8_gemm_kernel<<<8 * a.per_xcd, 64 * kGWaves, kGStages * kGStage, s>>>(a);
+  w8a8_gemm_kernel<<<8 * a.per_xcd, 64 * kGWaves, kGLds, s>>>(a);
   return hipGetLastError();
 }
 
