@@ -55,9 +55,9 @@ def layer_norm_rows(x_bits: np.ndarray, eps: float, gamma=None, beta=None):
     """(mu fp32 [M], rstd fp32 [M], y fp32 [M, K]) of reading 4.
 
     mu: the exact row sum (math.fsum of the fp32 values), divided by K in
-    fp64, rounded to fp32.  var: math.fsum of the exact squares of (x - mu)
-    (each a product of two fp32-representable values, exact in fp64), / K in
-    fp64; rstd = fp32(1 / sqrt(var + eps)) in fp64.
+    fp64, rounded to fp32.  var: math.fsum of the fp64 squares of (x - mu)
+    (x - mu itself exact in fp64), / K in fp64; rstd = fp32(1 / sqrt(var +
+    eps)) in fp64.
     """
     x = bf16_to_f32(x_bits)
     M, K = x.shape

@@ -41,9 +41,9 @@ constexpr int kRowChunks = kMaxRowK / (8 * 64); // 8-value chunks per lane
 // chunks 8 (l + 64 c) .. + 7 of the row as packed bf16 (c < K / 512) and
 // unpacks them in each pass: the sums, the normalised maximum, the codes.
 // LayerNorm: mu = fp32(sum_k x / K) with the sum in fp64; var = (sum_k
-// (x - mu)^2) / K in fp64 (x - mu exact in fp64); rstd = fp32(1 / sqrt(var +
-// eps)) in fp64; then, in fp32 and in this order, t = x - mu, t = t * rstd,
-// t = t * gamma, t = t + beta (gamma, beta optional).
+// (x - mu)^2) / K in fp64 (x - mu exact in fp64, squares accumulated by fma);
+// rstd = fp32(1 / sqrt(var + eps)) in fp64; then, in fp32 and in this order,
+// t = x - mu, t = t * rstd, t = t * gamma, t = t + beta (gamma, beta optional).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void rowquant_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const double d = (double)v[e] - (double)mu;
-          q += d * d;
+          q = __builtin_fma(d, d, q);
         }
       }
     }
