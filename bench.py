@@ -240,13 +240,25 @@ def w8a8_leg(sla, wl, steps, stream, dev):
 
     norm_ms = timed(lambda: sla.fused_norm_i8(x))
     gemm_ms = timed(lambda: sla.w8a8_linear(x8, sx, w8, sw, out=y))
+    del y
+    # context: the vendor library's INT8 product of the same codes (int32
+    # result, no scales) and its bf16 product of the unquantised operands
+    acc = torch._int_mm(x8, w8.t())
+    lib_i8_ms = timed(lambda: torch._int_mm(x8, w8.t()))
+    del acc
+    wt = w.t().contiguous()
+    yb = torch.matmul(x, wt)
+    lib_bf16_ms = timed(lambda: torch.matmul(x, wt))
+    del yb, wt
     ops = 2.0 * M * Nf * K
     tops = ops / (gemm_ms * 1e-3) / 1e12
     norm_bytes = M * K * 2 + M * K + M * 12
     gbps = norm_bytes / (norm_ms * 1e-3) / 1e9
-    log(f"[bench] w8a8: FusedNorm {norm_ms:.3f} ms, GEMM {gemm_ms:.3f} ms ({tops:.0f} TOPS)")
+    log(f"[bench] w8a8: FusedNorm {norm_ms:.3f} ms, GEMM {gemm_ms:.3f} ms ({tops:.0f} TOPS); "
+        f"library INT8 product {lib_i8_ms:.3f} ms, bf16 product {lib_bf16_ms:.3f} ms")
     return {"config": {"M": M, "K": K, "N": Nf, "layer": "Wan-14B FFN up-projection"},
             "fused_norm_ms": round(norm_ms, 4), "gemm_ms": round(gemm_ms, 4),
+            "library_int8_mm_ms": round(lib_i8_ms, 4), "library_bf16_mm_ms": round(lib_bf16_ms, 4),
             "gemm_roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_I8_OPS / 1e12,
                               "unit": "TOP/s", "frac": round(tops / (PEAK_I8_OPS / 1e12), 4),
                               "kernel": "w8a8_gemm_kernel"},
