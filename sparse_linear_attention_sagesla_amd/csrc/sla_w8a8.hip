@@ -20,6 +20,7 @@
 
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "sla_internal.h"
 #include "sla_quant.h"
@@ -34,14 +35,17 @@ typedef __attribute__((address_space(3))) unsigned char lds_byte;
 typedef __attribute__((address_space(3))) const v4i lds_v4i;
 
 constexpr int kRowWaves = 4;                   // rows per workgroup (one wave each)
-constexpr int kRowChunks = kMaxRowK / (8 * 64); // 8-value chunks per lane
+constexpr int kRowChunks = kMaxRowK / (8 * 64); // 8-value chunks per lane, longest rows
 
 // ---------------------------------------------------------------------------
 // Per-row quantiser / FusedNorm: one wave per row.  Lane l holds the 8-value
-// chunks 8 (l + 64 c) .. + 7 of the row as packed bf16 (c < K / 512) and
+// chunks 8 (l + 64 c) .. + 7 of the row as packed bf16 (c < kC, the kernel
+// is instantiated for a few chunk counts so short rows need few registers) and
 // unpacks them in each pass: the sums, the normalised maximum, the codes.
 // LayerNorm: mu = fp32(sum_k x / K) with the sum in fp64; var = (sum_k
 // (x - mu)^2) / K in fp64 (x - mu exact in fp64, squares accumulated by fma);
+// each lane keeps four partial sums (element e of a chunk into sum e % 4) so
+// the fp64 additions do not form one long dependent chain.
 // rstd = fp32(1 / sqrt(var + eps)) in fp64; then, in fp32 and in this order,
 // t = x - mu, t = t * rstd, t = t * gamma, t = t + beta (gamma, beta optional).
 // ---------------------------------------------------------------------------
@@ -51,27 +55,32 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-template <bool kNorm>
-__device__ __forceinline__ void norm_chunk(const uint4& u, int k0, float mu, float rstd,
-                                           const float* __restrict__ gamma,
-                                           const float* __restrict__ beta, float* y) {
+typedef __attribute__((address_space(3))) const v4f lds_v4f;
+
+// gamma (1 where absent) and beta (0 where absent) staged in LDS: lds_g[k],
+// lds_g[K + k].  Multiplying by 1 and adding 0 change no code: t * 1 = t, and
+// t + 0 differs from t only for t = -0, whose code is 0 either way.
+template <bool kNorm, bool kAffine>
+__device__ __forceinline__ void norm_chunk(const uint4& u, int k0, int K, float mu, float rstd,
+                                           const __attribute__((address_space(3))) float* lds_g,
+                                           float* y) {
   unpack_bf16x8(u, y);
   if (kNorm) {
-    float g[8], b[8];
-    if (gamma) {
-      *reinterpret_cast<float4*>(g) = *reinterpret_cast<const float4*>(gamma + k0);
-      *reinterpret_cast<float4*>(g + 4) = *reinterpret_cast<const float4*>(gamma + k0 + 4);
-    }
-    if (beta) {
-      *reinterpret_cast<float4*>(b) = *reinterpret_cast<const float4*>(beta + k0);
-      *reinterpret_cast<float4*>(b + 4) = *reinterpret_cast<const float4*>(beta + k0 + 4);
+    v4f g[2], b[2];
+    if (kAffine) {
+      g[0] = *(lds_v4f*)(lds_g + k0);
+      g[1] = *(lds_v4f*)(lds_g + k0 + 4);
+      b[0] = *(lds_v4f*)(lds_g + K + k0);
+      b[1] = *(lds_v4f*)(lds_g + K + k0 + 4);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float t = y[e] - mu;
       t = t * rstd;
-      if (gamma) t = t * g[e];
-      if (beta) t = t + b[e];
+      if (kAffine) {
+        t = t * g[e >> 2][e & 3];
+        t = t + b[e >> 2][e & 3];
+      }
       y[e] = t;
     }
   }
@@ -80,52 +89,57 @@ __device__ __forceinline__ void norm_chunk(const uint4& u, int k0, float mu, flo
 // Tells the compiler the packed row may have changed, so that each pass
 // unpacks it again instead of keeping every converted value alive across
 // passes (which does not fit in registers).
-__device__ __forceinline__ void launder(uint4 (&u)[kRowChunks]) {
+template <int kC>
+__device__ __forceinline__ void launder(uint4 (&u)[kC]) {
 #pragma unroll
-  for (int c = 0; c < kRowChunks; ++c) asm volatile("" : "+v"(u[c].x), "+v"(u[c].y), "+v"(u[c].z), "+v"(u[c].w));
+  for (int c = 0; c < kC; ++c) asm volatile("" : "+v"(u[c].x), "+v"(u[c].y), "+v"(u[c].z), "+v"(u[c].w));
 }
 
-template <bool kNorm>
-__global__ __launch_bounds__(64 * kRowWaves) void rowquant_kernel(
-    const uint16_t* __restrict__ x, int rows, int K, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float eps, int8_t* __restrict__ codes,
-    float* __restrict__ scale, float* __restrict__ mu_out, float* __restrict__ rstd_out) {
-  const int lane = threadIdx.x & 63;
-  const size_t row = (size_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
-  if (row >= (size_t)rows) return;
-  const uint16_t* xr = x + row * (size_t)K;
-  uint4 u[kRowChunks];
+// One row's chunks, as packed bf16: buffer loads over the row's K values, which
+// return zero past its end, so every load is issued unconditionally and all of
+// them are in flight together.
+template <int kC>
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ xr, int K, int lane,
+                                         uint4 (&u)[kC]) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xr), 0, 2 * K, 0x00020000);
 #pragma unroll
-  for (int c = 0; c < kRowChunks; ++c) {
-    const int k0 = 8 * (lane + 64 * c);
-    u[c] = k0 < K ? *reinterpret_cast<const uint4*>(xr + k0) : make_uint4(0, 0, 0, 0);
-  }
+  for (int c = 0; c < kC; ++c)
+    u[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (lane + 64 * c), 0, 0));
+}
+
+template <bool kNorm, bool kAffine, int kC>
+__device__ __forceinline__ void quant_row(uint4 (&u)[kC], size_t row, int K, int lane,
+                                          const __attribute__((address_space(3))) float* lds_g,
+                                          float eps,
+                                          int8_t* __restrict__ codes, float* __restrict__ scale,
+                                          float* __restrict__ mu_out, float* __restrict__ rstd_out) {
   float mu = 0.0f, rstd = 1.0f;
   if (kNorm) {
-    double s = 0.0;
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int c = 0; c < kRowChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
       float v[8];
       unpack_bf16x8(u[c], v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += (double)v[e];
+      for (int e = 0; e < 8; ++e) s[e & 3] += (double)v[e];
     }
-    mu = (float)(wave_sum_f64(s) / (double)K);
+    mu = (float)(wave_sum_f64((s[0] + s[1]) + (s[2] + s[3])) / (double)K);
     launder(u);
-    double q = 0.0;
+    double q[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int c = 0; c < kRowChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
       if (8 * (lane + 64 * c) < K) {
         float v[8];
         unpack_bf16x8(u[c], v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const double d = (double)v[e] - (double)mu;
-          q = __builtin_fma(d, d, q);
+          q[e & 3] = __builtin_fma(d, d, q[e & 3]);
         }
       }
     }
-    rstd = (float)(1.0 / sqrt(wave_sum_f64(q) / (double)K + (double)eps));
+    rstd = (float)(1.0 / sqrt(wave_sum_f64((q[0] + q[1]) + (q[2] + q[3])) / (double)K + (double)eps));
     launder(u);
     if (lane == 0) {
       if (mu_out) mu_out[row] = mu;
@@ -134,11 +148,11 @@ __global__ __launch_bounds__(64 * kRowWaves) void rowquant_kernel(
   }
   float a = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kRowChunks; ++c) {
+  for (int c = 0; c < kC; ++c) {
     const int k0 = 8 * (lane + 64 * c);
     if (k0 < K) {
       float y[8];
-      norm_chunk<kNorm>(u[c], k0, mu, rstd, gamma, beta, y);
+      norm_chunk<kNorm, kAffine>(u[c], k0, K, mu, rstd, lds_g, y);
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(y[e]));
     }
@@ -150,15 +164,40 @@ __global__ __launch_bounds__(64 * kRowWaves) void rowquant_kernel(
   launder(u);
   int8_t* cr = codes + row * (size_t)K;
 #pragma unroll
-  for (int c = 0; c < kRowChunks; ++c) {
+  for (int c = 0; c < kC; ++c) {
     const int k0 = 8 * (lane + 64 * c);
     if (k0 < K) {
       float y[8];
-      norm_chunk<kNorm>(u[c], k0, mu, rstd, gamma, beta, y);
+      norm_chunk<kNorm, kAffine>(u[c], k0, K, mu, rstd, lds_g, y);
       *reinterpret_cast<uint2*>(cr + k0) = code_row8(y, inv, live);
     }
   }
   if (lane == 0) scale[row] = sc;
+}
+
+// One wave per row.
+template <bool kNorm, bool kAffine, int kC>
+__global__ __launch_bounds__(64 * kRowWaves) void rowquant_kernel(
+    const uint16_t* __restrict__ x, int rows, int K, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float eps, int8_t* __restrict__ codes,
+    float* __restrict__ scale, float* __restrict__ mu_out, float* __restrict__ rstd_out) {
+  extern __shared__ float rq_lds[];
+  const auto lds_g = (const __attribute__((address_space(3))) float*)rq_lds;
+  const int lane = threadIdx.x & 63;
+  if (kAffine) {
+    for (int k = threadIdx.x; k < K; k += 64 * kRowWaves) {
+      rq_lds[k] = gamma ? gamma[k] : 1.0f;
+      rq_lds[K + k] = beta ? beta[k] : 0.0f;
+    }
+    __syncthreads();
+  }
+  // the row index as a scalar, so the row's buffer descriptor is one too
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t row = (size_t)blockIdx.x * kRowWaves + wave;
+  if (row >= (size_t)rows) return;
+  uint4 u[kC];
+  load_row(x + row * (size_t)K, K, lane, u);
+  quant_row<kNorm, kAffine>(u, row, K, lane, lds_g, eps, codes, scale, mu_out, rstd_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -359,12 +398,32 @@ hipError_t launch_rowquant(const uint16_t* x, int rows, int K, bool norm, const 
                            float* rstd, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const int blocks = (rows + kRowWaves - 1) / kRowWaves;
-  if (norm)
-    rowquant_kernel<true><<<blocks, 64 * kRowWaves, 0, s>>>(x, rows, K, gamma, beta, eps, codes, scale,
-                                                             mu, rstd);
-  else
-    rowquant_kernel<false><<<blocks, 64 * kRowWaves, 0, s>>>(x, rows, K, nullptr, nullptr, 0.0f, codes,
-                                                              scale, nullptr, nullptr);
+  const int chunks = (K + 511) / 512;  // 8-value chunks per lane
+  const size_t affine_lds = 8 * (size_t)K;  // gamma and beta as fp32
+  auto go = [&](auto kc) {
+    constexpr int C = decltype(kc)::value;
+    static std::once_flag once;
+    std::call_once(once, [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(rowquant_kernel<true, true, C>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 8 * kMaxRowK);
+    });
+    if (norm && (gamma || beta))
+      rowquant_kernel<true, true, C><<<blocks, 64 * kRowWaves, affine_lds, s>>>(
+          x, rows, K, gamma, beta, eps, codes, scale, mu, rstd);
+    else if (norm)
+      rowquant_kernel<true, false, C><<<blocks, 64 * kRowWaves, 0, s>>>(
+          x, rows, K, nullptr, nullptr, eps, codes, scale, mu, rstd);
+    else
+      rowquant_kernel<false, false, C><<<blocks, 64 * kRowWaves, 0, s>>>(
+          x, rows, K, nullptr, nullptr, 0.0f, codes, scale, nullptr, nullptr);
+  };
+  if (chunks <= 2) go(std::integral_constant<int, 2>());
+  else if (chunks <= 4) go(std::integral_constant<int, 4>());
+  else if (chunks <= 8) go(std::integral_constant<int, 8>());
+  else if (chunks <= 10) go(std::integral_constant<int, 10>());
+  else if (chunks <= 16) go(std::integral_constant<int, 16>());
+  else if (chunks <= 24) go(std::integral_constant<int, 24>());
+  else go(std::integral_constant<int, kRowChunks>());
   return hipGetLastError();
 }
 
