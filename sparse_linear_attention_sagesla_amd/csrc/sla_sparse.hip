@@ -443,13 +443,34 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return max((uint32_t)b[0], (uint32_t)b[1]);
 }
 
+// The head's linear state for the subtraction form, staged in LDS after the
+// tiles are done: H^T (fp16, 128 rows of 256 bytes, chunk c of row r kept at
+// c ^ (r & 15) like M^T, so the same lane offsets read it) at kHOff and z
+// (fp32 [128]) after it.  LDS-direct loads, so they fly while M^T is formed.
+constexpr int kHOff = 40 * 1024;
+__device__ __forceinline__ void issue_linear_state(const SparseArgs& a, size_t bh, lds_byte* smem,
+                                                   int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t hr = head_rsrc(a.h16t + bh * kD * kD, (size_t)kD * kD * 2);
+  const int r = 4 * wave + (lane >> 4);  // row within each 16-row round
+  const int voff = r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) lds_load16(hr, voff, 4096 * m, smem + kHOff + 4096 * m + 1024 * wave);
+  if (wave == 0) {
+    // lanes 32.. read past z and write zeros after it
+    const __amdgpu_buffer_rsrc_t zr = head_rsrc(a.z + bh * kD, (size_t)kD * 4);
+    lds_load16(zr, 16 * lane, 0, smem + kHOff + kD * kD * 2);
+  }
+}
+
 // The linear branch's share phi(Q) M for this lane's query (O^T layout, d =
 // 16dt + 4g + r) and phi(Q) z_M.  The workgroup's four waves hold M^T by
 // channel slices; M^T goes through LDS once as fp16 scaled by 2^-s so that
 // max|M| 2^-s lies in [2^14, 2^15), and comes back as A operands.
 __device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, const half8 fq[4],
                                              const LaneOffsets& lo, int wave, int lane,
-                                             v4f num[8], float& den) {
+                                             v4f num[8], float& den,
+                                             const SparseArgs* stage_state = nullptr,
+                                             size_t bh = 0) {
   constexpr int kZOff = kD * kD * 2;             // z_M, fp32 [128]
   constexpr int kRedOff = kZOff + kD * 4;        // per-wave maxima
   const int g = lane >> 4, l16 = lane & 15;
@@ -462,6 +483,7 @@ __device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, con
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S.mk[dt][x][r]));
   const uint32_t wm = wave_max_u32(__float_as_uint(mx));  // non-negative floats order as integers
   lds_barrier();  // every wave is done with the tile stages
+  if (stage_state) issue_linear_state(*stage_state, bh, smem, wave, lane);
   if (lane == 0) *(__attribute__((address_space(3))) uint32_t*)(smem + kRedOff + 4 * wave) = wm;
   if (lane < 32) *(__attribute__((address_space(3))) float*)(smem + kZOff + 4 * (32 * wave + lane)) = S.zk;
   lds_barrier();
@@ -508,18 +530,27 @@ __device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, con
 // Linear output in the subtraction form, from the kept share (nm, dm) that
 // linear_share returns: (phi(Q)H - phi(Q)M) / (phi(Q)z - phi(Q)z_M).  Returns
 // 1/den, 0 when the denominator is lost in rounding; den is in the staged
-// scale (phi/16 on both sides: 1/256 of the true denominator).
-__device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t bh, int g, int l16,
+// scale (phi/16 on both sides: 1/256 of the true denominator).  kStaged: H^T
+// and z come from LDS (issue_linear_state), else straight from memory.
+template <bool kStaged>
+__device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t bh, int g,
+                                                     const lds_byte* smem, const LaneOffsets& lo,
                                                      const half8 fq[4], const v4f nm[8], float dm,
                                                      v4f ol[8]) {
-  const _Float16* ht = reinterpret_cast<const _Float16*>(a.h16t) + bh * kD * kD;
   const float hs = a.hscale[bh];
+  if (kStaged) {
+    wait_loads();
+    lds_barrier();  // the staged H^T and z are in
+  }
+  typedef __attribute__((address_space(3))) const float lds_f;
   const float* zz = a.z + bh * kD;
   float dz = 0.0f;
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dz += (float)fq[cc][e] * zz[32 * cc + 8 * g + e];
+    for (int e = 0; e < 8; ++e)
+      dz += (float)fq[cc][e] * (kStaged ? *(lds_f*)(smem + kHOff + kD * kD * 2 + 4 * (32 * cc + 8 * g + e))
+                                        : zz[32 * cc + 8 * g + e]);
   dz += __shfl_xor(dz, 16);
   dz += __shfl_xor(dz, 32);
   // whole head minus the kept share; a denominator lost in rounding counts as 0
@@ -528,10 +559,12 @@ __device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     v4f num = v4f{0.f, 0.f, 0.f, 0.f};
-    const _Float16* hrow = ht + (size_t)(16 * dt + l16) * kD + 8 * g;
+    const _Float16* hrow = reinterpret_cast<const _Float16*>(a.h16t) + bh * kD * kD +
+                           (size_t)(16 * dt + (lo.rdM >> 8)) * kD + 8 * g;  // row 16dt + l16
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const half8 ah = *reinterpret_cast<const half8*>(hrow + 32 * cc);
+      const half8 ah = kStaged ? *(lds_half8*)(smem + kHOff + 4096 * dt + (lo.rdM ^ (64 * cc)))
+                               : *reinterpret_cast<const half8*>(hrow + 32 * cc);
       num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fq[cc], num, 0, 0, 0);
     }
     ol[dt] = (num * hs - nm[dt]) * inv_den;
@@ -545,7 +578,7 @@ __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a
                                              int qrow, bool qvalid, lds_byte* smem,
                                              const LaneOffsets& lo, int wave, int lane) {
   constexpr bool kLinAny = kMode != kSoftOnly;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int g = lane >> 4;
   float l = S.l_part + __shfl_xor(S.l_part, 16);
   l += __shfl_xor(l, 32);
   const float inv_l = (a.k > 0 && l > 0.0f) ? 1.0f / l : 0.0f;
@@ -558,14 +591,14 @@ __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a
     load_phi_q(a, bh, qrow, qvalid, g, fq);
     v4f nm[8];
     float dm;
-    linear_share(S, smem, fq, lo, wave, lane, nm, dm);
+    linear_share(S, smem, fq, lo, wave, lane, nm, dm, kMode == kSubtract ? &a : nullptr, bh);
     if (kMode == kDirect) {
       // numerator and denominator summed over the unselected blocks
       const float inv_den = dm > 0.0f ? 1.0f / dm : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) ol[dt] = nm[dt] * inv_den;
     } else {
-      linear_subtract_out(a, bh, g, l16, fq, nm, dm, ol);
+      linear_subtract_out<true>(a, bh, g, smem, lo, fq, nm, dm, ol);
     }
   }
 
@@ -1009,6 +1042,8 @@ constexpr int kBwdVOff = kK8Bytes;                        // V rows [64 keys][12
 constexpr int kBwdKtOff = kK8Bytes + kF16TileBytes;       // K^T [128][64 perm keys] bf16
 constexpr int kBwdStage = kK8Bytes + 2 * kF16TileBytes;   // 40 KB
 constexpr int kMRowOff = 33 * 1024;                       // M row-major, after linear_share's area
+static_assert(kHOff + kD * kD * 2 + 1024 <= 2 * (kK8Bytes + 2 * kF16TileBytes),
+              "staged linear state exceeds the forward stages");
 constexpr int kZOffShared = kD * kD * 2;                  // z_M as linear_share leaves it (fp32 [128])
 
 // Position of row t of a block in the permuted order of the transposed tiles
@@ -1205,7 +1240,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
     float dm;
     linear_share(S, smem, fq, lo, wave, lane, nm, dm);
     v4f ol[8];
-    const float inv_den = linear_subtract_out(a, bh, g, l16, fq, nm, dm, ol);
+    const float inv_den = linear_subtract_out<false>(a, bh, g, smem, lo, fq, nm, dm, ol);
     float up = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
