@@ -193,3 +193,38 @@ def test_batched_heads_match_single_calls():
         for h in range(H):
             r = O.sla_forward_head(Q[b, h], K[b, h], V[b, h], 64, 0.2, "elu1")
             assert_parity(out[b, h], r["out"], what=f"b{b} h{h}")
+
+
+def _sweep_configs(n=12, seed=2024):
+    """Seeded mixed configurations: batch and head counts, ragged lengths from one
+    token to a few thousand, keep fractions from 0 to 1 crossed with every
+    feature map (keep 0 only with a feature map: without one nothing is
+    computed), input scales and a channel offset (exercising the K mean
+    smoothing)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        out.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
+                        N=int(rng.integers(1, 2601)),
+                        keep=(0.0, 0.03, 0.1, 0.37, 0.8, 1.0)[c % 6],
+                        phi=("elu1", "relu", "none")[(c + c // 6) % 3],
+                        scale=float(rng.choice([0.5, 1.5, 3.0])),
+                        offset=float(rng.choice([0.0, 2.0])), seed=100 + 3 * c))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _sweep_configs(), ids=lambda c: f"B{c['B']}H{c['H']}N{c['N']}k{c['keep']}{c['phi']}")
+def test_attention_parity_config_sweep(cfg):
+    B, H, N = cfg["B"], cfg["H"], cfg["N"]
+    Q, K, V = (random_bf16((B, H, N, 128), cfg["seed"] + i, scale=cfg["scale"],
+                           offset=cfg["offset"] if i < 2 else 0.0) for i in range(3))
+    q, k, v = _case(f"sweep {cfg}", Q, K, V)
+    out = sla.attention(q, k, v, cfg["keep"], cfg["phi"], torch.float32)
+    outb = sla.attention(q, k, v, cfg["keep"], cfg["phi"], torch.bfloat16)
+    out = out.cpu().numpy()
+    assert np.isfinite(out).all()
+    for b in range(B):
+        for h in range(H):
+            r = O.sla_forward_head(Q[b, h], K[b, h], V[b, h], 64, cfg["keep"], cfg["phi"])
+            assert_parity(out[b, h], r["out"], what=f"b{b} h{h}")
+    assert np.array_equal(bf16_bits_of(outb), rne_bf16(out))
