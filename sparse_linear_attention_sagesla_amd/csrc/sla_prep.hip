@@ -145,27 +145,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   const int cc = t & 15;
   const int rr = t >> 4;
   const int rows = min(kBlk, N - blk * kBlk);
-  const uint16_t* src = (isk ? k : q) + ((size_t)bh * N + (size_t)blk * kBlk) * kD + cc * 8;
+  const uint16_t* src = (isk ? k : q) + ((size_t)bh * N + (size_t)blk * kBlk) * kD;
+  // the block's valid rows as a buffer, so rows past them read as zero and the
+  // four loads are issued together without a condition
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(src), 0, rows * kD * 2, 0x00020000);
   float m8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) m8[e] = isk ? mu[(size_t)bh * kD + cc * 8 + e] : 0.0f;
+  uint4 u[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    u[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rs, ((rr + 16 * m) * kD + cc * 8) * 2, 0, 0));
   float x[4][8];
   float amax = 0.0f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int r = rr + 16 * m;
-    if (r < rows) {
-      const uint4 u = *reinterpret_cast<const uint4*>(src + (size_t)r * kD);
-      unpack_bf16x8(u, x[m]);
-      if (isk) {
+    const bool valid = rr + 16 * m < rows;
+    unpack_bf16x8(u[m], x[m]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[m][e] = x[m][e] - m8[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[m][e]));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[m][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) {
+      x[m][e] = valid ? x[m][e] - m8[e] : 0.0f;
+      amax = fmaxf(amax, fabsf(x[m][e]));
     }
   }
 #pragma unroll
