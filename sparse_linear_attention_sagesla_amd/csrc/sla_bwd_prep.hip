@@ -209,19 +209,26 @@ __global__ __launch_bounds__(256) void grad_h_partial_kernel(const uint16_t* __r
     const float* ub = stats + ((size_t)bh * Nb + i) * 256 + 192;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      bf16x8 af[2];
+      // every operand of this half block first, unconditionally, so the loads
+      // are in flight together
+      bf16x8 af[2], bo[8];
+      v4f uq[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         af[mt] = *reinterpret_cast<const bf16x8*>(fb + (32 * wave + 16 * mt + l16) * kBlk + 32 * c + 8 * g);
 #pragma unroll
+      for (int et = 0; et < 8; ++et)
+        bo[et] = *reinterpret_cast<const bf16x8*>(db + (16 * et + l16) * kBlk + 32 * c + 8 * g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) uq[h] = *reinterpret_cast<const v4f*>(ub + 32 * c + 8 * g + 4 * h);
+#pragma unroll
       for (int et = 0; et < 8; ++et) {
-        const bf16x8 bo = *reinterpret_cast<const bf16x8*>(db + (16 * et + l16) * kBlk + 32 * c + 8 * g);
-        w[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], bo, w[0][et], 0, 0, 0);
-        w[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1], bo, w[1][et], 0, 0, 0);
+        w[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], bo[et], w[0][et], 0, 0, 0);
+        w[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1], bo[et], w[1][et], 0, 0, 0);
       }
       bf16x8 uv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) uv[e] = l16 == 0 ? (__bf16)ub[32 * c + 8 * g + e] : (__bf16)0.0f;
+      for (int e = 0; e < 8; ++e) uv[e] = l16 == 0 ? (__bf16)uq[e >> 2][e & 3] : (__bf16)0.0f;
       wz[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], uv, wz[0], 0, 0, 0);
       wz[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1], uv, wz[1], 0, 0, 0);
     }

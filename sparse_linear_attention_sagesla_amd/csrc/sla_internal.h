@@ -66,7 +66,7 @@ struct BwdWorkspace {
   float* G = nullptr;         // [BH, D, D] sum of (phi(Q)/den)^T dO over all rows
   float* gz = nullptr;        // [BH, D]    sum of (phi(Q)/den)^T u
 };
-constexpr int kGradChunks = 16;  // query-block chunks per head in the G reduction
+constexpr int kGradChunks = 32;  // query-block chunks per head in the G reduction
 
 // Stage launchers (all enqueue on `s`, return the launch status).
 // Block means and K block sums; also Q's INT8 codes and scales when q8 is set.
