@@ -561,12 +561,13 @@ __device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t
     v4f num = v4f{0.f, 0.f, 0.f, 0.f};
     const _Float16* hrow = reinterpret_cast<const _Float16*>(a.h16t) + bh * kD * kD +
                            (size_t)(16 * dt + (lo.rdM >> 8)) * kD + 8 * g;  // row 16dt + l16
+    half8 ah[4];  // the row's four fragments, loaded together
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const half8 ah = kStaged ? *(lds_half8*)(smem + kHOff + 4096 * dt + (lo.rdM ^ (64 * cc)))
-                               : *reinterpret_cast<const half8*>(hrow + 32 * cc);
-      num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fq[cc], num, 0, 0, 0);
-    }
+    for (int cc = 0; cc < 4; ++cc)
+      ah[cc] = kStaged ? *(lds_half8*)(smem + kHOff + 4096 * dt + (lo.rdM ^ (64 * cc)))
+                       : *reinterpret_cast<const half8*>(hrow + 32 * cc);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[cc], fq[cc], num, 0, 0, 0);
     ol[dt] = (num * hs - nm[dt]) * inv_den;
   }
   return inv_den;
@@ -1274,10 +1275,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       v4f ah = v4f{0.f, 0.f, 0.f, 0.f}, am = v4f{0.f, 0.f, 0.f, 0.f};
+      bf16x8 hv[4];  // the row's four fragments, loaded together
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        hv[ks] = *reinterpret_cast<const bf16x8*>(hrow + (16 * ct + l16) * kD + 32 * ks + 8 * g);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 hv = *reinterpret_cast<const bf16x8*>(hrow + (16 * ct + l16) * kD + 32 * ks + 8 * g);
-        ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, gf[ks], ah, 0, 0, 0);
+        ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv[ks], gf[ks], ah, 0, 0, 0);
         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row_frag(smem + kMRowOff, 16 * ct + l16, 4 * ks + g),
                                                      gf[ks], am, 0, 0, 0);
       }
