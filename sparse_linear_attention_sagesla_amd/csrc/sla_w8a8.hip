@@ -218,6 +218,8 @@ constexpr int kGWaves = 8;               // two per SIMD
 constexpr int kGOutRow = 2 * 128 + 16;   // LDS row of a wave's bf16 output (padded)
 constexpr int kGOutWave = 64 * kGOutRow; // a wave's 64 x 128 output in LDS
 constexpr int kGLds = kGStages * kGStage > kGWaves * kGOutWave ? kGStages * kGStage : kGWaves * kGOutWave;
+constexpr int kGScaleOff = kGLds;               // the tile's w scales, x scales, bias (1 KB each)
+constexpr int kGLdsTotal = kGLds + 3 * 1024;
 constexpr int kGroupM = 8;               // m tiles per group of the tile order
 
 struct GemmArgs {
@@ -279,6 +281,18 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
     for (int i = 0; i < 4; ++i) gemm_load(rx, voff[i], k0, st + kGStageHalf + 1024 * (4 * wave + i));
   };
 
+  // the epilogue's scales and bias for this tile go to LDS with the first stage,
+  // so it reads them there instead of waiting on memory (entries past N or M
+  // read as zero)
+  {
+    auto scale_rsrc = [](const float* p, int count) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, 4 * min(count, kGT), 0x00020000);
+    };
+    if (wave == 0) gemm_load(scale_rsrc(a.sw + n0, a.N - n0), 16 * lane, 0, smem + kGScaleOff);
+    if (wave == 1) gemm_load(scale_rsrc(a.sx + m0, a.M - m0), 16 * lane, 0, smem + kGScaleOff + 1024);
+    if (wave == 2 && a.bias) gemm_load(scale_rsrc(a.bias + n0, a.N - n0), 16 * lane, 0, smem + kGScaleOff + 2048);
+  }
+
   // wave w: output rows n in [128 (w & 1), +128), columns m in [64 (w >> 1), +64)
   const int wn = 128 * (wave & 1), wm = 64 * (wave >> 1);
   const int r32 = lane & 31, khalf = lane >> 5;
@@ -335,7 +349,8 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = m0 + wm + 32 * j + r32;
-    const float sxm = m < a.M ? a.sx[m] : 0.0f;
+    typedef __attribute__((address_space(3))) const float lds_f;
+    const float sxm = *(lds_f*)(smem + kGScaleOff + 1024 + 4 * (wm + 32 * j + r32));  // 0 past M
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -344,10 +359,10 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void w8a8_gemm_kernel(GemmArgs a) 
         const int n = n0 + wn + nl;
         v4f yv = v4f{0.f, 0.f, 0.f, 0.f};
         if (n < a.N) {
-          const v4f swv = *reinterpret_cast<const v4f*>(a.sw + n);
+          const v4f swv = *(lds_v4f*)(smem + kGScaleOff + 4 * (wn + nl));
 #pragma unroll
           for (int e = 0; e < 4; ++e) yv[e] = (float)acc[i][j][4 * q + e] * sxm * swv[e];
-          if (a.bias) yv += *reinterpret_cast<const v4f*>(a.bias + n);
+          if (a.bias) yv += *(lds_v4f*)(smem + kGScaleOff + 2048 + 4 * (wn + nl));
         }
         if (a.out_f32) {
           if (m < a.M && n < a.N)
@@ -449,9 +464,9 @@ hipError_t launch_w8a8_gemm(const int8_t* x8, const float* sx, const int8_t* w8,
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(w8a8_gemm_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGLdsTotal);
   });
-  w8a8_gemm_kernel<<<8 * a.per_xcd, 64 * kGWaves, kGLds, s>>>(a);
+  w8a8_gemm_kernel<<<8 * a.per_xcd, 64 * kGWaves, kGLdsTotal, s>>>(a);
   return hipGetLastError();
 }
 
