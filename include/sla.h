@@ -290,7 +290,8 @@ sla_status sla_fused_norm_i8(const void *x, int rows, int K, const float *gamma,
  *   bias fp32 [N] or NULL                                             (in)
  *   y [M, N], bf16 (round to nearest even) or fp32 per out_dtype       (out)
  * K must be a multiple of 128 (128 <= K <= 16384) and N of 4; M * K and
- * N * K below 2^31. */
+ * N * K below 2^31.  x8, w8, y, both scale arrays and bias are 16-byte
+ * aligned (SLA_ERR_INVALID_ARG otherwise). */
 sla_status sla_w8a8_linear(const int8_t *x8, const float *x_scale,
                            const int8_t *w8, const float *w_scale,
                            const float *bias, int M, int N, int K, void *y,

@@ -452,8 +452,8 @@ sla_status sla_w8a8_linear(const int8_t* x8, const float* x_scale, const int8_t*
                            const float* w_scale, const float* bias, int M, int N, int K, void* y,
                            int out_dtype, void* stream) {
   if (!x8 || !x_scale || !w8 || !w_scale || !y || M < 1 || N < 1) return SLA_ERR_INVALID_ARG;
-  if (!aligned16(x8) || !aligned16(w8) || !aligned16(w_scale) || !aligned16(y) ||
-      (bias && !aligned16(bias)))
+  if (!aligned16(x8) || !aligned16(w8) || !aligned16(x_scale) || !aligned16(w_scale) ||
+      !aligned16(y) || (bias && !aligned16(bias)))
     return SLA_ERR_INVALID_ARG;
   if (out_dtype != SLA_OUT_BF16 && out_dtype != SLA_OUT_F32) return SLA_ERR_INVALID_ARG;
   if (K < 128 || K > sla::kMaxRowK || K % 128 != 0 || N % 4 != 0) return SLA_ERR_UNSUPPORTED;

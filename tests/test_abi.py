@@ -180,5 +180,8 @@ def test_w8a8_entry_points_reject_bad_arguments():
     assert L.sla_w8a8_linear(*bad) == INVALID
     bad = list(args); bad[4] = MISALIGNED
     assert L.sla_w8a8_linear(*bad) == INVALID
+    for pos in (1, 3):                                # x_scale, w_scale
+        bad = list(args); bad[pos] = MISALIGNED
+        assert L.sla_w8a8_linear(*bad) == INVALID
     bad = list(args); bad[5] = 1 << 20; bad[7] = 4096  # M * K >= 2^31
     assert L.sla_w8a8_linear(*bad) == UNSUPPORTED
