@@ -280,6 +280,10 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
       for (int c = 0; c < 2; ++c) fk[x][c] = *(lds_half8*)(st + 2048 * x + (lo.rdK ^ (64 * c)));
     S.zk += zj;
   }
+  // The products below are most of the tile's matrix-core work.  The wave
+  // running them gets issue priority over the other workgroup's wave on this
+  // SIMD, whose softmax steps then fill the issue slots between them.
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -293,6 +297,7 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Walks `n` tiles listed in `list` through the two LDS stages.
