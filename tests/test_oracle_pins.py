@@ -268,6 +268,82 @@ def test_branch_decomposition_matches_token_level_construction():
     np.testing.assert_allclose(r["out"], soft + lin, atol=1e-12)
 
 
+def _complement_average(q64, k64, v64, phi_kind, unsel_rows, t):
+    """Token-level normalised linear attention of query t over the rows
+    ``unsel_rows``: a loop over the keys, each weight phi(q_t) . phi(k_u)."""
+    fq = O.phi(q64[t], phi_kind)
+    num = np.zeros(v64.shape[1])
+    den = 0.0
+    for u in unsel_rows:
+        w = float(np.dot(fq, O.phi(k64[u], phi_kind)))
+        num += w * v64[u]
+        den += w
+    return num, den
+
+
+def test_linear_rule_zero_denominator_relu():
+    """Reading R12 (normalised linear attention [TUT §2.1], zero when the
+    denominator vanishes).  A ReLU row whose every weight phi(q).phi(k_u)
+    over the unselected keys is zero, while those keys exist, gets O_l = 0
+    exactly, and its output is the softmax branch alone; other rows get the
+    token-level weighted average.  Built by sign structure, not by the
+    oracle's own denominator: rows 0-31 have phi(q) = 0 (every entry < 0),
+    rows 32-63 have features only on channels 0-7, where every unselected
+    key has phi(k) = 0."""
+    N, blk = 256, 64
+    rng = np.random.default_rng(7)
+    pos = lambda shape: rng.uniform(0.25, 2.0, shape)
+    q = pos((N, 128))
+    q[0:32] *= -1.0
+    q[32:64, 8:] *= -1.0
+    k = pos((N, 128))
+    for j in (0, 2):                                   # unselected blocks
+        k[j * blk:(j + 1) * blk, :8] *= -1.0
+    v = rng.standard_normal((N, 128)) + 1.0
+    qb, kb, vb = bf(q), bf(k), bf(v)
+    idx = np.array([[1, 3]] * 4, dtype=np.int32)       # every query block keeps 1 and 3
+    r = O.sla_forward_head(qb, kb, vb, block=blk, keep=0.5, phi_kind="relu", idx=idx)
+    q64, k64, v64 = (O.bf16_to_f64(x) for x in (qb, kb, vb))
+    unsel = np.r_[0:64, 128:192]
+    assert (r["out_linear"][:64] == 0.0).all()
+    np.testing.assert_array_equal(r["out"][:64], r["out_softmax"][:64])
+    for t in list(range(0, 64, 9)):
+        num, den = _complement_average(q64, k64, v64, "relu", unsel, t)
+        assert den == 0.0 and not num.any()
+    for t in list(range(64, N, 17)):
+        num, den = _complement_average(q64, k64, v64, "relu", unsel, t)
+        assert den > 0.0
+        np.testing.assert_allclose(r["out_linear"][t], num / den, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_rule_elu1_never_zero_and_empty_complement():
+    """elu+1 features are positive, so no row of a non-empty complement has a
+    zero denominator, even with large negative entries (weights near e^-60);
+    with every block kept the complement is empty, the linear branch is 0 and
+    the output is dense softmax attention on the INT8 logits."""
+    N, blk = 192, 64
+    rng = np.random.default_rng(8)
+    q = rng.uniform(-30.0, -20.0, (N, 128))
+    k = rng.uniform(-30.0, -20.0, (N, 128))
+    v = rng.standard_normal((N, 128))
+    qb, kb, vb = bf(q), bf(k), bf(v)
+    idx = np.array([[0]] * 3, dtype=np.int32)
+    r = O.sla_forward_head(qb, kb, vb, block=blk, keep=1 / 3, phi_kind="elu1", idx=idx)
+    q64, k64, v64 = (O.bf16_to_f64(x) for x in (qb, kb, vb))
+    for t in (0, 70, 191):
+        num, den = _complement_average(q64, k64, v64, "elu1", np.arange(64, N), t)
+        assert den > 0.0
+        np.testing.assert_allclose(r["out_linear"][t], num / den, rtol=1e-9, atol=1e-12)
+    full = O.sla_forward_head(qb, kb, vb, block=blk, keep=1.0, phi_kind="elu1")
+    assert not full["out_linear"].any()
+    bq = np.arange(N) // blk
+    qh = full["q8"][:N].astype(np.float64) * full["q_scale"][bq][:, None]
+    kh = full["k8"][:N].astype(np.float64) * full["k_scale"][bq][:, None]
+    lg = qh @ kh.T / math.sqrt(128)
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    np.testing.assert_allclose(full["out"], (p @ v64) / p.sum(1, keepdims=True), atol=1e-12)
+
+
 def test_single_token_returns_its_value():
     q, k, v = (random_bf16((1, 128), s) for s in (71, 72, 73))
     for keep, ph in ((1.0, "none"), (1.0, "elu1"), (0.5, "elu1")):
