@@ -23,19 +23,24 @@
  *  - Blocks: Nb = ceil(N / 64); the last block may be ragged; rows past N
  *    ("pad rows") never take part in any sum, maximum or softmax.
  *  - The caller allocates and owns every buffer, including the workspace
- *    (size from sla_workspace_size).  The library allocates no device memory.
- *    Its only global state is, per device, one side stream and two events
- *    that sla_attention_fwd creates on first use and keeps until exit; calls
- *    on different streams are independent as long as their workspaces differ.
- *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
- *    the call returns without synchronising.  Arguments are validated before
- *    anything is enqueued: on any error status nothing has been enqueued.
- *    SLA_ERR_DEVICE reports a failed kernel launch (hipGetLastError).
+ *    (size from sla_workspace_bytes, or sla_workspace_size per operation).
+ *    The library allocates no device memory and keeps no global mutable
+ *    state, so it may be called from several threads; calls on different
+ *    streams are independent as long as their workspaces differ.
+ *  - All work of a call is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream), in order, and the call returns without synchronising;
+ *    a call is capturable in a HIP graph, its first call included.
+ *    Arguments are validated before anything is enqueued: on any error
+ *    status nothing has been enqueued.  SLA_ERR_DEVICE reports a failed
+ *    kernel launch (hipGetLastError) or attribute set.
  *  - Outputs must not alias inputs or the workspace.
- *  - Numeric range: inputs must be finite.  The linear branch stages
- *    phi(Q)/16 and phi(K)/16 in fp16 and the softmax branch stages V in
- *    fp16, so |V| <= 65504 and phi values <= 360 (|Q|, |K| below about 359)
- *    keep every staged value in range.
+ *  - Numeric range: inputs must be finite.  V is staged in fp16, so |V| must
+ *    stay below 65504; entries below 2^-14 in magnitude keep an absolute
+ *    precision of 2^-25.  The linear branch stages phi(K)/16 in fp16
+ *    (phi(K) up to 2^20; elu+1 features below 2^-20, i.e. K entries below
+ *    about -13.8, count as zero) and phi(q) scaled per row so that its
+ *    largest feature lies in [1, 2) (the branch is a ratio, so the factor
+ *    cancels); features below 2^-24 of a row's largest count as zero.
  */
 #ifndef SLA_H_
 #define SLA_H_
@@ -84,9 +89,17 @@ typedef enum sla_op {
  * returns -1 if n_blocks < 1 or keep is NaN. */
 int32_t sla_topk_count(int32_t n_blocks, double keep);
 
+/* Workspace bytes of the SageSLA forward for this shape, keep and phi (an
+ * sla_phi): enough for each of sla_quantize_qk, sla_block_select and
+ * sla_attention_fwd on the same B, H, N.  Pure host function; returns 0 when
+ * the arguments are not a valid sla_attention_fwd call (as it validates
+ * them), so 0 never sizes a usable workspace. */
+size_t sla_workspace_bytes(int B, int H, int N, int d, int block, double keep,
+                           int phi);
+
 /* Workspace bytes `op` needs for this shape, written to *bytes.  `keep` and
- * `phi` matter only for SLA_OP_ATTENTION (pass 0 otherwise).  Pure host
- * function; validates like the op itself. */
+ * `phi` matter only for SLA_OP_ATTENTION and SLA_OP_ATTENTION_BWD (pass 0
+ * otherwise).  Pure host function; validates like the op itself. */
 sla_status sla_workspace_size(int op, int B, int H, int N, int d, int block,
                               double keep, int phi, size_t *bytes);
 
@@ -137,29 +150,18 @@ sla_status sla_block_select(const void *q, const void *k, int B, int H, int N,
  *   keep        kept fraction, 0..1; keep == 0 requires phi != NONE
  *   phi         sla_phi
  *   out         [B,H,N,128], bf16 or fp32 per out_dtype                 (out)
- *   out_linear  fp32 [B,H,N,128] linear branch alone; may be NULL       (out)
- * Workspace: SLA_OP_ATTENTION (holds codes, selection, fp16 staging and the
- * linear state, about 3 bytes/element of Q).
- * Streams: work is enqueued on `stream`, except the block scores (TOPK) and
- * the walk schedule (SCHEDULE), which run on a side stream the library
- * creates on first use for the current device (non-blocking, default
- * priority, kept until exit), forked after the statistics pass and joined
- * before the attention kernel by event edges.  When
- * `stream` has completed, so has the whole call; the call stays capturable.
- * Calls on several streams of one device share the side stream. */
+ * Workspace: sla_workspace_bytes (holds codes, selection, fp16 staging and
+ * the linear state, about 3 bytes per element of Q).  Every stage runs on
+ * `stream`, in the order listed under sla_stage. */
 sla_status sla_attention_fwd(const void *q, const void *k, const void *v,
                              int B, int H, int N, int d, int block, double keep,
-                             int phi, void *out, int out_dtype,
-                             float *out_linear, void *ws, size_t ws_bytes,
-                             void *stream);
+                             int phi, void *out, int out_dtype, void *ws,
+                             size_t ws_bytes, void *stream);
 
-/* Stages of sla_attention_fwd (see sla_attention_fwd_timed).  On the caller's
- * stream they run in the order STATS, KMEAN, LINEAR_PREP, LINEAR_FINAL,
- * SPARSE; TOPK and then SCHEDULE run on a library-owned side stream of the
- * device, after STATS and before SPARSE (event edges), overlapping the linear
- * staging.  The INT8 coding is
- * folded into STATS (Q) and LINEAR_PREP (K), so QUANTIZE, the coding as a pass
- * of its own (sla_quantize_qk), records nothing here. */
+/* Stages of sla_attention_fwd, all on the caller's stream in the order
+ * STATS, TOPK, SCHEDULE, KMEAN, LINEAR_PREP, LINEAR_FINAL, SPARSE.  The INT8
+ * coding is folded into STATS (Q) and LINEAR_PREP (K), so QUANTIZE, the
+ * coding as a pass of its own (sla_quantize_qk), records nothing here. */
 typedef enum sla_stage {
   SLA_STAGE_STATS = 0,        /* fp64 block sums, pooled block means of Q and K,  */
                               /* INT8 codes and scales of Q                       */
@@ -174,24 +176,23 @@ typedef enum sla_stage {
   SLA_N_STAGES = 8
 } sla_stage;
 
-/* sla_attention_fwd that also records caller-created HIP events (hipEvent_t,
- * same device) around its stages: stage_events[2*s] just before stage s is
- * enqueued and stage_events[2*s+1] just after.  With stage_events set, every
- * stage runs on `stream` in the order STATS, TOPK, SCHEDULE, KMEAN,
- * LINEAR_PREP, LINEAR_FINAL, SPARSE (no side stream), so that each is timed
- * alone; with NULL it is exactly sla_attention_fwd.  stage_events is NULL or holds
- * 2 * SLA_N_STAGES entries (SLA_N_STAGES grew from 7 to 8 in version 1.1.0),
- * any of which may be NULL; stages that a call skips (selection and schedule
- * when keep == 0, the schedule when the linear branch takes the direct form,
- * linear stages when phi == NONE, QUANTIZE always) record nothing.  Same
- * arguments, ownership and errors as sla_attention_fwd; a failed
- * hipEventRecord gives SLA_ERR_DEVICE. */
-sla_status sla_attention_fwd_timed(const void *q, const void *k, const void *v,
-                                   int B, int H, int N, int d, int block,
-                                   double keep, int phi, void *out,
-                                   int out_dtype, float *out_linear, void *ws,
-                                   size_t ws_bytes, void *stream,
-                                   void *const *stage_events);
+/* sla_attention_fwd with two optional extras, for tests and measurement:
+ *   out_linear    fp32 [B,H,N,128], the linear branch alone, or NULL   (out)
+ *   stage_events  NULL, or 2 * SLA_N_STAGES caller-created HIP events
+ *                 (hipEvent_t, same device; any entry may be NULL):
+ *                 stage_events[2*s] is recorded on `stream` just before
+ *                 stage s and stage_events[2*s+1] just after.  Stages a
+ *                 call skips (selection and schedule when keep == 0, the
+ *                 schedule when the linear branch takes the direct form,
+ *                 linear stages when phi == NONE, QUANTIZE always) record
+ *                 nothing.
+ * With both NULL it is exactly sla_attention_fwd.  Same arguments,
+ * ownership and errors; a failed hipEventRecord gives SLA_ERR_DEVICE. */
+sla_status sla_attention_fwd_ex(const void *q, const void *k, const void *v,
+                                int B, int H, int N, int d, int block,
+                                double keep, int phi, void *out, int out_dtype,
+                                float *out_linear, void *ws, size_t ws_bytes,
+                                void *stream, void *const *stage_events);
 
 /* Gradients of sla_attention_fwd (same q, k, v, keep, phi) for the output
  * gradient dout.  SLA is fine-tuned into the model it accelerates (news

@@ -43,14 +43,16 @@ def load() -> ctypes.CDLL:
     lib.sla_topk_count.restype = ctypes.c_int32
     lib.sla_workspace_size.argtypes = [c_int] * 6 + [c_double, c_int, ctypes.POINTER(c_size_t)]
     lib.sla_workspace_size.restype = c_int
+    lib.sla_workspace_bytes.argtypes = [c_int] * 5 + [c_double, c_int]
+    lib.sla_workspace_bytes.restype = c_size_t
     lib.sla_quantize_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 5 + [c_void_p] * 5 + [c_void_p, c_size_t, c_void_p]
     lib.sla_quantize_qk.restype = c_int
     lib.sla_block_select.argtypes = [c_void_p, c_void_p] + [c_int] * 5 + [c_double, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.sla_block_select.restype = c_int
-    lib.sla_attention_fwd.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.sla_attention_fwd.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_size_t, c_void_p]
     lib.sla_attention_fwd.restype = c_int
-    lib.sla_attention_fwd_timed.argtypes = lib.sla_attention_fwd.argtypes + [c_void_p]
-    lib.sla_attention_fwd_timed.restype = c_int
+    lib.sla_attention_fwd_ex.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]
+    lib.sla_attention_fwd_ex.restype = c_int
     lib.sla_attention_bwd.argtypes = [c_void_p] * 4 + [c_int] * 5 + [c_double, c_int] + [c_void_p] * 3 + [c_int, c_void_p, c_size_t, c_void_p]
     lib.sla_attention_bwd.restype = c_int
     lib.sla_attention_bwd_timed.argtypes = lib.sla_attention_bwd.argtypes + [c_void_p]
@@ -111,6 +113,12 @@ def workspace_size(op: int, B: int, H: int, N: int, keep: float = 0.0, phi="none
                                      PHI[phi] if isinstance(phi, str) else int(phi),
                                      ctypes.byref(out)), "sla_workspace_size")
     return out.value
+
+
+def workspace_bytes(B: int, H: int, N: int, keep: float, phi="elu1") -> int:
+    """Bytes of the forward workspace (0 for arguments no forward call accepts)."""
+    return int(load().sla_workspace_bytes(B, H, N, HEAD_DIM, BLOCK, float(keep),
+                                          PHI[phi] if isinstance(phi, str) else int(phi)))
 
 
 def _workspace(nbytes: int, device, ws):
@@ -175,9 +183,15 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0
     ph = PHI[phi] if isinstance(phi, str) else int(phi)
     nbytes = workspace_size(OP_ATTENTION, B, H, N, keep, ph)
     ws = _workspace(nbytes, dev, workspace)
-    _check(load().sla_attention_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep), ph,
-                                    _ptr(out), 1 if out_dtype == torch.float32 else 0, _ptr(lin),
-                                    _ptr(ws), ws.numel(), _stream(dev)), "sla_attention_fwd")
+    f32 = 1 if out_dtype == torch.float32 else 0
+    if lin is None:
+        _check(load().sla_attention_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep),
+                                        ph, _ptr(out), f32, _ptr(ws), ws.numel(), _stream(dev)),
+               "sla_attention_fwd")
+    else:
+        _check(load().sla_attention_fwd_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK,
+                                           float(keep), ph, _ptr(out), f32, _ptr(lin), _ptr(ws),
+                                           ws.numel(), _stream(dev), None), "sla_attention_fwd_ex")
     return (out, lin) if return_linear else out
 
 

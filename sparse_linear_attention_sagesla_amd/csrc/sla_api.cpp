@@ -6,7 +6,6 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <mutex>
 
 #include "../../include/sla.h"
 #include "sla_internal.h"
@@ -79,7 +78,7 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
       ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
       ws.hpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * D * sizeof(float)));
-      ws.zpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * sizeof(float)));
+      ws.zpart = reinterpret_cast<double*>(take(BH * sla::kLinChunks * D * sizeof(double)));
       ws.h16t = reinterpret_cast<uint16_t*>(take(BH * D * D * sizeof(uint16_t)));
       ws.hscale = reinterpret_cast<float*>(take(BH * sizeof(float)));
       ws.z = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
@@ -113,52 +112,21 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
       ws.sched = reinterpret_cast<int32_t*>(
           take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * s.k * sla::kGroup * sizeof(int32_t)));
     if (direct) {
-      ws.uidx = reinterpret_cast<int32_t*>(take(BH * Nb * (size_t)(s.Nb - s.k) * sizeof(int32_t)));
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
       ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
     } else if (phi != SLA_PHI_NONE && s.k < s.Nb) {
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
       ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
       ws.hpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * D * sizeof(float)));
-      ws.zpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * sizeof(float)));
-      ws.h16t = reinterpret_cast<uint16_t*>(take(BH * D * D * sizeof(uint16_t)));
-      ws.hscale = reinterpret_cast<float*>(take(BH * sizeof(float)));
-      ws.z = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
+      ws.zpart = reinterpret_cast<double*>(take(BH * sla::kLinChunks * D * sizeof(double)));
+      ws.hf = reinterpret_cast<float*>(take(BH * D * D * sizeof(float)));
+      ws.z64 = reinterpret_cast<double*>(take(BH * D * sizeof(double)));
     }
   }
   return off;
 }
 
 sla_status device_status(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_DEVICE; }
-
-// A side stream per device (non-blocking, default priority) on which the block
-// scores run while the caller's stream stages the linear branch: the fork and
-// the join are event edges, so the call stays asynchronous and capturable.
-// The fork/join sequence of a call is enqueued under the lock, so concurrent
-// calls never interleave their uses of the two events.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-hipError_t side_stream(SideStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideStream& ss = g_side[dev];
-  if (!ss.stream) {
-    e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-  }
-  *out = &ss;
-  return hipSuccess;
-}
 
 }  // namespace
 
@@ -190,6 +158,13 @@ sla_status sla_workspace_size(int op, int B, int H, int N, int d, int block, dou
   }
   *bytes = carve(op, make_shape(B, H, N, k), phi, nullptr, nullptr);
   return SLA_OK;
+}
+
+size_t sla_workspace_bytes(int B, int H, int N, int d, int block, double keep, int phi) {
+  size_t bytes = 0;
+  if (sla_workspace_size(SLA_OP_ATTENTION, B, H, N, d, block, keep, phi, &bytes) != SLA_OK) return 0;
+  if (phi == SLA_PHI_NONE && sla_topk_count((N + SLA_BLOCK - 1) / SLA_BLOCK, keep) == 0) return 0;
+  return bytes;
 }
 
 sla_status sla_quantize_qk(const void* q, const void* k, int B, int H, int N, int d, int block,
@@ -236,14 +211,14 @@ sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, i
   const auto* kb = static_cast<const uint16_t*>(k);
   hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, nullptr, nullptr, hs);
   if (e == hipSuccess)
-    e = sla::launch_block_topk(w.qbar, w.kbar, s, kblock_idx, kblock_mask, nullptr, hs);
+    e = sla::launch_block_topk(w.qbar, w.kbar, s, kblock_idx, kblock_mask, hs);
   return device_status(e);
 }
 
-sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, int B, int H,
-                                   int N, int d, int block, double keep, int phi, void* out,
-                                   int out_dtype, float* out_linear, void* ws, size_t ws_bytes,
-                                   void* stream, void* const* stage_events) {
+sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N,
+                                int d, int block, double keep, int phi, void* out, int out_dtype,
+                                float* out_linear, void* ws, size_t ws_bytes, void* stream,
+                                void* const* stage_events) {
   sla_status st = check_shape(B, H, N, d, block);
   if (st != SLA_OK) return st;
   if (!q || !k || !v || !out) return SLA_ERR_INVALID_ARG;
@@ -271,42 +246,25 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
   const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
   const bool direct = phi_eff != SLA_PHI_NONE && sla::linear_direct(s);
   hipError_t e = hipSuccess;
-  // runs one stage between its two optional events, on stream `on`
-  auto stage_on = [&](hipStream_t on, int id, auto&& launch) {
+  // runs one stage on the caller's stream between its two optional events
+  auto stage = [&](int id, auto&& launch) {
     if (e != hipSuccess) return;
     if (stage_events && stage_events[2 * id])
-      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id]), on);
+      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id]), hs);
     if (e == hipSuccess) e = launch();
     if (e == hipSuccess && stage_events && stage_events[2 * id + 1])
-      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + 1]), on);
+      e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + 1]), hs);
   };
-  auto stage = [&](int id, auto&& launch) { stage_on(hs, id, launch); };
-  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-  SideStream* side = nullptr;
-  // with stage events every stage runs on the caller's stream, one after
-  // another, so that each is timed alone
-  const bool fork = stage_events == nullptr;
   if (kk > 0) {
     stage(SLA_STAGE_STATS, [&] {
       return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs);
     });
-    // fork: the block scores and top-k need only the block means
-    hipStream_t sel = hs;
-    if (fork) {
-      side_lock.lock();
-      if (e == hipSuccess) e = side_stream(&side);
-      if (e == hipSuccess) e = hipEventRecord(side->fork, hs);
-      if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-      if (e == hipSuccess) sel = side->stream;
-    }
-    stage_on(sel, SLA_STAGE_TOPK, [&] {
-      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, direct ? w.uidx : nullptr, sel);
+    stage(SLA_STAGE_TOPK, [&] {
+      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, hs);
     });
-    // then the walk schedule, which needs only the kept lists
+    // the aligned walks of the query-block groups, from the kept lists alone
     if (!direct)
-      stage_on(sel, SLA_STAGE_SCHEDULE,
-               [&] { return sla::launch_group_schedule(w.idx, s, w.sched, sel); });
-    if (fork && e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+      stage(SLA_STAGE_SCHEDULE, [&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
   // Q is coded by the statistics pass and K by the staging pass (one read of
@@ -316,13 +274,10 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
                                    w.zpart, w.mu, kk > 0 ? w.k8 : nullptr, w.sk, hs);
   });
   if (phi_eff != SLA_PHI_NONE && !direct)
-    stage(SLA_STAGE_LINEAR_FINAL,
-          [&] { return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs); });
-  if (kk > 0 && fork) {
-    // join before the attention kernel
-    if (e == hipSuccess) e = hipStreamWaitEvent(hs, side->join, 0);
-    side_lock.unlock();
-  }
+    stage(SLA_STAGE_LINEAR_FINAL, [&] {
+      return sla::launch_linear_final(w.hpart, w.zpart, s, w.hf, w.z64, nullptr, nullptr, nullptr,
+                                      nullptr, hs);
+    });
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
                                   out_linear, hs);
@@ -332,9 +287,9 @@ sla_status sla_attention_fwd_timed(const void* q, const void* k, const void* v, 
 
 sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B, int H, int N,
                              int d, int block, double keep, int phi, void* out, int out_dtype,
-                             float* out_linear, void* ws, size_t ws_bytes, void* stream) {
-  return sla_attention_fwd_timed(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, out_linear,
-                                 ws, ws_bytes, stream, nullptr);
+                             void* ws, size_t ws_bytes, void* stream) {
+  return sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr, ws,
+                              ws_bytes, stream, nullptr);
 }
 
 sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, const void* dout,
@@ -380,7 +335,7 @@ sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, 
   mark(SLA_BWD_STAGE_FWD_STAGING, 0);
   if (kk > 0) {
     run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs); });
-    run([&] { return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, nullptr, hs); });
+    run([&] { return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, hs); });
     run([&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
     run([&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
@@ -390,7 +345,8 @@ sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, 
   });
   if (phi_eff != SLA_PHI_NONE)
     run([&] {
-      return sla::launch_linear_final(w.hpart, w.zpart, s, w.h16t, w.hscale, w.z, hs, bw.hb);
+      return sla::launch_linear_final(w.hpart, w.zpart, s, nullptr, nullptr, w.z, w.h16t, w.hscale,
+                                      bw.hb, hs);
     });
   mark(SLA_BWD_STAGE_FWD_STAGING, 1);
   // the backward's own staging
@@ -487,6 +443,6 @@ const char* sla_status_string(int status) {
   }
 }
 
-int sla_version(void) { return 10300; }
+int sla_version(void) { return 20000; }
 
 }  // extern "C"

@@ -18,6 +18,12 @@ constexpr int kMaxRowK = 16384;       // longest row of the W8A8 quantisers
 
 enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiRelu = 2 };
 
+// Lets `func` take up to `bytes` of dynamic LDS.  Set before every launch that
+// needs it, so the library holds no state of its own.
+inline hipError_t allow_lds(const void* func, int bytes) {
+  return hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 struct Shape {
   int B, H, N;
   int BH;   // B * H
@@ -37,17 +43,19 @@ struct Workspace {
   float* sq = nullptr;        // [BH, Nb]      block scales
   float* sk = nullptr;        // [BH, Nb]
   int32_t* idx = nullptr;     // [BH, Nb, k]   kept key blocks, ascending
-  int32_t* uidx = nullptr;    // [BH, Nb, Nb-k] the other key blocks (direct linear mode)
   int32_t* sched = nullptr;   // [BH, ceil(Nb/kGroup), k, kGroup] aligned walks of query-block
                               // groups: key block, -1 for none
   uint16_t* fk16 = nullptr;   // [BH, Nb, D, 64] fp16 phi(K)/16 per block, [channel][permuted key]
   uint16_t* v16 = nullptr;    // [BH, Nb, D, 64] fp16 V per block, [channel][permuted key]
   float* zb = nullptr;        // [BH, Nb, D]   fp32 per-block sum of phi(K)/16 over the keys
   float* hpart = nullptr;     // [BH, kLinChunks, D, D] partial phi(K)^T V
-  float* zpart = nullptr;     // [BH, kLinChunks, D]    partial sum phi(K)
-  uint16_t* h16t = nullptr;   // [BH, D(out), D(in)] fp16 H^T * 2^-s
-  float* hscale = nullptr;    // [BH] 2^s
-  float* z = nullptr;         // [BH, D] fp32 sum phi(K)/16
+  double* zpart = nullptr;    // [BH, kLinChunks, D]    partial sums of the block sums zb
+  float* hf = nullptr;        // [BH, 4, 8, 2, 64, 4] fp32 H = sum phi(K)/16 ^T V in the
+                              // attention kernel's M^T register layout (see sla_sparse.hip)
+  double* z64 = nullptr;      // [BH, D] fp64 sum of zb over all key blocks
+  uint16_t* h16t = nullptr;   // [BH, D(out), D(in)] fp16 H^T * 2^-s      (backward)
+  float* hscale = nullptr;    // [BH] 2^s                                  (backward)
+  float* z = nullptr;         // [BH, D] fp32 sum phi(K)/16               (backward)
 };
 
 // Extra device buffers of the backward (null when unused).
@@ -78,14 +86,17 @@ hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu
                            const Shape& sh, int8_t* q8, int8_t* k8, float* sq, float* sk,
                            bool k_only, hipStream_t s);
 hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
-                             int32_t* idx, uint32_t* mask, int32_t* uidx, hipStream_t s);
+                             int32_t* idx, uint32_t* mask, hipStream_t s);
 size_t topk_lds_bytes(int Nb, int* rows_per_group);
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
-                              float* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s);
-hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
-                               uint16_t* h16t, float* hscale, float* z, hipStream_t s,
-                               uint16_t* hb = nullptr);
+                              double* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s);
+// Whole-head linear state from the chunk partials.  The forward takes hf and
+// z64; the backward z, h16t, hscale and hb (bf16 H row-major); null outputs
+// are skipped.
+hipError_t launch_linear_final(float* hpart, const double* zpart, const Shape& sh, float* hf,
+                               double* z64, float* z, uint16_t* h16t, float* hscale,
+                               uint16_t* hb, hipStream_t s);
 // Linear-branch form: with few unselected blocks (Nb - k <= k) the branch is
 // summed directly over them; otherwise as whole-head sums minus the kept share.
 inline bool linear_direct(const Shape& sh) { return sh.Nb - sh.k <= sh.k; }

@@ -8,7 +8,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <mutex>
 
 #include "sla_internal.h"
 #include "sla_quant.h"
@@ -205,7 +204,7 @@ constexpr int kBins = 1024;
 template <int R>
 __global__ __launch_bounds__(256) void block_topk_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int Nb, int k,
-    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, int32_t* __restrict__ uidx) {
+    int32_t* __restrict__ idx, uint32_t* __restrict__ mask) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* qs = reinterpret_cast<double*>(smem);                              // [128][R]
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + R * kD * 8);           // [4][kBins]
@@ -399,8 +398,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
     }
     int32_t* out = idx + ((size_t)bh * Nb + i) * k;
     uint32_t* mrow = mask ? mask + ((size_t)bh * Nb + i) * ((Nb + 31) / 32) : nullptr;
-    int32_t* urow = uidx ? uidx + ((size_t)bh * Nb + i) * (Nb - k) : nullptr;
-    uint32_t base = 0, ubase = 0;
+    uint32_t base = 0;
     for (int jb = 0; jb < Nb; jb += 64) {
       const int j = jb + lane;
       const bool valid = j < Nb;
@@ -414,12 +412,6 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
         if (lane == 0) mrow[w0] = (uint32_t)sb;
         if (lane == 1 && w0 + 1 < (Nb + 31) / 32) mrow[w0 + 1] = (uint32_t)(sb >> 32);
       }
-      if (urow) {
-        const uint64_t ub = __ballot(valid && !sel);
-        const uint32_t upos = ubase + (uint32_t)__popcll(ub & lt_mask);
-        if (valid && !sel && upos < (uint32_t)(Nb - k)) urow[upos] = j;
-        ubase += (uint32_t)__popcll(ub);
-      }
       base += (uint32_t)__popcll(sb);
     }
   }
@@ -432,8 +424,9 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 //     [channel][permuted key] that the attention kernel reads as matrix-core
 //     operands (pad keys 0),
 //   * writes the block's sum of phi(K)/16 over its keys (fp32, per channel),
-//   * accumulates H = sum phi(K)^T V and z = sum phi(K) for the chunk
-//     (fp16 operands, fp32 accumulation, blocks in ascending order),
+//   * accumulates H = sum phi(K)^T V for the chunk (fp16 operands, fp32
+//     accumulation, blocks in ascending order) and the chunk's sum of those
+//     block sums in fp64,
 //   * when k8 is set, writes the INT8 codes and scale of the smoothed block
 //     K - mu (the quantiser's arithmetic, code_row8).
 // Permuted key order inside each 32-key half: position 8g+s holds key
@@ -460,7 +453,7 @@ template <int kMode>
 __global__ __launch_bounds__(256) void linear_prep_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int Nb, int phi,
     uint16_t* __restrict__ fk16, uint16_t* __restrict__ v16, float* __restrict__ zb,
-    float* __restrict__ hpart, float* __restrict__ zpart, const float* __restrict__ mu,
+    float* __restrict__ hpart, double* __restrict__ zpart, const float* __restrict__ mu,
     int8_t* __restrict__ k8, float* __restrict__ sk) {
   // LDS: transposed tiles [128 channels][64 positions] fp16 (see tpos)
   __shared__ __align__(16) _Float16 fkT[kD * kTRow];
@@ -486,7 +479,7 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 8; ++y) acc[x][y] = float4v{0.f, 0.f, 0.f, 0.f};
-  float zacc = 0.0f;
+  double zacc = 0.0;
   const bool quant = k8 != nullptr;  // workgroup-uniform
   const bool needk = kLinear || quant;
   float m8[8];
@@ -581,7 +574,7 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
         for (int e = 0; e < 8; ++e) zj += (float)hv[e];
       }
       zb[((size_t)bh * Nb + j) * kD + t] = zj;
-      if (kReduce) zacc += zj;
+      if (kReduce) zacc += (double)zj;
     }
     if (kReduce) {
       // H[c][e] += sum_pos fkT[c][pos] vT[e][pos]; wave owns c-tiles 2w, 2w+1
@@ -616,11 +609,24 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
   }
 }
 
-// Whole-head linear state, step 1: H (and z) as the chunk partials added in
-// chunk order.  Workgroup (bh, y) owns H elements [1024y, 1024y + 1024) and
-// writes the sum over chunk 0's slot (it alone reads and writes that range).
+// Position of H[c][d] (c: phi channel, d: value channel) in the attention
+// kernel's M^T register layout: wave w = c / 32 holds phi channels 32w + 16x +
+// l16 of value rows 16dt + 4g + r in lane 16g + l16, register (dt, x, r).
+__device__ __forceinline__ int h_frag_index(int c, int d) {
+  const int w = c >> 5, x = (c >> 4) & 1, l16 = c & 15;
+  const int dt = d >> 4, g = (d >> 2) & 3, r = d & 3;
+  return ((((w * 8 + dt) * 2 + x) * 64 + 16 * g + l16) << 2) + r;
+}
+
+// Whole-head linear state, step 1: H as the chunk partials added in chunk
+// order, and the fp64 sum of the chunk sums of the block sums zb.  Workgroup
+// (bh, y) owns H elements [1024y, 1024y + 1024) and writes the sum over chunk
+// 0's slot (it alone reads and writes that range) and, with hf set, into the
+// fragment layout.
 __global__ __launch_bounds__(256) void linear_sum_kernel(float* __restrict__ hpart,
-                                                         const float* __restrict__ zpart,
+                                                         const double* __restrict__ zpart,
+                                                         float* __restrict__ hf,
+                                                         double* __restrict__ z64,
                                                          float* __restrict__ z) {
   const int t = threadIdx.x;
   const int bh = blockIdx.x;
@@ -635,21 +641,23 @@ __global__ __launch_bounds__(256) void linear_sum_kernel(float* __restrict__ hpa
 #pragma unroll
     for (int c = 0; c < kLinChunks; ++c) s += v[c];
     hp[e] = s;
+    if (hf) hf[(size_t)bh * kD * kD + h_frag_index(e >> 7, e & 127)] = s;
   }
   if (blockIdx.y == 0 && t < kD) {
-    float v[kLinChunks];
+    double v[kLinChunks];
 #pragma unroll
     for (int c = 0; c < kLinChunks; ++c) v[c] = zpart[((size_t)bh * kLinChunks + c) * kD + t];
-    float s = 0.0f;
+    double s = 0.0;
 #pragma unroll
     for (int c = 0; c < kLinChunks; ++c) s += v[c];
-    z[(size_t)bh * kD + t] = s;
+    if (z64) z64[(size_t)bh * kD + t] = s;
+    if (z) z[(size_t)bh * kD + t] = (float)s;
   }
 }
 
-// Step 2: store H^T as fp16 scaled by 2^-s so that max|H| * 2^-s lies in
-// [2^14, 2^15), plus 2^s; with hb set, also H itself (row-major, unscaled)
-// as bf16 for the backward.
+// Step 2 (backward): store H^T as fp16 scaled by 2^-s so that max|H| * 2^-s
+// lies in [2^14, 2^15), plus 2^s; with hb set, also H itself (row-major,
+// unscaled) as bf16.
 __global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict__ hpart,
                                                          uint16_t* __restrict__ h16t,
                                                          float* __restrict__ hscale,
@@ -673,13 +681,15 @@ __global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict
   int s = 0;
   if (mx > 0.0f) s = ilogbf(mx) - 14;
   const float down = ldexpf(1.0f, -s);
-  if (t == 0) hscale[bh] = ldexpf(1.0f, s);
-  _Float16* out = reinterpret_cast<_Float16*>(h16t) + (size_t)bh * kD * kD;
+  if (t == 0 && hscale) hscale[bh] = ldexpf(1.0f, s);
+  if (h16t) {
+    _Float16* out = reinterpret_cast<_Float16*>(h16t) + (size_t)bh * kD * kD;
 #pragma unroll
-  for (int m = 0; m < 64; ++m) {
-    const int e = t + 256 * m;       // H[c][o] with c = e / 128, o = e % 128
-    const int c = e >> 7, o = e & 127;
-    out[(size_t)o * kD + c] = (_Float16)(hv[m] * down);
+    for (int m = 0; m < 64; ++m) {
+      const int e = t + 256 * m;     // H[c][o] with c = e / 128, o = e % 128
+      const int c = e >> 7, o = e & 127;
+      out[(size_t)o * kD + c] = (_Float16)(hv[m] * down);
+    }
   }
   if (hb) {
     __bf16* ob = reinterpret_cast<__bf16*>(hb) + (size_t)bh * kD * kD;
@@ -722,34 +732,28 @@ size_t topk_lds_bytes(int Nb, int* rows_per_group) {
 }
 
 hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
-                             int32_t* idx, uint32_t* mask, int32_t* uidx, hipStream_t s) {
+                             int32_t* idx, uint32_t* mask, hipStream_t s) {
   int R = 1;
   const size_t lds = topk_lds_bytes(sh.Nb, &R);
-  static std::once_flag once;
-  std::call_once(once, [] {
-    const int big = 160 * 1024;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<1>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<2>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<4>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(block_topk_kernel<8>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
-  });
+  const void* fn = R == 8   ? reinterpret_cast<const void*>(block_topk_kernel<8>)
+                   : R == 4 ? reinterpret_cast<const void*>(block_topk_kernel<4>)
+                   : R == 2 ? reinterpret_cast<const void*>(block_topk_kernel<2>)
+                            : reinterpret_cast<const void*>(block_topk_kernel<1>);
+  const hipError_t e = allow_lds(fn, (int)lds);
+  if (e != hipSuccess) return e;
   dim3 grid((sh.Nb + R - 1) / R, sh.BH);
   switch (R) {
-    case 8: block_topk_kernel<8><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
-    case 4: block_topk_kernel<4><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
-    case 2: block_topk_kernel<2><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
-    default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, uidx); break;
+    case 8: block_topk_kernel<8><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
+    case 4: block_topk_kernel<4><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
+    case 2: block_topk_kernel<2><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
+    default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
-                              float* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s) {
+                              double* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s) {
   dim3 grid(kLinChunks, sh.BH);
   if (phi == kPhiNone)
     linear_prep_kernel<0><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart, mu, k8, sk);
@@ -760,12 +764,12 @@ hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape&
   return hipGetLastError();
 }
 
-hipError_t launch_linear_final(float* hpart, const float* zpart, const Shape& sh,
-                               uint16_t* h16t, float* hscale, float* z, hipStream_t s,
-                               uint16_t* hb) {
-  linear_sum_kernel<<<dim3(sh.BH, kD * kD / 1024), 256, 0, s>>>(hpart, zpart, z);
+hipError_t launch_linear_final(float* hpart, const double* zpart, const Shape& sh, float* hf,
+                               double* z64, float* z, uint16_t* h16t, float* hscale,
+                               uint16_t* hb, hipStream_t s) {
+  linear_sum_kernel<<<dim3(sh.BH, kD * kD / 1024), 256, 0, s>>>(hpart, zpart, hf, z64, z);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || (!h16t && !hb)) return e;
   linear_cvt_kernel<<<sh.BH, 256, 0, s>>>(hpart, h16t, hscale, hb);
   return hipGetLastError();
 }

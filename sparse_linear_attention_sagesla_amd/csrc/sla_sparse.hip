@@ -22,21 +22,27 @@
 // rounding error on the dominant term of a peaked row); the accumulators are
 // rescaled only in tiles where some row's maximum rises.
 // Linear branch (same section, linear attention with phi = elu+1 / ReLU),
-// normalised, over the unselected blocks, in one of two forms:
-//   subtraction: numerator phi(Q)(H - M), denominator phi(Q)(z - z_M), with
-//                H, z the whole-head sums and M = sum phi(K_j)^T V_j,
-//                z_M = sum of the block sums of phi(K_j) over the kept tiles
-//                (kept tiles carry both branches);
+// normalised, over the unselected blocks U, in one of two forms:
+//   subtraction: H_U = H - M and z_U = z - z_M, with H, z the whole-head sums
+//                and M = sum phi(K_j)^T V_j, z_M = sum of the block sums of
+//                phi(K_j) over the kept tiles (kept tiles carry both
+//                branches); the differences are taken in fp32 (H, M) and
+//                fp64 (z, z_M) before anything is rounded to fp16, so their
+//                rounding is relative to the complement itself;
 //   direct:      M, z_M summed over the unselected tiles, walked after the
-//                kept ones (used when they are no more than the kept ones);
-//                numerator phi(Q)M, denominator phi(Q)z_M.
-// M is the query block's, shared by its four waves: at the end it is stored
-// once in LDS (fp16, power-of-two scaled) and multiplied by each wave's phi(Q).
+//                kept ones (used when they are no more than the kept ones).
+// The subtraction form still divides the rounding of the whole-head sums by
+// the unselected share f = phi(q)z_U / phi(q)z of a row's weight; a query
+// block with a valid row below kMinUnselectedShare falls back to the direct
+// walk, which is exact in form (a complement whose weights are all zero gives
+// a zero denominator and a zero output, as for the oracle).
+// The complement's sums are the query block's, shared by its four waves: at
+// the end they are stored once in LDS (fp16, power-of-two scaled) and
+// multiplied by each wave's phi(Q).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
-#include <mutex>
 
 #include "sla_internal.h"
 
@@ -183,14 +189,15 @@ struct SparseArgs {
   const float* sq;
   const float* sk;
   const int32_t* idx;
-  const int32_t* uidx;
   const int32_t* sched;
   const uint16_t* fk16;
   const uint16_t* v16;
   const float* zb;
-  const uint16_t* h16t;
-  const float* hscale;
-  const float* z;
+  const float* hf;        // whole-head H in the M^T register layout (forward)
+  const double* z64;      // whole-head sum of the block sums zb (forward)
+  const uint16_t* h16t;   // (backward)
+  const float* hscale;    // (backward)
+  const float* z;         // (backward)
   int N, Nb, Np, k;
   int phi;        // feature map for phi(Q)
   void* out;
@@ -204,7 +211,7 @@ struct State {
                   // row d = 16dt + 4g + r, phi channel 32w + 16x + l16
   float m_run;    // running log2-domain maximum (this lane's query)
   float l_part;   // this lane's share of the softmax normaliser
-  float zk;       // z_M, phi channel 32w + (lane & 31)
+  double zk;      // z_M, phi channel 32w + (lane & 31), summed in fp64
 };
 
 // Maximum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48).
@@ -278,7 +285,7 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int c = 0; c < 2; ++c) fk[x][c] = *(lds_half8*)(st + 2048 * x + (lo.rdK ^ (64 * c)));
-    S.zk += zj;
+    S.zk += (double)zj;
   }
   // The products below are most of the tile's matrix-core work.  The wave
   // running them gets issue priority over the other workgroup's wave on this
@@ -300,20 +307,47 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
   __builtin_amdgcn_s_setprio(0);
 }
 
-// Walks `n` tiles listed in `list` through the two LDS stages.
-template <bool kSoft, bool kLin>
-__device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_bytes,
-                                          const int32_t* list, int n, int stride,
-                                          const SparseArgs& a,
+// Key blocks of an ascending list, one per call (wave-uniform, in scalar
+// registers), clamped so a malformed list cannot address outside the staging
+// buffers.
+struct ListWalk {
+  const int32_t* list;
+  int Nb, p;
+  __device__ __forceinline__ int operator()() {
+    return min(max(ld_uniform(list, (size_t)p++), 0), Nb - 1);
+  }
+};
+
+// The key blocks an ascending list of k leaves out, ascending, one per call:
+// a merge of 0..Nb-1 against the list.  Every call advances, so a malformed
+// list still ends the walk (clamped to the last block).
+struct ComplementWalk {
+  const int32_t* sel;
+  int k, Nb, p, kv, j;
+  __device__ __forceinline__ ComplementWalk(const int32_t* s, int k_, int nb)
+      : sel(s), k(k_), Nb(nb), p(0), j(-1) {
+    kv = k > 0 ? ld_uniform(sel, 0) : Nb;
+  }
+  __device__ __forceinline__ int operator()() {
+    ++j;
+    while (j == kv) {
+      ++j;
+      ++p;
+      kv = p < k ? ld_uniform(sel, (size_t)p) : Nb;
+    }
+    return min(j, Nb - 1);
+  }
+};
+
+// Walks `n` tiles, the key block of each from `next` (called once per tile,
+// in order), through the two LDS stages.
+template <bool kSoft, bool kLin, typename Next>
+__device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_bytes, Next next,
+                                          int n, const SparseArgs& a,
                                           const TileSrc& src, size_t bh, const v4i qf[2],
                                           const LaneOffsets& lo, float qscale, int wave, int g) {
   if (n <= 0) return;
-  // wave-uniform key block of tile p (kept in scalar registers), clamped so a
-  // malformed list cannot address outside the staging buffers
-  auto block_of = [&](int p) {
-    return min(max(ld_uniform(list, (size_t)p * stride), 0), a.Nb - 1);
-  };
-  int j = block_of(0);
+  int j = next();
   issue_tile<kSoft, kLin>(smem, src, j, wave, lo);
   float zc = kLin ? load_zb(src, j, lo) : 0.0f;
   // lists are ascending, so only the last tile can be the ragged key block;
@@ -326,7 +360,7 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
       if (pp < nm) {
         lds_byte* cur = smem + half * stage_bytes;
         lds_byte* nxt = smem + (1 - half) * stage_bytes;
-        const int jn = block_of(pp + 1);
+        const int jn = next();
         wait_loads();
         lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
         issue_tile<kSoft, kLin>(nxt, src, jn, wave, lo);
@@ -433,7 +467,43 @@ __device__ __forceinline__ void init_query(const SparseArgs& a, size_t bh, int q
   }
   S.m_run = -INFINITY;
   S.l_part = 0.0f;
-  S.zk = 0.0f;
+  S.zk = 0.0;
+}
+
+// fp16 phi(Q) of this lane's query for the forward's linear branch, channels
+// 32cc + 8g + e (B operand of the products with the complement's sums), scaled
+// per row so that the row's largest feature lies in [1, 2).  The branch is a
+// ratio of two sums that are both linear in phi(q), so the factor cancels; it
+// keeps every row's features in fp16 range.  An elu+1 row whose entries are
+// all <= 0 takes exp(q - max q) (its largest feature exp(max q) scaled to 1),
+// so a row far below zero keeps its features.
+__device__ __forceinline__ void load_phi_q_row(const SparseArgs& a, size_t bh, int qrow,
+                                               bool qvalid, int g, half8 fq[4]) {
+  const uint16_t* qp = a.q + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD + 8 * g;
+  float x[4][8];
+  float xm = -INFINITY;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const uint4 u = *reinterpret_cast<const uint4*>(qp + 32 * cc);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[cc][e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+      xm = fmaxf(xm, x[cc][e]);
+    }
+  }
+  xm = fmaxf(xm, __shfl_xor(xm, 16));  // the row's 128 channels sit in lanes l16 + 16g
+  xm = fmaxf(xm, __shfl_xor(xm, 32));
+  const bool shifted = a.phi == kPhiElu1 && xm <= 0.0f;
+  const float fm = phi_apply(xm, a.phi);
+  const float sc = fm > 0.0f ? ldexpf(1.0f, -ilogbf(fm)) : 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = shifted ? __expf(x[cc][e] - xm) : phi_apply(x[cc][e], a.phi) * sc;
+      fq[cc][e] = qvalid ? (_Float16)f : (_Float16)0.0f;
+    }
 }
 
 // Maximum over the 64 lanes of a wave (DPP within rows, permlane across rows).
@@ -448,70 +518,48 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return max((uint32_t)b[0], (uint32_t)b[1]);
 }
 
-// The head's linear state for the subtraction form, staged in LDS after the
-// tiles are done: H^T (fp16, 128 rows of 256 bytes, chunk c of row r kept at
-// c ^ (r & 15) like M^T, so the same lane offsets read it) at kHOff and z
-// (fp32 [128]) after it.  LDS-direct loads, so they fly while M^T is formed.
-constexpr int kHOff = 40 * 1024;
-__device__ __forceinline__ void issue_linear_state(const SparseArgs& a, size_t bh, lds_byte* smem,
-                                                   int wave, int lane) {
-  const __amdgpu_buffer_rsrc_t hr = head_rsrc(a.h16t + bh * kD * kD, (size_t)kD * kD * 2);
-  const int r = 4 * wave + (lane >> 4);  // row within each 16-row round
-  const int voff = r * 256 + (((lane & 15) ^ (r & 15)) << 4);
-#pragma unroll
-  for (int m = 0; m < 8; ++m) lds_load16(hr, voff, 4096 * m, smem + kHOff + 4096 * m + 1024 * wave);
-  if (wave == 0) {
-    // lanes 32.. read past z and write zeros after it
-    const __amdgpu_buffer_rsrc_t zr = head_rsrc(a.z + bh * kD, (size_t)kD * 4);
-    lds_load16(zr, 16 * lane, 0, smem + kHOff + kD * kD * 2);
-  }
-}
+typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
-// The linear branch's share phi(Q) M for this lane's query (O^T layout, d =
-// 16dt + 4g + r) and phi(Q) z_M.  The workgroup's four waves hold M^T by
-// channel slices; M^T goes through LDS once as fp16 scaled by 2^-s so that
-// max|M| 2^-s lies in [2^14, 2^15), and comes back as A operands.
-__device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, const half8 fq[4],
-                                             const LaneOffsets& lo, int wave, int lane,
-                                             v4f num[8], float& den,
-                                             const SparseArgs* stage_state = nullptr,
-                                             size_t bh = 0) {
-  constexpr int kZOff = kD * kD * 2;             // z_M, fp32 [128]
-  constexpr int kRedOff = kZOff + kD * 4;        // per-wave maxima
-  const int g = lane >> 4, l16 = lane & 15;
+// Largest |x| of this lane's share of a matrix held in the M^T register layout.
+__device__ __forceinline__ float lane_absmax(const v4f x[8][2]) {
   float mx = 0.0f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S.mk[dt][x][r]));
-  const uint32_t wm = wave_max_u32(__float_as_uint(mx));  // non-negative floats order as integers
-  lds_barrier();  // every wave is done with the tile stages
-  if (stage_state) issue_linear_state(*stage_state, bh, smem, wave, lane);
-  if (lane == 0) *(__attribute__((address_space(3))) uint32_t*)(smem + kRedOff + 4 * wave) = wm;
-  if (lane < 32) *(__attribute__((address_space(3))) float*)(smem + kZOff + 4 * (32 * wave + lane)) = S.zk;
-  lds_barrier();
-  uint32_t m4 = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-    m4 = max(m4, *(__attribute__((address_space(3))) const uint32_t*)(smem + kRedOff + 4 * w));
-  const float mall = __uint_as_float(m4);
-  const int sh = mall > 0.0f ? ilogbf(mall) - 14 : 0;
-  const float down = ldexpf(1.0f, -sh);
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(x[dt][c][r]));
+  return mx;
+}
+
+// Power-of-two shift s that puts max * 2^-s in [2^14, 2^15) (0 for max = 0).
+__device__ __forceinline__ int stage_shift(float mx) { return mx > 0.0f ? ilogbf(mx) - 14 : 0; }
+
+// Stores the workgroup's 128x128 X^T, which the four waves hold in the M^T
+// register layout (row d = 16dt + 4g + r, column 32w + 16x + l16), in LDS at
+// [0, 32 KB) as fp16 times `down` (256-byte rows, chunk c of row r at
+// c ^ (r & 15)).
+__device__ __forceinline__ void store_xt(const v4f x[8][2], lds_byte* smem, float down, int wave,
+                                         int lane) {
   typedef __attribute__((address_space(3))) _Float16 lds_h;
+  const int g = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * dt + 4 * g + r;
-        const int ch = (4 * wave + 2 * x + (l16 >> 3)) ^ (row & 15);
-        *(lds_h*)(smem + row * 256 + ch * 16 + 2 * (l16 & 7)) = (_Float16)(S.mk[dt][x][r] * down);
+        const int ch = (4 * wave + 2 * c + (l16 >> 3)) ^ (row & 15);
+        *(lds_h*)(smem + row * 256 + ch * 16 + 2 * (l16 & 7)) = (_Float16)(x[dt][c][r] * down);
       }
-  lds_barrier();
-  const float up = ldexpf(1.0f, sh);
+}
+
+// phi(Q) X for this lane's query (O^T layout, d = 16dt + 4g + r) from the
+// staged X^T, times `up`.
+__device__ __forceinline__ void apply_xt(const lds_byte* smem, const LaneOffsets& lo,
+                                         const half8 fq[4], float up, v4f num[8]) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -522,40 +570,54 @@ __device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, con
     }
     num[dt] = acc * up;
   }
+}
+
+// phi(Q) M and phi(Q) z_M for this lane's query (O^T layout) from the
+// accumulated M^T and z_M: M^T goes through LDS once as fp16 (power-of-two
+// scaled) and comes back as A operands; z_M is left in LDS at kZOff as fp32.
+constexpr int kZOff = kD * kD * 2;             // z_M, fp32 [128]
+constexpr int kRedOff = kZOff + kD * 4;        // per-wave maxima
+__device__ __forceinline__ void linear_share(const State& S, lds_byte* smem, const half8 fq[4],
+                                             const LaneOffsets& lo, int wave, int lane,
+                                             v4f num[8], float& den) {
+  const int g = lane >> 4;
+  const uint32_t wm = wave_max_u32(__float_as_uint(lane_absmax(S.mk)));  // non-negative floats order as integers
+  lds_barrier();  // every wave is done with the tile stages
+  if (lane == 0) *(lds_u32*)(smem + kRedOff + 4 * wave) = wm;
+  if (lane < 32) *(lds_float*)(smem + kZOff + 4 * (32 * wave + lane)) = (float)S.zk;
+  lds_barrier();
+  uint32_t m4 = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m4 = max(m4, *(const lds_u32*)(smem + kRedOff + 4 * w));
+  const int sh = stage_shift(__uint_as_float(m4));
+  store_xt(S.mk, smem, ldexpf(1.0f, -sh), wave, lane);
+  lds_barrier();
+  apply_xt(smem, lo, fq, ldexpf(1.0f, sh), num);
   float d = 0.0f;
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      d += (float)fq[cc][e] * *(__attribute__((address_space(3))) const float*)(smem + kZOff + 4 * (32 * cc + 8 * g + e));
+      d += (float)fq[cc][e] * *(const lds_float*)(smem + kZOff + 4 * (32 * cc + 8 * g + e));
   d += __shfl_xor(d, 16);
   den = d + __shfl_xor(d, 32);
 }
 
-// Linear output in the subtraction form, from the kept share (nm, dm) that
-// linear_share returns: (phi(Q)H - phi(Q)M) / (phi(Q)z - phi(Q)z_M).  Returns
-// 1/den, 0 when the denominator is lost in rounding; den is in the staged
-// scale (phi/16 on both sides: 1/256 of the true denominator).  kStaged: H^T
-// and z come from LDS (issue_linear_state), else straight from memory.
-template <bool kStaged>
+// Linear output of the backward's query side in the subtraction form, from
+// the kept share (nm, dm) that linear_share returns: (phi(Q)H - phi(Q)M) /
+// (phi(Q)z - phi(Q)z_M), with H^T fp16-scaled and z from the backward's
+// linear state.  Returns 1/den, 0 when the denominator is lost in rounding;
+// den is in the staged scale (phi/16 on both sides: 1/256 of the true one).
 __device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t bh, int g,
-                                                     const lds_byte* smem, const LaneOffsets& lo,
-                                                     const half8 fq[4], const v4f nm[8], float dm,
-                                                     v4f ol[8]) {
+                                                     const LaneOffsets& lo, const half8 fq[4],
+                                                     const v4f nm[8], float dm, v4f ol[8]) {
   const float hs = a.hscale[bh];
-  if (kStaged) {
-    wait_loads();
-    lds_barrier();  // the staged H^T and z are in
-  }
-  typedef __attribute__((address_space(3))) const float lds_f;
   const float* zz = a.z + bh * kD;
   float dz = 0.0f;
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      dz += (float)fq[cc][e] * (kStaged ? *(lds_f*)(smem + kHOff + kD * kD * 2 + 4 * (32 * cc + 8 * g + e))
-                                        : zz[32 * cc + 8 * g + e]);
+    for (int e = 0; e < 8; ++e) dz += (float)fq[cc][e] * zz[32 * cc + 8 * g + e];
   dz += __shfl_xor(dz, 16);
   dz += __shfl_xor(dz, 32);
   // whole head minus the kept share; a denominator lost in rounding counts as 0
@@ -568,9 +630,7 @@ __device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t
                            (size_t)(16 * dt + (lo.rdM >> 8)) * kD + 8 * g;  // row 16dt + l16
     half8 ah[4];  // the row's four fragments, loaded together
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      ah[cc] = kStaged ? *(lds_half8*)(smem + kHOff + 4096 * dt + (lo.rdM ^ (64 * cc)))
-                       : *reinterpret_cast<const half8*>(hrow + 32 * cc);
+    for (int cc = 0; cc < 4; ++cc) ah[cc] = *reinterpret_cast<const half8*>(hrow + 32 * cc);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) num = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[cc], fq[cc], num, 0, 0, 0);
     ol[dt] = (num * hs - nm[dt]) * inv_den;
@@ -578,10 +638,25 @@ __device__ __forceinline__ float linear_subtract_out(const SparseArgs& a, size_t
   return inv_den;
 }
 
+// Smallest unselected share f = phi(q)z_U / phi(q)z of a valid row that the
+// subtraction form serves; a query block with a row below it takes the
+// direct walk.  With f >= 1/16 the whole-head and kept sums' fp32 rounding
+// (a relative 2^-24 per term, over a few hundred sequential sums) stays
+// below about 4e-4 of the branch's value scale.
+constexpr float kMinUnselectedShare = 1.0f / 16.0f;
+
+// Epilogue LDS of the subtraction form (the tile stages are free by then):
+// [0, 32 KB) the complement's H_U^T, then z_U and z (fp32 [128] each), then
+// per-wave words (maxima, fallback flags).
+constexpr int kEpZU = kD * kD * 2;
+constexpr int kEpZ = kEpZU + kD * 4;
+constexpr int kEpRed = kEpZ + kD * 4;
+
 // Normalise, add the linear branch, store this lane's query row.
 template <int kMode>
-__device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a, size_t bh,
-                                             int qrow, bool qvalid, lds_byte* smem,
+__device__ __forceinline__ void finish_query(State& S, const SparseArgs& a, size_t bh, int i,
+                                             int qrow, bool qvalid, lds_byte* smem, int stage_bytes,
+                                             const TileSrc& src, const v4i qf[2],
                                              const LaneOffsets& lo, int wave, int lane) {
   constexpr bool kLinAny = kMode != kSoftOnly;
   const int g = lane >> 4;
@@ -594,17 +669,88 @@ __device__ __forceinline__ void finish_query(const State& S, const SparseArgs& a
   for (int dt = 0; dt < 8; ++dt) ol[dt] = v4f{0.f, 0.f, 0.f, 0.f};
   if (kLinAny) {
     half8 fq[4];
-    load_phi_q(a, bh, qrow, qvalid, g, fq);
-    v4f nm[8];
-    float dm;
-    linear_share(S, smem, fq, lo, wave, lane, nm, dm, kMode == kSubtract ? &a : nullptr, bh);
-    if (kMode == kDirect) {
+    load_phi_q_row(a, bh, qrow, qvalid, g, fq);
+    bool direct = kMode == kDirect;
+    if (kMode == kSubtract) {
+      // whole-head sums: z (fp64, this lane's channel 32w + (lane & 31)) and
+      // H in this lane's M^T fragments, loaded together
+      const double zh = a.z64[bh * kD + 32 * wave + (lane & 31)];
+      const v4f* hp = reinterpret_cast<const v4f*>(a.hf) + (bh * 4 + wave) * (16 * 64) + lane;
+      v4f hr[8][2];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) hr[dt][c] = hp[(2 * dt + c) * 64];
+      const float zu = (float)fmax(zh - S.zk, 0.0);  // z_U, one rounding of the fp64 difference
+      lds_barrier();  // every wave is done with the tile stages
+      if (lane < 32) {
+        *(lds_float*)(smem + kEpZU + 4 * (32 * wave + lane)) = zu;
+        *(lds_float*)(smem + kEpZ + 4 * (32 * wave + lane)) = (float)zh;
+      }
+      lds_barrier();
+      float du = 0.0f, dz = 0.0f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 32 * cc + 8 * g + e;
+          const float f = (float)fq[cc][e];
+          du += f * *(const lds_float*)(smem + kEpZU + 4 * c);
+          dz += f * *(const lds_float*)(smem + kEpZ + 4 * c);
+        }
+      du += __shfl_xor(du, 16);
+      du += __shfl_xor(du, 32);
+      dz += __shfl_xor(dz, 16);
+      dz += __shfl_xor(dz, 32);
+      const bool need = qvalid && dz > 0.0f && du < kMinUnselectedShare * dz;
+      // H_U = H - M, taken in fp32 before anything is rounded to fp16
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) S.mk[dt][c] = hr[dt][c] - S.mk[dt][c];
+      const uint32_t wm = wave_max_u32(__float_as_uint(lane_absmax(S.mk)));
+      const uint32_t wneed = __builtin_amdgcn_ballot_w64(need) != 0 ? 1u : 0u;
+      if (lane == 0) {
+        *(lds_u32*)(smem + kEpRed + 4 * wave) = wm;
+        *(lds_u32*)(smem + kEpRed + 16 + 4 * wave) = wneed;
+      }
+      lds_barrier();
+      uint32_t m4 = 0, any = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        m4 = max(m4, *(const lds_u32*)(smem + kEpRed + 4 * w));
+        any |= *(const lds_u32*)(smem + kEpRed + 16 + 4 * w);
+      }
+      if (!any) {
+        const int sh = stage_shift(__uint_as_float(m4));
+        store_xt(S.mk, smem, ldexpf(1.0f, -sh), wave, lane);
+        lds_barrier();
+        v4f num[8];
+        apply_xt(smem, lo, fq, ldexpf(1.0f, sh), num);
+        const float inv_den = du > 0.0f ? 1.0f / du : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) ol[dt] = num[dt] * inv_den;
+      } else {
+        // a row's unselected share is too small for the subtraction: sum the
+        // complement directly
+        direct = true;
+        lds_barrier();  // every wave has read the words above; the stages are refilled next
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) S.mk[dt][0] = S.mk[dt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+        S.zk = 0.0;
+        const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
+        run_tiles<false, true>(S, smem, stage_bytes, ComplementWalk(sel, a.k, a.Nb), a.Nb - a.k, a,
+                               src, bh, qf, lo, 0.0f, wave, g);
+      }
+    }
+    if (direct) {
       // numerator and denominator summed over the unselected blocks
+      v4f nm[8];
+      float dm;
+      linear_share(S, smem, fq, lo, wave, lane, nm, dm);
       const float inv_den = dm > 0.0f ? 1.0f / dm : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) ol[dt] = nm[dt] * inv_den;
-    } else {
-      linear_subtract_out<true>(a, bh, g, smem, lo, fq, nm, dm, ol);
     }
   }
 
@@ -678,13 +824,13 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
     const int32_t* col = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
     run_sched<kLinAny>(S, smem, stage_bytes, col, a.k, a, src, bh, qf, lo, qscale, wave, g);
   } else {
-    const int nu = a.Nb - a.k;
     const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
-    const int32_t* usel = a.uidx + (bh * a.Nb + i) * (size_t)nu;
-    run_tiles<true, false>(S, smem, stage_bytes, sel, a.k, 1, a, src, bh, qf, lo, qscale, wave, g);
-    run_tiles<false, true>(S, smem, stage_bytes, usel, nu, 1, a, src, bh, qf, lo, qscale, wave, g);
+    run_tiles<true, false>(S, smem, stage_bytes, ListWalk{sel, a.Nb, 0}, a.k, a, src, bh, qf, lo,
+                           qscale, wave, g);
+    run_tiles<false, true>(S, smem, stage_bytes, ComplementWalk(sel, a.k, a.Nb), a.Nb - a.k, a,
+                           src, bh, qf, lo, qscale, wave, g);
   }
-  finish_query<kMode>(S, a, bh, qrow, qvalid, smem, lo, wave, lane);
+  finish_query<kMode>(S, a, bh, i, qrow, qvalid, smem, stage_bytes, src, qf, lo, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1048,9 +1194,8 @@ constexpr int kBwdVOff = kK8Bytes;                        // V rows [64 keys][12
 constexpr int kBwdKtOff = kK8Bytes + kF16TileBytes;       // K^T [128][64 perm keys] bf16
 constexpr int kBwdStage = kK8Bytes + 2 * kF16TileBytes;   // 40 KB
 constexpr int kMRowOff = 33 * 1024;                       // M row-major, after linear_share's area
-static_assert(kHOff + kD * kD * 2 + 1024 <= 2 * (kK8Bytes + 2 * kF16TileBytes),
-              "staged linear state exceeds the forward stages");
-constexpr int kZOffShared = kD * kD * 2;                  // z_M as linear_share leaves it (fp32 [128])
+static_assert(kRedOff + 16 <= kMRowOff, "linear_share's LDS area overlaps the row-major M");
+constexpr int kZOffShared = kZOff;                        // z_M as linear_share leaves it (fp32 [128])
 
 // Position of row t of a block in the permuted order of the transposed tiles
 // (inside each 32-row half: rows 4g..4g+3 at 8g.., rows 16+4g.. at 8g+4..).
@@ -1246,7 +1391,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
     float dm;
     linear_share(S, smem, fq, lo, wave, lane, nm, dm);
     v4f ol[8];
-    const float inv_den = linear_subtract_out<false>(a, bh, g, smem, lo, fq, nm, dm, ol);
+    const float inv_den = linear_subtract_out(a, bh, g, lo, fq, nm, dm, ol);
     float up = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -1674,11 +1819,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
 template <int kMode>
 hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
   constexpr size_t stage = (size_t)kK8Bytes + kF16TileBytes + (kMode != kSoftOnly ? kF16TileBytes : 0);
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * stage));
-  });
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>), (int)(2 * stage));
+  if (e != hipSuccess) return e;
   // grouped walks need every member's workgroup, so the block count is rounded up
   const int slots = kMode == kDirect ? sh.Nb : kGroup * ((sh.Nb + kGroup - 1) / kGroup);
   sparse_fwd_kernel<kMode><<<dim3(slots, sh.BH), 256, 2 * stage, s>>>(a);
@@ -1696,14 +1838,15 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.sq = ws.sq;
   a.sk = ws.sk;
   a.idx = ws.idx;
-  a.uidx = ws.uidx;
   a.sched = ws.sched;
   a.fk16 = ws.fk16;
   a.v16 = ws.v16;
   a.zb = ws.zb;
-  a.h16t = ws.h16t;
-  a.hscale = ws.hscale;
-  a.z = ws.z;
+  a.hf = ws.hf;
+  a.z64 = ws.z64;
+  a.h16t = nullptr;
+  a.hscale = nullptr;
+  a.z = nullptr;
   a.N = sh.N;
   a.Nb = sh.Nb;
   a.Np = sh.Np;
@@ -1751,13 +1894,10 @@ hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* do
   b.grad_f32 = grad_f32;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
   const int slots = kGroup * ((sh.Nb + kGroup - 1) / kGroup);
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kBwdStage);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_q_kernel<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kBwdStage);
-  });
+  const hipError_t e = allow_lds(lin ? reinterpret_cast<const void*>(bwd_q_kernel<true>)
+                                     : reinterpret_cast<const void*>(bwd_q_kernel<false>),
+                                 2 * kBwdStage);
+  if (e != hipSuccess) return e;
   if (lin)
     bwd_q_kernel<true><<<dim3(slots, sh.BH), 256, 2 * kBwdStage, s>>>(b);
   else
@@ -1793,13 +1933,10 @@ hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* d
   a.dv = dv;
   a.grad_f32 = grad_f32;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_kv_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kKvStage);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_kv_kernel<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kKvStage);
-  });
+  const hipError_t e = allow_lds(lin ? reinterpret_cast<const void*>(bwd_kv_kernel<true>)
+                                     : reinterpret_cast<const void*>(bwd_kv_kernel<false>),
+                                 2 * kKvStage);
+  if (e != hipSuccess) return e;
   if (lin)
     bwd_kv_kernel<true><<<dim3(sh.Nb, sh.BH), 256, 2 * kKvStage, s>>>(a);
   else
@@ -1810,13 +1947,11 @@ hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* d
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
                                  hipStream_t s) {
   if (sh.k <= 0) return hipSuccess;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(group_schedule_kernel<kGroup>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  });
+  const size_t lds = group_schedule_lds(sh.Nb, sh.k, kGroup);
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(group_schedule_kernel<kGroup>), (int)lds);
+  if (e != hipSuccess) return e;
   const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
-  group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, group_schedule_lds(sh.Nb, sh.k, kGroup), s>>>(
+  group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, lds, s>>>(
       idx, sh.Nb, sh.k, sh.N != sh.Nb * kBlk ? 1 : 0, sched);
   return hipGetLastError();
 }

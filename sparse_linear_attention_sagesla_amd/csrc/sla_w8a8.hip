@@ -19,7 +19,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <mutex>
 #include <type_traits>
 
 #include "sla_internal.h"
@@ -415,30 +414,32 @@ hipError_t launch_rowquant(const uint16_t* x, int rows, int K, bool norm, const 
   const int blocks = (rows + kRowWaves - 1) / kRowWaves;
   const int chunks = (K + 511) / 512;  // 8-value chunks per lane
   const size_t affine_lds = 8 * (size_t)K;  // gamma and beta as fp32
-  auto go = [&](auto kc) {
+  auto go = [&](auto kc) -> hipError_t {
     constexpr int C = decltype(kc)::value;
-    static std::once_flag once;
-    std::call_once(once, [] {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(rowquant_kernel<true, true, C>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 8 * kMaxRowK);
-    });
-    if (norm && (gamma || beta))
+    if (norm && (gamma || beta)) {
+      const hipError_t e = allow_lds(reinterpret_cast<const void*>(rowquant_kernel<true, true, C>),
+                                     (int)affine_lds);
+      if (e != hipSuccess) return e;
       rowquant_kernel<true, true, C><<<blocks, 64 * kRowWaves, affine_lds, s>>>(
           x, rows, K, gamma, beta, eps, codes, scale, mu, rstd);
-    else if (norm)
+    } else if (norm) {
       rowquant_kernel<true, false, C><<<blocks, 64 * kRowWaves, 0, s>>>(
           x, rows, K, nullptr, nullptr, eps, codes, scale, mu, rstd);
-    else
+    } else {
       rowquant_kernel<false, false, C><<<blocks, 64 * kRowWaves, 0, s>>>(
           x, rows, K, nullptr, nullptr, 0.0f, codes, scale, nullptr, nullptr);
+    }
+    return hipSuccess;
   };
-  if (chunks <= 2) go(std::integral_constant<int, 2>());
-  else if (chunks <= 4) go(std::integral_constant<int, 4>());
-  else if (chunks <= 8) go(std::integral_constant<int, 8>());
-  else if (chunks <= 10) go(std::integral_constant<int, 10>());
-  else if (chunks <= 16) go(std::integral_constant<int, 16>());
-  else if (chunks <= 24) go(std::integral_constant<int, 24>());
-  else go(std::integral_constant<int, kRowChunks>());
+  hipError_t e;
+  if (chunks <= 2) e = go(std::integral_constant<int, 2>());
+  else if (chunks <= 4) e = go(std::integral_constant<int, 4>());
+  else if (chunks <= 8) e = go(std::integral_constant<int, 8>());
+  else if (chunks <= 10) e = go(std::integral_constant<int, 10>());
+  else if (chunks <= 16) e = go(std::integral_constant<int, 16>());
+  else if (chunks <= 24) e = go(std::integral_constant<int, 24>());
+  else e = go(std::integral_constant<int, kRowChunks>());
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
@@ -461,11 +462,8 @@ hipError_t launch_w8a8_gemm(const int8_t* x8, const float* sx, const int8_t* w8,
   const int tiles = a.Mt * a.Nt;
   a.per_xcd = (tiles + 7) / 8;
   a.out_f32 = out_f32;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(w8a8_gemm_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kGLdsTotal);
-  });
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(w8a8_gemm_kernel), kGLdsTotal);
+  if (e != hipSuccess) return e;
   w8a8_gemm_kernel<<<8 * a.per_xcd, 64 * kGWaves, kGLdsTotal, s>>>(a);
   return hipGetLastError();
 }

@@ -172,6 +172,36 @@ def make_dout(wl: Workload | str, heads=None) -> np.ndarray:
     return out
 
 
+def peaked_inputs(N: int, hot_blocks, hot: float, cold: float, seed: int,
+                  neg_rows: int = 0, k_spread: float = 0.25, block: int = 64, d: int = D_HEAD):
+    """Q, K, V bf16 bits [N, d] with a fixed block structure (edge-case tests).
+
+    With E a standard normal clipped to [-3, 3] (so 1 + E/4 lies in
+    [0.25, 1.75]): Q = 1 + E/4, except the first ``neg_rows`` rows of every
+    block, which are -(1 + E/4); K rows of the blocks in ``hot_blocks`` are
+    hot * (1 + s E) and all other K rows cold * (1 + s E), s = ``k_spread``
+    (K draws its own E); V = 1 + N(0,1)/2.
+    Every query block then sees the hot key blocks above all others, and
+    ``cold`` sets how much the other blocks weigh against them.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 91])))
+
+    def e(shape):
+        return np.clip(rng.standard_normal(shape, dtype=np.float32), -3.0, 3.0)
+
+    q = np.float32(1.0) + np.float32(0.25) * e((N, d))
+    if neg_rows:
+        blk_row = np.arange(N) % block
+        q[blk_row < neg_rows] *= np.float32(-1.0)
+    rows_hot = np.zeros(N, dtype=bool)
+    for j in hot_blocks:
+        rows_hot[j * block:min(N, (j + 1) * block)] = True
+    mag = np.where(rows_hot, np.float32(hot), np.float32(cold)).astype(np.float32)
+    k = mag[:, None] * (np.float32(1.0) + np.float32(k_spread) * e((N, d)))
+    v = np.float32(1.0) + np.float32(0.5) * rng.standard_normal((N, d), dtype=np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
 def random_bf16(shape, seed: int, scale: float = 1.0, offset: float = 0.0) -> np.ndarray:
     """Plain N(offset, scale^2) bf16 bits, for edge-case tests."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77])))

@@ -77,8 +77,62 @@ def test_workspace_size_validation_and_growth():
 
 def _attn(q=FAKE, k=FAKE, v=FAKE, B=1, H=2, N=2048, d=128, block=64, keep=0.1, phi=1,
           out=FAKE, out_dtype=1, out_lin=NULL, ws=FAKE, ws_bytes=0):
-    return lib().sla_attention_fwd(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype,
-                                   out_lin, ws, ws_bytes, NULL)
+    ex = lib().sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype,
+                                    out_lin, ws, ws_bytes, NULL, NULL)
+    if out_lin.value is None:
+        plain = lib().sla_attention_fwd(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype,
+                                        ws, ws_bytes, NULL)
+        assert plain == ex
+    return ex
+
+
+def _prototype(name):
+    """Parameter list of `name` in include/sla.h, whitespace and comments removed."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
+    assert m, name
+    return [" ".join(p.split()) for p in m.group(1).split(",")]
+
+
+def test_boundary_entry_points_match_the_hot_path_contract():
+    """The three calls of the forward and the workspace query take exactly the
+    arguments of the hot-path contract: device pointers, sizes, block, keep,
+    phi, caller-owned workspace and the stream; no out_linear, no side stream."""
+    assert _prototype("sla_quantize_qk") == [
+        "const void *q", "const void *k", "int B", "int H", "int N", "int d", "int block",
+        "int8_t *q_i8", "int8_t *k_i8", "float *q_scale", "float *k_scale", "float *k_mean",
+        "void *ws", "size_t ws_bytes", "void *stream"]
+    assert _prototype("sla_block_select") == [
+        "const void *q", "const void *k", "int B", "int H", "int N", "int d", "int block",
+        "double keep", "int32_t *kblock_idx", "uint32_t *kblock_mask", "void *ws",
+        "size_t ws_bytes", "void *stream"]
+    assert _prototype("sla_attention_fwd") == [
+        "const void *q", "const void *k", "const void *v", "int B", "int H", "int N", "int d",
+        "int block", "double keep", "int phi", "void *out", "int out_dtype", "void *ws",
+        "size_t ws_bytes", "void *stream"]
+    assert _prototype("sla_workspace_bytes") == [
+        "int B", "int H", "int N", "int d", "int block", "double keep", "int phi"]
+    assert _prototype("sla_debug_qk_i32")[-1] == "void *stream"
+
+
+@pytest.mark.parametrize("B,H,N,keep,phi", [(1, 2, 2048, 0.1, 1), (1, 40, 75600, 0.1, 1),
+                                            (2, 3, 1000, 0.0, 2), (1, 1, 64, 1.0, 0),
+                                            (1, 4, 4096, 0.6, 1)])
+def test_workspace_bytes_covers_every_forward_call(B, H, N, keep, phi):
+    L = lib()
+    n = L.sla_workspace_bytes(B, H, N, 128, 64, keep, phi)
+    assert n == _ws(2, B=B, H=H, N=N, keep=keep, phi=phi)[1] > 0
+    assert n >= _ws(0, B=B, H=H, N=N)[1] and n >= _ws(1, B=B, H=H, N=N)[1]
+
+
+def test_workspace_bytes_is_zero_for_invalid_calls():
+    L = lib()
+    assert L.sla_workspace_bytes(1, 2, 2048, 64, 64, 0.1, 1) == 0       # d
+    assert L.sla_workspace_bytes(1, 2, 2048, 128, 32, 0.1, 1) == 0      # block
+    assert L.sla_workspace_bytes(0, 2, 2048, 128, 64, 0.1, 1) == 0      # B
+    assert L.sla_workspace_bytes(1, 2, 2048, 128, 64, 1.5, 1) == 0      # keep
+    assert L.sla_workspace_bytes(1, 2, 2048, 128, 64, 0.1, 9) == 0      # phi
+    assert L.sla_workspace_bytes(1, 2, 2048, 128, 64, 0.0, 0) == 0      # nothing to compute
 
 
 def test_attention_rejects_bad_arguments_before_launch():

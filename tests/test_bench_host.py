@@ -74,3 +74,28 @@ def test_committed_traffic_profile_names_its_source_hash():
             fields[key.strip()] = val.strip()
     assert len(fields.get("kernel_source_sha256", "")) == 64
     assert int(fields["traffic_bytes_per_launch"]) > 0
+
+
+def test_cpu_baseline_host_logic():
+    """The CPU-baseline leg on the tiny workload: one process per head, its
+    sample flagged and described, and the parity / selection summaries exact
+    when they are handed the oracle's own output and selection."""
+    import bench
+    from oracle import sla_oracle as O
+    from sparse_linear_attention_sagesla_amd.inputs import WORKLOADS, make_head
+    wl = WORKLOADS["tiny"]
+    blocks = sorted(set(np.linspace(0, 31, 6).astype(int).tolist()))
+    rows, idx = [], []
+    for h in range(wl.H):
+        q, k, v = make_head(wl, 0, h)
+        r = O.sla_forward_head(q, k, v, 64, 0.1, "elu1", query_blocks=blocks)
+        rows.append(r["out"].astype(np.float32))
+        idx.append(r["idx"])
+    base, parity, ties, used = bench.cpu_baseline(wl, 0.1, "elu1", np.stack(rows),
+                                                  np.stack(idx)[None], blocks_per_head=6)
+    assert used == blocks
+    assert base["sampled"] is True and base["kind"] == "oracle" and base["cores"] == 2
+    assert base["nproc"] >= 1 and base["cpu_model"] and base["value"] > 0
+    assert 0 < base["sample_fraction"] <= 1
+    assert parity["max_abs"] < 1e-6 and parity["rel_l2"] < 1e-7   # fp32 rounding only
+    assert ties == {"heads": 2, "rows_differing": 0, "near_ties_excused": 0, "unexcused": 0}

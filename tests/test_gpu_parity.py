@@ -176,6 +176,21 @@ def test_linear_branch_with_structured_values():
                           what=f"structured linear keep={keep} {phi} h{h}")
 
 
+def test_small_magnitude_values(tiny):
+    """V of magnitude 1e-4 (most entries below fp16's normal range once
+    staged): the staging keeps an absolute precision of 2^-25, far below the
+    output's scale, so the relative bar still holds."""
+    from sparse_linear_attention_sagesla_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    Q, K, V = tiny
+    V = f32_to_bf16_bits(bf16_bits_to_f32(V) * np.float32(1e-4))
+    q, k, v = _case("small V", Q, K, V)
+    for keep, phi in ((0.1, "elu1"), (1.0, "none")):
+        out = sla.attention(q, k, v, keep, phi, torch.float32).cpu().numpy()
+        for h in range(2):
+            r = _oracle_out(Q, K, V, keep, phi, h)
+            assert_parity(out[0, h], r["out"], atol=2e-7, what=f"small V keep={keep} {phi} h{h}")
+
+
 def test_attention_deterministic(tiny):
     Q, K, V = tiny
     q, k, v = _case("determinism", Q, K, V)

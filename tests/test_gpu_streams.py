@@ -1,12 +1,17 @@
 """The attention call on two caller streams at once, and inside a captured graph.
 
-A call forks its block scores and walk schedule to a side stream that the
-library owns and joins them back with event edges before the attention
-kernel.  Calls running on two streams at once, and a captured HIP graph
-replayed several times with other work between the replays, must give the
-same output bits as plain calls on one stream (every kernel is
-deterministic).
+A call enqueues all its work on the caller's stream and the library keeps no
+state between calls.  Calls running on two streams at once, and a captured
+HIP graph replayed several times with other work between the replays, must
+give the same output bits as plain calls on one stream (every kernel is
+deterministic); so must a graph captured around the very first call a fresh
+process makes.
 """
+import os
+import subprocess
+import sys
+import textwrap
+
 import numpy as np
 import pytest
 
@@ -65,3 +70,40 @@ def test_graph_capture_replays(keep, phi):
         torch.cuda.synchronize()
         print(f"[graph] keep {keep} phi {phi} replay {rep}", flush=True)
         assert torch.equal(out, eager), f"replay {rep}"
+
+
+FIRST_CALL_IN_CAPTURE = textwrap.dedent("""
+    import sys
+    sys.path.insert(0, sys.argv[1])
+    import torch
+    import sparse_linear_attention_sagesla_amd as sla
+    from sparse_linear_attention_sagesla_amd.inputs import random_bf16
+    shape = (1, 3, 64 * 40 - 23, 128)
+    q, k, v = (torch.from_numpy(random_bf16(shape, 41 + t).view("int16")).view(torch.bfloat16).cuda()
+               for t in range(3))
+    att = sla.SLAAttention(*shape[:3], keep=0.1, phi="elu1", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):      # the process's first library call
+        out = att(q, k, v)
+    outs = []
+    for rep in range(3):
+        att.out.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    eager = sla.attention(q, k, v, 0.1, "elu1", torch.float32)
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, eager) for o in outs), "replay differs from the eager call"
+    print("first call captured: ok", flush=True)
+""")
+
+
+def test_first_call_of_a_process_inside_graph_capture():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("[graph] fresh process, first call captured", flush=True)
+    res = subprocess.run([sys.executable, "-c", FIRST_CALL_IN_CAPTURE, root], capture_output=True,
+                         text=True, timeout=240)
+    print(res.stdout[-2000:], res.stderr[-2000:], flush=True)
+    assert res.returncode == 0 and "first call captured: ok" in res.stdout
