@@ -80,33 +80,41 @@ def _head_streams(seed: int, b: int, h: int):
     return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3)]
 
 
+# Every step below is element-wise float32 arithmetic in a fixed order (no
+# matrix products), so the bits do not depend on the BLAS library, its thread
+# count or the threads that call it.
+
 def _rank8(rng: np.random.Generator, N: int, d: int) -> np.ndarray:
     U = rng.standard_normal((N, 8), dtype=np.float32)
     A = rng.standard_normal((8, d), dtype=np.float32)
     E = rng.standard_normal((N, d), dtype=np.float32)
-    return U @ A + np.float32(0.5) * E
+    x = U[:, 0:1] * A[0]
+    for r in range(1, 8):
+        x = x + U[:, r:r + 1] * A[r]
+    return x + np.float32(0.5) * E
 
 
-def _interp_matrix(n: int, spacing: int = 4) -> np.ndarray:
-    """Linear interpolation weights from a lattice every `spacing` samples to n samples."""
-    m = (n - 1) // spacing + 2
-    L = np.zeros((n, m), dtype=np.float32)
-    for x in range(n):
-        i0, f = divmod(x, spacing)
-        f = f / spacing
-        L[x, i0] += 1.0 - f
-        L[x, i0 + 1] += f
-    return L
+def _interp_axis(x: np.ndarray, n: int, axis: int, spacing: int = 4) -> np.ndarray:
+    """Linear interpolation along `axis` from a lattice every `spacing` samples
+    to n samples: sample t = (1 - f) x[i] + f x[i + 1], i = t // spacing,
+    f = (t % spacing) / spacing."""
+    t = np.arange(n)
+    f = ((t % spacing) / spacing).astype(np.float32)
+    shape = [1] * x.ndim
+    shape[axis] = n
+    a = np.take(x, t // spacing, axis=axis)
+    b = np.take(x, t // spacing + 1, axis=axis)
+    return a * (np.float32(1.0) - f).reshape(shape) + b * f.reshape(shape)
 
 
 def _smooth_field(rng: np.random.Generator, grid, d: int) -> np.ndarray:
     T, Hg, W = grid
-    Lt, Lh, Lw = _interp_matrix(T), _interp_matrix(Hg), _interp_matrix(W)
-    lat = rng.standard_normal((Lt.shape[1], Lh.shape[1], Lw.shape[1], d), dtype=np.float32)
-    # separable trilinear interpolation: contract W, then Hg, then T
-    f = np.einsum("we,abec->abwc", Lw, lat, optimize=True)
-    f = np.einsum("hb,abwc->ahwc", Lh, f, optimize=True)
-    f = np.einsum("ta,ahwc->thwc", Lt, f, optimize=True)
+    m = [(n - 1) // 4 + 2 for n in grid]
+    lat = rng.standard_normal((m[0], m[1], m[2], d), dtype=np.float32)
+    # separable trilinear interpolation: along W, then Hg, then T
+    f = _interp_axis(lat, W, 2)
+    f = _interp_axis(f, Hg, 1)
+    f = _interp_axis(f, T, 0)
     f = f.reshape(T * Hg * W, d)
     std = f.std(axis=0, dtype=np.float64).astype(np.float32)
     return f / std
