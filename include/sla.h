@@ -55,13 +55,16 @@ extern "C" {
 #define SLA_BLOCK 64
 #define SLA_HEAD_DIM 128
 #define SLA_MAX_TOKENS (1 << 20)
+#define SLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum sla_status {
   SLA_OK = 0,
   SLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, keep outside [0,1], ... */
   SLA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement     */
   SLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
-  SLA_ERR_DEVICE = 4       /* a HIP call or kernel launch failed              */
+  SLA_ERR_DEVICE = 4,      /* a HIP call or kernel launch failed              */
+  SLA_ERR_SCRATCH = 5      /* shape needs more than sla_attention_fwd_noalloc's
+                              static scratch (SLA_NOALLOC_SCRATCH_BYTES)       */
 } sla_status;
 
 typedef enum sla_phi {
@@ -193,6 +196,25 @@ sla_status sla_attention_fwd_ex(const void *q, const void *k, const void *v,
                                 double keep, int phi, void *out, int out_dtype,
                                 float *out_linear, void *ws, size_t ws_bytes,
                                 void *stream, void *const *stage_events);
+
+/* sla_attention_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a static device array of the library,
+ * SLA_NOALLOC_SCRATCH_BYTES (64 MiB) on each device, which that device holds
+ * until the process ends.  The call itself allocates nothing; the caller
+ * passes inputs and output as for sla_attention_fwd (same arguments,
+ * numerics and errors, bit-identical output).  Shapes whose workspace
+ * (sla_workspace_bytes) exceeds the scratch are rejected with
+ * SLA_ERR_SCRATCH before anything is enqueued (e.g. B*H = 2 at N = 2048 needs
+ * 6.3 MiB, one head at N = 32760 27 MiB).  Every call on a device shares its
+ * scratch and nothing in it needs to start at zero; calls that overlap on one
+ * device (other streams, other threads) race on it, so the caller orders
+ * them.  The first call on a device looks up the scratch's device address
+ * (kept per device for the life of the process). */
+sla_status sla_attention_fwd_noalloc(const void *q, const void *k,
+                                     const void *v, int B, int H, int N, int d,
+                                     int block, double keep, int phi, void *out,
+                                     int out_dtype, void *stream);
 
 /* Gradients of sla_attention_fwd (same q, k, v, keep, phi) for the output
  * gradient dout.  SLA is fine-tuned into the model it accelerates (news

@@ -14,7 +14,9 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 
-SLA_OK, SLA_ERR_INVALID_ARG, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_DEVICE = range(5)
+(SLA_OK, SLA_ERR_INVALID_ARG, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_DEVICE,
+ SLA_ERR_SCRATCH) = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 PHI = {"none": 0, "elu1": 1, "relu": 2}
 OP_QUANTIZE, OP_SELECT, OP_ATTENTION, OP_ATTENTION_BWD = 0, 1, 2, 3
 BLOCK = 64
@@ -53,6 +55,8 @@ def load() -> ctypes.CDLL:
     lib.sla_attention_fwd.restype = c_int
     lib.sla_attention_fwd_ex.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]
     lib.sla_attention_fwd_ex.restype = c_int
+    lib.sla_attention_fwd_noalloc.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p]
+    lib.sla_attention_fwd_noalloc.restype = c_int
     lib.sla_attention_bwd.argtypes = [c_void_p] * 4 + [c_int] * 5 + [c_double, c_int] + [c_void_p] * 3 + [c_int, c_void_p, c_size_t, c_void_p]
     lib.sla_attention_bwd.restype = c_int
     lib.sla_attention_bwd_timed.argtypes = lib.sla_attention_bwd.argtypes + [c_void_p]
@@ -193,6 +197,23 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0
                                            float(keep), ph, _ptr(out), f32, _ptr(lin), _ptr(ws),
                                            ws.numel(), _stream(dev), None), "sla_attention_fwd_ex")
     return (out, lin) if return_linear else out
+
+
+def attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                      keep: float = 0.1, phi: str = "elu1"):
+    """SageSLA forward into a preallocated ``out`` (bf16 or fp32), with the
+    library's static device scratch as workspace: nothing is allocated."""
+    q, k, v = _bhnd(q, "q"), _bhnd(k, "k"), _bhnd(v, "v")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if out.shape != q.shape or out.dtype not in (torch.bfloat16, torch.float32) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 or fp32 tensor of q's shape")
+    B, H, N, d = q.shape
+    ph = PHI[phi] if isinstance(phi, str) else int(phi)
+    _check(load().sla_attention_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep),
+                                            ph, _ptr(out), 1 if out.dtype == torch.float32 else 0,
+                                            _stream(q.device)), "sla_attention_fwd_noalloc")
+    return out
 
 
 def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,

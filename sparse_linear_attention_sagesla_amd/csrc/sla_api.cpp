@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sla.h"
 #include "sla_internal.h"
@@ -128,6 +129,54 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
 
 sla_status device_status(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_DEVICE; }
 
+// The workspace of sla_attention_fwd_noalloc: a static device array, one copy
+// per device, alive until the process ends.  In host code its name is only a
+// stand-in; kernels get the device address that hipGetSymbolAddress returns,
+// looked up once per device (with that device current) and kept here.
+static_assert(SLA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[SLA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Argument checks of the forward that come before the workspace.
+sla_status check_fwd_args(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                          int block, double keep, int phi, const void* out, int out_dtype,
+                          const float* out_linear) {
+  sla_status st = check_shape(B, H, N, d, block);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !v || !out) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (out_linear && !aligned16(out_linear)))
+    return SLA_ERR_INVALID_ARG;
+  if (std::isnan(keep) || keep < 0.0 || keep > 1.0) return SLA_ERR_INVALID_ARG;
+  if (phi < SLA_PHI_NONE || phi > SLA_PHI_RELU) return SLA_ERR_INVALID_ARG;
+  if (out_dtype != SLA_OUT_BF16 && out_dtype != SLA_OUT_F32) return SLA_ERR_INVALID_ARG;
+  const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
+  const int kk = sla_topk_count(Nb, keep);
+  if (kk == 0 && phi == SLA_PHI_NONE) return SLA_ERR_INVALID_ARG;
+  int R = 1;
+  if (kk > 0 && sla::topk_lds_bytes(Nb, &R) > 160 * 1024) return SLA_ERR_UNSUPPORTED;
+  return SLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,20 +268,11 @@ sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int
                                 int d, int block, double keep, int phi, void* out, int out_dtype,
                                 float* out_linear, void* ws, size_t ws_bytes, void* stream,
                                 void* const* stage_events) {
-  sla_status st = check_shape(B, H, N, d, block);
+  const sla_status st =
+      check_fwd_args(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, out_linear);
   if (st != SLA_OK) return st;
-  if (!q || !k || !v || !out) return SLA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-      (out_linear && !aligned16(out_linear)))
-    return SLA_ERR_INVALID_ARG;
-  if (std::isnan(keep) || keep < 0.0 || keep > 1.0) return SLA_ERR_INVALID_ARG;
-  if (phi < SLA_PHI_NONE || phi > SLA_PHI_RELU) return SLA_ERR_INVALID_ARG;
-  if (out_dtype != SLA_OUT_BF16 && out_dtype != SLA_OUT_F32) return SLA_ERR_INVALID_ARG;
   const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
   const int kk = sla_topk_count(Nb, keep);
-  if (kk == 0 && phi == SLA_PHI_NONE) return SLA_ERR_INVALID_ARG;
-  int R = 1;
-  if (kk > 0 && sla::topk_lds_bytes(Nb, &R) > 160 * 1024) return SLA_ERR_UNSUPPORTED;
   const Shape s = make_shape(B, H, N, kk);
   const size_t need = carve(SLA_OP_ATTENTION, s, phi, nullptr, nullptr);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
@@ -290,6 +330,20 @@ sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B,
                              void* ws, size_t ws_bytes, void* stream) {
   return sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr, ws,
                               ws_bytes, stream, nullptr);
+}
+
+sla_status sla_attention_fwd_noalloc(const void* q, const void* k, const void* v, int B, int H,
+                                     int N, int d, int block, double keep, int phi, void* out,
+                                     int out_dtype, void* stream) {
+  const sla_status st = check_fwd_args(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr);
+  if (st != SLA_OK) return st;
+  const size_t need = sla_workspace_bytes(B, H, N, d, block, keep, phi);
+  if (need == 0 || need > SLA_NOALLOC_SCRATCH_BYTES) return SLA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return SLA_ERR_DEVICE;
+  return sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr, ws,
+                              SLA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, const void* dout,
@@ -439,6 +493,8 @@ const char* sla_status_string(int status) {
     case SLA_ERR_UNSUPPORTED: return "SLA_ERR_UNSUPPORTED: shape or option not supported";
     case SLA_ERR_WORKSPACE: return "SLA_ERR_WORKSPACE: workspace missing or too small";
     case SLA_ERR_DEVICE: return "SLA_ERR_DEVICE: HIP launch failed";
+    case SLA_ERR_SCRATCH:
+      return "SLA_ERR_SCRATCH: shape needs more workspace than the 64 MiB static scratch";
     default: return "unknown sla_status";
   }
 }

@@ -239,3 +239,22 @@ def test_w8a8_entry_points_reject_bad_arguments():
         assert L.sla_w8a8_linear(*bad) == INVALID
     bad = list(args); bad[5] = 1 << 20; bad[7] = 4096  # M * K >= 2^31
     assert L.sla_w8a8_linear(*bad) == UNSUPPORTED
+
+
+def test_noalloc_validates_on_the_host():
+    """sla_attention_fwd_noalloc rejects bad arguments and shapes beyond its
+    static scratch before any device call."""
+    L = lib()
+    f = L.sla_attention_fwd_noalloc
+    f.restype = ctypes.c_int
+
+    def call(B=1, H=2, N=2048, d=128, keep=0.1, phi=1, q=FAKE, out=FAKE, out_dtype=1):
+        return f(q, FAKE, FAKE, B, H, N, d, 64, ctypes.c_double(keep), phi, out, out_dtype, NULL)
+
+    assert call(H=40, N=75600) == 5                      # SLA_ERR_SCRATCH
+    assert b"scratch" in L.sla_status_string(5)
+    assert call(d=64) == UNSUPPORTED
+    assert call(q=NULL) == INVALID
+    assert call(out=MISALIGNED) == INVALID
+    assert call(keep=0.0, phi=0) == INVALID
+    assert call(out_dtype=3) == INVALID
