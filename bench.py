@@ -221,6 +221,56 @@ def cpu_baseline(wl, keep, phi, gpu_out_rows=None, gpu_idx=None, blocks_per_head
     return out, parity, ties, blocks
 
 
+def lowbit_leg(lib, _lib, op, q, k, v, wl, keep, phi, f16_equiv, exact_sparse_ms, steps, stream):
+    """sla_attention_fwd_lowbit (phi(K) of the linear branch in FP8) on the same
+    inputs: ms per call, and the attention kernel's time and roofline from
+    calls with stage events (same algorithmic work as the exact forward)."""
+    import torch
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    ph = _lib.PHI[phi]
+
+    def call(events=None):
+        ev = (ctypes.c_void_p * len(events))(*events) if events else None
+        rc = lib.sla_attention_fwd_ex(
+            _lib._ptr(q), _lib._ptr(k), _lib._ptr(v), B, H, N, d, 64, float(keep), ph,
+            _lib._ptr(op.out), 0, None, _lib._ptr(op.workspace), op.workspace.numel(),
+            ctypes.c_void_p(stream.cuda_stream), ev, _lib.OPT_PHI_K_FP8)
+        if rc != 0:
+            raise RuntimeError(lib.sla_status_string(rc).decode())
+
+    call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    hip = HipEvents()
+    evs = [hip.create(2 * len(STAGES)) for _ in range(steps)]
+    for e in evs:
+        call(e)
+    torch.cuda.synchronize()
+    si = STAGES.index("sparse")
+    sparse_ms = float(np.mean([hip.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]))
+    for e in evs:
+        hip.destroy(e)
+    achieved = f16_equiv / (sparse_ms * 1e-3) / 1e12
+    log(f"[bench] lowbit: {ms:.3f} ms/call, attention kernel {sparse_ms:.3f} ms")
+    return {"ms_per_call": round(ms, 4), "steps": steps, "sparse_ms": round(sparse_ms, 4),
+            "sparse_speedup_vs_exact": round(exact_sparse_ms / sparse_ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                         "peak": PEAK_F16_FLOPS / 1e12, "unit": "TFLOP/s",
+                         "frac": round(achieved / (PEAK_F16_FLOPS / 1e12), 4),
+                         "kernel": "sparse_fwd_kernel (FP8 phi(K))",
+                         "note": "the products stay INT8 and fp16 (phi(K) is decoded to fp16 "
+                                 "as it is read), so the peak is the fp16 one; 32 instead of "
+                                 "40 KB staged per kept pair"},
+            "note": "opt-in: linear branch's phi(K) as FP8 e4m3 with one power-of-two scale "
+                    "per key block"}
+
+
 def backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, fwd_ms, steps, stream, dev):
     """sla_attention_bwd on the same inputs and a seeded dO: ms per call (one
     warmup call, then `steps` timed calls back to back, bf16 gradients)."""
@@ -364,6 +414,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3,
                     help="also time this many sla_attention_bwd calls (0: skip)")
+    ap.add_argument("--lowbit-steps", type=int, default=5,
+                    help="also time this many calls of the lower-bit forward (0: skip)")
     ap.add_argument("--w8a8-steps", type=int, default=5,
                     help="also time this many FusedNorm + W8A8 GEMM calls at the Wan-14B "
                          "FFN shape (0: skip)")
@@ -425,7 +477,7 @@ def main():
             rc = lib.sla_attention_fwd_ex(
                 _lib._ptr(q), _lib._ptr(k), _lib._ptr(v), B, H, N, d, 64, float(keep), ph,
                 _lib._ptr(op.out), 0, None, _lib._ptr(op.workspace), op.workspace.numel(),
-                ctypes.c_void_p(stream.cuda_stream), ev)
+                ctypes.c_void_p(stream.cuda_stream), ev, 0)
         if rc != 0:
             raise RuntimeError(lib.sla_status_string(rc).decode())
 
@@ -513,6 +565,9 @@ def main():
         "call_roofline_frac": round(ideal_s / (ms_step * 1e-3), 4),
         "roofline": roofline,
     }
+    if args.lowbit_steps > 0 and linear:
+        rec["lowbit"] = lowbit_leg(lib, _lib, op, q, k, v, wl, keep, phi, f16_equiv,
+                                   stage_ms["sparse"], args.lowbit_steps, stream)
     if args.backward_steps > 0:
         rec["backward"] = backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, ms_step,
                                        args.backward_steps, stream, dev)

@@ -179,7 +179,10 @@ typedef enum sla_stage {
   SLA_N_STAGES = 8
 } sla_stage;
 
-/* sla_attention_fwd with two optional extras, for tests and measurement:
+/* Options of sla_attention_fwd_ex (bit flags). */
+#define SLA_OPT_PHI_K_FP8 1 /* lower-bit option, see sla_attention_fwd_lowbit */
+
+/* sla_attention_fwd with optional extras, for tests and measurement:
  *   out_linear    fp32 [B,H,N,128], the linear branch alone, or NULL   (out)
  *   stage_events  NULL, or 2 * SLA_N_STAGES caller-created HIP events
  *                 (hipEvent_t, same device; any entry may be NULL):
@@ -189,13 +192,35 @@ typedef enum sla_stage {
  *                 schedule when the linear branch takes the direct form,
  *                 linear stages when phi == NONE, QUANTIZE always) record
  *                 nothing.
- * With both NULL it is exactly sla_attention_fwd.  Same arguments,
+ *   options       0, or SLA_OPT_PHI_K_FP8 (other bits: SLA_ERR_INVALID_ARG)
+ * With NULL, NULL, 0 it is exactly sla_attention_fwd.  Same arguments,
  * ownership and errors; a failed hipEventRecord gives SLA_ERR_DEVICE. */
 sla_status sla_attention_fwd_ex(const void *q, const void *k, const void *v,
                                 int B, int H, int N, int d, int block,
                                 double keep, int phi, void *out, int out_dtype,
                                 float *out_linear, void *ws, size_t ws_bytes,
-                                void *stream, void *const *stage_events);
+                                void *stream, void *const *stage_events,
+                                int options);
+
+/* The forward with a lower-bit linear branch, an opt-in variant with its own
+ * accuracy (the pages run SLA on low-bit INT8/INT4 SageAttention: commentary
+ * "清华开源TurboDiffusion加速框架", section "SageAttention与稀疏计算").  The
+ * linear branch's key features phi(K) are kept as FP8 e4m3 codes with one
+ * power-of-two scale per 64-key block: the block's largest feature m is
+ * scaled by 2^(7 - floor(log2 m)) into [128, 256) and every feature rounded
+ * to nearest-even e4m3 (three mantissa bits, subnormals below 2^-6).  The
+ * whole-head sums and the kept blocks' share use the same rounded features,
+ * so the result is the exact forward with phi(K) replaced by its rounded
+ * value (bit-level rounding decisions can differ from an fp64 evaluation of
+ * phi only where phi lies within an fp32 rounding of an e4m3 midpoint).  It
+ * moves 32 instead of 40 KB per kept (query block, key block) pair.  The
+ * softmax branch is unchanged.  Same arguments, workspace, ownership and
+ * errors as sla_attention_fwd. */
+sla_status sla_attention_fwd_lowbit(const void *q, const void *k,
+                                    const void *v, int B, int H, int N, int d,
+                                    int block, double keep, int phi, void *out,
+                                    int out_dtype, void *ws, size_t ws_bytes,
+                                    void *stream);
 
 /* sla_attention_fwd for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid

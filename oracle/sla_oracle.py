@@ -46,6 +46,10 @@ What the oracle computes, per (batch, head), with blocks of ``block`` tokens
  8. Backward (``sla_backward_head``): dQ, dK, dV of that output for a given
     output gradient, the selection held fixed, the INT8 rounding passed
     straight through [NEWS 方法论: SLA is fine-tuned into the model].
+ 9. Lower-bit option (``phi_k_fp8``): the linear branch's key features
+    phi(K) rounded to FP8 (e4m3) with one power-of-two scale per key block,
+    as a lower-bit variant of the low-bit attention arithmetic [COM: INT8 /
+    INT4 SageAttention]; see ``phi_k_e4m3_blocks``.
 
 The pages print the SLA formula as phi(Q)(T_k[phi(K)]^T V), which has no
 softmax part; read together with the description of SLA as low-rank
@@ -256,6 +260,42 @@ def select_head(q_bits, k_bits, block: int, keep: float):
 
 
 # --------------------------------------------------------------------------
+# 9: FP8 (e4m3) key features for the lower-bit option
+# --------------------------------------------------------------------------
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest FP8 e4m3 value, ties to the even mantissa.
+
+    e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; normal values
+    (1 + m/8) 2^(e-7) for e = 1..15 up to 448, subnormals (m/8) 2^-6.  The
+    spacing in [2^e, 2^(e+1)) is 2^(e-3), and 2^-9 below 2^-6.  Inputs here
+    are non-negative and below 448 (no overflow handling needed)."""
+    a = np.asarray(x, dtype=np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(a), 2.0 ** -6)))
+    q = 2.0 ** (e - 3)
+    return np.sign(a) * np.round(np.abs(a) / q) * q      # np.round: half to even
+
+
+def phi_k_e4m3_blocks(fk: np.ndarray, block: int) -> np.ndarray:
+    """phi(K) [N, d] rounded to e4m3 with one power-of-two scale per block.
+
+    Per block of `block` rows: m = the largest feature of the block (valid
+    rows, all channels); with e = floor(log2 m), the features are scaled by
+    2^(7-e) (so the largest lands in [128, 256), inside e4m3's range),
+    rounded to e4m3 and scaled back.  A block whose features are all zero
+    stays zero."""
+    fk = np.asarray(fk, dtype=np.float64)
+    out = np.zeros_like(fk)
+    for i in range(n_blocks(fk.shape[0], block)):
+        b = fk[i * block:(i + 1) * block]
+        m = float(b.max())
+        if m <= 0.0:
+            continue
+        s = 7 - math.floor(math.log2(m))
+        out[i * block:(i + 1) * block] = round_e4m3(b * 2.0 ** s) * 2.0 ** -s
+    return out
+
+
+# --------------------------------------------------------------------------
 # 5-7: the two branches and their sum
 # --------------------------------------------------------------------------
 def _rows_of(blocks, N: int, block: int) -> np.ndarray:
@@ -299,13 +339,14 @@ def softmax_branch_block(i, sel, q8, k8, sq, sk, v64, N, block, d,
     return (p @ v64[krows]) / p.sum(axis=1, keepdims=True), acc
 
 
-def linear_branch_block(i, sel, q64, k64, v64, N, block, phi_kind):
+def linear_branch_block(i, sel, q64, k64, v64, N, block, phi_kind, fk_all=None):
     """Normalised linear attention of query block i over the unselected blocks.
 
     Direct sums over U = valid rows of every key block not in ``sel``:
         out = phi(Q_i) H_U / (phi(Q_i) z_U),  H_U = phi(K_U)^T V_U,  z_U = sum phi(K_U)
     phi acts on the raw inputs [TUT §2.1].  Rows whose U is empty or whose
-    denominator is zero get 0.
+    denominator is zero get 0.  ``fk_all`` [N, d], when given, replaces
+    phi(K) (the lower-bit option's rounded features).
     """
     nb = n_blocks(N, block)
     qrows = np.arange(i * block, min(N, (i + 1) * block))
@@ -314,7 +355,7 @@ def linear_branch_block(i, sel, q64, k64, v64, N, block, phi_kind):
     out = np.zeros((qrows.size, v64.shape[1]))
     if urows.size == 0:
         return out
-    fk = phi(k64[urows], phi_kind)
+    fk = phi(k64[urows], phi_kind) if fk_all is None else fk_all[urows]
     H = fk.T @ v64[urows]
     z = fk.sum(axis=0)
     fq = phi(q64[qrows], phi_kind)
@@ -327,13 +368,15 @@ def linear_branch_block(i, sel, q64, k64, v64, N, block, phi_kind):
 
 def sla_forward_head(q_bits, k_bits, v_bits, block: int = 64, keep: float = 0.1,
                      phi_kind="elu1", query_blocks=None, quantize: bool = True,
-                     smooth: bool = True, idx=None):
+                     smooth: bool = True, idx=None, phi_k_fp8: bool = False):
     """SageSLA forward of one (batch, head); inputs are bf16 bits [N, d].
 
     ``query_blocks`` restricts the output to those query blocks (the selection,
     mean and quantisation still use the whole head).  ``quantize=False``
     replaces the INT8 logits with exact fp64 ones; ``idx`` overrides the
-    selection (for constructed masks).  Returns a dict with
+    selection (for constructed masks); ``phi_k_fp8`` takes the linear
+    branch's phi(K) rounded to e4m3 per key block (``phi_k_e4m3_blocks``).
+    Returns a dict with
     out / out_softmax / out_linear (fp64, rows of the requested blocks in
     order), rows, idx, scores, q8, k8, q_scale, k_scale, mu.
     """
@@ -349,6 +392,9 @@ def sla_forward_head(q_bits, k_bits, v_bits, block: int = 64, keep: float = 0.1,
         idx, scores = select_head(q_bits, k_bits, block, keep)
     q8, k8, sq, sk, mu = quantize_qk(q_bits, k_bits, block, smooth=smooth)
     q64, k64, v64 = bf16_to_f64(q_bits), bf16_to_f64(k_bits), bf16_to_f64(v_bits)
+    fk_all = None
+    if phi_k_fp8 and phi_kind != PHI_NONE:
+        fk_all = phi_k_e4m3_blocks(phi(k64, phi_kind), block)
     qb = list(range(nb)) if query_blocks is None else list(query_blocks)
     outs_s, outs_l, rows = [], [], []
     for i in qb:
@@ -358,7 +404,7 @@ def sla_forward_head(q_bits, k_bits, v_bits, block: int = 64, keep: float = 0.1,
                                       k64=None if quantize else k64)
         outs_s.append(os_)
         if phi_kind != PHI_NONE:
-            outs_l.append(linear_branch_block(i, sel, q64, k64, v64, N, block, phi_kind))
+            outs_l.append(linear_branch_block(i, sel, q64, k64, v64, N, block, phi_kind, fk_all))
         else:
             outs_l.append(np.zeros_like(os_))
         rows.append(np.arange(i * block, min(N, (i + 1) * block)))

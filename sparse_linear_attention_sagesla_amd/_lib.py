@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 PHI = {"none": 0, "elu1": 1, "relu": 2}
 OP_QUANTIZE, OP_SELECT, OP_ATTENTION, OP_ATTENTION_BWD = 0, 1, 2, 3
+OPT_PHI_K_FP8 = 1
 BLOCK = 64
 HEAD_DIM = 128
 
@@ -53,8 +54,10 @@ def load() -> ctypes.CDLL:
     lib.sla_block_select.restype = c_int
     lib.sla_attention_fwd.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_size_t, c_void_p]
     lib.sla_attention_fwd.restype = c_int
-    lib.sla_attention_fwd_ex.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]
+    lib.sla_attention_fwd_ex.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_int]
     lib.sla_attention_fwd_ex.restype = c_int
+    lib.sla_attention_fwd_lowbit.argtypes = lib.sla_attention_fwd.argtypes
+    lib.sla_attention_fwd_lowbit.restype = c_int
     lib.sla_attention_fwd_noalloc.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p]
     lib.sla_attention_fwd_noalloc.restype = c_int
     lib.sla_attention_bwd.argtypes = [c_void_p] * 4 + [c_int] * 5 + [c_double, c_int] + [c_void_p] * 3 + [c_int, c_void_p, c_size_t, c_void_p]
@@ -170,8 +173,11 @@ def block_select(q: torch.Tensor, k: torch.Tensor, keep: float, with_mask: bool 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0.1,
               phi: str = "elu1", out_dtype=torch.bfloat16, return_linear: bool = False,
-              out=None, workspace=None):
-    """SageSLA forward: softmax attention on the kept key blocks + linear attention on the rest."""
+              out=None, workspace=None, lowbit: bool = False):
+    """SageSLA forward: softmax attention on the kept key blocks + linear attention on the rest.
+
+    ``lowbit``: the opt-in variant with the linear branch's phi(K) in FP8
+    (sla_attention_fwd_lowbit)."""
     q, k, v = _bhnd(q, "q"), _bhnd(k, "k"), _bhnd(v, "v")
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
@@ -189,13 +195,15 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0
     ws = _workspace(nbytes, dev, workspace)
     f32 = 1 if out_dtype == torch.float32 else 0
     if lin is None:
-        _check(load().sla_attention_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep),
-                                        ph, _ptr(out), f32, _ptr(ws), ws.numel(), _stream(dev)),
-               "sla_attention_fwd")
+        fn = load().sla_attention_fwd_lowbit if lowbit else load().sla_attention_fwd
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep), ph, _ptr(out), f32,
+                  _ptr(ws), ws.numel(), _stream(dev)),
+               "sla_attention_fwd_lowbit" if lowbit else "sla_attention_fwd")
     else:
         _check(load().sla_attention_fwd_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK,
                                            float(keep), ph, _ptr(out), f32, _ptr(lin), _ptr(ws),
-                                           ws.numel(), _stream(dev), None), "sla_attention_fwd_ex")
+                                           ws.numel(), _stream(dev), None,
+                                           OPT_PHI_K_FP8 if lowbit else 0), "sla_attention_fwd_ex")
     return (out, lin) if return_linear else out
 
 

@@ -115,9 +115,11 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
     if (direct) {
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
       ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+      ws.fkscale = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
     } else if (phi != SLA_PHI_NONE && s.k < s.Nb) {
       ws.fk16 = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
       ws.zb = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+      ws.fkscale = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
       ws.hpart = reinterpret_cast<float*>(take(BH * sla::kLinChunks * D * D * sizeof(float)));
       ws.zpart = reinterpret_cast<double*>(take(BH * sla::kLinChunks * D * sizeof(double)));
       ws.hf = reinterpret_cast<float*>(take(BH * D * D * sizeof(float)));
@@ -267,10 +269,12 @@ sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, i
 sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N,
                                 int d, int block, double keep, int phi, void* out, int out_dtype,
                                 float* out_linear, void* ws, size_t ws_bytes, void* stream,
-                                void* const* stage_events) {
+                                void* const* stage_events, int options) {
   const sla_status st =
       check_fwd_args(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, out_linear);
   if (st != SLA_OK) return st;
+  if (options & ~SLA_OPT_PHI_K_FP8) return SLA_ERR_INVALID_ARG;
+  const bool fp8 = (options & SLA_OPT_PHI_K_FP8) != 0;
   const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
   const int kk = sla_topk_count(Nb, keep);
   const Shape s = make_shape(B, H, N, kk);
@@ -311,7 +315,7 @@ sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int
   // each), so the QUANTIZE stage does not run here
   stage(SLA_STAGE_LINEAR_PREP, [&] {
     return sla::launch_linear_prep(kb, vb, s, phi_eff, !direct, w.fk16, w.v16, w.zb, w.hpart,
-                                   w.zpart, w.mu, kk > 0 ? w.k8 : nullptr, w.sk, hs);
+                                   w.zpart, w.mu, kk > 0 ? w.k8 : nullptr, w.sk, fp8, w.fkscale, hs);
   });
   if (phi_eff != SLA_PHI_NONE && !direct)
     stage(SLA_STAGE_LINEAR_FINAL, [&] {
@@ -320,7 +324,7 @@ sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int
     });
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
-                                  out_linear, hs);
+                                  out_linear, fp8, hs);
   });
   return device_status(e);
 }
@@ -329,7 +333,14 @@ sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B,
                              int d, int block, double keep, int phi, void* out, int out_dtype,
                              void* ws, size_t ws_bytes, void* stream) {
   return sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr, ws,
-                              ws_bytes, stream, nullptr);
+                              ws_bytes, stream, nullptr, 0);
+}
+
+sla_status sla_attention_fwd_lowbit(const void* q, const void* k, const void* v, int B, int H,
+                                    int N, int d, int block, double keep, int phi, void* out,
+                                    int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr, ws,
+                              ws_bytes, stream, nullptr, SLA_OPT_PHI_K_FP8);
 }
 
 sla_status sla_attention_fwd_noalloc(const void* q, const void* k, const void* v, int B, int H,
@@ -343,7 +354,7 @@ sla_status sla_attention_fwd_noalloc(const void* q, const void* k, const void* v
   const hipError_t e = scratch_address(&ws);
   if (e != hipSuccess) return SLA_ERR_DEVICE;
   return sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr, ws,
-                              SLA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+                              SLA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, const void* dout,
@@ -395,7 +406,7 @@ sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, 
   }
   run([&] {
     return sla::launch_linear_prep(kb, vb, s, phi_eff, true, w.fk16, w.v16, w.zb, w.hpart, w.zpart,
-                                   w.mu, kk > 0 ? w.k8 : nullptr, w.sk, hs);
+                                   w.mu, kk > 0 ? w.k8 : nullptr, w.sk, false, nullptr, hs);
   });
   if (phi_eff != SLA_PHI_NONE)
     run([&] {
@@ -499,6 +510,6 @@ const char* sla_status_string(int status) {
   }
 }
 
-int sla_version(void) { return 20000; }
+int sla_version(void) { return 20100; }
 
 }  // extern "C"

@@ -48,6 +48,7 @@ struct Workspace {
   uint16_t* fk16 = nullptr;   // [BH, Nb, D, 64] fp16 phi(K)/16 per block, [channel][permuted key]
   uint16_t* v16 = nullptr;    // [BH, Nb, D, 64] fp16 V per block, [channel][permuted key]
   float* zb = nullptr;        // [BH, Nb, D]   fp32 per-block sum of phi(K)/16 over the keys
+  float* fkscale = nullptr;   // [BH, Nb]      FP8 phi(K) tiles (lower-bit option): code -> phi/16
   float* hpart = nullptr;     // [BH, kLinChunks, D, D] partial phi(K)^T V
   double* zpart = nullptr;    // [BH, kLinChunks, D]    partial sums of the block sums zb
   float* hf = nullptr;        // [BH, 4, 8, 2, 64, 4] fp32 H = sum phi(K)/16 ^T V in the
@@ -88,9 +89,12 @@ hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu
 hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
                              int32_t* idx, uint32_t* mask, hipStream_t s);
 size_t topk_lds_bytes(int Nb, int* rows_per_group);
+// fp8: stage phi(K) as e4m3 codes (8 KB per block, a head's blocks at the
+// start of its fk16 slice) with per-block decode scales in fkscale.
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
-                              double* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s);
+                              double* zpart, const float* mu, int8_t* k8, float* sk, bool fp8,
+                              float* fkscale, hipStream_t s);
 // Whole-head linear state from the chunk partials.  The forward takes hf and
 // z64; the backward z, h16t, hscale and hb (bf16 H row-major); null outputs
 // are skipped.
@@ -105,7 +109,7 @@ inline bool linear_direct(const Shape& sh) { return sh.Nb - sh.k <= sh.k; }
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
                                  hipStream_t s);
 hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
-                             void* out, int out_f32, float* out_linear, hipStream_t s);
+                             void* out, int out_f32, float* out_linear, bool fp8, hipStream_t s);
 // Backward launchers.
 // Per block: K^T, Q^T, dO^T as bf16 [channel][permuted row] (any may be null).
 hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* q, const uint16_t* dout,

@@ -18,6 +18,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float phi_apply(float x, int phi) {
   if (phi == kPhiElu1) return x > 0.0f ? x + 1.0f : __expf(x);
@@ -434,6 +435,13 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 // that feed the P.V product.
 // kMode: 0 = V staging only, 1 = V and phi(K) staging and block sums, 2 =
 // staging plus the H, z partial sums.
+// kF8 (lower-bit option): phi(K) is staged as FP8 e4m3 codes, [channel][64
+// permuted keys] in 64-byte rows (8 KB per block), with one power-of-two
+// scale per block: the block's largest feature m is scaled by 2^(7 - ilogb m)
+// into [128, 256) and every feature is rounded to nearest-even e4m3;
+// fkscale[block] = 2^(-(7 - ilogb m)) / 16 turns a code back into the fp16
+// staging scale (phi/16).  The block sums, the H partials and the attention
+// kernel all use the same decoded values.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int perm_pos(int key) {
   const int h = key >> 5, r = key & 31;
@@ -449,16 +457,21 @@ __device__ __forceinline__ int tpos(int c, int pos) {
   return c * kTRow + ((((pos >> 3) ^ (c >> 4)) & 7) << 3) + (pos & 7);
 }
 
-template <int kMode>
+template <int kMode, bool kF8>
 __global__ __launch_bounds__(256) void linear_prep_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int Nb, int phi,
     uint16_t* __restrict__ fk16, uint16_t* __restrict__ v16, float* __restrict__ zb,
     float* __restrict__ hpart, double* __restrict__ zpart, const float* __restrict__ mu,
-    int8_t* __restrict__ k8, float* __restrict__ sk) {
-  // LDS: transposed tiles [128 channels][64 positions] fp16 (see tpos)
+    int8_t* __restrict__ k8, float* __restrict__ sk, float* __restrict__ fkscale) {
+  // LDS: transposed tiles [128 channels][64 positions] fp16 (see tpos); with
+  // kF8 also the codes, 16 words per channel, word w of channel c kept at
+  // w ^ ((c >> 3) & 15) (the transposed writes of 16 channels 8 apart then
+  // hit 16 banks)
   __shared__ __align__(16) _Float16 fkT[kD * kTRow];
   __shared__ __align__(16) _Float16 vT[kD * kTRow];
+  __shared__ __align__(16) uint32_t fk8T[kF8 ? kD * 16 : 4];
   __shared__ float red[4];
+  __shared__ float red8[4];
   constexpr bool kLinear = kMode >= 1;
   constexpr bool kReduce = kMode >= 2;
   const int t = threadIdx.x;
@@ -505,7 +518,9 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
     uint4 rv[4], rk[4];
     load_raw(j, rv, rk);
     _Float16 fv[4][8], vv[4][8];
+    float pf[4][8];     // kF8: phi(K) in fp32 (pad rows 0)
     float amax = 0.0f;  // max |K - mu| over this lane's valid rows
+    float pmax = 0.0f;  // kF8: largest feature of this lane's valid rows
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int r = 4 * a + m;
@@ -515,7 +530,11 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         vv[m][e] = (_Float16)xv[e];
-        if (kLinear) fv[m][e] = (r < rows) ? (_Float16)(phi_apply(xk[e], phi) * kPhiScale) : (_Float16)0.0f;
+        if (kLinear && !kF8) fv[m][e] = (r < rows) ? (_Float16)(phi_apply(xk[e], phi) * kPhiScale) : (_Float16)0.0f;
+        if (kF8) {
+          pf[m][e] = (r < rows) ? phi_apply(xk[e], phi) : 0.0f;
+          pmax = fmaxf(pmax, pf[m][e]);
+        }
         if (quant && r < rows) amax = fmaxf(amax, fabsf(xk[e] - m8[e]));
       }
     }
@@ -524,6 +543,11 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
       for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
       if (lane == 0) red[wave] = amax;
     }
+    if (kF8) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) pmax = fmaxf(pmax, __shfl_xor(pmax, off));
+      if (lane == 0) red8[wave] = pmax;
+    }
     // transposed LDS writes: 4 consecutive keys -> 4 consecutive positions
     const int p0 = perm_pos(4 * a);
 #pragma unroll
@@ -531,10 +555,29 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
       const int c = cc * 8 + e;
       half4 hv = {vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
       *reinterpret_cast<half4*>(&vT[tpos(c, p0)]) = hv;
-      if (kLinear) {
+      if (kLinear && !kF8) {
         half4 hf = {fv[0][e], fv[1][e], fv[2][e], fv[3][e]};
         *reinterpret_cast<half4*>(&fkT[tpos(c, p0)]) = hf;
       }
+    }
+    if constexpr (kF8) {
+      __syncthreads();  // the block's largest feature is in red8
+      const float bm = fmaxf(fmaxf(red8[0], red8[1]), fmaxf(red8[2], red8[3]));
+      const int sh = bm > 0.0f ? 7 - ilogbf(bm) : 0;
+      const float up = ldexpf(1.0f, sh);        // largest feature -> [128, 256)
+      const float dq = ldexpf(1.0f, -sh - 4);   // code -> phi / 16
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = cc * 8 + e;
+        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(pf[0][e] * up, pf[1][e] * up, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pf[2][e] * up, pf[3][e] * up, w, true);
+        fk8T[c * 16 + ((p0 >> 2) ^ cc)] = w;
+        const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, dq, false);
+        const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, dq, true);
+        half4 hf = {lo.x, lo.y, hi.x, hi.y};
+        *reinterpret_cast<half4*>(&fkT[tpos(c, p0)]) = hf;
+      }
+      if (t == 0) fkscale[(size_t)bh * Nb + j] = dq;
     }
     __syncthreads();
     if (quant) {
@@ -562,7 +605,30 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
       for (int m = 0; m < 4; ++m) {
         const int q = t + 256 * m;
         dstv[q] = *reinterpret_cast<const uint4*>(&vT[tpos(q >> 3, 8 * (q & 7))]);
-        if (kLinear) dstf[q] = *reinterpret_cast<const uint4*>(&fkT[tpos(q >> 3, 8 * (q & 7))]);
+        if (kLinear && !kF8) dstf[q] = *reinterpret_cast<const uint4*>(&fkT[tpos(q >> 3, 8 * (q & 7))]);
+      }
+      if (kF8) {
+        // codes: 8 KB per block, 16-byte chunk q = 4c + k in linear order; a
+        // head's blocks start at its fp16 staging slice (the first half of it)
+        uint4* dst8 = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(fk16 + (size_t)bh * Nb * kD * kBlk) +
+                                               (size_t)j * kD * kBlk);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int q = t + 256 * m;
+          const int r = q >> 2, sw = (r >> 3) & 15;
+          // words 4k..4k+3 of row r sit at (4k + i) ^ sw
+          const uint4 u = reinterpret_cast<const uint4*>(fk8T)[r * 4 + ((q & 3) ^ (sw >> 2))];
+          uint32_t w[4] = {u.x, u.y, u.z, u.w};
+          if (sw & 1) {
+            const uint32_t t0 = w[0], t2 = w[2];
+            w[0] = w[1], w[1] = t0, w[2] = w[3], w[3] = t2;
+          }
+          if (sw & 2) {
+            const uint32_t t0 = w[0], t1 = w[1];
+            w[0] = w[2], w[1] = w[3], w[2] = t0, w[3] = t1;
+          }
+          dst8[q] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
       }
     }
     // per-block sum of phi(K)/16 over the keys, channel t
@@ -753,14 +819,19 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& 
 
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,
                               bool reduce, uint16_t* fk16, uint16_t* v16, float* zb, float* hpart,
-                              double* zpart, const float* mu, int8_t* k8, float* sk, hipStream_t s) {
+                              double* zpart, const float* mu, int8_t* k8, float* sk, bool fp8,
+                              float* fkscale, hipStream_t s) {
   dim3 grid(kLinChunks, sh.BH);
+#define SLA_PREP(M, F8)                                                                         \
+  linear_prep_kernel<M, F8><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, \
+                                                 zpart, mu, k8, sk, fkscale)
   if (phi == kPhiNone)
-    linear_prep_kernel<0><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart, mu, k8, sk);
+    SLA_PREP(0, false);
   else if (!reduce)
-    linear_prep_kernel<1><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart, mu, k8, sk);
+    fp8 ? SLA_PREP(1, true) : SLA_PREP(1, false);
   else
-    linear_prep_kernel<2><<<grid, 256, 0, s>>>(k, v, sh.N, sh.Nb, phi, fk16, v16, zb, hpart, zpart, mu, k8, sk);
+    fp8 ? SLA_PREP(2, true) : SLA_PREP(2, false);
+#undef SLA_PREP
   return hipGetLastError();
 }
 

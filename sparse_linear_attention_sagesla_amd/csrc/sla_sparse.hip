@@ -7,6 +7,8 @@
 //   K8_j   int8 [64 keys][128]      (8 KB)   -> S^T = K8_j Q8_i^T     (INT8 MFMA)
 //   V_j    fp16 [128][64 perm keys] (16 KB)  -> O^T += V_j^T P^T      (fp16 MFMA)
 //   phiK_j fp16 [128][64 perm keys] (16 KB)  -> M^T += V_j^T phiK_j   (fp16 MFMA)
+//          (lower-bit option: e4m3 codes, 8 KB, turned into fp16 with the
+//          block's decode scale as they are read)
 // Scores are computed transposed (keys x queries) so each lane ends up holding
 // one query's values for 16 keys; in that layout the exponentiated scores P are
 // already the B operand of the P.V product and never leave registers, and the
@@ -53,6 +55,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 typedef __attribute__((address_space(3))) const v4i lds_v4i;
@@ -76,11 +80,17 @@ __device__ __forceinline__ float phi_apply(float x, int phi) {
 // of row r at chunk ch ^ ((r >> 1) & 7); the final M^T (256-byte rows) keeps
 // chunk ch of row r at ch ^ (r & 15).  A 16-lane read group (16 consecutive
 // rows, same chunk) then touches 16 distinct 4-bank groups of the 64-bank LDS.
+// The FP8 phi(K) tile has 64-byte rows (one channel, 64 permuted keys) and
+// keeps 16-byte chunk ch of row r at ch ^ ((r >> 2) & 3); a 16-lane read group
+// (16 consecutive rows, same 8 bytes) then spreads over 16 distinct 4-bank
+// groups.
 struct LaneOffsets {
   int rd8;    // read byte offset of (row l16, chunk g) in a staged tile; chunk g+4: ^64
   int rdK;    // rd8 in rows 32w.. of the stage's phi(K) tile (w = this wave)
+  int rdF;    // FP8 phi(K): bytes 8g.. of row 32w + l16 (row + 16: +1024; keys + 32: ^32)
   int rdM;    // read byte offset of (row l16, chunk g) in M^T; chunk g+4cc: ^(64cc)
   int ld8;    // global byte offset (within the tile) this lane fetches
+  int ldF;    // the same for the FP8 phi(K) tile (64-byte rows)
   int zo;     // byte offset of this lane's phi channel 32w + (lane & 31) in a block sum
 };
 
@@ -94,6 +104,10 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
   const int row = 8 * wave + (lane >> 3);             // + 32m
   const int ch = (lane & 7) ^ ((row >> 1) & 7);
   o.ld8 = row * 128 + ch * 16;                        // + 4096m
+  const int frow = 32 * wave + l16;
+  o.rdF = kFOff + frow * 64 + (((g >> 1) ^ ((frow >> 2) & 3)) << 4) + 8 * (g & 1);
+  const int lrow = 16 * wave + (lane >> 2);           // + 64m
+  o.ldF = lrow * 64 + (((lane & 3) ^ ((lrow >> 2) & 3)) << 4);
   o.zo = 4 * (32 * wave + (lane & 31));
   return o;
 }
@@ -117,8 +131,9 @@ struct TileSrc {
 };
 
 // Issues this wave's share of a tile's LDS-direct loads into `st` (kW waves
-// per workgroup; each instruction round of the workgroup moves kW KB).
-template <bool kK8, bool kFK, int kW = 4>
+// per workgroup; each instruction round of the workgroup moves kW KB).  kF8:
+// the phi(K) tile is the 8 KB FP8 one.
+template <bool kK8, bool kFK, bool kF8 = false, int kW = 4>
 __device__ __forceinline__ void issue_tile(lds_byte* st, const TileSrc& src, int j, int wave,
                                            const LaneOffsets& lo) {
   constexpr int kRound = kW * 1024;
@@ -130,7 +145,11 @@ __device__ __forceinline__ void issue_tile(lds_byte* st, const TileSrc& src, int
     for (int m = 0; m < kK8Bytes / kRound; ++m)
       lds_load16(src.k8, lo.ld8, j * kK8Bytes + kRound * m, st + kRound * m + 1024 * wave);
   }
-  if (kFK) {
+  if (kFK && kF8) {
+#pragma unroll
+    for (int m = 0; m < kK8Bytes / kRound; ++m)
+      lds_load16(src.fk16, lo.ldF, j * kK8Bytes + kRound * m, st + kFOff + kRound * m + 1024 * wave);
+  } else if (kFK) {
 #pragma unroll
     for (int m = 0; m < kF16TileBytes / kRound; ++m)
       lds_load16(src.fk16, lo.ld8, j * kF16TileBytes + kRound * m, st + kFOff + kRound * m + 1024 * wave);
@@ -193,6 +212,7 @@ struct SparseArgs {
   const uint16_t* fk16;
   const uint16_t* v16;
   const float* zb;
+  const float* fkscale;   // FP8 phi(K) decode scale per key block (lower-bit option)
   const float* hf;        // whole-head H in the M^T register layout (forward)
   const double* z64;      // whole-head sum of the block sums zb (forward)
   const uint16_t* h16t;   // (backward)
@@ -226,10 +246,10 @@ __device__ __forceinline__ int rows_max(int x) {
 
 // One tile's computation from stage `st`.  kMask: the tile is the ragged last
 // key block (keys >= kvalid are padding and get weight 0).
-template <bool kSoft, bool kLin, bool kMask>
+template <bool kSoft, bool kLin, bool kMask, bool kF8 = false>
 __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const v4i qf[2],
                                              const LaneOffsets& lo, float cs, float zj,
-                                             int kvalid, int g) {
+                                             int kvalid, int g, float fs = 0.0f) {
   half8 pf[2], fk[2][2];
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
   if (kSoft) {
@@ -284,7 +304,19 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) fk[x][c] = *(lds_half8*)(st + 2048 * x + (lo.rdK ^ (64 * c)));
+      for (int c = 0; c < 2; ++c) {
+        if constexpr (kF8) {
+          // 8 e4m3 codes, decoded to fp16 with the block's scale fs
+          const u32x2 u = *(lds_u32x2*)(st + ((lo.rdF + 1024 * x) ^ (32 * c)));
+          const half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u.x, fs, false);
+          const half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u.x, fs, true);
+          const half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u.y, fs, false);
+          const half2v h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u.y, fs, true);
+          fk[x][c] = half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+        } else {
+          fk[x][c] = *(lds_half8*)(st + 2048 * x + (lo.rdK ^ (64 * c)));
+        }
+      }
     S.zk += (double)zj;
   }
   // The products below are most of the tile's matrix-core work.  The wave
@@ -341,15 +373,17 @@ struct ComplementWalk {
 
 // Walks `n` tiles, the key block of each from `next` (called once per tile,
 // in order), through the two LDS stages.
-template <bool kSoft, bool kLin, typename Next>
+template <bool kSoft, bool kLin, bool kF8, typename Next>
 __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_bytes, Next next,
                                           int n, const SparseArgs& a,
                                           const TileSrc& src, size_t bh, const v4i qf[2],
                                           const LaneOffsets& lo, float qscale, int wave, int g) {
   if (n <= 0) return;
+  auto fscale_of = [&](int j) { return kF8 ? ld_uniform(a.fkscale, bh * a.Nb + j) : 0.0f; };
   int j = next();
-  issue_tile<kSoft, kLin>(smem, src, j, wave, lo);
+  issue_tile<kSoft, kLin, kF8>(smem, src, j, wave, lo);
   float zc = kLin ? load_zb(src, j, lo) : 0.0f;
+  float fc = kLin ? fscale_of(j) : 0.0f;
   // lists are ascending, so only the last tile can be the ragged key block;
   // it is peeled off so the loop carries one compute variant
   const int nm = n - 1;
@@ -363,12 +397,14 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
         const int jn = next();
         wait_loads();
         lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
-        issue_tile<kSoft, kLin>(nxt, src, jn, wave, lo);
+        issue_tile<kSoft, kLin, kF8>(nxt, src, jn, wave, lo);
         const float zn = kLin ? load_zb(src, jn, lo) : 0.0f;
+        const float fn = kLin ? fscale_of(jn) : 0.0f;
         const float cs = kSoft ? qscale * ld_uniform(a.sk, bh * a.Nb + j) : 0.0f;
-        compute_tile<kSoft, kLin, false>(S, cur, qf, lo, cs, zc, kBlk, g);
+        compute_tile<kSoft, kLin, false, kF8>(S, cur, qf, lo, cs, zc, kBlk, g, fc);
         j = jn;
         zc = zn;
+        fc = fn;
       }
     }
   }
@@ -379,9 +415,9 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
     wait_loads();
     lds_barrier();
     if (kSoft && kvalid < kBlk)
-      compute_tile<kSoft, kLin, true>(S, cur, qf, lo, cs, zc, kvalid, g);
+      compute_tile<kSoft, kLin, true, kF8>(S, cur, qf, lo, cs, zc, kvalid, g, fc);
     else
-      compute_tile<kSoft, kLin, false>(S, cur, qf, lo, cs, zc, kvalid, g);
+      compute_tile<kSoft, kLin, false, kF8>(S, cur, qf, lo, cs, zc, kvalid, g, fc);
   }
   lds_barrier();  // the stages may be refilled by a following walk
 }
@@ -391,7 +427,7 @@ __device__ __forceinline__ void run_tiles(State& S, lds_byte* smem, int stage_by
 // INT8 scale of its key block, are read with scalar loads when its tile is
 // issued, a tile ahead of their use; reading entries earlier (a step further
 // ahead, or 64-step chunks in registers) measured slower.
-template <bool kLin>
+template <bool kLin, bool kF8 = false>
 __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_bytes,
                                           const int32_t* col, int n, const SparseArgs& a,
                                           const TileSrc& src, size_t bh, const v4i qf[2],
@@ -399,10 +435,12 @@ __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_by
   if (n <= 0) return;
   auto block_of = [&](int p) { return min(max(ld_uniform(col, (size_t)p * kGroup), 0), a.Nb - 1); };
   auto scale_of = [&](int j) { return ld_uniform(a.sk, bh * a.Nb + j); };
+  auto fscale_of = [&](int j) { return kF8 ? ld_uniform(a.fkscale, bh * a.Nb + j) : 0.0f; };
   int j = block_of(0);
-  issue_tile<true, kLin>(smem, src, j, wave, lo);
+  issue_tile<true, kLin, kF8>(smem, src, j, wave, lo);
   float zc = kLin ? load_zb(src, j, lo) : 0.0f;
   float sc = scale_of(j);
+  float fc = fscale_of(j);
   // the schedule puts a ragged key block only in the last step, which is
   // peeled off so the loop carries one compute variant
   const int nm = n - 1;
@@ -416,13 +454,15 @@ __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_by
         wait_loads();
         lds_barrier();  // tile pp is in LDS; every wave is done with tile pp-1
         const int jn = block_of(pp + 1);
-        issue_tile<true, kLin>(nxt, src, jn, wave, lo);
+        issue_tile<true, kLin, kF8>(nxt, src, jn, wave, lo);
         const float zn = kLin ? load_zb(src, jn, lo) : 0.0f;
         const float sn = scale_of(jn);
-        compute_tile<true, kLin, false>(S, cur, qf, lo, qscale * sc, zc, kBlk, g);
+        const float fn = fscale_of(jn);
+        compute_tile<true, kLin, false, kF8>(S, cur, qf, lo, qscale * sc, zc, kBlk, g, fc);
         j = jn;
         zc = zn;
         sc = sn;
+        fc = fn;
       }
     }
   }
@@ -432,9 +472,9 @@ __device__ __forceinline__ void run_sched(State& S, lds_byte* smem, int stage_by
   wait_loads();
   lds_barrier();
   if (kvalid < kBlk)
-    compute_tile<true, kLin, true>(S, cur, qf, lo, c, zc, kvalid, g);
+    compute_tile<true, kLin, true, kF8>(S, cur, qf, lo, c, zc, kvalid, g, fc);
   else
-    compute_tile<true, kLin, false>(S, cur, qf, lo, c, zc, kvalid, g);
+    compute_tile<true, kLin, false, kF8>(S, cur, qf, lo, c, zc, kvalid, g, fc);
 }
 
 // fp16 phi(Q)/16 of this lane's query, channels 32cc + 8g + e (B operand of
@@ -653,7 +693,7 @@ constexpr int kEpZ = kEpZU + kD * 4;
 constexpr int kEpRed = kEpZ + kD * 4;
 
 // Normalise, add the linear branch, store this lane's query row.
-template <int kMode>
+template <int kMode, bool kF8>
 __device__ __forceinline__ void finish_query(State& S, const SparseArgs& a, size_t bh, int i,
                                              int qrow, bool qvalid, lds_byte* smem, int stage_bytes,
                                              const TileSrc& src, const v4i qf[2],
@@ -739,8 +779,8 @@ __device__ __forceinline__ void finish_query(State& S, const SparseArgs& a, size
         for (int dt = 0; dt < 8; ++dt) S.mk[dt][0] = S.mk[dt][1] = v4f{0.f, 0.f, 0.f, 0.f};
         S.zk = 0.0;
         const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
-        run_tiles<false, true>(S, smem, stage_bytes, ComplementWalk(sel, a.k, a.Nb), a.Nb - a.k, a,
-                               src, bh, qf, lo, 0.0f, wave, g);
+        run_tiles<false, true, kF8>(S, smem, stage_bytes, ComplementWalk(sel, a.k, a.Nb),
+                                    a.Nb - a.k, a, src, bh, qf, lo, 0.0f, wave, g);
       }
     }
     if (direct) {
@@ -792,12 +832,13 @@ __device__ __forceinline__ TileSrc head_sources(const SparseArgs& a, size_t bh, 
 
 // One workgroup per query block.  Workgroups x, x+8, ..., x+8(kGroup-1) of a
 // head (same XCD, dispatched together) take the query blocks of one group.
-template <int kMode>
+template <int kMode, bool kF8>
 __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   lds_byte* smem = (lds_byte*)smem_raw;
   constexpr bool kLinAny = kMode != kSoftOnly;
-  constexpr int stage_bytes = kK8Bytes + kF16TileBytes + (kLinAny ? kF16TileBytes : 0);
+  constexpr int stage_bytes =
+      kK8Bytes + kF16TileBytes + (kLinAny ? (kF8 ? kK8Bytes : kF16TileBytes) : 0);
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -822,15 +863,15 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
   if (kMode != kDirect) {
     const int ngroups = (a.Nb + kGroup - 1) / kGroup;
     const int32_t* col = a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup;
-    run_sched<kLinAny>(S, smem, stage_bytes, col, a.k, a, src, bh, qf, lo, qscale, wave, g);
+    run_sched<kLinAny, kF8>(S, smem, stage_bytes, col, a.k, a, src, bh, qf, lo, qscale, wave, g);
   } else {
     const int32_t* sel = a.idx + (bh * a.Nb + i) * (size_t)a.k;
-    run_tiles<true, false>(S, smem, stage_bytes, ListWalk{sel, a.Nb, 0}, a.k, a, src, bh, qf, lo,
-                           qscale, wave, g);
-    run_tiles<false, true>(S, smem, stage_bytes, ComplementWalk(sel, a.k, a.Nb), a.Nb - a.k, a,
-                           src, bh, qf, lo, qscale, wave, g);
+    run_tiles<true, false, false>(S, smem, stage_bytes, ListWalk{sel, a.Nb, 0}, a.k, a, src, bh,
+                                  qf, lo, qscale, wave, g);
+    run_tiles<false, true, kF8>(S, smem, stage_bytes, ComplementWalk(sel, a.k, a.Nb), a.Nb - a.k,
+                                a, src, bh, qf, lo, qscale, wave, g);
   }
-  finish_query<kMode>(S, a, bh, i, qrow, qvalid, smem, stage_bytes, src, qf, lo, wave, lane);
+  finish_query<kMode, kF8>(S, a, bh, i, qrow, qvalid, smem, stage_bytes, src, qf, lo, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1816,21 +1857,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
   }
 }
 
-template <int kMode>
+template <int kMode, bool kF8 = false>
 hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
-  constexpr size_t stage = (size_t)kK8Bytes + kF16TileBytes + (kMode != kSoftOnly ? kF16TileBytes : 0);
-  const hipError_t e = allow_lds(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode>), (int)(2 * stage));
+  constexpr size_t stage = (size_t)kK8Bytes + kF16TileBytes +
+                           (kMode != kSoftOnly ? (kF8 ? kK8Bytes : kF16TileBytes) : 0);
+  const hipError_t e =
+      allow_lds(reinterpret_cast<const void*>(sparse_fwd_kernel<kMode, kF8>), (int)(2 * stage));
   if (e != hipSuccess) return e;
   // grouped walks need every member's workgroup, so the block count is rounded up
   const int slots = kMode == kDirect ? sh.Nb : kGroup * ((sh.Nb + kGroup - 1) / kGroup);
-  sparse_fwd_kernel<kMode><<<dim3(slots, sh.BH), 256, 2 * stage, s>>>(a);
+  sparse_fwd_kernel<kMode, kF8><<<dim3(slots, sh.BH), 256, 2 * stage, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
-                             void* out, int out_f32, float* out_linear, hipStream_t s) {
+                             void* out, int out_f32, float* out_linear, bool fp8, hipStream_t s) {
   SparseArgs a;
   a.q = q;
   a.q8 = ws.q8;
@@ -1842,6 +1885,7 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.fk16 = ws.fk16;
   a.v16 = ws.v16;
   a.zb = ws.zb;
+  a.fkscale = ws.fkscale;
   a.hf = ws.hf;
   a.z64 = ws.z64;
   a.h16t = nullptr;
@@ -1856,9 +1900,10 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
   a.out_f32 = out_f32;
   a.out_linear = out_linear;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
-  if (lin && linear_direct(sh)) return launch_mode<kDirect>(a, sh, s);
   if (!lin) return launch_mode<kSoftOnly>(a, sh, s);
-  return launch_mode<kSubtract>(a, sh, s);
+  if (linear_direct(sh))
+    return fp8 ? launch_mode<kDirect, true>(a, sh, s) : launch_mode<kDirect>(a, sh, s);
+  return fp8 ? launch_mode<kSubtract, true>(a, sh, s) : launch_mode<kSubtract>(a, sh, s);
 }
 
 hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* dout,

@@ -78,11 +78,15 @@ def test_workspace_size_validation_and_growth():
 def _attn(q=FAKE, k=FAKE, v=FAKE, B=1, H=2, N=2048, d=128, block=64, keep=0.1, phi=1,
           out=FAKE, out_dtype=1, out_lin=NULL, ws=FAKE, ws_bytes=0):
     ex = lib().sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype,
-                                    out_lin, ws, ws_bytes, NULL, NULL)
+                                    out_lin, ws, ws_bytes, NULL, NULL, 0)
     if out_lin.value is None:
         plain = lib().sla_attention_fwd(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype,
                                         ws, ws_bytes, NULL)
-        assert plain == ex
+        low = lib().sla_attention_fwd_lowbit(q, k, v, B, H, N, d, block, keep, phi, out,
+                                             out_dtype, ws, ws_bytes, NULL)
+        assert plain == ex == low
+    assert lib().sla_attention_fwd_ex(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype,
+                                      out_lin, ws, ws_bytes, NULL, NULL, 1) == ex
     return ex
 
 
@@ -151,6 +155,9 @@ def test_attention_rejects_bad_arguments_before_launch():
     assert _attn(ws=NULL, ws_bytes=1 << 40) == WORKSPACE
     assert _attn(ws_bytes=1024) == WORKSPACE
     assert _attn(ws=MISALIGNED, ws_bytes=1 << 40) == WORKSPACE
+    bad_opt = lib().sla_attention_fwd_ex(FAKE, FAKE, FAKE, 1, 2, 2048, 128, 64, 0.1, 1, FAKE, 1,
+                                         NULL, FAKE, 1 << 40, NULL, NULL, 2)
+    assert bad_opt == INVALID
 
 
 def test_quantize_and_select_reject_bad_arguments_before_launch():

@@ -394,3 +394,62 @@ def test_generators_are_seeded_and_shaped():
     assert all((x == y).all() for x, y in zip(a, b))
     assert not (a[0] == c[0]).all()
     assert a[0].shape == (2048, 128) and a[0].dtype == np.uint16
+
+
+# ----------------------------------------------------- lower-bit option (FP8)
+def test_e4m3_rounding_against_the_format():
+    """e4m3 (OCP FP8: bias 7, 3 mantissa bits, subnormals (m/8) 2^-6, largest
+    448): representable values map to themselves; midpoints go to the even
+    mantissa; subnormal spacing is 2^-9."""
+    vals = sorted({(m / 8) * 2.0 ** -6 for m in range(8)} |
+                  {(1 + m / 8) * 2.0 ** (e - 7) for e in range(1, 16) for m in range(8)
+                   if not (e == 15 and m == 7)})
+    assert vals[-1] == 448.0 and len(vals) == 8 + 15 * 8 - 1
+    np.testing.assert_array_equal(O.round_e4m3(np.array(vals)), vals)
+    cases = {1.0625: 1.0, 1.1875: 1.25, 3.0 * 2.0 ** -10: 2.0 ** -8, 2.0 ** -10: 0.0,
+             2.0 ** -9: 2.0 ** -9, 100.0: 96.0, 104.0: 104.0, 108.0: 112.0, 250.0: 256.0,
+             0.3: 0.3125, 0.0: 0.0}
+    for x, want in cases.items():
+        assert O.round_e4m3(np.array([x]))[0] == want, x
+    rng = np.random.default_rng(3)
+    x = rng.uniform(2.0 ** -6, 448.0, 20000)
+    r = O.round_e4m3(x)
+    assert (np.abs(r - x) <= 2.0 ** -4 * x + 1e-300).all()       # half of 2^-3 relative
+    assert (np.diff(O.round_e4m3(np.sort(x))) >= 0).all()         # monotone
+
+
+def test_phi_k_fp8_block_scale():
+    """Per-block power-of-two scale: the block's largest feature lands in
+    [128, 256) before rounding, so features within a factor 2^-4 of it keep
+    three mantissa bits; features already on the scaled e4m3 grid are kept."""
+    fk = np.zeros((130, 4))
+    fk[0:64] = np.array([[300.0, 0.5, 1.0, 37.0]])        # block max 300 -> scale 2^-1
+    fk[64:128] = np.array([[1e-3, 2e-3, 3e-3, 5e-3]])     # block max 5e-3 -> scale 2^15
+    fk[128:] = 0.0                                         # all-zero block stays zero
+    r = O.phi_k_e4m3_blocks(fk, 64)
+    np.testing.assert_array_equal(r[0], [288.0, 0.5, 1.0, 36.0])   # 150 -> 144 (spacing 16)
+    s = 2.0 ** 15
+    np.testing.assert_array_equal(r[64], O.round_e4m3(fk[64] * s) / s)
+    assert 128 <= fk[64].max() * s < 256
+    assert not r[128:].any()
+
+
+def test_phi_k_fp8_equals_exact_mode_on_grid_inputs():
+    """With ReLU features already on each block's scaled e4m3 grid, the
+    lower-bit option is the exact forward, and in general its linear branch is
+    still a weighted average of the values (inside their range per channel)."""
+    N = 192
+    rng = np.random.default_rng(4)
+    q = rng.integers(-3, 6, (N, 128)).astype(np.float64) / 4
+    k = rng.integers(-3, 8, (N, 128)).astype(np.float64) / 8   # max 7/8 -> 3 bits suffice
+    v = rng.standard_normal((N, 128))
+    qb, kb, vb = bf(q), bf(k), bf(v)
+    a = O.sla_forward_head(qb, kb, vb, 64, 1 / 3, "relu")
+    b = O.sla_forward_head(qb, kb, vb, 64, 1 / 3, "relu", phi_k_fp8=True)
+    np.testing.assert_allclose(b["out"], a["out"], rtol=0, atol=1e-12)
+    kg = bf(rng.standard_normal((N, 128)) * 2)
+    c = O.sla_forward_head(qb, kg, vb, 64, 1 / 3, "elu1", phi_k_fp8=True)
+    e = O.sla_forward_head(qb, kg, vb, 64, 1 / 3, "elu1")
+    v64 = O.bf16_to_f64(vb)
+    assert (c["out_linear"] <= v64.max(0) + 1e-12).all() and (c["out_linear"] >= v64.min(0) - 1e-12).all()
+    assert 0 < np.abs(c["out_linear"] - e["out_linear"]).max() < 0.1
