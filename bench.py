@@ -403,6 +403,38 @@ def w8a8_leg(sla, wl, steps, stream, dev):
                                     "kernel": "rowquant_kernel<true>"}}
 
 
+def streaming_ceiling(dev, stream, mib=1024, reps=5):
+    """What plain streaming reaches on this GPU in this process: a device copy of
+    `mib` MiB (read + write bytes over time) and a read-only bf16 sum over
+    the same buffer, each the best of `reps` runs on `stream`."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    x = a.view(torch.bfloat16)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        times = []
+        for _ in range(reps):
+            start.record(stream)
+            fn()
+            end.record(stream)
+            torch.cuda.synchronize()
+            times.append(start.elapsed_time(end) * 1e-3)
+        return min(times)
+
+    with torch.cuda.stream(stream):
+        t_copy = best(lambda: b.copy_(a))
+        t_read = best(lambda: torch.sum(x, dtype=torch.float32))
+    del a, b, x
+    return {"copy_gbps": round(2 * n / t_copy / 1e9, 1), "read_gbps": round(n / t_read / 1e9, 1),
+            "bytes": n, "note": "device copy (read + write bytes) and bf16 sum (read bytes), best of "
+                                f"{reps}; stage_frac_of_copy divides each streaming stage's rate by the copy rate"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,6 +575,8 @@ def main():
     }
     bw = {n: round(bytes_io[n] / (stage_ms[n] * 1e-3) / 1e9, 1) for n in bytes_io if n in stage_ms}
     hbm_frac = {n: round(g * 1e9 / PEAK_HBM, 3) for n, g in bw.items()}
+    ceiling = streaming_ceiling(dev, stream)
+    ceil_frac = {n: round(g / ceiling["copy_gbps"], 3) for n, g in bw.items()}
     # whole call against its ideal: sparse work at the MFMA peaks, streaming
     # stages at the HBM peak, block scores at the fp64 vector peak
     ideal_s = ops_i8 / PEAK_I8_OPS + ops_16 / PEAK_F16_FLOPS
@@ -562,6 +596,8 @@ def main():
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "stage_hbm_gbps": bw,
         "stage_hbm_frac": hbm_frac,
+        "streaming_ceiling": ceiling,
+        "stage_frac_of_copy": ceil_frac,
         "call_roofline_frac": round(ideal_s / (ms_step * 1e-3), 4),
         "roofline": roofline,
     }

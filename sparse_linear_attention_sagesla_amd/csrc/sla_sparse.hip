@@ -841,7 +841,9 @@ __global__ __launch_bounds__(256, 2) void sparse_fwd_kernel(SparseArgs a) {
       kK8Bytes + kF16TileBytes + (kLinAny ? (kF8 ? kK8Bytes : kF16TileBytes) : 0);
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  // wave-uniform in a scalar register: the LDS destinations of the tile loads
+  // (M0) are then computed with scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4;
   const int l16 = lane & 15;
   const int x = blockIdx.x;
