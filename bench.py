@@ -345,6 +345,83 @@ def backward_leg(sla, lib, _lib, q, k, v, wl, keep, phi, fwd_ms, steps, stream, 
                         "unit": "TFLOP/s", "frac": round(ach / (PEAK_F16_FLOPS / 1e12), 4),
                         "kernel": "bwd_q_kernel" if name == "query" else "bwd_kv_kernel"}
         rec["roofline"] = rl
+    rec["training"] = training_leg(sla, lib, _lib, q, k, v, g, wl, keep, phi, ph, ws, grads, ms, steps,
+                                   stream, dev, P if kk > 0 else 0.0, linear)
+    return rec
+
+
+def training_leg(sla, lib, _lib, q, k, v, g, wl, keep, phi, ph, ws, grads, bwd_ms, steps, stream, dev,
+                 pairs_rows, linear):
+    """A training step's attention: sla_attention_fwd_train (the forward plus
+    its residuals) and sla_attention_bwd_saved (the backward from them), each
+    timed over `steps` calls after one warmup call; stage times of the saved
+    backward; the query side's matrix-core roofline on its (one-sweep) work."""
+    import torch
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    rbytes = sla.train_residual_bytes(B, H, N, keep, ph)
+    res = torch.empty(rbytes, dtype=torch.uint8, device=dev)
+    fws = torch.empty(sla.workspace_size(sla.OP_ATTENTION, B, H, N, keep, ph), dtype=torch.uint8,
+                      device=dev)
+    out = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def fwd():
+        rc = lib.sla_attention_fwd_train(_lib._ptr(q), _lib._ptr(k), _lib._ptr(v), B, H, N, d, 64,
+                                         float(keep), ph, _lib._ptr(out), 0, _lib._ptr(res), rbytes,
+                                         _lib._ptr(fws), fws.numel(), sp)
+        if rc != 0:
+            raise RuntimeError(lib.sla_status_string(rc).decode())
+
+    def bwd(events=None):
+        ev = (ctypes.c_void_p * len(events))(*events) if events else None
+        rc = lib.sla_attention_bwd_saved(_lib._ptr(q), _lib._ptr(k), _lib._ptr(v), _lib._ptr(g),
+                                         _lib._ptr(res), rbytes, B, H, N, d, 64, float(keep), ph,
+                                         *[_lib._ptr(x) for x in grads], 0, _lib._ptr(ws), ws.numel(),
+                                         sp, ev)
+        if rc != 0:
+            raise RuntimeError(lib.sla_status_string(rc).decode())
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    f_ms = timed(fwd)
+    b_ms = timed(bwd)
+    log(f"[bench] training: forward with residuals {f_ms:.3f} ms, saved backward {b_ms:.3f} ms")
+    hip = HipEvents()
+    evs = [hip.create(2 * len(BWD_STAGES)) for _ in range(steps)]
+    for e in evs:
+        bwd(e)
+    torch.cuda.synchronize()
+    kk = sla.topk_count(sla.n_blocks(N), keep)
+    stage_ms = {}
+    for si, name in enumerate(BWD_STAGES):
+        if (name == "columns" and kk == 0) or (name == "grad_h" and not linear):
+            continue
+        stage_ms[name] = float(np.mean([hip.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]))
+    for e in evs:
+        hip.destroy(e)
+    rec = {"forward_ms": round(f_ms, 4), "backward_ms": round(b_ms, 4),
+           "step_ms": round(f_ms + b_ms, 4), "residual_bytes": int(rbytes),
+           "backward_stages_ms": {n: round(x, 4) for n, x in stage_ms.items()},
+           "backward_speedup_vs_recompute": round(bwd_ms / b_ms, 3),
+           "note": "sla_attention_fwd_train + sla_attention_bwd_saved: the query side reads the "
+                   "forward's row statistics, outputs and kept share instead of re-walking the kept tiles"}
+    if kk > 0:
+        lin = 1.0 if linear else 0.0
+        i8, f16 = 2 * d * pairs_rows, 4 * d * pairs_rows + lin * 3 * 2 * d * d * N * B * H
+        ach = (0.5 * i8 + f16) / (stage_ms["query"] * 1e-3) / 1e12
+        rec["query_roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_FLOPS / 1e12,
+                                 "unit": "TFLOP/s", "frac": round(ach / (PEAK_F16_FLOPS / 1e12), 4),
+                                 "kernel": "bwd_q_kernel (saved form)"}
+    del res, fws, out
     return rec
 
 

@@ -298,6 +298,56 @@ sla_status sla_attention_bwd_timed(const void *q, const void *k, const void *v,
                                    size_t ws_bytes, void *stream,
                                    void *const *stage_events);
 
+/* ---- Training: a forward that keeps what the backward needs ----------------
+ * SLA is fine-tuned into the model it accelerates (news summary, section
+ * "方法论"), so a training step runs the forward and then the backward on the
+ * same q, k, v.  sla_attention_fwd_train is sla_attention_fwd that also
+ * writes, into a caller-owned residual buffer, what the backward's query side
+ * would otherwise recompute with a second pass over the kept tiles:
+ *   stats  fp32 [B,H,N,2]   per row: log2-domain maximum of the logits (+inf
+ *                           for a row without kept keys) and 1/l
+ *   os     fp32 [B,H,N,128] the softmax branch's normalised output
+ *   ol     fp32 [B,H,N,128] the linear branch's output          (linear only)
+ *   m      bf16 [B,H,Nb,128,128] per query block the kept tiles' share
+ *                           M = sum phi(K_j)^T V_j (phi(K)/16 scale, row =
+ *                           phi channel)            (subtraction form only)
+ *   zm     fp32 [B,H,Nb,128] the kept share of sum phi(K)/16 (same)
+ * each piece 256-byte aligned, in this order; the subtraction form is taken
+ * when the unselected key blocks outnumber the kept ones (Nb - k > k).
+ * sla_train_residual_bytes gives the size (0 for invalid arguments). */
+size_t sla_train_residual_bytes(int B, int H, int N, int d, int block,
+                                double keep, int phi);
+
+/* Same arguments, validation, ownership and errors as sla_attention_fwd, plus
+ * the residual buffer (device memory, 16-byte aligned, at least
+ * sla_train_residual_bytes; SLA_ERR_INVALID_ARG otherwise), every byte of
+ * which the call writes for valid rows.  Exact mode only (no lower-bit
+ * option).  The output equals sla_attention_fwd's bit for bit. */
+sla_status sla_attention_fwd_train(const void *q, const void *k,
+                                   const void *v, int B, int H, int N, int d,
+                                   int block, double keep, int phi, void *out,
+                                   int out_dtype, void *resid,
+                                   size_t resid_bytes, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/* sla_attention_bwd for the residuals of a sla_attention_fwd_train call on the
+ * same q, k, v, keep and phi (resid, resid_bytes as given to it): the query
+ * side takes the forward's row statistics, outputs and kept share from them
+ * instead of walking the kept tiles a second time.  Gradients equal
+ * sla_attention_bwd's to rounding (the linear output comes from the forward's
+ * fp32 H - M instead of a bf16-staged recomputation).  In the direct form
+ * (Nb - k <= k) the residuals hold no kept share and the call computes as
+ * sla_attention_bwd.  stage_events as sla_attention_bwd_timed (NULL: none).
+ * Errors as sla_attention_bwd; a null, misaligned or short resid gives
+ * SLA_ERR_INVALID_ARG. */
+sla_status sla_attention_bwd_saved(const void *q, const void *k, const void *v,
+                                   const void *dout, const void *resid,
+                                   size_t resid_bytes, int B, int H, int N,
+                                   int d, int block, double keep, int phi,
+                                   void *dq, void *dk, void *dv, int grad_dtype,
+                                   void *ws, size_t ws_bytes, void *stream,
+                                   void *const *stage_events);
+
 /* ---- W8A8 INT8 linear layers and FusedNorm ----------------------------------
  * Weights and activations of the linear layers quantised to 8 bits for the
  * INT8 units (news summary, opening component list; commentary, section

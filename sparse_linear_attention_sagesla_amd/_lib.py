@@ -64,6 +64,15 @@ def load() -> ctypes.CDLL:
     lib.sla_attention_bwd.restype = c_int
     lib.sla_attention_bwd_timed.argtypes = lib.sla_attention_bwd.argtypes + [c_void_p]
     lib.sla_attention_bwd_timed.restype = c_int
+    lib.sla_train_residual_bytes.argtypes = [c_int] * 5 + [c_double, c_int]
+    lib.sla_train_residual_bytes.restype = c_size_t
+    lib.sla_attention_fwd_train.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int,
+                                                                          c_void_p, c_size_t, c_void_p,
+                                                                          c_size_t, c_void_p]
+    lib.sla_attention_fwd_train.restype = c_int
+    lib.sla_attention_bwd_saved.argtypes = [c_void_p] * 5 + [c_size_t] + [c_int] * 5 + [c_double, c_int] + \
+        [c_void_p] * 3 + [c_int, c_void_p, c_size_t, c_void_p, c_void_p]
+    lib.sla_attention_bwd_saved.restype = c_int
     lib.sla_rowquant_i8.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
     lib.sla_rowquant_i8.restype = c_int
     lib.sla_fused_norm_i8.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, ctypes.c_float,
@@ -224,9 +233,46 @@ def attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: to
     return out
 
 
+def train_residual_bytes(B: int, H: int, N: int, keep: float, phi="elu1") -> int:
+    """Bytes of a training forward's residual buffer (sla_train_residual_bytes)."""
+    ph = PHI[phi] if isinstance(phi, str) else int(phi)
+    n = load().sla_train_residual_bytes(B, H, N, HEAD_DIM, BLOCK, float(keep), ph)
+    if n == 0:
+        raise SLAError(1, "sla_train_residual_bytes: invalid arguments")
+    return int(n)
+
+
+def attention_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0.1,
+                    phi: str = "elu1", out_dtype=torch.bfloat16, workspace=None):
+    """SageSLA forward that also keeps what the backward needs
+    (sla_attention_fwd_train): returns (out, residuals), residuals a uint8
+    tensor to pass to attention_bwd(..., residuals=...)."""
+    q, k, v = _bhnd(q, "q"), _bhnd(k, "k"), _bhnd(v, "v")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    B, H, N, d = q.shape
+    dev = q.device
+    out = torch.empty(B, H, N, d, dtype=out_dtype, device=dev)
+    ph = PHI[phi] if isinstance(phi, str) else int(phi)
+    res = torch.empty(train_residual_bytes(B, H, N, keep, ph), dtype=torch.uint8, device=dev)
+    ws = _workspace(workspace_size(OP_ATTENTION, B, H, N, keep, ph), dev, workspace)
+    _check(load().sla_attention_fwd_train(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep), ph,
+                                          _ptr(out), 1 if out_dtype == torch.float32 else 0,
+                                          _ptr(res), res.numel(), _ptr(ws), ws.numel(), _stream(dev)),
+           "sla_attention_fwd_train")
+    return out, res
+
+
 def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
-                  keep: float = 0.1, phi: str = "elu1", grad_dtype=torch.bfloat16, workspace=None):
-    """Gradients (dq, dk, dv) of the SageSLA forward for the output gradient dout."""
+                  keep: float = 0.1, phi: str = "elu1", grad_dtype=torch.bfloat16, workspace=None,
+                  residuals=None):
+    """Gradients (dq, dk, dv) of the SageSLA forward for the output gradient dout.
+
+    ``residuals``: the buffer of an attention_train call on the same q, k, v,
+    keep and phi (sla_attention_bwd_saved); None recomputes the forward's part
+    (sla_attention_bwd)."""
     q, k, v, dout = _bhnd(q, "q"), _bhnd(k, "k"), _bhnd(v, "v"), _bhnd(dout, "dout")
     if k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
         raise ValueError("q, k, v, dout must have the same shape")
@@ -238,10 +284,18 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch
     ph = PHI[phi] if isinstance(phi, str) else int(phi)
     nbytes = workspace_size(OP_ATTENTION_BWD, B, H, N, keep, ph)
     ws = _workspace(nbytes, dev, workspace)
-    _check(load().sla_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, BLOCK,
-                                    float(keep), ph, _ptr(dq), _ptr(dk), _ptr(dv),
-                                    1 if grad_dtype == torch.float32 else 0, _ptr(ws), ws.numel(),
-                                    _stream(dev)), "sla_attention_bwd")
+    f32 = 1 if grad_dtype == torch.float32 else 0
+    if residuals is None:
+        _check(load().sla_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, BLOCK,
+                                        float(keep), ph, _ptr(dq), _ptr(dk), _ptr(dv), f32, _ptr(ws),
+                                        ws.numel(), _stream(dev)), "sla_attention_bwd")
+    else:
+        if residuals.device != dev or residuals.dtype != torch.uint8 or not residuals.is_contiguous():
+            raise ValueError("residuals must be the contiguous uint8 buffer of attention_train")
+        _check(load().sla_attention_bwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(residuals),
+                                              residuals.numel(), B, H, N, d, BLOCK, float(keep), ph,
+                                              _ptr(dq), _ptr(dk), _ptr(dv), f32, _ptr(ws), ws.numel(),
+                                              _stream(dev), None), "sla_attention_bwd_saved")
     return dq, dk, dv
 
 

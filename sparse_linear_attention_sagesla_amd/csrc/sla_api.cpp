@@ -179,6 +179,33 @@ sla_status check_fwd_args(const void* q, const void* k, const void* v, int B, in
   return SLA_OK;
 }
 
+// A training forward's residuals in the caller's buffer (256-byte aligned
+// pieces): per-row statistics and softmax output, the linear output, and in
+// the subtraction form the kept share M and z_M per query block.  Returns the
+// bytes needed; fills *r when base is set.
+size_t carve_residuals(const Shape& s, int phi_eff, bool direct, unsigned char* base,
+                       sla::TrainResiduals* r) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~size_t(255);
+    return p;
+  };
+  const size_t BH = s.BH, N = s.N, Nb = s.Nb, D = SLA_HEAD_DIM;
+  sla::TrainResiduals t;
+  t.stats = reinterpret_cast<float*>(take(BH * N * 2 * sizeof(float)));
+  t.os = reinterpret_cast<float*>(take(BH * N * D * sizeof(float)));
+  if (phi_eff != SLA_PHI_NONE) {
+    t.ol = reinterpret_cast<float*>(take(BH * N * D * sizeof(float)));
+    if (!direct) {
+      t.m = reinterpret_cast<uint16_t*>(take(BH * Nb * D * D * sizeof(uint16_t)));
+      t.zm = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+    }
+  }
+  if (r) *r = t;
+  return off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,10 +293,15 @@ sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, i
   return device_status(e);
 }
 
-sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N,
-                                int d, int block, double keep, int phi, void* out, int out_dtype,
-                                float* out_linear, void* ws, size_t ws_bytes, void* stream,
-                                void* const* stage_events, int options) {
+}  // extern "C"
+
+namespace {
+
+// The forward; with `res` it also writes a training forward's residuals.
+sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                    int block, double keep, int phi, void* out, int out_dtype, float* out_linear,
+                    void* ws, size_t ws_bytes, void* stream, void* const* stage_events, int options,
+                    const sla::TrainResiduals* res) {
   const sla_status st =
       check_fwd_args(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, out_linear);
   if (st != SLA_OK) return st;
@@ -324,9 +356,51 @@ sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int
     });
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
-                                  out_linear, fp8, hs);
+                                  out_linear, fp8, res, hs);
   });
   return device_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+sla_status sla_attention_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N,
+                                int d, int block, double keep, int phi, void* out, int out_dtype,
+                                float* out_linear, void* ws, size_t ws_bytes, void* stream,
+                                void* const* stage_events, int options) {
+  return fwd_impl(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, out_linear, ws, ws_bytes,
+                  stream, stage_events, options, nullptr);
+}
+
+size_t sla_train_residual_bytes(int B, int H, int N, int d, int block, double keep, int phi) {
+  if (check_shape(B, H, N, d, block) != SLA_OK) return 0;
+  if (std::isnan(keep) || keep < 0.0 || keep > 1.0 || phi < SLA_PHI_NONE || phi > SLA_PHI_RELU) return 0;
+  const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
+  const int kk = sla_topk_count(Nb, keep);
+  if (kk == 0 && phi == SLA_PHI_NONE) return 0;
+  const Shape s = make_shape(B, H, N, kk);
+  const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
+  return carve_residuals(s, phi_eff, phi_eff != SLA_PHI_NONE && sla::linear_direct(s), nullptr, nullptr);
+}
+
+sla_status sla_attention_fwd_train(const void* q, const void* k, const void* v, int B, int H, int N,
+                                   int d, int block, double keep, int phi, void* out, int out_dtype,
+                                   void* resid, size_t resid_bytes, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  const sla_status st = check_fwd_args(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr);
+  if (st != SLA_OK) return st;
+  const size_t need = sla_train_residual_bytes(B, H, N, d, block, keep, phi);
+  if (!resid || !aligned16(resid) || resid_bytes < need) return SLA_ERR_INVALID_ARG;
+  const int Nb = (N + SLA_BLOCK - 1) / SLA_BLOCK;
+  const int kk = sla_topk_count(Nb, keep);
+  const Shape s = make_shape(B, H, N, kk);
+  const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
+  sla::TrainResiduals r;
+  carve_residuals(s, phi_eff, phi_eff != SLA_PHI_NONE && sla::linear_direct(s),
+                  static_cast<unsigned char*>(resid), &r);
+  return fwd_impl(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, r.ol, ws, ws_bytes, stream,
+                  nullptr, 0, &r);
 }
 
 sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B, int H, int N,
@@ -357,10 +431,17 @@ sla_status sla_attention_fwd_noalloc(const void* q, const void* k, const void* v
                               SLA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
-sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, const void* dout,
-                                   int B, int H, int N, int d, int block, double keep, int phi,
-                                   void* dq, void* dk, void* dv, int grad_dtype, void* ws,
-                                   size_t ws_bytes, void* stream, void* const* stage_events) {
+}  // extern "C"
+
+namespace {
+
+// The backward; with `resid` (a training forward's residuals) the query side
+// reads the forward's statistics, outputs and kept share instead of
+// recomputing them (not in the direct form, whose forward keeps no kept share).
+sla_status bwd_impl(const void* q, const void* k, const void* v, const void* dout,
+                    const void* resid, size_t resid_bytes, int B, int H, int N, int d, int block,
+                    double keep, int phi, void* dq, void* dk, void* dv, int grad_dtype, void* ws,
+                    size_t ws_bytes, void* stream, void* const* stage_events) {
   sla_status st = check_shape(B, H, N, d, block);
   if (st != SLA_OK) return st;
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return SLA_ERR_INVALID_ARG;
@@ -388,6 +469,15 @@ sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, 
   const auto* gb = static_cast<const uint16_t*>(dout);
   const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
   const int f32 = grad_dtype == SLA_OUT_F32 ? 1 : 0;
+  sla::TrainResiduals r;
+  const sla::TrainResiduals* res = nullptr;
+  if (resid) {
+    if (!aligned16(resid) || resid_bytes < sla_train_residual_bytes(B, H, N, d, block, keep, phi))
+      return SLA_ERR_INVALID_ARG;
+    const bool direct = phi_eff != SLA_PHI_NONE && sla::linear_direct(s);
+    carve_residuals(s, phi_eff, direct, static_cast<unsigned char*>(const_cast<void*>(resid)), &r);
+    if (!direct) res = &r;
+  }
   hipError_t e = hipSuccess;
   auto run = [&](auto&& launch) {
     if (e == hipSuccess) e = launch();
@@ -425,7 +515,7 @@ sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, 
     mark(SLA_BWD_STAGE_COLUMNS, 1);
   }
   mark(SLA_BWD_STAGE_QUERY, 0);
-  run([&] { return sla::launch_bwd_q(qb, vb, gb, w, bw, s, phi_eff, dq, f32, hs); });
+  run([&] { return sla::launch_bwd_q(qb, vb, gb, w, bw, s, phi_eff, dq, f32, res, hs); });
   mark(SLA_BWD_STAGE_QUERY, 1);
   if (phi_eff != SLA_PHI_NONE) {
     mark(SLA_BWD_STAGE_GRAD_H, 0);
@@ -436,6 +526,28 @@ sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, 
   run([&] { return sla::launch_bwd_kv(kb, vb, gb, w, bw, s, phi_eff, dk, dv, f32, hs); });
   mark(SLA_BWD_STAGE_KEY, 1);
   return device_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+sla_status sla_attention_bwd_timed(const void* q, const void* k, const void* v, const void* dout,
+                                   int B, int H, int N, int d, int block, double keep, int phi,
+                                   void* dq, void* dk, void* dv, int grad_dtype, void* ws,
+                                   size_t ws_bytes, void* stream, void* const* stage_events) {
+  return bwd_impl(q, k, v, dout, nullptr, 0, B, H, N, d, block, keep, phi, dq, dk, dv, grad_dtype, ws,
+                  ws_bytes, stream, stage_events);
+}
+
+sla_status sla_attention_bwd_saved(const void* q, const void* k, const void* v, const void* dout,
+                                   const void* resid, size_t resid_bytes, int B, int H, int N, int d,
+                                   int block, double keep, int phi, void* dq, void* dk, void* dv,
+                                   int grad_dtype, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* stage_events) {
+  if (!resid) return SLA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, dout, resid, resid_bytes, B, H, N, d, block, keep, phi, dq, dk, dv,
+                  grad_dtype, ws, ws_bytes, stream, stage_events);
 }
 
 sla_status sla_attention_bwd(const void* q, const void* k, const void* v, const void* dout,

@@ -108,8 +108,18 @@ inline bool linear_direct(const Shape& sh) { return sh.Nb - sh.k <= sh.k; }
 // needed by launch_sparse_fwd unless the linear branch takes the direct form.
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
                                  hipStream_t s);
+// What a training forward keeps for the backward (sla_attention_fwd_train);
+// m and zm only in the subtraction form.
+struct TrainResiduals {
+  float* stats = nullptr;   // [BH, N, 2] log2-domain row maximum (+inf: no weights), 1/l
+  float* os = nullptr;      // [BH, N, 128] normalised softmax-branch output
+  float* ol = nullptr;      // [BH, N, 128] linear-branch output
+  uint16_t* m = nullptr;    // [BH, Nb, 128, 128] bf16 kept share M, staged scale (phi/16)
+  float* zm = nullptr;      // [BH, Nb, 128] kept share of z, staged scale
+};
 hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
-                             void* out, int out_f32, float* out_linear, bool fp8, hipStream_t s);
+                             void* out, int out_f32, float* out_linear, bool fp8,
+                             const TrainResiduals* res, hipStream_t s);
 // Backward launchers.
 // Per block: K^T, Q^T, dO^T as bf16 [channel][permuted row] (any may be null).
 hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* q, const uint16_t* dout,
@@ -118,9 +128,11 @@ hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* q, const u
 // Column lists: for every key block, the query blocks whose kept list holds it.
 hipError_t launch_column_lists(const int32_t* idx, const Shape& sh, uint32_t* maskT,
                                int32_t* coff, int32_t* cidx, hipStream_t s);
+// Query side of the backward; with `res` (a training forward's residuals) the
+// forward's statistics, outputs and kept share are read instead of recomputed.
 hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* dout,
                         const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
-                        void* dq, int grad_f32, hipStream_t s);
+                        void* dq, int grad_f32, const TrainResiduals* res, hipStream_t s);
 // G = sum over all rows of (phi(Q)/den)^T dO and g_z (from bwd_q's outputs).
 hipError_t launch_grad_h(const BwdWorkspace& bw, const Shape& sh, hipStream_t s);
 hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* dout,

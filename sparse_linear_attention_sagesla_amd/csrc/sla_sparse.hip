@@ -223,6 +223,11 @@ struct SparseArgs {
   void* out;
   int out_f32;
   float* out_linear;
+  // what a training forward keeps for the backward (null otherwise)
+  float* res_stats;     // [BH, N, 2] per row: log2-domain maximum, 1/l
+  float* res_os;        // [BH, N, 128] softmax branch's normalised output
+  uint16_t* res_m;      // [BH, Nb, 128, 128] bf16 kept share M (staged scale), row = phi channel
+  float* res_zm;        // [BH, Nb, 128] kept share of z (staged scale)
 };
 
 struct State {
@@ -692,6 +697,43 @@ constexpr int kEpZU = kD * kD * 2;
 constexpr int kEpZ = kEpZU + kD * 4;
 constexpr int kEpRed = kEpZ + kD * 4;
 
+// The kept tiles' share of the linear state of query block i, as a training
+// forward keeps it for the backward: M = sum phi(K_j)^T V_j over the kept
+// tiles, row-major bf16 (row = phi channel 32w + 16x + l16, this lane's four
+// entries 16dt + 4g + r of each row), and z_M per channel (fp32).
+__device__ __forceinline__ void save_kept_share(const State& S, const SparseArgs& a, size_t bh, int i,
+                                                int wave, int lane) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const int g = lane >> 4, l16 = lane & 15;
+  uint16_t* mb = a.res_m + (bh * a.Nb + i) * (size_t)(kD * kD);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int c = 32 * wave + 16 * x + l16;
+      const bf16x4 h4 = {(__bf16)S.mk[dt][x][0], (__bf16)S.mk[dt][x][1], (__bf16)S.mk[dt][x][2],
+                         (__bf16)S.mk[dt][x][3]};
+      *reinterpret_cast<bf16x4*>(mb + (size_t)c * kD + 16 * dt + 4 * g) = h4;
+    }
+  if (lane < 32) a.res_zm[(bh * a.Nb + i) * kD + 32 * wave + lane] = (float)S.zk;
+}
+
+// A training forward's per-row residuals: the softmax statistics (log2-domain
+// maximum, +inf for a row without weights, and 1/l) and the normalised
+// softmax output.
+__device__ __forceinline__ void save_row(const State& S, const SparseArgs& a, size_t bh, int qrow,
+                                         bool qvalid, float inv_l, int g) {
+  if (!qvalid) return;
+  const size_t row = bh * a.N + qrow;
+  if (g == 0) {
+    a.res_stats[2 * row] = inv_l > 0.0f ? S.m_run : INFINITY;
+    a.res_stats[2 * row + 1] = inv_l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<v4f*>(a.res_os + row * kD + 16 * dt + 4 * g) = S.o[dt] * inv_l;
+}
+
 // Normalise, add the linear branch, store this lane's query row.
 template <int kMode, bool kF8>
 __device__ __forceinline__ void finish_query(State& S, const SparseArgs& a, size_t bh, int i,
@@ -712,6 +754,7 @@ __device__ __forceinline__ void finish_query(State& S, const SparseArgs& a, size
     load_phi_q_row(a, bh, qrow, qvalid, g, fq);
     bool direct = kMode == kDirect;
     if (kMode == kSubtract) {
+      if (!kF8 && a.res_m) save_kept_share(S, a, bh, i, wave, lane);
       // whole-head sums: z (fp64, this lane's channel 32w + (lane & 31)) and
       // H in this lane's M^T fragments, loaded together
       const double zh = a.z64[bh * kD + 32 * wave + (lane & 31)];
@@ -794,6 +837,7 @@ __device__ __forceinline__ void finish_query(State& S, const SparseArgs& a, size
     }
   }
 
+  if (!kF8 && a.res_stats) save_row(S, a, bh, qrow, qvalid, inv_l, g);  // training: exact mode only
   if (qvalid) {
     const size_t orow = (bh * a.N + qrow) * kD;
 #pragma unroll
@@ -1307,6 +1351,12 @@ struct BwdQArgs {
   uint16_t* fqs;          // (phi(Q)/den)^T bf16 per block [BH, Nb, D, 64 permuted rows]
   void* dq;
   int grad_f32;
+  // a training forward's residuals (the saved form; null otherwise)
+  const float* res_stats;   // [BH, N, 2] log2-domain row maximum, 1/l
+  const float* res_os;      // [BH, N, D] normalised softmax-branch output
+  const float* res_ol;      // [BH, N, D] linear-branch output
+  const uint16_t* res_m;    // [BH, Nb, D, D] bf16 kept share M (staged scale)
+  const float* res_zm;      // [BH, Nb, D] kept share of z (staged scale)
 };
 
 struct BwdQSrc {
@@ -1363,7 +1413,9 @@ __device__ __forceinline__ void bwd_q_tile(const lds_byte* st, const v4i qf[2], 
     }
 }
 
-template <bool kLin>
+// kSaved: the forward's statistics, outputs and kept share come from a
+// training forward's residuals instead of a first sweep over the kept tiles.
+template <bool kLin, bool kSaved>
 __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   lds_byte* smem = (lds_byte*)smem_raw;
@@ -1389,14 +1441,22 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
   const int ngroups = (a.Nb + kGroup - 1) / kGroup;
   const int32_t* col =
       a.k > 0 ? a.sched + (bh * ngroups + i / kGroup) * (size_t)a.k * kGroup + i % kGroup : nullptr;
-  run_sched<kLin>(S, smem, kBwdStage, col, a.k, a, head_sources(a, bh, kLin), bh, qf, lo, qscale,
-                  wave, g);
+  if (!kSaved)
+    run_sched<kLin>(S, smem, kBwdStage, col, a.k, a, head_sources(a, bh, kLin), bh, qf, lo, qscale,
+                    wave, g);
 
   // softmax statistics of this lane's query and D = dO . O_s
-  float l = S.l_part + __shfl_xor(S.l_part, 16);
-  l += __shfl_xor(l, 32);
-  const float inv_l = (a.k > 0 && l > 0.0f && qvalid) ? 1.0f / l : 0.0f;
-  const float m_fin = inv_l > 0.0f ? S.m_run : INFINITY;  // rows without weights get P = 0
+  const size_t rrow = (size_t)bh * a.N + (qvalid ? qrow : 0);
+  float inv_l, m_fin;
+  if (kSaved) {
+    inv_l = (a.k > 0 && qvalid) ? b.res_stats[2 * rrow + 1] : 0.0f;
+    m_fin = inv_l > 0.0f ? b.res_stats[2 * rrow] : INFINITY;
+  } else {
+    float l = S.l_part + __shfl_xor(S.l_part, 16);
+    l += __shfl_xor(l, 32);
+    inv_l = (a.k > 0 && l > 0.0f && qvalid) ? 1.0f / l : 0.0f;
+    m_fin = inv_l > 0.0f ? S.m_run : INFINITY;  // rows without weights get P = 0
+  }
   const uint16_t* dorow = b.dout + ((size_t)bh * a.N + (qvalid ? qrow : 0)) * kD;
   v4f go[8];  // dO in the O^T layout, channel 16dt + 4g + r
 #pragma unroll
@@ -1407,12 +1467,16 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
   }
   float dpart = 0.0f;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < 8; ++dt) {
+    const v4f os = !kSaved ? S.o[dt]
+                   : qvalid ? *reinterpret_cast<const v4f*>(b.res_os + rrow * kD + 16 * dt + 4 * g)
+                            : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dpart += go[dt][r] * S.o[dt][r];
+    for (int r = 0; r < 4; ++r) dpart += go[dt][r] * os[r];
+  }
   dpart += __shfl_xor(dpart, 16);
   dpart += __shfl_xor(dpart, 32);
-  const float Dt = dpart * inv_l;
+  const float Dt = kSaved ? (inv_l > 0.0f ? dpart : 0.0f) : dpart * inv_l;
 
   // dO of this lane's query as B operands (channels 32ks + 8g + e)
   bf16x8 gf[4];
@@ -1430,11 +1494,38 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
   if (kLin) {
     half8 fq[4];
     load_phi_q(a, bh, qrow, qvalid, g, fq);
-    v4f nm[8];
-    float dm;
-    linear_share(S, smem, fq, lo, wave, lane, nm, dm);
+    const float* zmb = kSaved ? b.res_zm + ((size_t)bh * a.Nb + i) * kD : nullptr;
     v4f ol[8];
-    const float inv_den = linear_subtract_out(a, bh, g, lo, fq, nm, dm, ol);
+    float inv_den;
+    if (kSaved) {
+      // (phi(Q)z - phi(Q)z_M) in the staged scale, as linear_subtract_out
+      // forms it, and the forward's linear output
+      const float* zz0 = a.z + bh * kD;
+      float dz = 0.0f, dm = 0.0f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 32 * cc + 8 * g + e;
+          dz += (float)fq[cc][e] * zz0[c];
+          dm += (float)fq[cc][e] * zmb[c];
+        }
+      dz += __shfl_xor(dz, 16);
+      dz += __shfl_xor(dz, 32);
+      dm += __shfl_xor(dm, 16);
+      dm += __shfl_xor(dm, 32);
+      const float den = dz - dm;
+      inv_den = den > 1e-6f * dz ? 1.0f / den : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        ol[dt] = qvalid ? *reinterpret_cast<const v4f*>(b.res_ol + rrow * kD + 16 * dt + 4 * g)
+                        : v4f{0.f, 0.f, 0.f, 0.f};
+    } else {
+      v4f nm[8];
+      float dm;
+      linear_share(S, smem, fq, lo, wave, lane, nm, dm);
+      inv_den = linear_subtract_out(a, bh, g, lo, fq, nm, dm, ol);
+    }
     float up = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -1444,9 +1535,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
     up += __shfl_xor(up, 32);
     u = qvalid ? -up : 0.0f;
     // M (kept share, staged scale) row-major as bf16: row c = 32w + 16x + l16
-    // holds M[c][16dt + 4g + r]
+    // holds M[c][16dt + 4g + r] (the saved form reads it from the residuals)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 8 && !kSaved; ++dt)
 #pragma unroll
       for (int xx = 0; xx < 2; ++xx) {
         const int c = 32 * wave + 16 * xx + l16;
@@ -1468,22 +1559,27 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       v4f ah = v4f{0.f, 0.f, 0.f, 0.f}, am = v4f{0.f, 0.f, 0.f, 0.f};
-      bf16x8 hv[4];  // the row's four fragments, loaded together
+      bf16x8 hv[4], mv[4];  // the row's four fragments of H (and saved M), loaded together
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks) {
         hv[ks] = *reinterpret_cast<const bf16x8*>(hrow + (16 * ct + l16) * kD + 32 * ks + 8 * g);
+        if (kSaved)
+          mv[ks] = *reinterpret_cast<const bf16x8*>(b.res_m + ((size_t)bh * a.Nb + i) * (kD * kD) +
+                                                    (16 * ct + l16) * kD + 32 * ks + 8 * g);
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv[ks], gf[ks], ah, 0, 0, 0);
-        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row_frag(smem + kMRowOff, 16 * ct + l16, 4 * ks + g),
-                                                     gf[ks], am, 0, 0, 0);
+        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            kSaved ? mv[ks] : lds_row_frag(smem + kMRowOff, 16 * ct + l16, 4 * ks + g), gf[ks], am, 0, 0, 0);
       }
       const uint2 qw = *reinterpret_cast<const uint2*>(qrowp + 16 * ct + 4 * g);
       const float qv[4] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y)};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = 16 * ct + 4 * g + r;
-        const float zi = zz[c] - *(__attribute__((address_space(3))) const float*)(smem + kZOffShared + 4 * c);
+        const float zi =
+            zz[c] - (kSaved ? zmb[c] : *(__attribute__((address_space(3))) const float*)(smem + kZOffShared + 4 * c));
         const float dphi = (ah[r] - am[r] + u * zi) * (inv_den * 0.0625f);
         dqa[ct][r] = qvalid ? dphi * phi_slope(qv[r], a.phi) * kSqrtD : 0.0f;
         // phi(Q)/den, transposed into [c][permuted row] (region of M^T, now free)
@@ -1875,8 +1971,13 @@ hipError_t launch_mode(const SparseArgs& a, const Shape& sh, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
-                             void* out, int out_f32, float* out_linear, bool fp8, hipStream_t s) {
+                             void* out, int out_f32, float* out_linear, bool fp8,
+                             const TrainResiduals* res, hipStream_t s) {
   SparseArgs a;
+  a.res_stats = res ? res->stats : nullptr;
+  a.res_os = res ? res->os : nullptr;
+  a.res_m = res ? res->m : nullptr;
+  a.res_zm = res ? res->zm : nullptr;
   a.q = q;
   a.q8 = ws.q8;
   a.k8 = ws.k8;
@@ -1910,8 +2011,13 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
 
 hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* dout,
                         const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
-                        void* dq, int grad_f32, hipStream_t s) {
+                        void* dq, int grad_f32, const TrainResiduals* res, hipStream_t s) {
   BwdQArgs b;
+  b.res_stats = res ? res->stats : nullptr;
+  b.res_os = res ? res->os : nullptr;
+  b.res_ol = res ? res->ol : nullptr;
+  b.res_m = res ? res->m : nullptr;
+  b.res_zm = res ? res->zm : nullptr;
   SparseArgs& a = b.f;
   a = SparseArgs{};
   a.q = q;
@@ -1941,15 +2047,14 @@ hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* do
   b.grad_f32 = grad_f32;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
   const int slots = kGroup * ((sh.Nb + kGroup - 1) / kGroup);
-  const hipError_t e = allow_lds(lin ? reinterpret_cast<const void*>(bwd_q_kernel<true>)
-                                     : reinterpret_cast<const void*>(bwd_q_kernel<false>),
-                                 2 * kBwdStage);
-  if (e != hipSuccess) return e;
-  if (lin)
-    bwd_q_kernel<true><<<dim3(slots, sh.BH), 256, 2 * kBwdStage, s>>>(b);
-  else
-    bwd_q_kernel<false><<<dim3(slots, sh.BH), 256, 2 * kBwdStage, s>>>(b);
-  return hipGetLastError();
+  auto launch = [&](auto kernel) {
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel), 2 * kBwdStage);
+    if (e != hipSuccess) return e;
+    kernel<<<dim3(slots, sh.BH), 256, 2 * kBwdStage, s>>>(b);
+    return hipGetLastError();
+  };
+  if (res) return lin ? launch(bwd_q_kernel<true, true>) : launch(bwd_q_kernel<false, true>);
+  return lin ? launch(bwd_q_kernel<true, false>) : launch(bwd_q_kernel<false, false>);
 }
 
 hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* dout,

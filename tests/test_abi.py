@@ -265,3 +265,71 @@ def test_noalloc_validates_on_the_host():
     assert call(out=MISALIGNED) == INVALID
     assert call(keep=0.0, phi=0) == INVALID
     assert call(out_dtype=3) == INVALID
+
+
+def _train_res_bytes(B, H, N, keep, phi):
+    """The residual layout of sla_attention_fwd_train, from its documentation."""
+    up = lambda n: (n + 255) // 256 * 256
+    nb = (N + 63) // 64
+    k = O.topk_count(nb, keep)
+    lin = phi != 0 and k < nb
+    n = up(B * H * N * 2 * 4) + up(B * H * N * 128 * 4)
+    if lin:
+        n += up(B * H * N * 128 * 4)
+        if nb - k > k:
+            n += up(B * H * nb * 128 * 128 * 2) + up(B * H * nb * 128 * 4)
+    return n
+
+
+@pytest.mark.parametrize("B,H,N,keep,phi", [(1, 2, 2048, 0.1, 1), (1, 2, 2048, 0.1, 0), (2, 3, 1000, 0.6, 2),
+                                            (1, 1, 1, 0.0, 1), (1, 40, 75600, 0.1, 1), (1, 2, 130, 1.0, 1)])
+def test_train_residual_bytes_follow_the_documented_layout(B, H, N, keep, phi):
+    L = lib()
+    L.sla_train_residual_bytes.restype = ctypes.c_size_t
+    got = L.sla_train_residual_bytes(B, H, N, 128, 64, ctypes.c_double(keep), phi)
+    assert got == _train_res_bytes(B, H, N, keep, phi)
+    assert _lib.train_residual_bytes(B, H, N, keep, phi) == got
+
+
+def test_train_residual_bytes_zero_for_invalid_calls():
+    L = lib()
+    L.sla_train_residual_bytes.restype = ctypes.c_size_t
+    f = lambda **kw: L.sla_train_residual_bytes(kw.get("B", 1), kw.get("H", 2), kw.get("N", 2048),
+                                                kw.get("d", 128), kw.get("block", 64),
+                                                ctypes.c_double(kw.get("keep", 0.1)), kw.get("phi", 1))
+    assert f() > 0
+    for bad in (dict(d=64), dict(block=32), dict(N=0), dict(keep=1.5), dict(keep=float("nan")),
+                dict(phi=3), dict(keep=0.0, phi=0)):
+        assert f(**bad) == 0, bad
+
+
+def test_training_entry_points_reject_bad_arguments_before_launch():
+    """sla_attention_fwd_train and sla_attention_bwd_saved check the residual
+    buffer (null, misaligned, too small) with the other arguments, before any
+    device call."""
+    L = lib()
+    L.sla_attention_fwd_train.restype = ctypes.c_int
+    L.sla_attention_bwd_saved.restype = ctypes.c_int
+    need = _train_res_bytes(1, 2, 2048, 0.1, 1)
+
+    def fwd(res=FAKE, res_bytes=need, ws=NULL, ws_bytes=0, q=FAKE, d=128):
+        return L.sla_attention_fwd_train(q, FAKE, FAKE, 1, 2, 2048, d, 64, ctypes.c_double(0.1), 1, FAKE, 0,
+                                         res, ctypes.c_size_t(res_bytes), ws, ctypes.c_size_t(ws_bytes), NULL)
+
+    assert fwd(res=NULL) == INVALID
+    assert fwd(res=MISALIGNED) == INVALID
+    assert fwd(res_bytes=need - 256) == INVALID
+    assert fwd(q=NULL) == INVALID
+    assert fwd(d=64) == UNSUPPORTED
+    assert fwd() == WORKSPACE                      # residuals fine, no workspace
+
+    def bwd(res=FAKE, res_bytes=need, ws=FAKE, ws_bytes=1 << 40, g=FAKE):
+        return L.sla_attention_bwd_saved(FAKE, FAKE, FAKE, g, res, ctypes.c_size_t(res_bytes), 1, 2, 2048, 128,
+                                         64, ctypes.c_double(0.1), 1, FAKE, FAKE, FAKE, 0, ws,
+                                         ctypes.c_size_t(ws_bytes), NULL, NULL)
+
+    assert bwd(res=NULL) == INVALID
+    assert bwd(res=MISALIGNED) == INVALID
+    assert bwd(res_bytes=need - 1) == INVALID
+    assert bwd(g=NULL) == INVALID
+    assert bwd(ws=NULL) == WORKSPACE
