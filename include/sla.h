@@ -263,7 +263,7 @@ sla_status sla_attention_fwd_noalloc(const void *q, const void *k,
  *                 (out; every element written)
  * Arithmetic: INT8 matrix cores for the logits, bf16 matrix cores with fp32
  * accumulation for every other product (P and dS rounded to bf16), fp32
- * elsewhere.  Workspace: SLA_OP_ATTENTION_BWD (about 14 bytes per element of
+ * elsewhere.  Workspace: SLA_OP_ATTENTION_BWD (about 13 bytes per element of
  * Q at keep 0.1).  All work runs on `stream`.  Errors as sla_attention_fwd;
  * dout and the three outputs must be 16-byte aligned. */
 sla_status sla_attention_bwd(const void *q, const void *k, const void *v,
@@ -276,7 +276,7 @@ sla_status sla_attention_bwd(const void *q, const void *k, const void *v,
 typedef enum sla_bwd_stage {
   SLA_BWD_STAGE_FWD_STAGING = 0, /* the forward's statistics, selection, walk
                                     schedule, K mean and linear staging           */
-  SLA_BWD_STAGE_TRANSPOSE = 1,   /* K^T, Q^T, dO^T per block                      */
+  SLA_BWD_STAGE_TRANSPOSE = 1,   /* K^T, dO^T per block                           */
   SLA_BWD_STAGE_COLUMNS = 2,     /* per key block, the query blocks keeping it    */
   SLA_BWD_STAGE_QUERY = 3,       /* query side: dQ, row statistics                */
   SLA_BWD_STAGE_GRAD_H = 4,      /* whole-head linear-gradient sums               */

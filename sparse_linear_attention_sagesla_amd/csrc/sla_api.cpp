@@ -91,9 +91,8 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
       b.gz = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
     }
     b.kt = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
-    b.qt = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
     b.dot = reinterpret_cast<uint16_t*>(take(BH * Np * D * sizeof(uint16_t)));
-    b.stats = reinterpret_cast<float*>(take(BH * Nb * 256 * sizeof(float)));
+    b.stats = reinterpret_cast<float*>(take(BH * Nb * sla::kBwdStatFloats * sizeof(float)));
     if (s.k > 0) {
       b.maskT = reinterpret_cast<uint32_t*>(take(BH * Nb * (size_t)((s.Nb + 31) / 32) * sizeof(uint32_t)));
       b.coff = reinterpret_cast<int32_t*>(take(BH * (Nb + 1) * sizeof(int32_t)));
@@ -506,8 +505,7 @@ sla_status bwd_impl(const void* q, const void* k, const void* v, const void* dou
   mark(SLA_BWD_STAGE_FWD_STAGING, 1);
   // the backward's own staging
   mark(SLA_BWD_STAGE_TRANSPOSE, 0);
-  run([&] { return sla::launch_transpose_blocks(kk > 0 ? kb : nullptr, kk > 0 ? qb : nullptr, gb, s,
-                                                bw.kt, bw.qt, bw.dot, hs); });
+  run([&] { return sla::launch_transpose_blocks(kk > 0 ? kb : nullptr, gb, s, bw.kt, bw.dot, hs); });
   mark(SLA_BWD_STAGE_TRANSPOSE, 1);
   if (kk > 0) {
     mark(SLA_BWD_STAGE_COLUMNS, 0);
@@ -523,7 +521,7 @@ sla_status bwd_impl(const void* q, const void* k, const void* v, const void* dou
     mark(SLA_BWD_STAGE_GRAD_H, 1);
   }
   mark(SLA_BWD_STAGE_KEY, 0);
-  run([&] { return sla::launch_bwd_kv(kb, vb, gb, w, bw, s, phi_eff, dk, dv, f32, hs); });
+  run([&] { return sla::launch_bwd_kv(qb, kb, vb, gb, w, bw, s, phi_eff, dk, dv, f32, hs); });
   mark(SLA_BWD_STAGE_KEY, 1);
   return device_status(e);
 }

@@ -33,14 +33,12 @@ constexpr int kTPitch = 136;  // LDS row pitch in bf16 (272 bytes)
 
 __global__ __launch_bounds__(256) void transpose_blocks_kernel(const uint16_t* __restrict__ x0,
                                                                const uint16_t* __restrict__ x1,
-                                                               const uint16_t* __restrict__ x2,
                                                                uint16_t* __restrict__ o0,
-                                                               uint16_t* __restrict__ o1,
-                                                               uint16_t* __restrict__ o2, int N,
+                                                               uint16_t* __restrict__ o1, int N,
                                                                int Nb) {
   __shared__ __align__(16) uint16_t tile[kBlk * kTPitch];
-  const uint16_t* x = blockIdx.z == 0 ? x0 : (blockIdx.z == 1 ? x1 : x2);
-  uint16_t* o = blockIdx.z == 0 ? o0 : (blockIdx.z == 1 ? o1 : o2);
+  const uint16_t* x = blockIdx.z == 0 ? x0 : x1;
+  uint16_t* o = blockIdx.z == 0 ? o0 : o1;
   if (!x || !o) return;
   const int t = threadIdx.x;
   const int blk = blockIdx.x;
@@ -206,7 +204,7 @@ __global__ __launch_bounds__(256) void grad_h_partial_kernel(const uint16_t* __r
     const size_t base = ((size_t)bh * Nb + i) * (kD * kBlk);
     const uint16_t* fb = fqs + base;
     const uint16_t* db = dot + base;
-    const float* ub = stats + ((size_t)bh * Nb + i) * 256 + 192;
+    const float* ub = stats + ((size_t)bh * Nb + i) * kBwdStatFloats + 192;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       // every operand of this half block first, unconditionally, so the loads
@@ -272,10 +270,9 @@ __global__ __launch_bounds__(256) void grad_h_final_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* q, const uint16_t* dout,
-                                   const Shape& sh, uint16_t* kt, uint16_t* qt, uint16_t* dot,
-                                   hipStream_t s) {
-  transpose_blocks_kernel<<<dim3(sh.Nb, sh.BH, 3), 256, 0, s>>>(k, q, dout, kt, qt, dot, sh.N, sh.Nb);
+hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* dout, const Shape& sh,
+                                   uint16_t* kt, uint16_t* dot, hipStream_t s) {
+  transpose_blocks_kernel<<<dim3(sh.Nb, sh.BH, 2), 256, 0, s>>>(k, dout, kt, dot, sh.N, sh.Nb);
   return hipGetLastError();
 }
 

@@ -63,10 +63,10 @@ struct Workspace {
 struct BwdWorkspace {
   uint16_t* hb = nullptr;     // [BH, D, D]     bf16 H row-major (staged scale, phi/16)
   uint16_t* kt = nullptr;     // [BH, Nb, D, 64] bf16 K^T per block, [channel][permuted key]
-  uint16_t* qt = nullptr;     // [BH, Nb, D, 64] bf16 Q^T per block
   uint16_t* dot = nullptr;    // [BH, Nb, D, 64] bf16 dO^T per block
   uint16_t* fqs = nullptr;    // [BH, Nb, D, 64] bf16 (phi(Q)/den)^T per block
-  float* stats = nullptr;     // [BH, Nb, 4, 64] per row: log2 max, 1/l, D, u (permuted)
+  float* stats = nullptr;     // [BH, Nb, kBwdStatFloats] per row: log2 max, 1/l, D (row
+                              // order), u (permuted order)
   uint32_t* maskT = nullptr;  // [BH, Nb, ceil(Nb/32)] query blocks keeping each key block
   int32_t* coff = nullptr;    // [BH, Nb + 1] column starts in cidx (per head)
   int32_t* cidx = nullptr;    // [BH, Nb * k] query blocks per key block (group order)
@@ -76,6 +76,7 @@ struct BwdWorkspace {
   float* gz = nullptr;        // [BH, D]    sum of (phi(Q)/den)^T u
 };
 constexpr int kGradChunks = 32;  // query-block chunks per head in the G reduction
+constexpr int kBwdStatFloats = 4 * kBlk;  // per query block: four rows of 64 statistics
 
 // Stage launchers (all enqueue on `s`, return the launch status).
 // Block means and K block sums; also Q's INT8 codes and scales when q8 is set.
@@ -121,10 +122,9 @@ hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape
                              void* out, int out_f32, float* out_linear, bool fp8,
                              const TrainResiduals* res, hipStream_t s);
 // Backward launchers.
-// Per block: K^T, Q^T, dO^T as bf16 [channel][permuted row] (any may be null).
-hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* q, const uint16_t* dout,
-                                   const Shape& sh, uint16_t* kt, uint16_t* qt, uint16_t* dot,
-                                   hipStream_t s);
+// Per block: K^T, dO^T as bf16 [channel][permuted row] (either may be null).
+hipError_t launch_transpose_blocks(const uint16_t* k, const uint16_t* dout, const Shape& sh,
+                                   uint16_t* kt, uint16_t* dot, hipStream_t s);
 // Column lists: for every key block, the query blocks whose kept list holds it.
 hipError_t launch_column_lists(const int32_t* idx, const Shape& sh, uint32_t* maskT,
                                int32_t* coff, int32_t* cidx, hipStream_t s);
@@ -135,7 +135,7 @@ hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* do
                         void* dq, int grad_f32, const TrainResiduals* res, hipStream_t s);
 // G = sum over all rows of (phi(Q)/den)^T dO and g_z (from bwd_q's outputs).
 hipError_t launch_grad_h(const BwdWorkspace& bw, const Shape& sh, hipStream_t s);
-hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                          const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
                          void* dk, void* dv, int grad_f32, hipStream_t s);
 // W8A8: per-row INT8 codes of a bf16 [rows, K] matrix, LayerNorm-ed first

@@ -1597,7 +1597,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
     }
   }
   if (lane < 16) {
-    float* st4 = b.stats + ((size_t)bh * a.Nb + i) * 256;
+    float* st4 = b.stats + ((size_t)bh * a.Nb + i) * kBwdStatFloats;
     st4[tl] = m_fin;
     st4[64 + tl] = inv_l;
     st4[128 + tl] = Dt;
@@ -1655,30 +1655,79 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
 
 // ---------------------------------------------------------------------------
 // Key side: one workgroup per key block j (four waves, 16 keys each), walking
-// the query blocks that keep j (shared with the group's other key blocks first).  Per query block i it stages the
-// INT8 Q codes, dO rows, dO^T, Q^T, (phi(Q)/den)^T and the row statistics:
+// the query blocks that keep j (shared with the group's other key blocks
+// first).  Per query block i it stages the INT8 Q codes, the dO and Q rows,
+// (phi(Q)/den)^T and the row statistics:
 //   S, P (the forward's weights), dP = dO V^T, dS
 //   dV += P^T dO,  dK += dS^T Q,  W += (phi(Q)/den)^T dO,  w += (phi(Q)/den)^T u
-// then the linear gradient through G - W and g_z - w.
+// then the linear gradient through G - W and g_z - w.  dV, W and dK contract
+// over the query rows and take dO and Q column-wise: those operands come from
+// the row-major tiles through transposing LDS reads.
 // ---------------------------------------------------------------------------
 constexpr int kKvDoOff = kK8Bytes;                        // dO rows [64][128] bf16
-constexpr int kKvDotOff = kK8Bytes + kF16TileBytes;       // dO^T [128][64 perm] bf16
-constexpr int kKvQtOff = kK8Bytes + 2 * kF16TileBytes;    // Q^T
-constexpr int kKvFqOff = kK8Bytes + 3 * kF16TileBytes;    // (phi(Q)/den)^T
-constexpr int kKvStOff = kK8Bytes + 4 * kF16TileBytes;    // 4 x 64 fp32 statistics
-constexpr int kKvStage = kKvStOff + 1024;                  // 73 KB
+constexpr int kKvQOff = kK8Bytes + kF16TileBytes;         // Q rows [64][128] bf16
+constexpr int kKvFqOff = kK8Bytes + 2 * kF16TileBytes;    // (phi(Q)/den)^T [128][64 perm] bf16
+constexpr int kKvStOff = kK8Bytes + 3 * kF16TileBytes;    // 4 x 64 fp32 statistics
+constexpr int kKvStatBytes = 4 * kBwdStatFloats;
+constexpr int kKvStage = kKvStOff + kKvStatBytes;         // 57 KB
+
+// 256-byte-row tiles of the key side keep 16-byte chunk ch of row r at
+// ch ^ kv_swz(r), so that neither of the two read shapes meets a bank
+// conflict: a transposing read (per half wave: 8 consecutive rows from a
+// multiple of 8, one 32-byte segment each) needs the segment index distinct
+// over each aligned 8 rows; a 16-byte row fragment read (per half wave: rows
+// 16tt..16tt+15, an aligned pair of chunks) spreads over 512 bytes of banks,
+// so it needs the segment index distinct over the even and over the odd
+// rows of 16.  (r & 7) ^ (r >> 3 & 1) is both.
+__device__ __forceinline__ int kv_swz(int r) { return ((r & 7) ^ ((r >> 3) & 1)) << 1; }
+
+// Byte offset a lane fetches when a wave moves a 1 KB round (4 rows) of such a
+// tile into LDS (round m of the workgroup: rows 16m..16m+15, + 4096m bytes).
+__device__ __forceinline__ int kv_row_ld(int wave, int lane) {
+  const int r = 4 * wave + (lane >> 4);
+  return r * 256 + (((lane & 15) ^ kv_swz(r)) << 4);
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Transposing read of 16-bit data: in each 16-lane group, lane i receives
+// element i % 4 of the 8-byte pieces addressed by lanes i/4, i/4 + 4, i/4 + 8,
+// i/4 + 12 (in that order).
+__device__ __forceinline__ v4s tr_read(const lds_byte* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+}
+
+// Matrix-core fragment of a row-major tile X [64 rows][128 channels] taken
+// column-wise: lane (l16, g) gets X[row][n0 + l16] for the eight rows
+// 32c + 4g + e and 32c + 16 + 4g + e (e = 0..3) -- the k slots a score tile's
+// rows occupy.  `off` is the lane's offset for channels n0.. (kv_tr_off).
+__device__ __forceinline__ bf16x8 tr_frag(const lds_byte* tile, int c, int off) {
+  const v4s lo = tr_read(tile + (32 * c) * 256 + off);
+  const v4s hi = tr_read(tile + (32 * c + 16) * 256 + off);
+  const v4s both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// The lane's byte offset for tr_frag over channels 16t..16t+15: it addresses
+// row 4g + l16/4 (+ 32c + 16h), channels 16t + 4 (l16 % 4)..
+__device__ __forceinline__ int kv_tr_off(int lane, int t) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int x = 4 * g + (l16 >> 2);
+  const int pos = (2 * t + ((l16 & 3) >> 1)) ^ kv_swz(x);
+  return x * 256 + (pos << 4) + 8 * (l16 & 1);
+}
 
 struct BwdKvArgs {
   const int8_t* q8;
   const int8_t* k8;
   const float* sq;
   const float* sk;
+  const uint16_t* q;      // Q bf16 [BH, N, D]
   const uint16_t* kin;    // K bf16 [BH, N, D]
   const uint16_t* v;      // V bf16 [BH, N, D]
   const uint16_t* dout;   // dO bf16 [BH, N, D]
-  const uint16_t* qt;     // Q^T bf16 per block
-  const uint16_t* dot;    // dO^T bf16 per block
-  const uint16_t* fqs;    // (phi(Q)/den)^T bf16 per block
+  const uint16_t* fqs;    // (phi(Q)/den)^T bf16 per block [BH, Nb, D, 64 permuted rows]
   const float* stats;     // [BH, Nb, 4, 64]
   const int32_t* coff;    // [BH, Nb + 1] column starts within the head's list
   const int32_t* cidx;    // [BH, Nb * k] query blocks keeping each key block
@@ -1690,31 +1739,97 @@ struct BwdKvArgs {
   int grad_f32;
 };
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over `bytes` bytes at `base` (the layout the buffer
+// resource builtin produces: raw, stride 0, 32-bit data format).
+__device__ __forceinline__ u32x4 kv_rsrc(const void* base, size_t bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xffffu, (unsigned)bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from rsrc[voff] into LDS at lds + 16 * lane.  Issued from
+// inline assembly because the compiler makes every transposing LDS read wait
+// for all outstanding global->LDS loads (it cannot tell that they fill the
+// other stage), which would serialise each tile's math behind the next
+// tile's loads.  The instruction has no register results; the loads are
+// awaited explicitly (wait_loads + lds_barrier) before their stage is read,
+// and M0 is restored, so the compiler's view of every register stays valid.
+__device__ __forceinline__ void kv_dma16(u32x4 rsrc, int voff, const lds_byte* lds) {
+  // the stage address is wave-uniform; say so, also inside lane-masked code
+  const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(size_t)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(la)
+      : "memory");
+}
+
 struct BwdKvSrc {
-  __amdgpu_buffer_rsrc_t q8, dout, dot, qt, fqs, stats;
+  u32x4 q8, dout, q, fqs, stats;
 };
+
+// The lane's LDS offsets of the key side, fixed for the kernel.
+struct KvLane {
+  int rd8;      // INT8 Q tile (128-byte rows), as LaneOffsets::rd8
+  int ld8;      // its global fetch offset
+  int rld;      // global fetch offset in the 256-byte-row tiles (kv_row_ld)
+  int rf[4];    // dO row fragment: row l16, chunk 4ks + g (+ 4096 tt for rows 16tt..)
+  int tr[8];    // tr_frag offsets for channels 16t..
+};
+
+__device__ __forceinline__ KvLane kv_lane(int wave, int lane) {
+  const LaneOffsets lo = lane_offsets(wave, lane);
+  const int l16 = lane & 15, g = lane >> 4;
+  KvLane o;
+  o.rd8 = lo.rd8;
+  o.ld8 = lo.ld8;
+  o.rld = kv_row_ld(wave, lane);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) o.rf[ks] = l16 * 256 + (((4 * ks + g) ^ kv_swz(l16)) << 4);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) o.tr[t] = kv_tr_off(lane, t);
+  return o;
+}
+
+// Issues this wave's share of query block i's staging into `st`.  The raw
+// dO and Q rows are addressed through the lane offset, so the buffer's range
+// check covers the rows past N (they read as zero).
+// global->LDS load instructions per wave per staged block
+template <bool kLin>
+constexpr int kv_loads() { return kLin ? 15 : 11; }
+constexpr int kKvStages = 2;   // staged query blocks: one in use, one in flight
+
+// Waits until at most n of this wave's global->LDS loads are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_loads_but() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
 
 template <bool kLin>
 __device__ __forceinline__ void issue_kv_tile(lds_byte* st, const BwdKvSrc& src, int i, int wave,
-                                              const LaneOffsets& lo, int vld, int lane) {
+                                              const KvLane& kl, int lane) {
+  const int rows = i * kF16TileBytes + kl.rld;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    lds_load16(src.dout, vld, i * kF16TileBytes + 4096 * m, st + kKvDoOff + 4096 * m + 1024 * wave);
+  for (int m = 0; m < 4; ++m) kv_dma16(src.dout, rows + 4096 * m, st + kKvDoOff + 4096 * m + 1024 * wave);
 #pragma unroll
   for (int m = 0; m < 2; ++m)
-    lds_load16(src.q8, lo.ld8, i * kK8Bytes + 4096 * m, st + 4096 * m + 1024 * wave);
+    kv_dma16(src.q8, i * kK8Bytes + 4096 * m + kl.ld8, st + 4096 * m + 1024 * wave);
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    lds_load16(src.dot, lo.ld8, i * kF16TileBytes + 4096 * m, st + kKvDotOff + 4096 * m + 1024 * wave);
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    lds_load16(src.qt, lo.ld8, i * kF16TileBytes + 4096 * m, st + kKvQtOff + 4096 * m + 1024 * wave);
+  for (int m = 0; m < 4; ++m) kv_dma16(src.q, rows + 4096 * m, st + kKvQOff + 4096 * m + 1024 * wave);
   if (kLin) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      lds_load16(src.fqs, lo.ld8, i * kF16TileBytes + 4096 * m, st + kKvFqOff + 4096 * m + 1024 * wave);
+      kv_dma16(src.fqs, i * kF16TileBytes + 4096 * m + kl.ld8, st + kKvFqOff + 4096 * m + 1024 * wave);
   }
-  if (wave == 0) lds_load16(src.stats, 16 * lane, i * 1024, st + kKvStOff);
+  // the statistics: 256 bytes per wave, so every wave issues kv_loads() loads
+  if (lane < 16) kv_dma16(src.stats, i * kKvStatBytes + 256 * wave + 16 * lane, st + kKvStOff + 256 * wave);
 }
 
 struct KvAcc {
@@ -1726,18 +1841,18 @@ struct KvAcc {
 
 template <bool kLin>
 __device__ __forceinline__ void kv_tile(const lds_byte* st, const v4i kf[2], const bf16x8 vf[4],
-                                        const LaneOffsets& lo, float cs, int wave, int g, int l16,
+                                        const KvLane& kl, float cs, int wave, int g, int l16,
                                         KvAcc& A) {
   v4i s[4];
-  qk_tile(st, kf, lo.rd8, s);  // s[tt][r] = S[row 16tt + 4g + r][key l16]
+  qk_tile(st, kf, kl.rd8, s);  // s[tt][r] = S[row 16tt + 4g + r][key l16]
   v4f dp[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     dp[tt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row_frag(st + kKvDoOff, 16 * tt + l16, 4 * ks + g),
-                                                       vf[ks], dp[tt], 0, 0, 0);
+      dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          *(lds_bf16x8*)(st + kKvDoOff + 4096 * tt + kl.rf[ks]), vf[ks], dp[tt], 0, 0, 0);
   }
   bf16x8 pa[2], dsa[2];
 #pragma unroll
@@ -1759,9 +1874,10 @@ __device__ __forceinline__ void kv_tile(const lds_byte* st, const v4i kf[2], con
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        af[mt][c] = *(lds_bf16x8*)(st + kKvFqOff + (2 * wave + mt) * 2048 + (lo.rd8 ^ (64 * c)));
+        af[mt][c] = *(lds_bf16x8*)(st + kKvFqOff + (2 * wave + mt) * 2048 + (kl.rd8 ^ (64 * c)));
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      // u per k slot 4h + e (row 32c + 16h + 4g + e)
       const v4f u0 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g));
       const v4f u1 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g + 4));
 #pragma unroll
@@ -1771,21 +1887,29 @@ __device__ __forceinline__ void kv_tile(const lds_byte* st, const v4i kf[2], con
       }
     }
   }
+  // per 32-row step c: the column-wise dO fragments (dV, W) and Q fragments
+  // (dK), read kAhead fragments ahead of the products that take them (the
+  // compiler interleaves the rest)
+  constexpr int kAhead = 6;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
+    bf16x8 F[16];
 #pragma unroll
-    for (int et = 0; et < 8; ++et) {
-      const bf16x8 bo = *(lds_bf16x8*)(st + kKvDotOff + et * 2048 + (lo.rd8 ^ (64 * c)));
-      A.dv[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[c], bo, A.dv[et], 0, 0, 0);
-      if (kLin) {
-        A.w[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], bo, A.w[0][et], 0, 0, 0);
-        A.w[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], bo, A.w[1][et], 0, 0, 0);
+    for (int f = 0; f < kAhead; ++f)
+      F[f] = tr_frag(st + (f < 8 ? kKvDoOff : kKvQOff), c, kl.tr[f & 7]);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      if (f + kAhead < 16)
+        F[f + kAhead] = tr_frag(st + (f + kAhead < 8 ? kKvDoOff : kKvQOff), c, kl.tr[(f + kAhead) & 7]);
+      if (f < 8) {
+        A.dv[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[c], F[f], A.dv[f], 0, 0, 0);
+        if (kLin) {
+          A.w[0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], F[f], A.w[0][f], 0, 0, 0);
+          A.w[1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], F[f], A.w[1][f], 0, 0, 0);
+        }
+      } else {
+        A.dk[f - 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], F[f], A.dk[f - 8], 0, 0, 0);
       }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const bf16x8 bq = *(lds_bf16x8*)(st + kKvQtOff + ct * 2048 + (lo.rd8 ^ (64 * c)));
-      A.dk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], bq, A.dk[ct], 0, 0, 0);
     }
     if (kLin) {
       A.wz[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], ub[c], A.wz[0], 0, 0, 0);
@@ -1800,7 +1924,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
   lds_byte* smem = (lds_byte*)smem_raw;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4;
   const int l16 = lane & 15;
   // workgroups x, x+8, x+16, x+24 (one XCD, dispatched together) take four
@@ -1811,7 +1935,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
   const int full = gridDim.x - gridDim.x % span;
   const int j = x < full ? x - x % span + kGroup * (x & 7) + (x % span) / 8 : x;
   const size_t bh = blockIdx.y;
-  const LaneOffsets lo = lane_offsets(wave, lane);
+  const KvLane kl = kv_lane(wave, lane);
   const int krow = j * kBlk + 16 * wave + l16;  // this lane's key as a B/A operand row
   const bool kvalid = krow < a.N;
   v4i kf[2];
@@ -1839,40 +1963,40 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
   if (n > 0) {
     const int32_t* list = a.cidx + bh * (size_t)a.Nb * a.k + c0;
     BwdKvSrc src;
-    const size_t f16_head = (size_t)a.Np * kD * 2;
-    src.q8 = head_rsrc(a.q8 + bh * (size_t)a.Np * kD, (size_t)a.Np * kD);
-    src.dout = head_rsrc(a.dout + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
-    src.dot = head_rsrc(a.dot + bh * (size_t)a.Np * kD, f16_head);
-    src.qt = head_rsrc(a.qt + bh * (size_t)a.Np * kD, f16_head);
-    src.fqs = head_rsrc(kLin ? a.fqs + bh * (size_t)a.Np * kD : a.qt, f16_head);
-    src.stats = head_rsrc(a.stats + bh * (size_t)a.Nb * 256, (size_t)a.Nb * 1024);
-    const int vld = row256_ld(wave, lane);
+    src.q8 = kv_rsrc(a.q8 + bh * (size_t)a.Np * kD, (size_t)a.Np * kD);
+    src.dout = kv_rsrc(a.dout + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
+    src.q = kv_rsrc(a.q + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
+    src.fqs = kv_rsrc(kLin ? a.fqs + bh * (size_t)a.Np * kD : a.q, (size_t)a.Np * kD * 2);
+    src.stats = kv_rsrc(a.stats + bh * (size_t)a.Nb * kBwdStatFloats, (size_t)a.Nb * kKvStatBytes);
     const float ks = a.sk[bh * a.Nb + j] * (kInvSqrtD * kLog2e);
     auto block_of = [&](int p) { return min(max(ld_uniform(list, (size_t)p), 0), a.Nb - 1); };
-    int i = block_of(0);
-    issue_kv_tile<kLin>(smem, src, i, wave, lo, vld, lane);
-    float si = ld_uniform(a.sq, bh * a.Nb + i);
-    for (int p = 0; p < n; p += 2) {
+    auto scale_of = [&](int p) { return ld_uniform(a.sq, bh * a.Nb + block_of(p)); };
+    // a ring of kKvStages stages: block p in stage p % kKvStages, the next
+    // kKvStages - 1 blocks in flight while p is computed
+    float sc[kKvStages];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int pp = p + half;
-        if (pp < n) {
-          lds_byte* cur = smem + half * kKvStage;
-          lds_byte* nxt = smem + (1 - half) * kKvStage;
-          wait_loads();
-          lds_barrier();  // block pp is in LDS; every wave is done with block pp-1
-          int in = i;
-          float sn = si;
-          if (pp + 1 < n) {
-            in = block_of(pp + 1);
-            issue_kv_tile<kLin>(nxt, src, in, wave, lo, vld, lane);
-            sn = ld_uniform(a.sq, bh * a.Nb + in);
-          }
-          kv_tile<kLin>(cur, kf, vf, lo, si * ks, wave, g, l16, A);
-          i = in;
-          si = sn;
-        }
+    for (int q = 0; q < kKvStages - 1; ++q) {
+      if (q < n) issue_kv_tile<kLin>(smem + q * kKvStage, src, block_of(q), wave, kl, lane);
+      sc[q] = q < n ? scale_of(q) : 0.0f;
+    }
+    int stage = 0;
+    for (int p = 0; p < n; ++p) {
+      if (kKvStages > 2 && p + kKvStages - 2 < n)
+        wait_loads_but<(kKvStages - 2) * kv_loads<kLin>()>();  // later blocks stay in flight
+      else
+        wait_loads();
+      lds_barrier();  // block p is in LDS; every wave is done with block p-1
+      const int pn = p + kKvStages - 1;
+      sc[kKvStages - 1] = 0.0f;
+      if (pn < n) {
+        const int sn = stage == 0 ? kKvStages - 1 : stage - 1;  // pn's stage: block p-1's
+        issue_kv_tile<kLin>(smem + sn * kKvStage, src, block_of(pn), wave, kl, lane);
+        sc[kKvStages - 1] = scale_of(pn);
       }
+      kv_tile<kLin>(smem + stage * kKvStage, kf, vf, kl, sc[0] * ks, wave, g, l16, A);
+#pragma unroll
+      for (int q = 0; q < kKvStages - 1; ++q) sc[q] = sc[q + 1];
+      stage = stage == kKvStages - 1 ? 0 : stage + 1;
     }
   }
 
@@ -2057,7 +2181,7 @@ hipError_t launch_bwd_q(const uint16_t* q, const uint16_t* v, const uint16_t* do
   return lin ? launch(bwd_q_kernel<true, false>) : launch(bwd_q_kernel<false, false>);
 }
 
-hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                          const Workspace& ws, const BwdWorkspace& bw, const Shape& sh, int phi,
                          void* dk, void* dv, int grad_f32, hipStream_t s) {
   BwdKvArgs a;
@@ -2065,11 +2189,10 @@ hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* d
   a.k8 = ws.k8;
   a.sq = ws.sq;
   a.sk = ws.sk;
+  a.q = q;
   a.kin = k;
   a.v = v;
   a.dout = dout;
-  a.qt = bw.qt;
-  a.dot = bw.dot;
   a.fqs = bw.fqs;
   a.stats = bw.stats;
   a.coff = sh.k > 0 ? bw.coff : nullptr;
@@ -2085,15 +2208,13 @@ hipError_t launch_bwd_kv(const uint16_t* k, const uint16_t* v, const uint16_t* d
   a.dv = dv;
   a.grad_f32 = grad_f32;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
-  const hipError_t e = allow_lds(lin ? reinterpret_cast<const void*>(bwd_kv_kernel<true>)
-                                     : reinterpret_cast<const void*>(bwd_kv_kernel<false>),
-                                 2 * kKvStage);
-  if (e != hipSuccess) return e;
-  if (lin)
-    bwd_kv_kernel<true><<<dim3(sh.Nb, sh.BH), 256, 2 * kKvStage, s>>>(a);
-  else
-    bwd_kv_kernel<false><<<dim3(sh.Nb, sh.BH), 256, 2 * kKvStage, s>>>(a);
-  return hipGetLastError();
+  auto launch = [&](auto kernel) {
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel), kKvStages * kKvStage);
+    if (e != hipSuccess) return e;
+    kernel<<<dim3(sh.Nb, sh.BH), 256, kKvStages * kKvStage, s>>>(a);
+    return hipGetLastError();
+  };
+  return lin ? launch(bwd_kv_kernel<true>) : launch(bwd_kv_kernel<false>);
 }
 
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
