@@ -1775,22 +1775,27 @@ struct BwdKvSrc {
   u32x4 q8, dout, q, fqs, stats;
 };
 
-// The lane's LDS offsets of the key side, fixed for the kernel.
+// The key side runs 4 score waves (softmax branch) and, with the linear
+// branch, 4 linear waves (W, w) per workgroup: two waves per SIMD, so the
+// vector work of one overlaps the matrix-core work of the other.
+template <bool kLin>
+constexpr int kv_waves() { return kLin ? 8 : 4; }
+// global->LDS load instructions per wave per staged block (every wave the same)
+template <bool kLin>
+constexpr int kv_loads() { return kLin ? 8 : 11; }
+constexpr int kKvStages = 2;   // staged query blocks: one in use, one in flight
+
+// The lane's LDS offsets of a score wave, fixed for the kernel.
 struct KvLane {
   int rd8;      // INT8 Q tile (128-byte rows), as LaneOffsets::rd8
-  int ld8;      // its global fetch offset
-  int rld;      // global fetch offset in the 256-byte-row tiles (kv_row_ld)
   int rf[4];    // dO row fragment: row l16, chunk 4ks + g (+ 4096 tt for rows 16tt..)
   int tr[8];    // tr_frag offsets for channels 16t..
 };
 
-__device__ __forceinline__ KvLane kv_lane(int wave, int lane) {
-  const LaneOffsets lo = lane_offsets(wave, lane);
+__device__ __forceinline__ KvLane kv_lane(int lane) {
   const int l16 = lane & 15, g = lane >> 4;
   KvLane o;
-  o.rd8 = lo.rd8;
-  o.ld8 = lo.ld8;
-  o.rld = kv_row_ld(wave, lane);
+  o.rd8 = l16 * 128 + ((g ^ ((l16 >> 1) & 7)) << 4);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) o.rf[ks] = l16 * 256 + (((4 * ks + g) ^ kv_swz(l16)) << 4);
 #pragma unroll
@@ -1798,13 +1803,48 @@ __device__ __forceinline__ KvLane kv_lane(int wave, int lane) {
   return o;
 }
 
+// Global fetch offsets of a wave's share of the staging (W waves; a round of
+// the workgroup moves W KB): in the 128-byte-row tiles (INT8 codes,
+// (phi(Q)/den)^T; row 8w + lane/8 of each round) and in the 256-byte-row tiles
+// (dO, Q; row 4w + lane/16 of each round).
+struct KvLoad {
+  int ld8, rld;
+};
+
+__device__ __forceinline__ KvLoad kv_load_offsets(int wave, int lane) {
+  const int row = 8 * wave + (lane >> 3);
+  return KvLoad{row * 128 + (((lane & 7) ^ ((row >> 1) & 7)) << 4), kv_row_ld(wave, lane)};
+}
+
 // Issues this wave's share of query block i's staging into `st`.  The raw
 // dO and Q rows are addressed through the lane offset, so the buffer's range
 // check covers the rows past N (they read as zero).
-// global->LDS load instructions per wave per staged block
 template <bool kLin>
-constexpr int kv_loads() { return kLin ? 15 : 11; }
-constexpr int kKvStages = 2;   // staged query blocks: one in use, one in flight
+__device__ __forceinline__ void issue_kv_tile(lds_byte* st, const BwdKvSrc& src, int i, int wave,
+                                              const KvLoad& ko, int lane) {
+  constexpr int kW = kv_waves<kLin>();
+  constexpr int kRound = 1024 * kW;
+  const int rows = i * kF16TileBytes + ko.rld;
+#pragma unroll
+  for (int m = 0; m < kF16TileBytes / kRound; ++m)
+    kv_dma16(src.dout, rows + kRound * m, st + kKvDoOff + kRound * m + 1024 * wave);
+#pragma unroll
+  for (int m = 0; m < kK8Bytes / kRound; ++m)
+    kv_dma16(src.q8, i * kK8Bytes + kRound * m + ko.ld8, st + kRound * m + 1024 * wave);
+#pragma unroll
+  for (int m = 0; m < kF16TileBytes / kRound; ++m)
+    kv_dma16(src.q, rows + kRound * m, st + kKvQOff + kRound * m + 1024 * wave);
+  if (kLin) {
+#pragma unroll
+    for (int m = 0; m < kF16TileBytes / kRound; ++m)
+      kv_dma16(src.fqs, i * kF16TileBytes + kRound * m + ko.ld8, st + kKvFqOff + kRound * m + 1024 * wave);
+  }
+  // the statistics, 1024 / kW bytes per wave
+  constexpr int kSt = kKvStatBytes / kW;
+  if (lane < kSt / 16) kv_dma16(src.stats, i * kKvStatBytes + kSt * wave + 16 * lane, st + kKvStOff + kSt * wave);
+}
+static_assert(kF16TileBytes / 8192 * 3 + kK8Bytes / 8192 + 1 == kv_loads<true>(), "load count (8 waves)");
+static_assert(kF16TileBytes / 4096 * 2 + kK8Bytes / 4096 + 1 == kv_loads<false>(), "load count (4 waves)");
 
 // Waits until at most n of this wave's global->LDS loads are outstanding.
 template <int n>
@@ -1812,37 +1852,52 @@ __device__ __forceinline__ void wait_loads_but() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
 
-template <bool kLin>
-__device__ __forceinline__ void issue_kv_tile(lds_byte* st, const BwdKvSrc& src, int i, int wave,
-                                              const KvLane& kl, int lane) {
-  const int rows = i * kF16TileBytes + kl.rld;
+// The walk over the key block's column (n query blocks from `list`), the same
+// loads, waits and barriers in every wave: a ring of kKvStages stages, block
+// p in stage p % kKvStages, the next kKvStages - 1 blocks in flight while p is
+// computed by tile(stage, scale of block p).
+template <bool kLin, typename Tile>
+__device__ __forceinline__ void kv_walk(lds_byte* smem, const BwdKvSrc& src, const int32_t* list,
+                                        int n, const float* sq_head, int Nb, int wave, int lane,
+                                        Tile&& tile) {
+  const KvLoad ko = kv_load_offsets(wave, lane);
+  auto block_of = [&](int p) { return min(max(ld_uniform(list, (size_t)p), 0), Nb - 1); };
+  auto scale_of = [&](int p) { return ld_uniform(sq_head, (size_t)block_of(p)); };
+  float sc[kKvStages];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) kv_dma16(src.dout, rows + 4096 * m, st + kKvDoOff + 4096 * m + 1024 * wave);
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    kv_dma16(src.q8, i * kK8Bytes + 4096 * m + kl.ld8, st + 4096 * m + 1024 * wave);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) kv_dma16(src.q, rows + 4096 * m, st + kKvQOff + 4096 * m + 1024 * wave);
-  if (kLin) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      kv_dma16(src.fqs, i * kF16TileBytes + 4096 * m + kl.ld8, st + kKvFqOff + 4096 * m + 1024 * wave);
+  for (int q = 0; q < kKvStages - 1; ++q) {
+    if (q < n) issue_kv_tile<kLin>(smem + q * kKvStage, src, block_of(q), wave, ko, lane);
+    sc[q] = q < n ? scale_of(q) : 0.0f;
   }
-  // the statistics: 256 bytes per wave, so every wave issues kv_loads() loads
-  if (lane < 16) kv_dma16(src.stats, i * kKvStatBytes + 256 * wave + 16 * lane, st + kKvStOff + 256 * wave);
+  int stage = 0;
+  for (int p = 0; p < n; ++p) {
+    if (kKvStages > 2 && p + kKvStages - 2 < n)
+      wait_loads_but<(kKvStages - 2) * kv_loads<kLin>()>();  // later blocks stay in flight
+    else
+      wait_loads();
+    lds_barrier();  // block p is in LDS; every wave is done with block p-1
+    const int pn = p + kKvStages - 1;
+    sc[kKvStages - 1] = 0.0f;
+    if (pn < n) {
+      const int sn = stage == 0 ? kKvStages - 1 : stage - 1;  // pn's stage: block p-1's
+      issue_kv_tile<kLin>(smem + sn * kKvStage, src, block_of(pn), wave, ko, lane);
+      sc[kKvStages - 1] = scale_of(pn);
+    }
+    tile(smem + stage * kKvStage, sc[0]);
+#pragma unroll
+    for (int q = 0; q < kKvStages - 1; ++q) sc[q] = sc[q + 1];
+    stage = stage == kKvStages - 1 ? 0 : stage + 1;
+  }
 }
 
-struct KvAcc {
-  v4f dv[8];     // dV[key 4g + r][e 16et + l16]
-  v4f dk[8];     // dK[key 4g + r][c 16ct + l16] (units of 1/sqrt(d))
-  v4f w[2][8];   // W[c = 32w + 16mt + 4g + r][e = 16et + l16]
-  v4f wz[2];     // w[c] in the lanes with l16 == 0
-};
-
-template <bool kLin>
-__device__ __forceinline__ void kv_tile(const lds_byte* st, const v4i kf[2], const bf16x8 vf[4],
-                                        const KvLane& kl, float cs, int wave, int g, int l16,
-                                        KvAcc& A) {
+// One staged query block for a score wave (16 keys): S, P, dP, dS, then
+// dV += P^T dO and, unless kSplit, dK += dS^T Q.  kSplit: dS goes to this
+// lane's slot of `ds` and, after a workgroup barrier, the linear wave on the
+// same SIMD takes dK.
+template <bool kSplit>
+__device__ __forceinline__ void kv_score_tile(const lds_byte* st, const v4i kf[2], const bf16x8 vf[4],
+                                              const KvLane& kl, float cs, int g, v4f dv[8],
+                                              v4f dk[8], lds_byte* ds) {
   v4i s[4];
   qk_tile(st, kf, kl.rd8, s);  // s[tt][r] = S[row 16tt + 4g + r][key l16]
   v4f dp[4];
@@ -1868,74 +1923,104 @@ __device__ __forceinline__ void kv_tile(const lds_byte* st, const v4i kf[2], con
       dsa[tt >> 1][4 * (tt & 1) + r] = (__bf16)(p * (dp[tt][r] - dd[r]));
     }
   }
-  bf16x8 af[2][2], ub[2];
-  if (kLin) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        af[mt][c] = *(lds_bf16x8*)(st + kKvFqOff + (2 * wave + mt) * 2048 + (kl.rd8 ^ (64 * c)));
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      // u per k slot 4h + e (row 32c + 16h + 4g + e)
-      const v4f u0 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g));
-      const v4f u1 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g + 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ub[c][e] = l16 == 0 ? (__bf16)u0[e] : (__bf16)0.0f;
-        ub[c][4 + e] = l16 == 0 ? (__bf16)u1[e] : (__bf16)0.0f;
-      }
-    }
+  if (kSplit) {
+    *(__attribute__((address_space(3))) bf16x8*)ds = dsa[0];
+    *(__attribute__((address_space(3))) bf16x8*)(ds + 16) = dsa[1];
+    lds_barrier();  // dS is in LDS for the linear waves
   }
-  // per 32-row step c: the column-wise dO fragments (dV, W) and Q fragments
-  // (dK), read kAhead fragments ahead of the products that take them (the
-  // compiler interleaves the rest)
+  // per 32-row step c: the column-wise dO fragments (dV) and Q fragments (dK),
+  // read kAhead fragments ahead of the products that take them
+  constexpr int kF = kSplit ? 8 : 16;
   constexpr int kAhead = 6;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    bf16x8 F[16];
+    bf16x8 F[kF];
 #pragma unroll
-    for (int f = 0; f < kAhead; ++f)
-      F[f] = tr_frag(st + (f < 8 ? kKvDoOff : kKvQOff), c, kl.tr[f & 7]);
+    for (int f = 0; f < kAhead; ++f) F[f] = tr_frag(st + (f < 8 ? kKvDoOff : kKvQOff), c, kl.tr[f & 7]);
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      if (f + kAhead < 16)
+    for (int f = 0; f < kF; ++f) {
+      if (f + kAhead < kF)
         F[f + kAhead] = tr_frag(st + (f + kAhead < 8 ? kKvDoOff : kKvQOff), c, kl.tr[(f + kAhead) & 7]);
-      if (f < 8) {
-        A.dv[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[c], F[f], A.dv[f], 0, 0, 0);
-        if (kLin) {
-          A.w[0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], F[f], A.w[0][f], 0, 0, 0);
-          A.w[1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], F[f], A.w[1][f], 0, 0, 0);
-        }
-      } else {
-        A.dk[f - 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], F[f], A.dk[f - 8], 0, 0, 0);
-      }
-    }
-    if (kLin) {
-      A.wz[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], ub[c], A.wz[0], 0, 0, 0);
-      A.wz[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], ub[c], A.wz[1], 0, 0, 0);
+      if (f < 8)
+        dv[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[c], F[f], dv[f], 0, 0, 0);
+      else
+        dk[f - 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], F[f], dk[f - 8], 0, 0, 0);
     }
   }
 }
 
+// One staged query block for a linear wave (phi channels 32 lw..32 lw + 31):
+// W += (phi(Q)/den)^T dO and w += (phi(Q)/den)^T u; then, once the score wave
+// on this SIMD has put dS in its slot of `ds`, dK += dS^T Q for its keys.
+__device__ __forceinline__ void kv_linear_tile(const lds_byte* st, const KvLane& kl, int lw, int g,
+                                               int l16, v4f w[2][8], v4f wz[2], v4f dk[8],
+                                               const lds_byte* ds) {
+  bf16x8 af[2][2], ub[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      af[mt][c] = *(lds_bf16x8*)(st + kKvFqOff + (2 * lw + mt) * 2048 + (kl.rd8 ^ (64 * c)));
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    // u per k slot 4h + e (row 32c + 16h + 4g + e)
+    const v4f u0 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g));
+    const v4f u1 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g + 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ub[c][e] = l16 == 0 ? (__bf16)u0[e] : (__bf16)0.0f;
+      ub[c][4 + e] = l16 == 0 ? (__bf16)u1[e] : (__bf16)0.0f;
+    }
+  }
+  constexpr int kAhead = 4;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    bf16x8 F[8];
+#pragma unroll
+    for (int f = 0; f < kAhead; ++f) F[f] = tr_frag(st + kKvDoOff, c, kl.tr[f]);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      if (f + kAhead < 8) F[f + kAhead] = tr_frag(st + kKvDoOff, c, kl.tr[f + kAhead]);
+      w[0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], F[f], w[0][f], 0, 0, 0);
+      w[1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], F[f], w[1][f], 0, 0, 0);
+    }
+    wz[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], ub[c], wz[0], 0, 0, 0);
+    wz[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], ub[c], wz[1], 0, 0, 0);
+  }
+  lds_barrier();  // the score waves' dS is in LDS
+  bf16x8 dsa[2];
+  dsa[0] = *(lds_bf16x8*)ds;
+  dsa[1] = *(lds_bf16x8*)(ds + 16);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    bf16x8 F[8];
+#pragma unroll
+    for (int f = 0; f < kAhead; ++f) F[f] = tr_frag(st + kKvQOff, c, kl.tr[f]);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      if (f + kAhead < 8) F[f + kAhead] = tr_frag(st + kKvQOff, c, kl.tr[f + kAhead]);
+      dk[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], F[f], dk[f], 0, 0, 0);
+    }
+  }
+}
+
+// LDS of the linear gradient (after the walk): G - W as bf16 both row-major
+// (rows = phi channel) and transposed, and g_z - w in fp32.
+constexpr int kGaOff = 0, kGbOff = 32 * 1024, kGzOff = 64 * 1024;
+static_assert(kGzOff + 4 * kD <= kKvStages * kKvStage, "the linear gradient's LDS fits the stages");
+// dS hand-over slots (with the linear branch): 32 bytes per lane of the 4 score waves
+constexpr int kKvDsOff = kKvStages * kKvStage;
 template <bool kLin>
-__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  lds_byte* smem = (lds_byte*)smem_raw;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int g = lane >> 4;
-  const int l16 = lane & 15;
-  // workgroups x, x+8, x+16, x+24 (one XCD, dispatched together) take four
-  // consecutive key blocks, whose columns overlap, so their staged query
-  // blocks meet in that XCD's L2
-  const int x = blockIdx.x;
-  const int span = 8 * kGroup;
-  const int full = gridDim.x - gridDim.x % span;
-  const int j = x < full ? x - x % span + kGroup * (x & 7) + (x % span) / 8 : x;
-  const size_t bh = blockIdx.y;
-  const KvLane kl = kv_lane(wave, lane);
+constexpr int kv_lds_bytes() { return kKvStages * kKvStage + (kLin ? 4 * 64 * 32 : 0); }
+
+// Score wave: the keys 16 wave.. of block j; dV (and, without the linear
+// branch, dK).
+template <bool kLin>
+__device__ __forceinline__ void kv_score_role(const BwdKvArgs& a, lds_byte* smem, const BwdKvSrc& src,
+                                              const int32_t* list, int n, int j, size_t bh, int wave,
+                                              int lane) {
+  const int g = lane >> 4, l16 = lane & 15;
+  const KvLane kl = kv_lane(lane);
   const int krow = j * kBlk + 16 * wave + l16;  // this lane's key as a B/A operand row
   const bool kvalid = krow < a.N;
   v4i kf[2];
@@ -1947,113 +2032,41 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
     const uint4 w = *reinterpret_cast<const uint4*>(vrow + 32 * ks + 8 * g);
     vf[ks] = kvalid ? __builtin_bit_cast(bf16x8, w) : bf16x8{};
   }
-  KvAcc A;
+  v4f dv[8], dk[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    A.dv[e] = v4f{0.f, 0.f, 0.f, 0.f};
-    A.dk[e] = v4f{0.f, 0.f, 0.f, 0.f};
-    A.w[0][e] = v4f{0.f, 0.f, 0.f, 0.f};
-    A.w[1][e] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  A.wz[0] = A.wz[1] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 8; ++e) dv[e] = dk[e] = v4f{0.f, 0.f, 0.f, 0.f};
+  const float ks = n > 0 ? a.sk[bh * a.Nb + j] * (kInvSqrtD * kLog2e) : 0.0f;
+  lds_byte* ds = smem + kKvDsOff + 32 * (64 * wave + lane);
+  kv_walk<kLin>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float si) {
+    kv_score_tile<kLin>(st, kf, vf, kl, si * ks, g, dv, dk, ds);
+  });
 
-  // this key block's column, clamped to the head's list
-  const int c0 = a.coff ? min(max(a.coff[bh * (a.Nb + 1) + j], 0), a.Nb * a.k) : 0;
-  const int n = a.coff ? min(a.coff[bh * (a.Nb + 1) + j + 1], a.Nb * a.k) - c0 : 0;
-  if (n > 0) {
-    const int32_t* list = a.cidx + bh * (size_t)a.Nb * a.k + c0;
-    BwdKvSrc src;
-    src.q8 = kv_rsrc(a.q8 + bh * (size_t)a.Np * kD, (size_t)a.Np * kD);
-    src.dout = kv_rsrc(a.dout + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
-    src.q = kv_rsrc(a.q + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
-    src.fqs = kv_rsrc(kLin ? a.fqs + bh * (size_t)a.Np * kD : a.q, (size_t)a.Np * kD * 2);
-    src.stats = kv_rsrc(a.stats + bh * (size_t)a.Nb * kBwdStatFloats, (size_t)a.Nb * kKvStatBytes);
-    const float ks = a.sk[bh * a.Nb + j] * (kInvSqrtD * kLog2e);
-    auto block_of = [&](int p) { return min(max(ld_uniform(list, (size_t)p), 0), a.Nb - 1); };
-    auto scale_of = [&](int p) { return ld_uniform(a.sq, bh * a.Nb + block_of(p)); };
-    // a ring of kKvStages stages: block p in stage p % kKvStages, the next
-    // kKvStages - 1 blocks in flight while p is computed
-    float sc[kKvStages];
-#pragma unroll
-    for (int q = 0; q < kKvStages - 1; ++q) {
-      if (q < n) issue_kv_tile<kLin>(smem + q * kKvStage, src, block_of(q), wave, kl, lane);
-      sc[q] = q < n ? scale_of(q) : 0.0f;
-    }
-    int stage = 0;
-    for (int p = 0; p < n; ++p) {
-      if (kKvStages > 2 && p + kKvStages - 2 < n)
-        wait_loads_but<(kKvStages - 2) * kv_loads<kLin>()>();  // later blocks stay in flight
-      else
-        wait_loads();
-      lds_barrier();  // block p is in LDS; every wave is done with block p-1
-      const int pn = p + kKvStages - 1;
-      sc[kKvStages - 1] = 0.0f;
-      if (pn < n) {
-        const int sn = stage == 0 ? kKvStages - 1 : stage - 1;  // pn's stage: block p-1's
-        issue_kv_tile<kLin>(smem + sn * kKvStage, src, block_of(pn), wave, kl, lane);
-        sc[kKvStages - 1] = scale_of(pn);
-      }
-      kv_tile<kLin>(smem + stage * kKvStage, kf, vf, kl, sc[0] * ks, wave, g, l16, A);
-#pragma unroll
-      for (int q = 0; q < kKvStages - 1; ++q) sc[q] = sc[q + 1];
-      stage = stage == kKvStages - 1 ? 0 : stage + 1;
-    }
-  }
-
-  // linear gradient through G - W and g_z - w
-  v4f dfk[8], dvl[8];
-  constexpr int kGaOff = 0, kGbOff = 32 * 1024, kGzOff = 64 * 1024;
+  // the linear branch's share of dV: phi(K) (G - W), G - W written by the
+  // linear waves
+  v4f dvl[8];
   if (kLin) {
     lds_barrier();  // every wave is done with the stages
-    const float* Gh = a.G + bh * kD * kD;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int et = 0; et < 8; ++et)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = 32 * wave + 16 * mt + 4 * g + r;
-          const int e = 16 * et + l16;
-          const __bf16 gv = (__bf16)(Gh[c * kD + e] - A.w[mt][et][r]);
-          *(__attribute__((address_space(3))) __bf16*)(smem + kGaOff + c * 256 +
-                                                      ((((e >> 3) ^ (c & 15)) & 15) << 4) + 2 * (e & 7)) = gv;
-          *(__attribute__((address_space(3))) __bf16*)(smem + kGbOff + e * 256 +
-                                                      ((((c >> 3) ^ (e & 15)) & 15) << 4) + 2 * (c & 7)) = gv;
-        }
-    if (l16 == 0) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = 32 * wave + 16 * mt + 4 * g + r;
-          *(__attribute__((address_space(3))) float*)(smem + kGzOff + 4 * c) = a.gz[bh * kD + c] - A.wz[mt][r];
-        }
-    }
-    lds_barrier();
-    // phi(K) of this lane's key as A operands (channels 32ks + 8g + e)
+    lds_barrier();  // the linear waves have written G - W and g_z - w
+    // phi(K) of this lane's key as A operands (channels 32q + 8g + e)
     const uint16_t* krp = a.kin + ((size_t)bh * a.N + (kvalid ? krow : 0)) * kD;
     bf16x8 fk[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 w = *reinterpret_cast<const uint4*>(krp + 32 * ks + 8 * g);
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = *reinterpret_cast<const uint4*>(krp + 32 * q + 8 * g);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float xv = (e & 1) ? bf16_hi(ww[e >> 1]) : bf16_lo(ww[e >> 1]);
-        fk[ks][e] = kvalid ? (__bf16)phi_apply(xv, a.phi) : (__bf16)0.0f;
+        fk[q][e] = kvalid ? (__bf16)phi_apply(xv, a.phi) : (__bf16)0.0f;
       }
     }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      dfk[ct] = v4f{0.f, 0.f, 0.f, 0.f};
       dvl[ct] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        dfk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ks], lds_row_frag(smem + kGaOff, 16 * ct + l16, 4 * ks + g),
-                                                          dfk[ct], 0, 0, 0);
-        dvl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[ks], lds_row_frag(smem + kGbOff, 16 * ct + l16, 4 * ks + g),
+      for (int q = 0; q < 4; ++q)
+        dvl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[q], lds_row_frag(smem + kGbOff, 16 * ct + l16, 4 * q + g),
                                                           dvl[ct], 0, 0, 0);
-      }
     }
   }
   // outputs: lane holds keys 16w + 4g + r, channel 16ct + l16
@@ -2065,18 +2078,124 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdKvArgs a) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const int c = 16 * ct + l16;
-      float dkv = A.dk[ct][r] * kInvSqrtD;
-      float dvv = A.dv[ct][r];
-      if (kLin) {
-        const uint16_t kb = a.kin[orow + c];
-        const float gzh = *(__attribute__((address_space(3))) const float*)(smem + kGzOff + 4 * c);
-        dkv += (dfk[ct][r] + gzh) * phi_slope(bf16_lo(kb), a.phi);
-        dvv += dvl[ct][r];
-      }
-      store_one(a.dk, orow + c, dkv, a.grad_f32);
-      store_one(a.dv, orow + c, dvv, a.grad_f32);
+      store_one(a.dv, orow + c, kLin ? dv[ct][r] + dvl[ct][r] : dv[ct][r], a.grad_f32);
+      if (!kLin) store_one(a.dk, orow + c, dk[ct][r] * kInvSqrtD, a.grad_f32);
     }
   }
+}
+
+// Linear wave lw = wave - 4: W and w over phi channels 32 lw.., the softmax
+// branch's dK of score wave lw's keys, then G - W and g_z - w into LDS and
+// the keys' whole dK.
+__device__ __forceinline__ void kv_linear_role(const BwdKvArgs& a, lds_byte* smem, const BwdKvSrc& src,
+                                               const int32_t* list, int n, int j, size_t bh, int wave,
+                                               int lane) {
+  const int g = lane >> 4, l16 = lane & 15;
+  const int lw = wave - 4;
+  const KvLane kl = kv_lane(lane);
+  v4f w[2][8], wz[2], dk[8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    wz[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int et = 0; et < 8; ++et) w[mt][et] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) dk[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  const lds_byte* ds = smem + kKvDsOff + 32 * (64 * lw + lane);
+  kv_walk<true>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float) {
+    kv_linear_tile(st, kl, lw, g, l16, w, wz, dk, ds);
+  });
+  lds_barrier();  // every wave is done with the stages
+  const float* Gh = a.G + bh * kD * kD;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int et = 0; et < 8; ++et)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 32 * lw + 16 * mt + 4 * g + r;
+        const int e = 16 * et + l16;
+        const __bf16 gv = (__bf16)(Gh[c * kD + e] - w[mt][et][r]);
+        *(__attribute__((address_space(3))) __bf16*)(smem + kGaOff + c * 256 +
+                                                    ((((e >> 3) ^ (c & 15)) & 15) << 4) + 2 * (e & 7)) = gv;
+        *(__attribute__((address_space(3))) __bf16*)(smem + kGbOff + e * 256 +
+                                                    ((((c >> 3) ^ (e & 15)) & 15) << 4) + 2 * (c & 7)) = gv;
+      }
+  if (l16 == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 32 * lw + 16 * mt + 4 * g + r;
+        *(__attribute__((address_space(3))) float*)(smem + kGzOff + 4 * c) = a.gz[bh * kD + c] - wz[mt][r];
+      }
+  }
+  lds_barrier();  // G - W and g_z - w are in LDS
+  // the linear branch's share of dK: (V (G - W)^T + g_z - w) phi'(K) for the
+  // keys 16 lw..
+  const int krow = j * kBlk + 16 * lw + l16;
+  const bool kvalid = krow < a.N;
+  const uint16_t* vrow = a.v + ((size_t)bh * a.N + (kvalid ? krow : 0)) * kD;
+  bf16x8 vf[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 u = *reinterpret_cast<const uint4*>(vrow + 32 * q + 8 * g);
+    vf[q] = kvalid ? __builtin_bit_cast(bf16x8, u) : bf16x8{};
+  }
+  v4f dfk[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    dfk[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dfk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[q], lds_row_frag(smem + kGaOff, 16 * ct + l16, 4 * q + g),
+                                                        dfk[ct], 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int kr = j * kBlk + 16 * lw + 4 * g + r;
+    if (kr >= a.N) continue;
+    const size_t orow = (bh * a.N + kr) * kD;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const int c = 16 * ct + l16;
+      const uint16_t kb = a.kin[orow + c];
+      const float gzh = *(__attribute__((address_space(3))) const float*)(smem + kGzOff + 4 * c);
+      store_one(a.dk, orow + c, dk[ct][r] * kInvSqrtD + (dfk[ct][r] + gzh) * phi_slope(bf16_lo(kb), a.phi),
+                a.grad_f32);
+    }
+  }
+}
+
+template <bool kLin>
+__global__ __launch_bounds__(kv_waves<kLin>() * 64, 1) void bwd_kv_kernel(BwdKvArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_byte* smem = (lds_byte*)smem_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // workgroups x, x+8, x+16, x+24 (one XCD, dispatched together) take four
+  // consecutive key blocks, whose columns overlap, so their staged query
+  // blocks meet in that XCD's L2
+  const int x = blockIdx.x;
+  const int span = 8 * kGroup;
+  const int full = gridDim.x - gridDim.x % span;
+  const int j = x < full ? x - x % span + kGroup * (x & 7) + (x % span) / 8 : x;
+  const size_t bh = blockIdx.y;
+  // this key block's column, clamped to the head's list
+  const int c0 = a.coff ? min(max(a.coff[bh * (a.Nb + 1) + j], 0), a.Nb * a.k) : 0;
+  const int n = a.coff ? min(a.coff[bh * (a.Nb + 1) + j + 1], a.Nb * a.k) - c0 : 0;
+  const int32_t* list = a.cidx ? a.cidx + bh * (size_t)a.Nb * a.k + c0 : nullptr;
+  BwdKvSrc src;
+  src.q8 = kv_rsrc(a.q8 + bh * (size_t)a.Np * kD, (size_t)a.Np * kD);
+  src.dout = kv_rsrc(a.dout + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
+  src.q = kv_rsrc(a.q + bh * (size_t)a.N * kD, (size_t)a.N * kD * 2);
+  src.fqs = kv_rsrc(kLin ? a.fqs + bh * (size_t)a.Np * kD : a.q, (size_t)a.Np * kD * 2);
+  src.stats = kv_rsrc(a.stats + bh * (size_t)a.Nb * kBwdStatFloats, (size_t)a.Nb * kKvStatBytes);
+  if (!kLin || wave < 4)
+    kv_score_role<kLin>(a, smem, src, list, max(n, 0), j, bh, wave, lane);
+  else
+    kv_linear_role(a, smem, src, list, max(n, 0), j, bh, wave, lane);
 }
 
 template <int kMode, bool kF8 = false>
@@ -2208,13 +2327,14 @@ hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v
   a.dv = dv;
   a.grad_f32 = grad_f32;
   const bool lin = phi != kPhiNone && sh.k < sh.Nb;
-  auto launch = [&](auto kernel) {
-    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel), kKvStages * kKvStage);
+  auto launch = [&](auto kernel, int threads, int lds) {
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel), lds);
     if (e != hipSuccess) return e;
-    kernel<<<dim3(sh.Nb, sh.BH), 256, kKvStages * kKvStage, s>>>(a);
+    kernel<<<dim3(sh.Nb, sh.BH), threads, lds, s>>>(a);
     return hipGetLastError();
   };
-  return lin ? launch(bwd_kv_kernel<true>) : launch(bwd_kv_kernel<false>);
+  return lin ? launch(bwd_kv_kernel<true>, 64 * kv_waves<true>(), kv_lds_bytes<true>())
+             : launch(bwd_kv_kernel<false>, 64 * kv_waves<false>(), kv_lds_bytes<false>());
 }
 
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
