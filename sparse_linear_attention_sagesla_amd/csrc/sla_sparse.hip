@@ -1784,6 +1784,11 @@ constexpr int kv_waves() { return kLin ? 8 : 4; }
 template <bool kLin>
 constexpr int kv_loads() { return kLin ? 8 : 11; }
 constexpr int kKvStages = 2;   // staged query blocks: one in use, one in flight
+// dS hand-over slots (with the linear branch): for each of the two 16-byte
+// halves, 16 bytes per lane of the 4 score waves (lane-contiguous, so each
+// access is free of bank conflicts)
+constexpr int kKvDsOff = kKvStages * kKvStage;
+constexpr int kKvDsHalf = 4 * 64 * 16;
 
 // The lane's LDS offsets of a score wave, fixed for the kernel.
 struct KvLane {
@@ -1925,7 +1930,7 @@ __device__ __forceinline__ void kv_score_tile(const lds_byte* st, const v4i kf[2
   }
   if (kSplit) {
     *(__attribute__((address_space(3))) bf16x8*)ds = dsa[0];
-    *(__attribute__((address_space(3))) bf16x8*)(ds + 16) = dsa[1];
+    *(__attribute__((address_space(3))) bf16x8*)(ds + kKvDsHalf) = dsa[1];
     lds_barrier();  // dS is in LDS for the linear waves
   }
   // per 32-row step c: the column-wise dO fragments (dV) and Q fragments (dK),
@@ -1990,7 +1995,7 @@ __device__ __forceinline__ void kv_linear_tile(const lds_byte* st, const KvLane&
   lds_barrier();  // the score waves' dS is in LDS
   bf16x8 dsa[2];
   dsa[0] = *(lds_bf16x8*)ds;
-  dsa[1] = *(lds_bf16x8*)(ds + 16);
+  dsa[1] = *(lds_bf16x8*)(ds + kKvDsHalf);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     bf16x8 F[8];
@@ -2008,10 +2013,8 @@ __device__ __forceinline__ void kv_linear_tile(const lds_byte* st, const KvLane&
 // (rows = phi channel) and transposed, and g_z - w in fp32.
 constexpr int kGaOff = 0, kGbOff = 32 * 1024, kGzOff = 64 * 1024;
 static_assert(kGzOff + 4 * kD <= kKvStages * kKvStage, "the linear gradient's LDS fits the stages");
-// dS hand-over slots (with the linear branch): 32 bytes per lane of the 4 score waves
-constexpr int kKvDsOff = kKvStages * kKvStage;
 template <bool kLin>
-constexpr int kv_lds_bytes() { return kKvStages * kKvStage + (kLin ? 4 * 64 * 32 : 0); }
+constexpr int kv_lds_bytes() { return kKvStages * kKvStage + (kLin ? 2 * kKvDsHalf : 0); }
 
 // Score wave: the keys 16 wave.. of block j; dV (and, without the linear
 // branch, dK).
@@ -2036,7 +2039,7 @@ __device__ __forceinline__ void kv_score_role(const BwdKvArgs& a, lds_byte* smem
 #pragma unroll
   for (int e = 0; e < 8; ++e) dv[e] = dk[e] = v4f{0.f, 0.f, 0.f, 0.f};
   const float ks = n > 0 ? a.sk[bh * a.Nb + j] * (kInvSqrtD * kLog2e) : 0.0f;
-  lds_byte* ds = smem + kKvDsOff + 32 * (64 * wave + lane);
+  lds_byte* ds = smem + kKvDsOff + 16 * (64 * wave + lane);
   kv_walk<kLin>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float si) {
     kv_score_tile<kLin>(st, kf, vf, kl, si * ks, g, dv, dk, ds);
   });
@@ -2102,7 +2105,7 @@ __device__ __forceinline__ void kv_linear_role(const BwdKvArgs& a, lds_byte* sme
   }
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) dk[ct] = v4f{0.f, 0.f, 0.f, 0.f};
-  const lds_byte* ds = smem + kKvDsOff + 32 * (64 * lw + lane);
+  const lds_byte* ds = smem + kKvDsOff + 16 * (64 * lw + lane);
   kv_walk<true>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float) {
     kv_linear_tile(st, kl, lw, g, l16, w, wz, dk, ds);
   });
