@@ -303,7 +303,8 @@ sla_status sla_attention_bwd_timed(const void *q, const void *k, const void *v,
  * "方法论"), so a training step runs the forward and then the backward on the
  * same q, k, v.  sla_attention_fwd_train is sla_attention_fwd that also
  * writes, into a caller-owned residual buffer, what the backward's query side
- * would otherwise recompute with a second pass over the kept tiles:
+ * would otherwise recompute with a second pass over the kept tiles, and the
+ * forward's staging that the backward would otherwise rebuild:
  *   stats  fp32 [B,H,N,2]   per row: log2-domain maximum of the logits (+inf
  *                           for a row without kept keys) and 1/l
  *   os     fp32 [B,H,N,128] the softmax branch's normalised output
@@ -312,8 +313,18 @@ sla_status sla_attention_bwd_timed(const void *q, const void *k, const void *v,
  *                           M = sum phi(K_j)^T V_j (phi(K)/16 scale, row =
  *                           phi channel)            (subtraction form only)
  *   zm     fp32 [B,H,Nb,128] the kept share of sum phi(K)/16 (same)
+ *   then, except in the direct form, when k > 0:
+ *   codes  q8 int8 [B,H,Nb*64,128], sq fp32 [B,H,Nb],
+ *                           k8 int8 [B,H,Nb*64,128], sk fp32 [B,H,Nb] (as
+ *                           sla_quantize_qk), idx int32 [B,H,Nb,k] (as
+ *                           sla_block_select), and the query-block groups'
+ *                           aligned walks int32 [B,H,ceil(Nb/4),k,4]
+ *   and, with the linear branch: hb bf16 [B,H,128,128] H = sum phi(K)^T V
+ *                           (phi(K)/16 scale, row = phi channel), z fp32
+ *                           [B,H,128] sum phi(K)/16
  * each piece 256-byte aligned, in this order; the subtraction form is taken
- * when the unselected key blocks outnumber the kept ones (Nb - k > k).
+ * when the unselected key blocks outnumber the kept ones (Nb - k > k), the
+ * direct form otherwise (with the linear branch on).
  * sla_train_residual_bytes gives the size (0 for invalid arguments). */
 size_t sla_train_residual_bytes(int B, int H, int N, int d, int block,
                                 double keep, int phi);
@@ -333,7 +344,8 @@ sla_status sla_attention_fwd_train(const void *q, const void *k,
 /* sla_attention_bwd for the residuals of a sla_attention_fwd_train call on the
  * same q, k, v, keep and phi (resid, resid_bytes as given to it): the query
  * side takes the forward's row statistics, outputs and kept share from them
- * instead of walking the kept tiles a second time.  Gradients equal
+ * instead of walking the kept tiles a second time, and the forward's codes,
+ * selection, walks and linear state replace the backward's own staging.  Gradients equal
  * sla_attention_bwd's to rounding (the linear output comes from the forward's
  * fp32 H - M instead of a bf16-staged recomputation).  In the direct form
  * (Nb - k <= k) the residuals hold no kept share and the call computes as

@@ -180,8 +180,10 @@ sla_status check_fwd_args(const void* q, const void* k, const void* v, int B, in
 
 // A training forward's residuals in the caller's buffer (256-byte aligned
 // pieces): per-row statistics and softmax output, the linear output, and in
-// the subtraction form the kept share M and z_M per query block.  Returns the
-// bytes needed; fills *r when base is set.
+// the subtraction form the kept share M and z_M per query block, then the
+// forward's staging that the backward takes over (INT8 codes and scales,
+// kept lists and walks when k > 0; H in bf16 and z with the linear branch).
+// Returns the bytes needed; fills *r when base is set.
 size_t carve_residuals(const Shape& s, int phi_eff, bool direct, unsigned char* base,
                        sla::TrainResiduals* r) {
   size_t off = 0;
@@ -199,6 +201,22 @@ size_t carve_residuals(const Shape& s, int phi_eff, bool direct, unsigned char* 
     if (!direct) {
       t.m = reinterpret_cast<uint16_t*>(take(BH * Nb * D * D * sizeof(uint16_t)));
       t.zm = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+    }
+  }
+  if (!direct) {
+    const size_t Np = s.Np, K = s.k > 0 ? s.k : 0;
+    if (K > 0) {
+      t.q8 = reinterpret_cast<int8_t*>(take(BH * Np * D));
+      t.sq = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
+      t.k8 = reinterpret_cast<int8_t*>(take(BH * Np * D));
+      t.sk = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
+      t.idx = reinterpret_cast<int32_t*>(take(BH * Nb * K * sizeof(int32_t)));
+      t.sched = reinterpret_cast<int32_t*>(
+          take(BH * (size_t)((s.Nb + sla::kGroup - 1) / sla::kGroup) * K * sla::kGroup * sizeof(int32_t)));
+    }
+    if (phi_eff != SLA_PHI_NONE) {
+      t.hb = reinterpret_cast<uint16_t*>(take(BH * D * D * sizeof(uint16_t)));
+      t.z = reinterpret_cast<float*>(take(BH * D * sizeof(float)));
     }
   }
   if (r) *r = t;
@@ -320,6 +338,16 @@ sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, i
   // the linear branch exists only when some key block is left out
   const int phi_eff = (kk < Nb) ? phi : SLA_PHI_NONE;
   const bool direct = phi_eff != SLA_PHI_NONE && sla::linear_direct(s);
+  // a training forward writes the codes, kept lists and walks into the
+  // residuals, where the backward takes them over
+  if (res && res->q8) {
+    w.q8 = res->q8;
+    w.sq = res->sq;
+    w.k8 = res->k8;
+    w.sk = res->sk;
+    w.idx = res->idx;
+    w.sched = res->sched;
+  }
   hipError_t e = hipSuccess;
   // runs one stage on the caller's stream between its two optional events
   auto stage = [&](int id, auto&& launch) {
@@ -350,8 +378,8 @@ sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, i
   });
   if (phi_eff != SLA_PHI_NONE && !direct)
     stage(SLA_STAGE_LINEAR_FINAL, [&] {
-      return sla::launch_linear_final(w.hpart, w.zpart, s, w.hf, w.z64, nullptr, nullptr, nullptr,
-                                      nullptr, hs);
+      return sla::launch_linear_final(w.hpart, w.zpart, s, w.hf, w.z64, res ? res->z : nullptr,
+                                      nullptr, nullptr, res ? res->hb : nullptr, hs);
     });
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
@@ -485,19 +513,34 @@ sla_status bwd_impl(const void* q, const void* k, const void* v, const void* dou
     if (e == hipSuccess && stage_events && stage_events[2 * id + end])
       e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + end]), hs);
   };
-  // the forward's staging: codes, selection, walk schedule, linear state
+  // the forward's staging: codes, selection, walk schedule, linear state (a
+  // training forward's residuals hold them)
   mark(SLA_BWD_STAGE_FWD_STAGING, 0);
-  if (kk > 0) {
+  if (res) {
+    if (kk > 0) {
+      w.q8 = r.q8;
+      w.sq = r.sq;
+      w.k8 = r.k8;
+      w.sk = r.sk;
+      w.idx = r.idx;
+      w.sched = r.sched;
+    }
+    if (phi_eff != SLA_PHI_NONE) {
+      w.z = r.z;
+      bw.hb = r.hb;
+    }
+  } else if (kk > 0) {
     run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs); });
     run([&] { return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, hs); });
     run([&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
     run([&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
-  run([&] {
-    return sla::launch_linear_prep(kb, vb, s, phi_eff, true, w.fk16, w.v16, w.zb, w.hpart, w.zpart,
-                                   w.mu, kk > 0 ? w.k8 : nullptr, w.sk, false, nullptr, hs);
-  });
-  if (phi_eff != SLA_PHI_NONE)
+  if (!res)
+    run([&] {
+      return sla::launch_linear_prep(kb, vb, s, phi_eff, true, w.fk16, w.v16, w.zb, w.hpart, w.zpart,
+                                     w.mu, kk > 0 ? w.k8 : nullptr, w.sk, false, nullptr, hs);
+    });
+  if (!res && phi_eff != SLA_PHI_NONE)
     run([&] {
       return sla::launch_linear_final(w.hpart, w.zpart, s, nullptr, nullptr, w.z, w.h16t, w.hscale,
                                       bw.hb, hs);

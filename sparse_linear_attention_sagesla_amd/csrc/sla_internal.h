@@ -117,6 +117,15 @@ struct TrainResiduals {
   float* ol = nullptr;      // [BH, N, 128] linear-branch output
   uint16_t* m = nullptr;    // [BH, Nb, 128, 128] bf16 kept share M, staged scale (phi/16)
   float* zm = nullptr;      // [BH, Nb, 128] kept share of z, staged scale
+  // the forward's staging, taken over by the backward (null in the direct form)
+  int8_t* q8 = nullptr;     // [BH, Np, 128] INT8 codes of Q and K, scales per block
+  float* sq = nullptr;      // [BH, Nb]
+  int8_t* k8 = nullptr;     // [BH, Np, 128]
+  float* sk = nullptr;      // [BH, Nb]
+  int32_t* idx = nullptr;   // [BH, Nb, k] kept key blocks
+  int32_t* sched = nullptr; // [BH, ceil(Nb/kGroup), k, kGroup] aligned walks
+  uint16_t* hb = nullptr;   // [BH, 128, 128] bf16 H row-major, staged scale  (linear only)
+  float* z = nullptr;       // [BH, 128] fp32 sum of phi(K)/16              (linear only)
 };
 hipError_t launch_sparse_fwd(const uint16_t* q, const Workspace& ws, const Shape& sh, int phi,
                              void* out, int out_f32, float* out_linear, bool fp8,

@@ -274,10 +274,18 @@ def _train_res_bytes(B, H, N, keep, phi):
     k = O.topk_count(nb, keep)
     lin = phi != 0 and k < nb
     n = up(B * H * N * 2 * 4) + up(B * H * N * 128 * 4)
+    direct = lin and nb - k <= k
     if lin:
         n += up(B * H * N * 128 * 4)
-        if nb - k > k:
+        if not direct:
             n += up(B * H * nb * 128 * 128 * 2) + up(B * H * nb * 128 * 4)
+    if not direct:
+        if k > 0:
+            codes = B * H * nb * 64 * 128
+            n += up(codes) + up(B * H * nb * 4) + up(codes) + up(B * H * nb * 4)
+            n += up(B * H * nb * k * 4) + up(B * H * ((nb + 3) // 4) * k * 4 * 4)
+        if lin:
+            n += up(B * H * 128 * 128 * 2) + up(B * H * 128 * 4)
     return n
 
 

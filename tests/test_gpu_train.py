@@ -43,6 +43,43 @@ def _views(res, B, H, N, keep, phi):
     return stats, os_, ol
 
 
+def test_train_residuals_hold_the_forwards_codes_and_selection():
+    """The staging a training forward leaves for the backward (INT8 codes and
+    scales, kept lists), at the documented offsets, equals what the stand-alone
+    entry points sla_quantize_qk and sla_block_select return, bit for bit."""
+    B, H, N, keep = 1, 2, 64 * 9 - 23, 0.3   # 9 blocks, 3 kept: subtraction form
+    Q, K, V = (random_bf16((B, H, N, 128), s) for s in (221, 222, 223))
+    q, k, v = (to_dev(x) for x in (Q, K, V))
+    print(f"[case] train residual staging N={N} keep={keep}", flush=True)
+    _, res = sla.attention_train(q, k, v, keep, "elu1", torch.float32)
+    q8, k8, sq, sk, _ = sla.quantize_qk(q, k)
+    idx = sla.block_select(q, k, keep)
+    torch.cuda.synchronize()
+    up = lambda n: (n + 255) // 256 * 256
+    nb = O.n_blocks(N, 64)
+    kk = O.topk_count(nb, keep)
+    assert nb - kk > kk
+    off = (up(B * H * N * 8) + 2 * up(B * H * N * 512) + up(B * H * nb * 128 * 128 * 2)
+           + up(B * H * nb * 128 * 4))
+    f = res.view(torch.uint8)
+
+    def take(nbytes, dtype, shape):
+        nonlocal off
+        t = f[off:off + nbytes].view(dtype).view(*shape)
+        off += up(nbytes)
+        return t
+
+    codes = B * H * nb * 64 * 128
+    r_q8 = take(codes, torch.int8, (B, H, nb * 64, 128))
+    r_sq = take(B * H * nb * 4, torch.float32, (B, H, nb))
+    r_k8 = take(codes, torch.int8, (B, H, nb * 64, 128))
+    r_sk = take(B * H * nb * 4, torch.float32, (B, H, nb))
+    r_idx = take(B * H * nb * kk * 4, torch.int32, (B, H, nb, kk))
+    assert torch.equal(r_q8, q8) and torch.equal(r_k8, k8)
+    assert torch.equal(r_sq, sq) and torch.equal(r_sk, sk)
+    assert torch.equal(r_idx, idx)
+
+
 @pytest.mark.parametrize("keep,phi", CASES)
 def test_train_forward_output_and_residuals(keep, phi):
     N = 64 * 9 - 23
