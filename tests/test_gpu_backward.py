@@ -56,11 +56,12 @@ def _run(Q, K, V, G, keep, phi, grad_dtype=torch.float32):
 
 def _compare(Q, K, V, G, keep, phi, tag):
     got = _run(Q, K, V, G, keep, phi)
-    for h in range(Q.shape[1]):
-        r = O.sla_backward_head(Q[0, h], K[0, h], V[0, h], G[0, h], block=64, keep=keep,
-                                phi_kind=phi)
-        for i, name in enumerate(("dq", "dk", "dv")):
-            _check(f"{tag} h{h} {name}", got[i][0, h], r[name])
+    for b in range(Q.shape[0]):
+        for h in range(Q.shape[1]):
+            r = O.sla_backward_head(Q[b, h], K[b, h], V[b, h], G[b, h], block=64, keep=keep,
+                                    phi_kind=phi)
+            for i, name in enumerate(("dq", "dk", "dv")):
+                _check(f"{tag} b{b} h{h} {name}", got[i][b, h], r[name])
 
 
 @pytest.mark.parametrize("keep,phi", [(0.3, "elu1"), (0.3, "relu"), (0.3, "none"),
@@ -69,6 +70,14 @@ def test_backward_parity_ragged(keep, phi):
     N = 64 * 9 - 23  # nine blocks, the last with 41 rows
     Q, K, V, G = (random_bf16((1, 2, N, 128), s) for s in (101, 102, 103, 104))
     _compare(Q, K, V, G, keep, phi, f"ragged keep={keep} {phi}")
+
+
+@pytest.mark.parametrize("keep,phi", [(0.3, "elu1"), (1.0, "relu")])
+def test_backward_parity_batched(keep, phi):
+    # B = 2, H = 3: every (batch, head) slice of the key and query sides
+    N = 64 * 6 - 9
+    Q, K, V, G = (random_bf16((2, 3, N, 128), s) for s in (131, 132, 133, 134))
+    _compare(Q, K, V, G, keep, phi, f"batched keep={keep} {phi}")
 
 
 def test_backward_parity_tiny_workload():
