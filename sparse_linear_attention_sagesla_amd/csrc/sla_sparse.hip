@@ -1654,10 +1654,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs b) {
 }
 
 // ---------------------------------------------------------------------------
-// Key side: one workgroup per key block j (four waves, 16 keys each), walking
-// the query blocks that keep j (shared with the group's other key blocks
-// first).  Per query block i it stages the INT8 Q codes, the dO and Q rows,
-// (phi(Q)/den)^T and the row statistics:
+// Key side: one workgroup per key block j, walking the query blocks that keep
+// j (shared with the group's other key blocks first); the waves and their
+// roles are described at kv_waves.  Per query block i it stages the INT8 Q
+// codes, the dO and Q rows, (phi(Q)/den)^T and the row statistics:
 //   S, P (the forward's weights), dP = dO V^T, dS
 //   dV += P^T dO,  dK += dS^T Q,  W += (phi(Q)/den)^T dO,  w += (phi(Q)/den)^T u
 // then the linear gradient through G - W and g_z - w.  dV, W and dK contract
@@ -1681,8 +1681,9 @@ constexpr int kKvStage = kKvStOff + kKvStatBytes;         // 57 KB
 // rows of 16.  (r & 7) ^ (r >> 3 & 1) is both.
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 7) ^ ((r >> 3) & 1)) << 1; }
 
-// Byte offset a lane fetches when a wave moves a 1 KB round (4 rows) of such a
-// tile into LDS (round m of the workgroup: rows 16m..16m+15, + 4096m bytes).
+// Byte offset a lane fetches when wave w moves its 1 KB (4 rows, 4w..4w+3 of
+// the workgroup's round; a round of W waves covers 4W rows) of such a tile
+// into LDS.
 __device__ __forceinline__ int kv_row_ld(int wave, int lane) {
   const int r = 4 * wave + (lane >> 4);
   return r * 256 + (((lane & 15) ^ kv_swz(r)) << 4);
