@@ -202,6 +202,24 @@ sla_status sla_attention_fwd_ex(const void *q, const void *k, const void *v,
                                 void *stream, void *const *stage_events,
                                 int options);
 
+/* sla_attention_fwd with the selection on a second stream: after the
+ * statistics pass (on `stream`), the block scores, the top-k selection and the
+ * walk schedule run on `side` while the K mean and the linear staging run on
+ * `stream`; `stream` waits for `side` before the attention kernel.  `side` is
+ * a caller-owned HIP stream of the same device (hipStream_t; NULL or equal to
+ * `stream`: exactly sla_attention_fwd).  The call creates two HIP events and
+ * releases them (the runtime frees them once the work they mark is done); it
+ * allocates no device memory.  The output equals sla_attention_fwd's bit for
+ * bit (the same kernels on the same data).  Work left on `side` after the
+ * call: none that `stream` does not wait for.  Same arguments, ownership and
+ * errors as sla_attention_fwd; a failed event or stream call gives
+ * SLA_ERR_DEVICE. */
+sla_status sla_attention_fwd_fork(const void *q, const void *k, const void *v,
+                                  int B, int H, int N, int d, int block,
+                                  double keep, int phi, void *out,
+                                  int out_dtype, void *ws, size_t ws_bytes,
+                                  void *stream, void *side);
+
 /* The forward with a lower-bit linear branch, an opt-in variant with its own
  * accuracy (the pages run SLA on low-bit INT8/INT4 SageAttention: commentary
  * "清华开源TurboDiffusion加速框架", section "SageAttention与稀疏计算").  The

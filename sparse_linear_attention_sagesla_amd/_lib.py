@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
     lib.sla_attention_fwd.restype = c_int
     lib.sla_attention_fwd_ex.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_int]
     lib.sla_attention_fwd_ex.restype = c_int
+    lib.sla_attention_fwd_fork.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p, c_size_t, c_void_p, c_void_p]
+    lib.sla_attention_fwd_fork.restype = c_int
     lib.sla_attention_fwd_lowbit.argtypes = lib.sla_attention_fwd.argtypes
     lib.sla_attention_fwd_lowbit.restype = c_int
     lib.sla_attention_fwd_noalloc.argtypes = [c_void_p] * 3 + [c_int] * 5 + [c_double, c_int, c_void_p, c_int, c_void_p]
@@ -182,11 +184,13 @@ def block_select(q: torch.Tensor, k: torch.Tensor, keep: float, with_mask: bool 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0.1,
               phi: str = "elu1", out_dtype=torch.bfloat16, return_linear: bool = False,
-              out=None, workspace=None, lowbit: bool = False):
+              out=None, workspace=None, lowbit: bool = False, side_stream=None):
     """SageSLA forward: softmax attention on the kept key blocks + linear attention on the rest.
 
     ``lowbit``: the opt-in variant with the linear branch's phi(K) in FP8
-    (sla_attention_fwd_lowbit)."""
+    (sla_attention_fwd_lowbit).  ``side_stream`` (a torch.cuda.Stream of q's
+    device): the selection runs on it, concurrently with the linear staging
+    (sla_attention_fwd_fork); not with ``return_linear`` or ``lowbit``."""
     q, k, v = _bhnd(q, "q"), _bhnd(k, "k"), _bhnd(v, "v")
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
@@ -203,6 +207,13 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: float = 0
     nbytes = workspace_size(OP_ATTENTION, B, H, N, keep, ph)
     ws = _workspace(nbytes, dev, workspace)
     f32 = 1 if out_dtype == torch.float32 else 0
+    if side_stream is not None:
+        if lin is not None or lowbit:
+            raise ValueError("side_stream is not combined with return_linear or lowbit")
+        _check(load().sla_attention_fwd_fork(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep), ph,
+                                             _ptr(out), f32, _ptr(ws), ws.numel(), _stream(dev),
+                                             side_stream.cuda_stream), "sla_attention_fwd_fork")
+        return out
     if lin is None:
         fn = load().sla_attention_fwd_lowbit if lowbit else load().sla_attention_fwd
         _check(fn(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, BLOCK, float(keep), ph, _ptr(out), f32,

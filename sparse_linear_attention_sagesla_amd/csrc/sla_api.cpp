@@ -315,10 +315,14 @@ sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, i
 namespace {
 
 // The forward; with `res` it also writes a training forward's residuals.
+// The forward.  With `side` (a second caller-owned stream, other than
+// `stream`), the selection (block scores, top-k, walk schedule) runs on it,
+// forked after the statistics pass and joined before the attention kernel,
+// concurrently with the K mean and the linear staging on `stream`.
 sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                     int block, double keep, int phi, void* out, int out_dtype, float* out_linear,
                     void* ws, size_t ws_bytes, void* stream, void* const* stage_events, int options,
-                    const sla::TrainResiduals* res) {
+                    const sla::TrainResiduals* res, void* side = nullptr) {
   const sla_status st =
       check_fwd_args(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, out_linear);
   if (st != SLA_OK) return st;
@@ -358,16 +362,29 @@ sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, i
     if (e == hipSuccess && stage_events && stage_events[2 * id + 1])
       e = hipEventRecord(static_cast<hipEvent_t>(stage_events[2 * id + 1]), hs);
   };
+  // the selection's stream, and the fork and join events when it is `side`
+  hipStream_t sel = hs;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (side && side != stream && kk > 0) {
+    sel = static_cast<hipStream_t>(side);
+    e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+  }
   if (kk > 0) {
     stage(SLA_STAGE_STATS, [&] {
       return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs);
     });
+    if (fork && e == hipSuccess) {
+      e = hipEventRecord(fork, hs);
+      if (e == hipSuccess) e = hipStreamWaitEvent(sel, fork, 0);
+    }
     stage(SLA_STAGE_TOPK, [&] {
-      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, hs);
+      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, sel);
     });
     // the aligned walks of the query-block groups, from the kept lists alone
     if (!direct)
-      stage(SLA_STAGE_SCHEDULE, [&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
+      stage(SLA_STAGE_SCHEDULE, [&] { return sla::launch_group_schedule(w.idx, s, w.sched, sel); });
+    if (join && e == hipSuccess) e = hipEventRecord(join, sel);
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
   // Q is coded by the statistics pass and K by the staging pass (one read of
@@ -381,10 +398,14 @@ sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, i
       return sla::launch_linear_final(w.hpart, w.zpart, s, w.hf, w.z64, res ? res->z : nullptr,
                                       nullptr, nullptr, res ? res->hb : nullptr, hs);
     });
+  if (join && e == hipSuccess) e = hipStreamWaitEvent(hs, join, 0);
   stage(SLA_STAGE_SPARSE, [&] {
     return sla::launch_sparse_fwd(qb, w, s, phi_eff, out, out_dtype == SLA_OUT_F32 ? 1 : 0,
                                   out_linear, fp8, res, hs);
   });
+  // released by the runtime once the recorded work has completed
+  if (fork) hipEventDestroy(fork);
+  if (join) hipEventDestroy(join);
   return device_status(e);
 }
 
@@ -428,6 +449,13 @@ sla_status sla_attention_fwd_train(const void* q, const void* k, const void* v, 
                   static_cast<unsigned char*>(resid), &r);
   return fwd_impl(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, r.ol, ws, ws_bytes, stream,
                   nullptr, 0, &r);
+}
+
+sla_status sla_attention_fwd_fork(const void* q, const void* k, const void* v, int B, int H, int N,
+                                  int d, int block, double keep, int phi, void* out, int out_dtype,
+                                  void* ws, size_t ws_bytes, void* stream, void* side) {
+  return fwd_impl(q, k, v, B, H, N, d, block, keep, phi, out, out_dtype, nullptr, ws, ws_bytes,
+                  stream, nullptr, 0, nullptr, side);
 }
 
 sla_status sla_attention_fwd(const void* q, const void* k, const void* v, int B, int H, int N,

@@ -267,6 +267,26 @@ def test_noalloc_validates_on_the_host():
     assert call(out_dtype=3) == INVALID
 
 
+def test_fork_entry_rejects_bad_arguments_before_launch():
+    """sla_attention_fwd_fork validates like sla_attention_fwd before it
+    creates events or touches either stream."""
+    L = lib()
+    L.sla_attention_fwd_fork.restype = ctypes.c_int
+
+    def call(q=FAKE, out=FAKE, d=128, keep=0.1, phi=1, out_dtype=0, ws=FAKE, ws_bytes=1 << 40):
+        return L.sla_attention_fwd_fork(q, FAKE, FAKE, 1, 2, 2048, d, 64, ctypes.c_double(keep), phi, out,
+                                        out_dtype, ws, ctypes.c_size_t(ws_bytes), NULL, FAKE)
+
+    assert call(q=NULL) == INVALID
+    assert call(out=MISALIGNED) == INVALID
+    assert call(d=64) == UNSUPPORTED
+    assert call(keep=1.5) == INVALID
+    assert call(keep=0.0, phi=0) == INVALID
+    assert call(out_dtype=3) == INVALID
+    assert call(ws=NULL) == WORKSPACE
+    assert call(ws_bytes=4096) == WORKSPACE
+
+
 def _train_res_bytes(B, H, N, keep, phi):
     """The residual layout of sla_attention_fwd_train, from its documentation."""
     up = lambda n: (n + 255) // 256 * 256
