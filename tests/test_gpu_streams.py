@@ -72,6 +72,30 @@ def test_graph_capture_replays(keep, phi):
         assert torch.equal(out, eager), f"replay {rep}"
 
 
+def test_fork_inside_graph_capture():
+    """sla_attention_fwd_fork captured: the fork and join become graph
+    dependencies between the selection and the staging branches."""
+    q, k, v = _inputs(51)
+    keep, phi = 0.1, "elu1"
+    eager = sla.attention(q, k, v, keep, phi, torch.float32).clone()
+    out = torch.empty(SHAPE, dtype=torch.float32, device=q.device)
+    ws = torch.empty(sla.workspace_bytes(*SHAPE[:3], keep, phi), dtype=torch.uint8, device=q.device)
+    side = torch.cuda.Stream()
+    sla.attention(q, k, v, keep, phi, torch.float32, out=out, workspace=ws, side_stream=side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sla.attention(q, k, v, keep, phi, torch.float32, out=out, workspace=ws, side_stream=side)
+    for rep in range(3):
+        out.fill_(7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] fork replay {rep}", flush=True)
+        assert torch.equal(out, eager), f"replay {rep}"
+
+
 FIRST_CALL_IN_CAPTURE = textwrap.dedent("""
     import sys
     sys.path.insert(0, sys.argv[1])
