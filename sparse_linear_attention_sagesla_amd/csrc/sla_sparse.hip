@@ -1785,9 +1785,13 @@ constexpr int kv_waves() { return kLin ? 8 : 4; }
 template <bool kLin>
 constexpr int kv_loads() { return kLin ? 8 : 11; }
 constexpr int kKvStages = 2;   // staged query blocks: one in use, one in flight
-// dS hand-over slots (with the linear branch): for each of the two 16-byte
-// halves, 16 bytes per lane of the 4 score waves (lane-contiguous, so each
-// access is free of bank conflicts)
+// dS hand-over slots (with the linear branch), two sets used by alternate
+// blocks: for each of the two 16-byte halves, 16 bytes per lane of the 4
+// score waves (lane-contiguous, so each access is free of bank conflicts).
+// The score waves write block p's dS into set p % 2 during block p; the
+// linear waves read it at the start of block p + 1, after the walk's
+// barrier, and set p % 2 is written again only after the next barrier, so
+// the hand-over needs no barrier of its own.
 constexpr int kKvDsOff = kKvStages * kKvStage;
 constexpr int kKvDsHalf = 4 * 64 * 16;
 
@@ -1889,7 +1893,7 @@ __device__ __forceinline__ void kv_walk(lds_byte* smem, const BwdKvSrc& src, con
       issue_kv_tile<kLin>(smem + sn * kKvStage, src, block_of(pn), wave, ko, lane);
       sc[kKvStages - 1] = scale_of(pn);
     }
-    tile(smem + stage * kKvStage, sc[0]);
+    tile(smem + stage * kKvStage, sc[0], p);
 #pragma unroll
     for (int q = 0; q < kKvStages - 1; ++q) sc[q] = sc[q + 1];
     stage = stage == kKvStages - 1 ? 0 : stage + 1;
@@ -1898,8 +1902,8 @@ __device__ __forceinline__ void kv_walk(lds_byte* smem, const BwdKvSrc& src, con
 
 // One staged query block for a score wave (16 keys): S, P, dP, dS, then
 // dV += P^T dO and, unless kSplit, dK += dS^T Q.  kSplit: dS goes to this
-// lane's slot of `ds` and, after a workgroup barrier, the linear wave on the
-// same SIMD takes dK.
+// lane's slot of `ds` (the block's slot set), and the linear wave on the same
+// SIMD takes dK one block later.
 template <bool kSplit>
 __device__ __forceinline__ void kv_score_tile(const lds_byte* st, const v4i kf[2], const bf16x8 vf[4],
                                               const KvLane& kl, float cs, int g, v4f dv[8],
@@ -1932,7 +1936,6 @@ __device__ __forceinline__ void kv_score_tile(const lds_byte* st, const v4i kf[2
   if (kSplit) {
     *(__attribute__((address_space(3))) bf16x8*)ds = dsa[0];
     *(__attribute__((address_space(3))) bf16x8*)(ds + kKvDsHalf) = dsa[1];
-    lds_barrier();  // dS is in LDS for the linear waves
   }
   // per 32-row step c: the column-wise dO fragments (dV) and Q fragments (dK),
   // read kAhead fragments ahead of the products that take them
@@ -1955,12 +1958,24 @@ __device__ __forceinline__ void kv_score_tile(const lds_byte* st, const v4i kf[2
   }
 }
 
-// One staged query block for a linear wave (phi channels 32 lw..32 lw + 31):
-// W += (phi(Q)/den)^T dO and w += (phi(Q)/den)^T u; then, once the score wave
-// on this SIMD has put dS in its slot of `ds`, dK += dS^T Q for its keys.
+// dK += dS^T Q for the 16 keys of the score wave on this SIMD, from its dS
+// slots at `ds` and the Q fragments bq held since that block was staged.
+__device__ __forceinline__ void kv_dk8(const bf16x8 bq[2][8], const lds_byte* ds, v4f dk[8]) {
+  const bf16x8 dsa[2] = {*(lds_bf16x8*)ds, *(lds_bf16x8*)(ds + kKvDsHalf)};
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dk[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], bq[c][q], dk[q], 0, 0, 0);
+}
+
+// One staged query block p for a linear wave (phi channels 32 lw..32 lw + 31):
+// first the softmax branch's dK of block p - 1 (its dS and Q fragments are
+// ready by now), then W += (phi(Q)/den)^T dO and w += (phi(Q)/den)^T u, and
+// last block p's Q fragments into bq for the next call.
 __device__ __forceinline__ void kv_linear_tile(const lds_byte* st, const KvLane& kl, int lw, int g,
-                                               int l16, v4f w[2][8], v4f wz[2], v4f dk[8],
-                                               const lds_byte* ds) {
+                                               int l16, int p, v4f w[2][8], v4f wz[2], v4f dk[8],
+                                               bf16x8 bq[2][8], const lds_byte* ds) {
+  if (p > 0) kv_dk8(bq, ds + ((p - 1) & 1) * 2 * kKvDsHalf, dk);
   bf16x8 af[2][2], ub[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -1969,7 +1984,6 @@ __device__ __forceinline__ void kv_linear_tile(const lds_byte* st, const KvLane&
       af[mt][c] = *(lds_bf16x8*)(st + kKvFqOff + (2 * lw + mt) * 2048 + (kl.rd8 ^ (64 * c)));
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    // u per k slot 4h + e (row 32c + 16h + 4g + e)
     const v4f u0 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g));
     const v4f u1 = *(lds_v4f*)(st + kKvStOff + 768 + 4 * (32 * c + 8 * g + 4));
 #pragma unroll
@@ -1993,21 +2007,10 @@ __device__ __forceinline__ void kv_linear_tile(const lds_byte* st, const KvLane&
     wz[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][c], ub[c], wz[0], 0, 0, 0);
     wz[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][c], ub[c], wz[1], 0, 0, 0);
   }
-  lds_barrier();  // the score waves' dS is in LDS
-  bf16x8 dsa[2];
-  dsa[0] = *(lds_bf16x8*)ds;
-  dsa[1] = *(lds_bf16x8*)(ds + kKvDsHalf);
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    bf16x8 F[8];
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int f = 0; f < kAhead; ++f) F[f] = tr_frag(st + kKvQOff, c, kl.tr[f]);
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      if (f + kAhead < 8) F[f + kAhead] = tr_frag(st + kKvQOff, c, kl.tr[f + kAhead]);
-      dk[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[c], F[f], dk[f], 0, 0, 0);
-    }
-  }
+    for (int q = 0; q < 8; ++q) bq[c][q] = tr_frag(st + kKvQOff, c, kl.tr[q]);
 }
 
 // LDS of the linear gradient (after the walk): G - W as bf16 both row-major
@@ -2015,7 +2018,8 @@ __device__ __forceinline__ void kv_linear_tile(const lds_byte* st, const KvLane&
 constexpr int kGaOff = 0, kGbOff = 32 * 1024, kGzOff = 64 * 1024;
 static_assert(kGzOff + 4 * kD <= kKvStages * kKvStage, "the linear gradient's LDS fits the stages");
 template <bool kLin>
-constexpr int kv_lds_bytes() { return kKvStages * kKvStage + (kLin ? 2 * kKvDsHalf : 0); }
+constexpr int kv_lds_bytes() { return kKvStages * kKvStage + (kLin ? 4 * kKvDsHalf : 0); }
+static_assert(kv_lds_bytes<true>() <= 160 * 1024, "the key side's LDS fits one CU");
 
 // Score wave: the keys 16 wave.. of block j; dV (and, without the linear
 // branch, dK).
@@ -2041,8 +2045,8 @@ __device__ __forceinline__ void kv_score_role(const BwdKvArgs& a, lds_byte* smem
   for (int e = 0; e < 8; ++e) dv[e] = dk[e] = v4f{0.f, 0.f, 0.f, 0.f};
   const float ks = n > 0 ? a.sk[bh * a.Nb + j] * (kInvSqrtD * kLog2e) : 0.0f;
   lds_byte* ds = smem + kKvDsOff + 16 * (64 * wave + lane);
-  kv_walk<kLin>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float si) {
-    kv_score_tile<kLin>(st, kf, vf, kl, si * ks, g, dv, dk, ds);
+  kv_walk<kLin>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float si, int p) {
+    kv_score_tile<kLin>(st, kf, vf, kl, si * ks, g, dv, dk, ds + (p & 1) * 2 * kKvDsHalf);
   });
 
   // the linear branch's share of dV: phi(K) (G - W), G - W written by the
@@ -2107,10 +2111,12 @@ __device__ __forceinline__ void kv_linear_role(const BwdKvArgs& a, lds_byte* sme
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) dk[ct] = v4f{0.f, 0.f, 0.f, 0.f};
   const lds_byte* ds = smem + kKvDsOff + 16 * (64 * lw + lane);
-  kv_walk<true>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float) {
-    kv_linear_tile(st, kl, lw, g, l16, w, wz, dk, ds);
+  bf16x8 bq[2][8];
+  kv_walk<true>(smem, src, list, n, a.sq + bh * a.Nb, a.Nb, wave, lane, [&](const lds_byte* st, float, int p) {
+    kv_linear_tile(st, kl, lw, g, l16, p, w, wz, dk, bq, ds);
   });
-  lds_barrier();  // every wave is done with the stages
+  lds_barrier();  // every wave is done with the stages; the last block's dS is in LDS
+  if (n > 0) kv_dk8(bq, ds + ((n - 1) & 1) * 2 * kKvDsHalf, dk);
   const float* Gh = a.G + bh * kD * kD;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
