@@ -87,3 +87,48 @@ def test_large_union_with_triangle(phi):
     keep = 220 / 600
     assert O.topk_count(nb, keep) == 220
     _check(Q, K, V, keep, phi, sets, [0, 1, 2, 3, 4, 301, 599])
+
+
+# The backward's key side walks the columns of the selection (for each key
+# block, the query blocks that keep it), ordered by how many of the key
+# block's group of four share each query block, so that columns of different
+# lengths and owner sets that overlap like a triangle are both walked.  A
+# column walk that missed or repeated a query block would move dK and dV far
+# outside the backward's tolerance.
+
+def _check_backward(Q, K, V, keep, phi, seed, tag):
+    from test_gpu_backward import _check
+    N = Q.shape[0]
+    G = random_bf16((N, D), seed)
+    q, k, v, g = (to_dev(x.reshape(1, 1, N, D)) for x in (Q, K, V, G))
+    print(f"[case] column walks {tag} N={N} keep={keep:.4f} {phi}", flush=True)
+    got = [x.float().cpu().numpy()[0, 0]
+           for x in sla.attention_bwd(q, k, v, g, keep=keep, phi=phi, grad_dtype=torch.float32)]
+    r = O.sla_backward_head(Q, K, V, G, block=64, keep=keep, phi_kind=phi)
+    for x, name in zip(got, ("dq", "dk", "dv")):
+        _check(f"column walks {tag} {name}", x, r[name])
+
+
+@pytest.mark.parametrize("phi", ["none", "elu1"])
+def test_backward_column_walks_triangle(phi):
+    # columns 0, 1, 2 hold query blocks {0, 2}, {0, 1}, {1, 2}: the owner sets
+    # form a triangle; columns 3..8 have lengths 0 to 4
+    sets = [{0, 1}, {1, 2}, {2, 0}, {3, 4}, {5, 6}, {5, 6}, {5, 6}, {5, 6}, {7, 8}]
+    N = 9 * 64 - 10
+    Q, K, V = _build(N, list(range(9)), sets, seed=41)
+    _check_backward(Q, K, V, 2 / 9, phi, 45, "triangle")
+
+
+def test_backward_column_walks_large_union():
+    # 600 query blocks keeping two of key blocks 0, 1, 2 in turn: the first
+    # group's three columns of 400 query blocks each form a triangle over a
+    # union of 600 (columns longer than a wave's 64 lanes take several rounds
+    # of the list builder); the other columns are empty
+    nb = 600
+    pairs = [{0, 1}, {1, 2}, {2, 0}]
+    sets = [pairs[i % 3] for i in range(nb)]
+    N = nb * 64 - 7
+    Q, K, V = _build(N, [0, 1, 2] + [3] * (nb - 3), sets, seed=47)
+    keep = 2 / nb
+    assert O.topk_count(nb, keep) == 2
+    _check_backward(Q, K, V, keep, "none", 48, "large union")
