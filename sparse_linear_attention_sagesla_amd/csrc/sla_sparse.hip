@@ -1079,14 +1079,16 @@ __device__ __forceinline__ void greedy_steps_regs(uint32_t (&u)[kR], int k, uint
 }
 
 // Groups of four: the same greedy over per-owner-set queues.  The union is
-// sorted (stably, so by block within a set) into 15 queues, one per owner set;
-// lane L < 15 holds the head of queue L, so a pick is one wave-wide maximum
-// over the heads whose set is free.  Returns false, leaving the schedule to
-// the general greedy, when a step would need a block split between steps.
-__device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint32_t* q, int k,
-                                               uint32_t full, uint32_t last_busy, int lane,
-                                               const SchedOut& out) {
-  constexpr uint32_t kSets[16] = {15, 7, 11, 13, 14, 3, 5, 6, 9, 10, 12, 1, 2, 4, 8, 0};
+// sorted (stably, so by block within a set) into 15 queues, one per owner set
+// (queue t holds the set kSets[t]); the lane holding queue t's head finds a
+// pick as one maximum over the heads whose set is free.
+constexpr uint32_t kSets[16] = {15, 7, 11, 13, 14, 3, 5, 6, 9, 10, 12, 1, 2, 4, 8, 0};
+constexpr uint64_t kSetsPacked = 0x08421ca9653edb7full;  // kSets[t] in bits 4t..4t+3
+
+// The queues of a union uni[0, n) at q (by the whole wave); returns queue
+// t_of's range [head, end) of q.
+__device__ __forceinline__ void queue_layout(const uint32_t* uni, int n, uint32_t* q, int lane, int t_of,
+                                             int& mine_head, int& mine_end) {
   const uint64_t below = (1ull << lane) - 1ull;
   // queue sizes and stable positions (all counts are wave-uniform)
   int cnt[16];
@@ -1098,12 +1100,13 @@ __device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint3
 #pragma unroll
     for (int t = 0; t < 15; ++t) cnt[t] += __popcll(__ballot(m == kSets[t]));
   }
-  int off[16], mine_head = 0, mine_end = 0;
+  int off[16];
   int run = 0;
+  mine_head = mine_end = 0;
 #pragma unroll
   for (int t = 0; t < 15; ++t) {
     off[t] = run;
-    if (lane == t) mine_head = run, mine_end = run + cnt[t];
+    if (t_of == t) mine_head = run, mine_end = run + cnt[t];
     run += cnt[t];
   }
   for (int base = 0; base < n; base += 64) {
@@ -1116,11 +1119,18 @@ __device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint3
       off[t] += __popcll(bal);
     }
   }
+}
+
+// One group per wave: lane L < 15 holds the head of queue L, so a pick is one
+// wave-wide maximum.  Returns false, leaving the schedule to the general
+// greedy, when a step would need a block split between steps.
+__device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint32_t* q, int k,
+                                               uint32_t full, uint32_t last_busy, int lane,
+                                               const SchedOut& out) {
+  int mine_head, mine_end;
+  queue_layout(uni, n, q, lane, lane, mine_head, mine_end);
   __syncthreads();
-  uint32_t set = 0u;
-#pragma unroll
-  for (int t = 0; t < 15; ++t)
-    if (lane == t) set = kSets[t];
+  const uint32_t set = lane < 15 ? (uint32_t)(kSetsPacked >> (4 * lane)) & 15u : 0u;
   const uint32_t size = (uint32_t)__popc(set);
   uint32_t hj = mine_head < mine_end ? q[mine_head] : 0xffffffu;
 
@@ -1148,22 +1158,20 @@ __device__ __forceinline__ bool greedy_queues4(const uint32_t* uni, int n, uint3
 
 // One wave per group: sched[((bh, grp, s) * kG) + u] = key block of member u
 // (query block kG*grp + u) in step s.  Members past the last block get -1.
+// The union of group grp's kept blocks (one wave; the workgroup is that
+// wave): own = owner byte of key block j in byte j&3 of word j>>2, then uni =
+// the union, ascending key block, entry = block << 8 | owners.  Writes -1 for
+// members past the last query block and the ragged last key block's last
+// step; returns the union's size, the members and the members busy with the
+// ragged block in the last step.
 template <int kG>
-__global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx,
-                                                            int Nb, int k, int ragged,
-                                                            int32_t* __restrict__ sched) {
-  extern __shared__ uint32_t gsm[];
-  const int lane = threadIdx.x;
-  const int grp = blockIdx.x;
-  const size_t bh = blockIdx.y;
-  const int ngroups = (Nb + kG - 1) / kG;
+__device__ __forceinline__ int group_union(const int32_t* __restrict__ idx, size_t bh, int Nb, int k,
+                                           int grp, int ragged, uint32_t* own, uint32_t* uni, int lane,
+                                           const SchedOut& out, uint32_t& full, uint32_t& last_busy) {
   const int first = grp * kG;
   const int members = min(kG, Nb - first);
-  const uint32_t full = (1u << members) - 1u;
+  full = (1u << members) - 1u;
   const int words = (Nb + 3) / 4;
-  uint32_t* own = gsm;          // owner byte of key block j: byte j&3 of word j>>2
-  uint32_t* uni = gsm + words;  // union, ascending key block
-  const SchedOut out{sched + (bh * ngroups + grp) * (size_t)k * kG};
   auto clampj = [&](int j) { return min(max(j, 0), Nb - 1); };
 
   for (int w = lane; w < words; w += 64) own[w] = 0u;
@@ -1191,7 +1199,7 @@ __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __res
     for (int s = 0; s < k; ++s) out.put((size_t)s * kG + lane, -1);
   // A ragged last key block goes to the last step of every member that keeps
   // it, so the attention kernel masks padding only in its peeled last step.
-  uint32_t last_busy = 0u;
+  last_busy = 0u;
   if (ragged && n > 0 && k > 0) {
     const uint32_t v = uni[n - 1];  // the union is ascending
     if ((int)(v >> 8) == Nb - 1) {
@@ -1202,8 +1210,13 @@ __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __res
       __syncthreads();
     }
   }
+  return n;
+}
 
-  if (kG == 4 && greedy_queues4(uni, n, uni + n, k, full, last_busy, lane, out)) return;
+// The general greedy over a group's union (registers when it fits, else LDS).
+template <int kG>
+__device__ __forceinline__ void greedy_general(uint32_t* uni, int n, int k, uint32_t full, uint32_t last_busy,
+                                               int lane, const SchedOut& out) {
   if (n <= 64 * kSchedRegs) {
     // the union fits in registers: kSchedRegs entries per lane, 0 = empty
     uint32_t u[kSchedRegs];
@@ -1213,6 +1226,110 @@ __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __res
   } else {
     UnionLds ent{uni, n, lane};
     greedy_steps<kG>(ent, k, full, last_busy, lane, out);
+  }
+}
+
+// One wave per group: sched[((bh, grp, s) * kG) + u] = key block of member u
+// (query block kG*grp + u) in step s.  Members past the last block get -1.
+template <int kG>
+__global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx,
+                                                            int Nb, int k, int ragged,
+                                                            int32_t* __restrict__ sched) {
+  extern __shared__ uint32_t gsm[];
+  const int lane = threadIdx.x;
+  const int grp = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int ngroups = (Nb + kG - 1) / kG;
+  const int words = (Nb + 3) / 4;
+  uint32_t* own = gsm;
+  uint32_t* uni = gsm + words;
+  const SchedOut out{sched + (bh * ngroups + grp) * (size_t)k * kG};
+  uint32_t full, last_busy;
+  const int n = group_union<kG>(idx, bh, Nb, k, grp, ragged, own, uni, lane, out, full, last_busy);
+  if (kG == 4 && greedy_queues4(uni, n, uni + n, k, full, last_busy, lane, out)) return;
+  greedy_general<kG>(uni, n, k, full, last_busy, lane, out);
+}
+
+// Maximum over the 16 lanes of each row of the wave (DPP only).
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, true));   // lane ^ 2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, true));  // 8-lane mirror
+  return max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, true));  // 16-lane mirror
+}
+
+// LDS words of the four-group kernel: owner bytes and a union (rebuilt for
+// each group in turn), and the four groups' queues.
+inline size_t group_schedule_x4_lds(int Nb, int k) {
+  const size_t cap = std::min<size_t>((size_t)Nb, (size_t)kGroup * k);
+  return 4 * (((size_t)Nb + 3) / 4 + 5 * cap);
+}
+
+// Four groups of four per wave: the union and queues of each are built by the
+// whole wave in turn, then row r (lanes 16r..16r+15) runs the queue greedy of
+// group 4 * blockIdx.x + r, lane 16r + t holding the head of queue t, so one
+// pick is a 16-lane maximum and serves the four groups at once.  A group whose
+// walk would need a block split between steps is then redone by the general
+// greedy (the same schedule as the one-group kernel gives).
+__global__ __launch_bounds__(64) void group_schedule_x4_kernel(const int32_t* __restrict__ idx, int Nb,
+                                                               int k, int ragged,
+                                                               int32_t* __restrict__ sched) {
+  extern __shared__ uint32_t gsm[];
+  const int lane = threadIdx.x, row = lane >> 4, l16 = lane & 15;
+  const size_t bh = blockIdx.y;
+  const int ngroups = (Nb + kGroup - 1) / kGroup;
+  const int words = (Nb + 3) / 4;
+  const int cap = min(Nb, kGroup * k);
+  uint32_t* own = gsm;
+  uint32_t* uni = gsm + words;
+  uint32_t* queues = uni + cap;
+  auto out_of = [&](int grp) { return SchedOut{sched + (bh * ngroups + grp) * (size_t)k * kGroup}; };
+  int head = 0, end = 0;
+  uint32_t full = 0u, last_busy = 0u;  // this row's group (none: full = 0)
+  for (int q = 0; q < 4; ++q) {
+    const int grp = 4 * blockIdx.x + q;
+    if (grp >= ngroups) break;
+    uint32_t f, lb;
+    const int n = group_union<kGroup>(idx, bh, Nb, k, grp, ragged, own, uni, lane, out_of(grp), f, lb);
+    int h, e;
+    queue_layout(uni, n, queues + q * cap, lane, l16, h, e);
+    if (row == q) head = h, end = e, full = f, last_busy = lb;
+    __syncthreads();  // own and uni are rebuilt for the next group
+  }
+  const uint32_t* myq = queues + row * cap;
+  const uint32_t set = l16 < 15 ? (uint32_t)(kSetsPacked >> (4 * l16)) & 15u : 0u;
+  const uint32_t size = (uint32_t)__popc(set);
+  uint32_t hj = head < end ? myq[head] : 0xffffffu;
+  const SchedOut out = out_of(min(4 * (int)blockIdx.x + row, ngroups - 1));  // written only with a group
+  bool failed = false;  // row-uniform
+  for (int s = 0; s < k; ++s) {
+    uint32_t freem = failed ? 0u : s == k - 1 ? full & ~last_busy : full;
+    while (__ballot(freem != 0u)) {
+      // most owners among the free members, then lowest block
+      const bool ok = set && !(set & ~freem) && head < end;
+      const uint32_t key = ok ? (size << 24) | (0xffffffu - hj) : 0u;
+      const uint32_t top = row_max_u32(key);
+      const bool pick = top != 0u;
+      if (!pick && freem) failed = true;
+      const uint32_t rowbits = (uint32_t)(__ballot(pick && key == top) >> (16 * row)) & 0xffffu;
+      const int h = pick ? __builtin_ctz(rowbits) : 0;
+      const uint32_t bm = pick ? (uint32_t)(kSetsPacked >> (4 * h)) & 15u : 0u;
+      if (pick && l16 == h) {
+        ++head;
+        hj = head < end ? myq[head] : 0xffffffu;
+      }
+      if (l16 < 4 && ((bm >> l16) & 1u)) out.put((size_t)s * 4 + l16, (int32_t)(0xffffffu - (top & 0xffffffu)));
+      freem = pick ? freem & ~bm : 0u;
+    }
+  }
+  const uint64_t redo = __ballot(failed && l16 == 0);
+  for (int q = 0; q < 4; ++q) {
+    if (!((redo >> (16 * q)) & 1ull)) continue;
+    const int grp = 4 * blockIdx.x + q;
+    __syncthreads();
+    uint32_t f, lb;
+    const int n = group_union<kGroup>(idx, bh, Nb, k, grp, ragged, own, uni, lane, out_of(grp), f, lb);
+    greedy_general<kGroup>(uni, n, k, f, lb, lane, out_of(grp));
   }
 }
 
@@ -2350,12 +2467,19 @@ hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
                                  hipStream_t s) {
   if (sh.k <= 0) return hipSuccess;
+  const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
+  const int ragged = sh.N != sh.Nb * kBlk ? 1 : 0;
+  const size_t lds4 = group_schedule_x4_lds(sh.Nb, sh.k);
+  if (lds4 <= 32 * 1024) {
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(group_schedule_x4_kernel), (int)lds4);
+    if (e != hipSuccess) return e;
+    group_schedule_x4_kernel<<<dim3((ngroups + 3) / 4, sh.BH), 64, lds4, s>>>(idx, sh.Nb, sh.k, ragged, sched);
+    return hipGetLastError();
+  }
   const size_t lds = group_schedule_lds(sh.Nb, sh.k, kGroup);
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(group_schedule_kernel<kGroup>), (int)lds);
   if (e != hipSuccess) return e;
-  const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
-  group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, lds, s>>>(
-      idx, sh.Nb, sh.k, sh.N != sh.Nb * kBlk ? 1 : 0, sched);
+  group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, lds, s>>>(idx, sh.Nb, sh.k, ragged, sched);
   return hipGetLastError();
 }
 
