@@ -132,3 +132,20 @@ def test_backward_column_walks_large_union():
     keep = 2 / nb
     assert O.topk_count(nb, keep) == 2
     _check_backward(Q, K, V, keep, "none", 48, "large union")
+
+
+def test_one_group_kernel_for_large_unions():
+    # 1700 key blocks at keep 0.3 (k = 510): four groups' queues would not fit
+    # the four-group kernel's LDS, so the walks come from the one-group kernel;
+    # sampled query blocks cover a whole group and the ragged last one
+    nb = 1700
+    N = nb * 64 - 13
+    Q, K, V = (random_bf16((N, D), s) for s in (61, 62, 63))
+    keep = 0.3
+    assert O.topk_count(nb, keep) == 510
+    q, k, v = (to_dev(x.reshape(1, 1, N, D)) for x in (Q, K, V))
+    print(f"[case] one-group schedule kernel N={N} keep={keep}", flush=True)
+    out = sla.attention(q, k, v, keep, "elu1", torch.float32).cpu().numpy()[0, 0]
+    blocks = [0, 1, 2, 3, 850, nb - 1]
+    r = O.sla_forward_head(Q, K, V, 64, keep, "elu1", query_blocks=blocks)
+    assert_parity(out[r["rows"]], r["out"], what=f"one-group schedule N={N}")
