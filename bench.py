@@ -124,11 +124,13 @@ def _cpu_model() -> str:
 def _oracle_sample_job(job):
     """One worker of the CPU baseline: the fp64 oracle on one head, timed once
     for a single query block and once for the whole sample (the difference
-    splits per-head setup from per-block time).  Single-threaded BLAS."""
+    splits per-head setup from per-block time), after one untimed call so that
+    first-use costs fall in neither.  Single-threaded BLAS."""
     from oracle import sla_oracle as O
     from sparse_linear_attention_sagesla_amd.inputs import WORKLOADS, make_head
     name, h, blocks, keep, phi = job
     q, k, v = make_head(WORKLOADS[name], 0, h)
+    O.sla_forward_head(q, k, v, 64, keep, phi, query_blocks=blocks[:1])
     t0 = time.perf_counter()
     O.sla_forward_head(q, k, v, 64, keep, phi, query_blocks=blocks[:1])
     t1 = time.perf_counter()
@@ -198,7 +200,7 @@ def cpu_baseline(wl, keep, phi, gpu_out_rows=None, gpu_idx=None, blocks_per_head
                 os.environ.pop(v_, None)
             else:
                 os.environ[v_] = old
-    per_block = float(np.mean([(full - one) / (len(blocks) - 1) for _, one, full, _ in res]))
+    per_block = max(float(np.mean([(full - one) / max(len(blocks) - 1, 1) for _, one, full, _ in res])), 0.0)
     setup = float(np.mean([max(one - per_block, 0.0) for _, one, _, _ in res]))
     work_s = wl.B * wl.H * (setup + nb * per_block)
     out = {"value": 1e3 * work_s / cores, "unit": "ms/call", "cores": cores, "kind": "oracle",
