@@ -482,6 +482,38 @@ def w8a8_leg(sla, wl, steps, stream, dev):
                                     "kernel": "rowquant_kernel<true>"}}
 
 
+def dense_gemm_reference(dev, stream, n=16384, reps=3):
+    """What the vendor library's dense fp16 product (torch.matmul, hipBLASLt)
+    reaches on this GPU in this process: an n x n x n product, fp32
+    accumulation, fp16 output, the best of `reps` runs after two untimed ones.
+    It is the same matrix-core instruction family the attention kernel's P.V
+    and linear-branch products use, on a plain dense GEMM: a practical
+    ceiling beside the datasheet peak, for context."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, generator=g, dtype=torch.float16)
+    b = torch.randn(n, n, device=dev, generator=g, dtype=torch.float16)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    with torch.cuda.stream(stream):
+        for it in range(reps + 2):
+            start.record(stream)
+            c = torch.matmul(a, b)
+            end.record(stream)
+            torch.cuda.synchronize()
+            if it >= 2:
+                times.append(start.elapsed_time(end) * 1e-3)
+            del c
+    del a, b
+    t = min(times)
+    tflops = 2.0 * n ** 3 / t / 1e12
+    return {"kernel": "torch.matmul fp16 (hipBLASLt)", "shape": [n, n, n], "ms": round(t * 1e3, 4),
+            "achieved": round(tflops, 1), "unit": "TFLOP/s",
+            "frac_of_peak": round(tflops / (PEAK_F16_FLOPS / 1e12), 4),
+            "note": f"best of {reps}; the attention kernel's roofline.frac_of_dense_gemm divides its "
+                    "achieved rate by this one"}
+
+
 def streaming_ceiling(dev, stream, mib=1024, reps=5):
     """What plain streaming reaches on this GPU in this process: a device copy of
     `mib` MiB (read + write bytes over time) and a read-only bf16 sum over
@@ -685,6 +717,8 @@ def main():
     bw = {n: round(bytes_io[n] / (stage_ms[n] * 1e-3) / 1e9, 1) for n in bytes_io if n in stage_ms}
     hbm_frac = {n: round(g * 1e9 / PEAK_HBM, 3) for n, g in bw.items()}
     ceiling = streaming_ceiling(dev, stream)
+    gemm_ref = dense_gemm_reference(dev, stream)
+    roofline["frac_of_dense_gemm"] = round(achieved / gemm_ref["achieved"], 4)
     ceil_frac = {n: round(g / ceiling["copy_gbps"], 3) for n, g in bw.items()}
     # whole call against its ideal: sparse work at the MFMA peaks, streaming
     # stages at the HBM peak, block scores at the fp64 vector peak
@@ -706,6 +740,7 @@ def main():
         "stage_hbm_gbps": bw,
         "stage_hbm_frac": hbm_frac,
         "streaming_ceiling": ceiling,
+        "dense_gemm_reference": gemm_ref,
         "stage_frac_of_copy": ceil_frac,
         "call_roofline_frac": round(ideal_s / (ms_step * 1e-3), 4),
         "roofline": roofline,

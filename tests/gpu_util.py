@@ -1,4 +1,9 @@
-"""Helpers shared by the GPU tests: device transfer and the parity criteria."""
+"""Helpers shared by the GPU tests: device transfer, the parity criteria and
+the pool of oracle worker processes."""
+import concurrent.futures as cf
+import multiprocessing as mp
+import os
+
 import numpy as np
 
 ATOL = 2e-3       # max-abs tolerance on the fp32 output
@@ -59,3 +64,19 @@ def selection_mismatches(gpu_idx: np.ndarray, ora_idx: np.ndarray, scores: np.nd
             else:
                 bad += 1
     return rows, excused, bad
+
+
+def oracle_pool():
+    """Single-threaded oracle worker processes, at most 16 (the host share of
+    one GPU), started with `spawn` (no GPU state crosses into them)."""
+    saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+    for v in saved:
+        os.environ[v] = "1"
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    ex = cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"))
+    for v, old in saved.items():
+        if old is None:
+            os.environ.pop(v)
+        else:
+            os.environ[v] = old
+    return ex, n

@@ -7,7 +7,7 @@ only small results cross the process boundary.
 import numpy as np
 
 from oracle import sla_oracle as O
-from sparse_linear_attention_sagesla_amd.inputs import WORKLOADS, make_head
+from sparse_linear_attention_sagesla_amd.inputs import WORKLOADS, make_dout, make_head
 
 
 def sampled_blocks(job):
@@ -47,3 +47,17 @@ def codes(job):
     name, h = job
     q, k, _ = make_head(WORKLOADS[name], 0, h)
     return (h,) + tuple(O.quantize_qk(q, k, 64))
+
+
+def backward_key_share(job):
+    """The oracle backward of head h restricted to the listed query blocks:
+    (dK rows, dV rows) of the listed key blocks, the share those query
+    blocks contribute (with phi = none, the query blocks that keep a key block
+    are the only ones that touch its rows)."""
+    name, h, keep, phi, key_blocks, query_blocks = job
+    wl = WORKLOADS[name]
+    q, k, v = make_head(wl, 0, h)
+    g = make_dout(wl, heads=[h])[0, 0]
+    r = O.sla_backward_head(q, k, v, g, 64, keep, phi, query_blocks=query_blocks)
+    rows = np.concatenate([np.arange(j * 64, min(wl.N, (j + 1) * 64)) for j in key_blocks])
+    return r["dk"][rows], r["dv"][rows]

@@ -10,10 +10,6 @@ that the benchmark times must equal the round-to-nearest-even of the fp32
 output everywhere that is checked.  The oracle runs in a pool of worker
 processes, each regenerating its head from the seeded generator.
 """
-import concurrent.futures as cf
-import multiprocessing as mp
-import os
-
 import numpy as np
 import pytest
 
@@ -21,7 +17,7 @@ from oracle import sla_oracle as O
 from sparse_linear_attention_sagesla_amd.inputs import WORKLOADS, make_inputs
 
 import oracle_jobs
-from gpu_util import assert_parity, bf16_bits_of, errors, rne_bf16, to_dev
+from gpu_util import assert_parity, bf16_bits_of, errors, oracle_pool, rne_bf16, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -42,17 +38,7 @@ def _inputs(name):
 
 @pytest.fixture(scope="module")
 def pool():
-    """Single-threaded oracle workers, at most 16 (the host share of one GPU)."""
-    saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
-    for v in saved:
-        os.environ[v] = "1"
-    n = max(1, min(16, len(os.sched_getaffinity(0))))
-    ex = cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"))
-    for v, old in saved.items():
-        if old is None:
-            os.environ.pop(v)
-        else:
-            os.environ[v] = old
+    ex, _ = oracle_pool()
     yield ex
     ex.shutdown()
 
