@@ -46,6 +46,16 @@ Shape make_shape(int B, int H, int N, int k) {
 
 // Carves the workspace for `op`; with base == nullptr only the size is computed.
 // The backward's extra buffers go to `bw`.
+sla::TopkFilter topk_filter(const Workspace& w) {
+  sla::TopkFilter f;
+  f.scores = w.topk_scores;
+  f.ksplit = w.ksplit;
+  f.kflag = w.kflag;
+  f.kbar_rm = w.kbar_rm;
+  f.redo = w.redo;
+  return f;
+}
+
 size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
              sla::BwdWorkspace* bw = nullptr) {
   size_t off = 0;
@@ -60,6 +70,13 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
   ws.ksum = reinterpret_cast<double*>(take(BH * Nb * D * sizeof(double)));
   ws.qbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
   ws.kbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+  if (const size_t fb = sla::topk_filter_bytes(s.BH, s.Nb)) {
+    ws.ksplit = reinterpret_cast<uint16_t*>(take(BH * ((Nb + 15) / 16) * 4 * 3 * 512 * sizeof(uint16_t)));
+    ws.kflag = take(BH * Nb);
+    ws.kbar_rm = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+    ws.redo = take(BH * Nb);
+    ws.topk_scores = reinterpret_cast<float*>(take(fb));
+  }
   if (op == SLA_OP_ATTENTION_BWD) {
     // the forward's buffers in the subtraction form, then the backward's
     const bool lin = phi != SLA_PHI_NONE && s.k < s.Nb;
@@ -278,7 +295,7 @@ sla_status sla_quantize_qk(const void* q, const void* k, int B, int H, int N, in
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
-  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, q_i8, q_scale, hs);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, q_i8, q_scale, nullptr, nullptr, nullptr, hs);
   if (e == hipSuccess) e = sla::launch_key_mean(w.ksum, s, k_mean, hs);
   if (e == hipSuccess)
     e = sla::launch_quantize(qb, kb, k_mean, s, q_i8, k_i8, q_scale, k_scale, true, hs);
@@ -304,9 +321,9 @@ sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, i
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
-  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, nullptr, nullptr, hs);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, nullptr, nullptr, w.ksplit, w.kflag, w.kbar_rm, hs);
   if (e == hipSuccess)
-    e = sla::launch_block_topk(w.qbar, w.kbar, s, kblock_idx, kblock_mask, hs);
+    e = sla::launch_block_topk(w.qbar, w.kbar, topk_filter(w), s, kblock_idx, kblock_mask, hs);
   return device_status(e);
 }
 
@@ -372,14 +389,14 @@ sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, i
   }
   if (kk > 0) {
     stage(SLA_STAGE_STATS, [&] {
-      return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs);
+      return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, w.ksplit, w.kflag, w.kbar_rm, hs);
     });
     if (fork && e == hipSuccess) {
       e = hipEventRecord(fork, hs);
       if (e == hipSuccess) e = hipStreamWaitEvent(sel, fork, 0);
     }
     stage(SLA_STAGE_TOPK, [&] {
-      return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, sel);
+      return sla::launch_block_topk(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, sel);
     });
     // the aligned walks of the query-block groups, from the kept lists alone
     if (!direct)
@@ -558,8 +575,8 @@ sla_status bwd_impl(const void* q, const void* k, const void* v, const void* dou
       bw.hb = r.hb;
     }
   } else if (kk > 0) {
-    run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, hs); });
-    run([&] { return sla::launch_block_topk(w.qbar, w.kbar, s, w.idx, nullptr, hs); });
+    run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, w.ksplit, w.kflag, w.kbar_rm, hs); });
+    run([&] { return sla::launch_block_topk(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, hs); });
     run([&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
     run([&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }

@@ -37,6 +37,12 @@ struct Workspace {
   double* ksum = nullptr;     // [BH, Nb, D]   fp64 K block sums (for the K mean)
   float* qbar = nullptr;      // [BH, Nb, D]   fp32 Q block means
   float* kbar = nullptr;      // [BH, D, Nb]   fp32 K block means, channel-major
+  // the filtered top-k (where it runs: Nb <= 1728; null otherwise)
+  uint16_t* ksplit = nullptr; // [BH, ceil(Nb/16), 4, 3, 64, 8] bf16 splits of kbar
+  uint8_t* kflag = nullptr;   // [BH, Nb]      key block mean out of the filter's range
+  float* kbar_rm = nullptr;   // [BH, Nb, D]   fp32 K block means, row-major
+  float* topk_scores = nullptr;  // [BH, Nb, Nb] approximate scores, then [BH, Nb, 8] row maxima
+  uint8_t* redo = nullptr;    // [BH, Nb]      rows handed to the exact top-k
   float* mu = nullptr;        // [BH, D]       K channel mean
   int8_t* q8 = nullptr;       // [BH, Np, D]   INT8 codes
   int8_t* k8 = nullptr;       // [BH, Np, D]
@@ -82,13 +88,26 @@ constexpr int kBwdStatFloats = 4 * kBlk;  // per query block: four rows of 64 st
 // Block means and K block sums; also Q's INT8 codes and scales when q8 is set.
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
                               double* ksum, float* qbar, float* kbar, int8_t* q8, float* sq,
-                              hipStream_t s);
+                              uint16_t* ksplit, uint8_t* kflag, float* kbar_rm, hipStream_t s);
 hipError_t launch_key_mean(const double* ksum, const Shape& sh, float* mu, hipStream_t s);
 hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu,
                            const Shape& sh, int8_t* q8, int8_t* k8, float* sq, float* sk,
                            bool k_only, hipStream_t s);
-hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
-                             int32_t* idx, uint32_t* mask, hipStream_t s);
+// The filtered top-k's buffers (all null: the exact kernel selects every row).
+struct TopkFilter {
+  float* scores = nullptr;
+  const uint16_t* ksplit = nullptr;
+  const uint8_t* kflag = nullptr;
+  const float* kbar_rm = nullptr;
+  uint8_t* redo = nullptr;
+};
+// Bytes of TopkFilter::scores for BH heads of Nb blocks; 0 where the filter does not run.
+size_t topk_filter_bytes(int BH, int Nb);
+// Kept lists (and the optional bitmask): the filtered passes and then the
+// exact kernel on the rows they hand over where `f` is set and the filter
+// applies, else the exact kernel on every row.
+hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFilter& f,
+                             const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s);
 size_t topk_lds_bytes(int Nb, int* rows_per_group);
 // fp8: stage phi(K) as e4m3 codes (8 KB per block, a head's blocks at the
 // start of its fk16 slice) with per-block decode scales in fkscale.

@@ -25,6 +25,36 @@ __device__ __forceinline__ float phi_apply(float x, int phi) {
   return fmaxf(x, 0.0f);
 }
 
+// bf16 splits of the fp32 block means for the filtered top-k (below): x =
+// x_h + x_l + e with x_h = bf16(x) and x_l = bf16(x - x_h) (the difference is
+// exact in fp32), |e| <= 2^-18 |x|; |x_h| beside them.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split_bf16(float x, __bf16& h, __bf16& l, __bf16& a) {
+  h = (__bf16)x;
+  const float fh = (float)h;
+  l = (__bf16)(x - fh);
+  a = (__bf16)fabsf(fh);
+}
+
+// A non-zero mean outside [2^-60, 2^60] (or not finite) is outside the
+// filtered top-k's range: its rows take the exact kernel.
+__device__ __forceinline__ bool out_of_range(float x) {
+  const float a = fabsf(x);
+  return a != 0.0f && !(a >= 0x1p-60f && a <= 0x1p60f);
+}
+
+// Layout of the K splits: per head, per tile of 16 key blocks, per k-step s
+// of 32 channels, the hi, lo and |hi| operands as the 64 lanes of the matrix
+// core hold them (lane 16g + n: key block 16 tile + n, channels 32s + 8g ..
+// 32s + 8g + 7), 1 KB each.
+constexpr int kSplitTileElems = 4 * 3 * 512;  // bf16 per tile
+__device__ __forceinline__ size_t ksplit_index(int bh, int Nb, int j, int c) {
+  const int tl = j >> 4, n = j & 15, s = c >> 5, g = (c >> 3) & 3, e = c & 7;
+  return ((size_t)bh * ((Nb + 15) >> 4) + tl) * kSplitTileElems + (size_t)s * 3 * 512 + (16 * g + n) * 8 + e;
+}
+
 // ---------------------------------------------------------------------------
 // Block statistics, and the Q quantiser.  One workgroup per (block, b*h):
 // lane t loads rows t/16 + 16m (m < 4), channels 8*(t%16).. of Q and K (one
@@ -39,7 +69,8 @@ __device__ __forceinline__ float phi_apply(float x, int phi) {
 __global__ __launch_bounds__(256) void block_stats_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int N, int Nb,
     double* __restrict__ ksum, float* __restrict__ qbar, float* __restrict__ kbar,
-    int8_t* __restrict__ q8, float* __restrict__ sq) {
+    int8_t* __restrict__ q8, float* __restrict__ sq, uint16_t* __restrict__ ksplit,
+    uint8_t* __restrict__ kflag, float* __restrict__ kbar_rm) {
   __shared__ __align__(16) uint16_t tile[2][kBlk][kD];  // bf16 Q, K rows of the block
   __shared__ float red[4];
   const int t = threadIdx.x;
@@ -79,6 +110,7 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
     if ((t & 63) == 0) red[t >> 6] = amax;
   }
   __syncthreads();
+  bool kbad = false;
   {
     // sums in ascending row order
     const int tensor = t >> 7, c = t & 127;
@@ -91,7 +123,21 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
       // channel-major, so the scoring pass reads consecutive key blocks
       kbar[((size_t)bh * kD + c) * Nb + blk] = mean;
       ksum[((size_t)bh * Nb + blk) * kD + c] = acc;
+      if (ksplit) {
+        __bf16 h, l, a;
+        split_bf16(mean, h, l, a);
+        uint16_t* d = ksplit + ksplit_index(bh, Nb, blk, c);
+        d[0] = __builtin_bit_cast(uint16_t, h);
+        d[512] = __builtin_bit_cast(uint16_t, l);
+        d[1024] = __builtin_bit_cast(uint16_t, a);
+        kbad = out_of_range(mean);
+        kbar_rm[((size_t)bh * Nb + blk) * kD + c] = mean;  // row-major, for the filter's fp64 scores
+      }
     }
+  }
+  if (ksplit) {
+    const int any_bad = __syncthreads_or(kbad ? 1 : 0);
+    if (t == 0) kflag[(size_t)bh * Nb + blk] = any_bad ? 1 : 0;
   }
   if (!q8) return;
   float scale, inv;
@@ -205,7 +251,7 @@ constexpr int kBins = 1024;
 template <int R>
 __global__ __launch_bounds__(256) void block_topk_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int Nb, int k,
-    int32_t* __restrict__ idx, uint32_t* __restrict__ mask) {
+    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, const uint8_t* __restrict__ redo) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* qs = reinterpret_cast<double*>(smem);                              // [128][R]
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + R * kD * 8);           // [4][kBins]
@@ -218,6 +264,12 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
   const float* kb = kbar + (size_t)bh * kD * Nb;  // [128][Nb]
+  if (redo) {
+    // after the filtered pass: only the rows it handed over
+    bool any = false;
+    for (int r = 0; r < R && i0 + r < Nb; ++r) any |= redo[(size_t)bh * Nb + i0 + r] != 0;
+    if (!any) return;  // uniform over the workgroup
+  }
 
   for (int e = t; e < R * kD; e += 256) {
     const int r = e % R, c = e / R;
@@ -280,6 +332,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   for (int r = wave; r < R; r += 4) {
     const int i = i0 + r;
     if (i >= Nb) break;  // wave-uniform; no block barrier follows
+    if (redo && !redo[(size_t)bh * Nb + i]) continue;
     const double* sr = sc + (size_t)r * Nb;
     double mn = INFINITY, mx = -INFINITY;
     for (int j = lane; j < Nb; j += 64) {
@@ -416,6 +469,380 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
       base += (uint32_t)__popcll(sb);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Filtered block top-k: the same kept lists as block_topk_kernel, with the
+// fp64 scores computed only for the key blocks whose fate they decide.
+// block_scores_approx_kernel (matrix cores, 32 query blocks per workgroup):
+// with the bf16 splits x = x_h + x_l + e of the means (split_bf16; the K ones
+// written by the statistics pass), the approximate score s~_ij = sum_c q_h k_h
+// + q_h k_l + q_l k_h takes exact bf16 products with fp32 accumulation, and
+// a_ij = sum_c |q_h||k_h| is accumulated beside it.  The dropped terms (q_l k_l
+// and the e parts) are below 2^-16.4 sum|q||k|, the fp32 accumulation of the
+// 384 products below 2^-14.4 sum|q||k| even with truncating adds, and
+// sum|q||k| <= a_ij (1 + 2^-7), so the exact fp64 score s_ij of
+// block_topk_kernel lies within E_i = 2^-12 max_j a_ij + 2^-100 of s~_ij for
+// every key block j of row i.  (Inside the range of out_of_range no product
+// overflows, and denormal products are covered by the 2^-100.)  It writes s~
+// (fp32 [Nb][Nb] per head) and, per row and wave, the largest a_ij (NaN when
+// a mean of the row or of the head's K is out of range).
+// block_topk_approx_select_kernel (one wave per row): T = the k-th largest s~
+// (the histogram of block_topk_kernel on s~).  At least k key blocks have s >=
+// T - E and fewer than k have s > T + E, so the k-th largest s lies in
+// [T - E, T + E]: key blocks with s~ > T + 2E are kept, those with s~ < T - 2E
+// are not, and the ones in between (a handful on smooth inputs) get their fp64
+// score, computed as block_topk_kernel does, and are ranked by (score desc,
+// index asc) for the places the certain ones leave.  A row with more than 64
+// such key blocks or more than 64 approximate scores in the threshold bucket
+// (large groups of equal scores), or with means out of range, sets its redo
+// flag instead, and block_topk_kernel (redo mode) selects it afterwards.
+// ---------------------------------------------------------------------------
+constexpr int kSRows = 32;   // query blocks per scoring workgroup (two row tiles)
+constexpr int kSWaves = 4;   // waves per scoring workgroup
+constexpr int kFSlots = 27;  // key blocks per lane of a row held in registers (Nb <= 1728)
+constexpr int kBWaves = 4;   // rows per selecting workgroup (one wave each)
+
+__global__ __launch_bounds__(64 * kSWaves) void block_scores_approx_kernel(
+    const float* __restrict__ qbar, const uint16_t* __restrict__ ksplit,
+    const uint8_t* __restrict__ kflag, int Nb, float* __restrict__ scores,
+    float* __restrict__ amaxp) {
+  const int t = threadIdx.x;
+  // the wave index in a scalar register: tile offsets are uniform
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63, g = lane >> 4, l16 = lane & 15;
+  const int bh = blockIdx.y;
+  const int i0 = blockIdx.x * kSRows;
+  const int ntiles = (Nb + 15) >> 4;
+
+  // A operands: row tile rt, row l16 (query block i0 + 16 rt + l16), channels 32s + 8g + e
+  bf16x8 ah[2][4], al[2][4], aa[2][4];
+  bool qbad[2] = {false, false};
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int iq = min(i0 + 16 * rt + l16, Nb - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float* qp = qbar + ((size_t)bh * Nb + iq) * kD + 32 * s + 8 * g;
+      const float4v u0 = *reinterpret_cast<const float4v*>(qp);
+      const float4v u1 = *reinterpret_cast<const float4v*>(qp + 4);
+      const float x[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qbad[rt] |= out_of_range(x[e]);
+        __bf16 h, l, a;
+        split_bf16(x[e], h, l, a);
+        ah[rt][s][e] = h;
+        al[rt][s][e] = l;
+        aa[rt][s][e] = a;
+      }
+    }
+  }
+
+  // B operands of tile t: 12 whole 16-byte loads per lane from the split
+  // layout (several workgroups per CU hide their latency)
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(ksplit) + (size_t)bh * ntiles * kSplitTileElems, 0,
+      ntiles * kSplitTileElems * 2, 0x00020000);
+  float amx[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  bool kbad = false;
+  auto load_tile = [&](v4i (&kv)[12], int tile) {
+#pragma unroll
+    for (int m = 0; m < 12; ++m)
+      kv[m] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                          sr, 16 * lane, (tile * kSplitTileElems + 512 * m) * 2, 0));
+  };
+  auto run_tile = [&](const v4i (&kv)[12], int tile) {
+    const int j = 16 * tile + l16;
+    if (j < Nb) kbad |= kflag[(size_t)bh * Nb + j] != 0;
+    float4v acc[2], aca[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) acc[rt] = aca[rt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 bh8 = __builtin_bit_cast(bf16x8, kv[3 * s]);
+      const bf16x8 bl8 = __builtin_bit_cast(bf16x8, kv[3 * s + 1]);
+      const bf16x8 ba8 = __builtin_bit_cast(bf16x8, kv[3 * s + 2]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rt][s], bh8, acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rt][s], bl8, acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[rt][s], bh8, acc[rt], 0, 0, 0);
+        aca[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa[rt][s], ba8, aca[rt], 0, 0, 0);
+      }
+    }
+    // the lane holds rows 16 rt + 4g + r of key block j
+    if (j < Nb) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + 16 * rt + 4 * g + r;
+          if (i < Nb) scores[((size_t)bh * Nb + i) * Nb + j] = acc[rt][r];
+          amx[rt][r] = fmaxf(amx[rt][r], aca[rt][r]);
+        }
+    }
+  };
+  for (int tile = wave; tile < ntiles; tile += kSWaves) {
+    v4i kv[12];
+    load_tile(kv, tile);
+    run_tile(kv, tile);
+  }
+  // per row and wave: the largest a over the 16 lanes of the row group, NaN
+  // when the row's means or any K mean this wave met are out of range
+  const bool kbw = __builtin_amdgcn_ballot_w64(kbad) != 0;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const uint64_t qm = __builtin_amdgcn_ballot_w64(qbad[rt]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = amx[rt][r];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const int x = 4 * g + r;  // the row within the tile
+      const bool rbad = ((qm >> x) | (qm >> (x + 16)) | (qm >> (x + 32)) | (qm >> (x + 48))) & 1ull;
+      const int i = i0 + 16 * rt + x;
+      if (l16 == 0 && i < Nb)
+        amaxp[((size_t)bh * Nb + i) * kSWaves + wave] = (rbad || kbw) ? __builtin_nanf("") : m;
+    }
+  }
+}
+
+// fp32 bounds of a window [lo, hi] given in fp64: for every fp32 x,
+// lo <= x <= hi exactly when lo32 <= x <= hi32, and x > hi exactly when x > hi32.
+__device__ __forceinline__ float next_up(float x) {  // the least float above a finite x
+  if (x == 0.0f) return __uint_as_float(1u);
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float(x > 0.0f ? u + 1u : u - 1u);
+}
+
+__device__ __forceinline__ void window_f32(double lo, double hi, float& lo32, float& hi32) {
+  lo32 = (float)lo;
+  if ((double)lo32 < lo) lo32 = next_up(lo32);
+  hi32 = (float)hi;
+  if ((double)hi32 > hi) hi32 = -next_up(-hi32);
+}
+
+__global__ __launch_bounds__(64 * kBWaves) void block_topk_approx_select_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar_rm,
+    const float* __restrict__ scores, const float* __restrict__ amaxp, int Nb, int k,
+    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, uint8_t* __restrict__ redo) {
+  __shared__ uint32_t hist_all[kBWaves][kBins];
+  __shared__ double cand_s_all[kBWaves][64];
+  __shared__ int cand_j_all[kBWaves][64];
+  const int t = threadIdx.x;
+  // the wave index in a scalar register: the row and its q-bar are uniform
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * kBWaves + wave;
+  if (i >= Nb) return;  // no workgroup barrier in this kernel
+  uint32_t* h = hist_all[wave];
+  double* cs = cand_s_all[wave];
+  int* cj = cand_j_all[wave];
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int mwords = (Nb + 31) / 32;
+  const int nslots = (Nb + 63) >> 6;  // <= kFSlots
+  const size_t row = (size_t)bh * Nb + i;
+  int32_t* out = idx + row * k;
+  uint32_t* mrow = mask ? mask + row * mwords : nullptr;
+  if (k >= Nb) {  // every key block
+    for (int j = lane; j < Nb; j += 64) out[j] = j;
+    if (mrow)
+      for (int w = lane; w < mwords; w += 64)
+        mrow[w] = (w + 1) * 32 <= Nb ? 0xffffffffu : ((1u << (Nb - 32 * w)) - 1u);
+    if (lane == 0) redo[row] = 0;
+    return;
+  }
+  // the row's approximate scores in registers (key block 64u + lane in slot u)
+  const float* srow = scores + row * Nb;
+  float v[kFSlots];
+#pragma unroll
+  for (int u = 0; u < kFSlots; ++u) {
+    if (u >= nslots) continue;
+    const int j = 64 * u + lane;
+    v[u] = j < Nb ? srow[j] : 0.0f;
+  }
+  float am = lane < kSWaves ? amaxp[row * kSWaves + lane] : 0.0f;
+  bool bad = __builtin_amdgcn_ballot_w64(am != am) != 0;  // a NaN partial: out of range
+#pragma unroll
+  for (int off = 1; off < kSWaves; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+  am = __shfl(am, 0);
+  float mnf = INFINITY, mxf = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kFSlots; ++u) {
+    if (u >= nslots) continue;
+    if (64 * u + lane < Nb) {
+      mnf = fminf(mnf, v[u]);
+      mxf = fmaxf(mxf, v[u]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mnf = fminf(mnf, __shfl_xor(mnf, off));
+    mxf = fmaxf(mxf, __shfl_xor(mxf, off));
+  }
+  bad |= !(mxf > mnf);  // equal approximate scores: the exact kernel
+  double T = 0.0;
+  if (!bad) {
+    // a monotone map of the scores onto the buckets (fp32 rounding keeps the
+    // order, and the same map serves the histogram and the gather)
+    float scale = (float)kBins / (mxf - mnf);
+    if (!(scale < 1e30f)) scale = 1e30f;
+    auto bucket = [&](float x) { return (int)fminf((x - mnf) * scale, (float)(kBins - 1)); };
+#pragma unroll
+    for (int q = 0; q < kBins / 64; ++q) h[lane * (kBins / 64) + q] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < kFSlots; ++u) {
+      if (u >= nslots) continue;
+      if (64 * u + lane < Nb) atomicAdd(&h[bucket(v[u])], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    constexpr int kPer = kBins / 64;
+    uint32_t cnt[kPer];
+    uint32_t local = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      cnt[q] = h[kBins - 1 - kPer * lane - q];
+      local += cnt[q];
+    }
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t x = __shfl_up(incl, off);
+      if (lane >= off) incl += x;
+    }
+    uint32_t before = incl - local;
+    int B = -1;
+    uint32_t need = 0, nc = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      if (B < 0 && before < (uint32_t)k && before + cnt[q] >= (uint32_t)k) {
+        B = kBins - 1 - kPer * lane - q;
+        need = (uint32_t)k - before;
+        nc = cnt[q];
+      }
+      before += cnt[q];
+    }
+    const int src = __ffsll((unsigned long long)__ballot(B >= 0)) - 1;
+    B = __shfl(B, src);
+    need = __shfl(need, src);
+    nc = __shfl(nc, src);
+    bad |= nc > 64;
+    if (!bad) {
+      // the need-th largest approximate score of bucket B (cs as scratch)
+      uint32_t base = 0;
+#pragma unroll
+      for (int u = 0; u < kFSlots; ++u) {
+        if (u >= nslots) continue;
+        const bool in = 64 * u + lane < Nb && bucket(v[u]) == B;
+        const uint64_t bb = __ballot(in);
+        if (in) cs[base + (uint32_t)__popcll(bb & lt_mask)] = (double)v[u];
+        base += (uint32_t)__popcll(bb);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      bool mine = false;
+      double my_s = 0.0;
+      if ((uint32_t)lane < nc) {
+        my_s = cs[lane];
+        uint32_t rank = 0;
+        for (uint32_t c = 0; c < nc; ++c)
+          rank += (cs[c] > my_s || (cs[c] == my_s && c < (uint32_t)lane)) ? 1u : 0u;
+        mine = rank == need - 1;
+      }
+      T = __shfl(my_s, __ffsll((unsigned long long)__ballot(mine)) - 1);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      __builtin_amdgcn_wave_barrier();  // cs is reused below
+    }
+  }
+  // the window [T - 2E, T + 2E], widened so that its fp64 rounding stays outside
+  const double E = 0x1p-12 * (double)am + 0x1p-100;
+  float lo, hi;
+  window_f32(T - 2.0 * E * (1.0 + 0x1p-30), T + 2.0 * E * (1.0 + 0x1p-30), lo, hi);
+  uint32_t n_in = 0, n_amb = 0;
+  if (!bad) {
+#pragma unroll
+    for (int u = 0; u < kFSlots; ++u) {
+      if (u >= nslots) continue;
+      const int j = 64 * u + lane;
+      const float x = v[u];
+      const bool amb = j < Nb && x >= lo && x <= hi;
+      const uint64_t ba = __ballot(amb);
+      const uint32_t pos = n_amb + (uint32_t)__popcll(ba & lt_mask);
+      if (amb && pos < 64) cj[pos] = j;
+      n_amb += (uint32_t)__popcll(ba);
+      n_in += (uint32_t)__popcll(__ballot(j < Nb && x > hi));
+    }
+    // >= 1 and <= n_amb places for the listed ones by the bound
+    bad |= n_amb > 64 || n_in >= (uint32_t)k || (uint32_t)k - n_in > n_amb;
+  }
+  if (bad) {
+    if (lane == 0) redo[row] = 1;
+    return;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  // fp64 scores of the listed key blocks in block_topk_kernel's order
+  // (channels ascending, one rounding per step), from the row-major k-bar:
+  // a lane's 128 means in 16-byte loads, 32 channels in flight at a time
+  const float* qr = qbar + row * kD;
+  double my_s = 0.0;
+  int my_j = 0;
+  if ((uint32_t)lane < n_amb) {
+    my_j = cj[lane];
+    const float4v* kp = reinterpret_cast<const float4v*>(kbar_rm + ((size_t)bh * Nb + my_j) * kD);
+    for (int c0 = 0; c0 < kD; c0 += 32) {
+      float4v kv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kv[e] = kp[c0 / 4 + e];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) my_s = fma((double)qr[c0 + e], (double)kv[e >> 2][e & 3], my_s);
+    }
+    cs[lane] = my_s;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t need = (uint32_t)k - n_in;
+  bool mine = false;
+  if ((uint32_t)lane < n_amb) {
+    uint32_t rank = 0;
+    for (uint32_t c = 0; c < n_amb; ++c)
+      rank += (cs[c] > my_s || (cs[c] == my_s && cj[c] < my_j)) ? 1u : 0u;
+    mine = rank == need - 1;
+  }
+  const int who = __ffsll((unsigned long long)__ballot(mine)) - 1;
+  const double Ts = __shfl(my_s, who);
+  const int Tj = __shfl(my_j, who);
+  uint32_t base = 0, abase = 0;
+#pragma unroll
+  for (int u = 0; u < kFSlots; ++u) {
+    if (u >= nslots) continue;
+    const int jb = 64 * u;
+    const int j = jb + lane;
+    const bool valid = j < Nb;
+    const float x = v[u];
+    const bool amb = valid && x >= lo && x <= hi;
+    const uint64_t ba = __ballot(amb);
+    bool sel = valid && x > hi;
+    if (amb) {
+      const double ex = cs[abase + (uint32_t)__popcll(ba & lt_mask)];
+      sel = ex > Ts || (ex == Ts && j <= Tj);
+    }
+    abase += (uint32_t)__popcll(ba);
+    const uint64_t sb = __ballot(sel);
+    const uint32_t pos = base + (uint32_t)__popcll(sb & lt_mask);
+    if (sel && pos < (uint32_t)k) out[pos] = j;
+    if (mrow) {
+      const int w0 = jb >> 5;
+      if (lane == 0) mrow[w0] = (uint32_t)sb;
+      if (lane == 1 && w0 + 1 < mwords) mrow[w0 + 1] = (uint32_t)(sb >> 32);
+    }
+    base += (uint32_t)__popcll(sb);
+  }
+  if (lane == 0) redo[row] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -768,9 +1195,10 @@ __global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict
 
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
                               double* ksum, float* qbar, float* kbar, int8_t* q8, float* sq,
-                              hipStream_t s) {
+                              uint16_t* ksplit, uint8_t* kflag, float* kbar_rm, hipStream_t s) {
   dim3 grid(sh.Nb, sh.BH);
-  block_stats_kernel<<<grid, 256, 0, s>>>(q, k, sh.N, sh.Nb, ksum, qbar, kbar, q8, sq);
+  block_stats_kernel<<<grid, 256, 0, s>>>(q, k, sh.N, sh.Nb, ksum, qbar, kbar, q8, sq, ksplit, kflag,
+                                          kbar_rm);
   return hipGetLastError();
 }
 
@@ -797,22 +1225,44 @@ size_t topk_lds_bytes(int Nb, int* rows_per_group) {
   return bytes(R);
 }
 
-hipError_t launch_block_topk(const float* qbar, const float* kbar, const Shape& sh,
-                             int32_t* idx, uint32_t* mask, hipStream_t s) {
+// Bytes of the filtered top-k's approximate scores and row maxima, 0 where
+// it does not run (rows too long for its registers).
+size_t topk_filter_bytes(int BH, int Nb) {
+  if (Nb > 64 * kFSlots) return 0;
+  return (size_t)BH * Nb * ((size_t)Nb + kSWaves) * 4;
+}
+
+hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFilter& f,
+                             const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s) {
   int R = 1;
   const size_t lds = topk_lds_bytes(sh.Nb, &R);
   const void* fn = R == 8   ? reinterpret_cast<const void*>(block_topk_kernel<8>)
                    : R == 4 ? reinterpret_cast<const void*>(block_topk_kernel<4>)
                    : R == 2 ? reinterpret_cast<const void*>(block_topk_kernel<2>)
                             : reinterpret_cast<const void*>(block_topk_kernel<1>);
-  const hipError_t e = allow_lds(fn, (int)lds);
+  hipError_t e = allow_lds(fn, (int)lds);
   if (e != hipSuccess) return e;
+  // the filtered passes where they apply; then the exact kernel for the rows
+  // they hand over (all rows without them)
+  const uint8_t* todo = nullptr;
+  if (f.scores && f.ksplit && f.kflag && f.kbar_rm && f.redo && sh.Nb <= 64 * kFSlots) {
+    float* amaxp = f.scores + (size_t)sh.BH * sh.Nb * sh.Nb;
+    block_scores_approx_kernel<<<dim3((sh.Nb + kSRows - 1) / kSRows, sh.BH), 64 * kSWaves, 0, s>>>(
+        qbar, f.ksplit, f.kflag, sh.Nb, f.scores, amaxp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    block_topk_approx_select_kernel<<<dim3((sh.Nb + kBWaves - 1) / kBWaves, sh.BH), 64 * kBWaves, 0, s>>>(
+        qbar, f.kbar_rm, f.scores, amaxp, sh.Nb, sh.k, idx, mask, f.redo);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    todo = f.redo;
+  }
   dim3 grid((sh.Nb + R - 1) / R, sh.BH);
   switch (R) {
-    case 8: block_topk_kernel<8><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
-    case 4: block_topk_kernel<4><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
-    case 2: block_topk_kernel<2><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
-    default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask); break;
+    case 8: block_topk_kernel<8><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
+    case 4: block_topk_kernel<4><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
+    case 2: block_topk_kernel<2><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
+    default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
   }
   return hipGetLastError();
 }
