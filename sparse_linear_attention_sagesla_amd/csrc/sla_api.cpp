@@ -52,6 +52,7 @@ sla::TopkFilter topk_filter(const Workspace& w) {
   f.ksplit = w.ksplit;
   f.kflag = w.kflag;
   f.kbar_rm = w.kbar_rm;
+  f.knorm = w.knorm;
   f.redo = w.redo;
   return f;
 }
@@ -71,9 +72,10 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
   ws.qbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
   ws.kbar = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
   if (const size_t fb = sla::topk_filter_bytes(s.BH, s.Nb)) {
-    ws.ksplit = reinterpret_cast<uint16_t*>(take(BH * ((Nb + 15) / 16) * 4 * 3 * 512 * sizeof(uint16_t)));
+    ws.ksplit = reinterpret_cast<uint16_t*>(take(BH * ((Nb + 15) / 16) * 4 * 2 * 512 * sizeof(uint16_t)));
     ws.kflag = take(BH * Nb);
     ws.kbar_rm = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
+    ws.knorm = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
     ws.redo = take(BH * Nb);
     ws.topk_scores = reinterpret_cast<float*>(take(fb));
   }
@@ -295,7 +297,7 @@ sla_status sla_quantize_qk(const void* q, const void* k, int B, int H, int N, in
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
-  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, q_i8, q_scale, nullptr, nullptr, nullptr, hs);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, q_i8, q_scale, nullptr, nullptr, nullptr, nullptr, hs);
   if (e == hipSuccess) e = sla::launch_key_mean(w.ksum, s, k_mean, hs);
   if (e == hipSuccess)
     e = sla::launch_quantize(qb, kb, k_mean, s, q_i8, k_i8, q_scale, k_scale, true, hs);
@@ -321,7 +323,7 @@ sla_status sla_block_select(const void* q, const void* k, int B, int H, int N, i
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
-  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, nullptr, nullptr, w.ksplit, w.kflag, w.kbar_rm, hs);
+  hipError_t e = sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, nullptr, nullptr, w.ksplit, w.kflag, w.kbar_rm, w.knorm, hs);
   if (e == hipSuccess)
     e = sla::launch_block_topk(w.qbar, w.kbar, topk_filter(w), s, kblock_idx, kblock_mask, hs);
   return device_status(e);
@@ -389,7 +391,7 @@ sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, i
   }
   if (kk > 0) {
     stage(SLA_STAGE_STATS, [&] {
-      return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, w.ksplit, w.kflag, w.kbar_rm, hs);
+      return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, w.ksplit, w.kflag, w.kbar_rm, w.knorm, hs);
     });
     if (fork && e == hipSuccess) {
       e = hipEventRecord(fork, hs);
@@ -575,7 +577,7 @@ sla_status bwd_impl(const void* q, const void* k, const void* v, const void* dou
       bw.hb = r.hb;
     }
   } else if (kk > 0) {
-    run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, w.ksplit, w.kflag, w.kbar_rm, hs); });
+    run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, w.ksplit, w.kflag, w.kbar_rm, w.knorm, hs); });
     run([&] { return sla::launch_block_topk(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, hs); });
     run([&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
     run([&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });

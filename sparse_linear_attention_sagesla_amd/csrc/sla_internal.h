@@ -38,9 +38,10 @@ struct Workspace {
   float* qbar = nullptr;      // [BH, Nb, D]   fp32 Q block means
   float* kbar = nullptr;      // [BH, D, Nb]   fp32 K block means, channel-major
   // the filtered top-k (where it runs: Nb <= 1728; null otherwise)
-  uint16_t* ksplit = nullptr; // [BH, ceil(Nb/16), 4, 3, 64, 8] bf16 splits of kbar
+  uint16_t* ksplit = nullptr; // [BH, ceil(Nb/16), 4, 2, 64, 8] bf16 splits of kbar
   uint8_t* kflag = nullptr;   // [BH, Nb]      key block mean out of the filter's range
   float* kbar_rm = nullptr;   // [BH, Nb, D]   fp32 K block means, row-major
+  float* knorm = nullptr;     // [BH, Nb]      upper bound of each K block mean's 2-norm
   float* topk_scores = nullptr;  // [BH, Nb, Nb] approximate scores, then [BH, Nb, 8] row maxima
   uint8_t* redo = nullptr;    // [BH, Nb]      rows handed to the exact top-k
   float* mu = nullptr;        // [BH, D]       K channel mean
@@ -88,7 +89,8 @@ constexpr int kBwdStatFloats = 4 * kBlk;  // per query block: four rows of 64 st
 // Block means and K block sums; also Q's INT8 codes and scales when q8 is set.
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
                               double* ksum, float* qbar, float* kbar, int8_t* q8, float* sq,
-                              uint16_t* ksplit, uint8_t* kflag, float* kbar_rm, hipStream_t s);
+                              uint16_t* ksplit, uint8_t* kflag, float* kbar_rm, float* knorm,
+                              hipStream_t s);
 hipError_t launch_key_mean(const double* ksum, const Shape& sh, float* mu, hipStream_t s);
 hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu,
                            const Shape& sh, int8_t* q8, int8_t* k8, float* sq, float* sk,
@@ -99,6 +101,7 @@ struct TopkFilter {
   const uint16_t* ksplit = nullptr;
   const uint8_t* kflag = nullptr;
   const float* kbar_rm = nullptr;
+  const float* knorm = nullptr;
   uint8_t* redo = nullptr;
 };
 // Bytes of TopkFilter::scores for BH heads of Nb blocks; 0 where the filter does not run.

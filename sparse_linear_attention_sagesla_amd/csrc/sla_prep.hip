@@ -27,15 +27,19 @@ __device__ __forceinline__ float phi_apply(float x, int phi) {
 
 // bf16 splits of the fp32 block means for the filtered top-k (below): x =
 // x_h + x_l + e with x_h = bf16(x) and x_l = bf16(x - x_h) (the difference is
-// exact in fp32), |e| <= 2^-18 |x|; |x_h| beside them.
+// exact in fp32), |e| <= 2^-18 |x|.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void split_bf16(float x, __bf16& h, __bf16& l, __bf16& a) {
+__device__ __forceinline__ void split_bf16(float x, __bf16& h, __bf16& l) {
   h = (__bf16)x;
-  const float fh = (float)h;
-  l = (__bf16)(x - fh);
-  a = (__bf16)fabsf(fh);
+  l = (__bf16)(x - (float)h);
+}
+
+__device__ __forceinline__ float next_up(float x) {  // the least float above a finite x
+  if (x == 0.0f) return __uint_as_float(1u);
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float(x > 0.0f ? u + 1u : u - 1u);
 }
 
 // A non-zero mean outside [2^-60, 2^60] (or not finite) is outside the
@@ -46,13 +50,13 @@ __device__ __forceinline__ bool out_of_range(float x) {
 }
 
 // Layout of the K splits: per head, per tile of 16 key blocks, per k-step s
-// of 32 channels, the hi, lo and |hi| operands as the 64 lanes of the matrix
-// core hold them (lane 16g + n: key block 16 tile + n, channels 32s + 8g ..
+// of 32 channels, the hi and lo operands as the 64 lanes of the matrix core
+// hold them (lane 16g + n: key block 16 tile + n, channels 32s + 8g ..
 // 32s + 8g + 7), 1 KB each.
-constexpr int kSplitTileElems = 4 * 3 * 512;  // bf16 per tile
+constexpr int kSplitTileElems = 4 * 2 * 512;  // bf16 per tile
 __device__ __forceinline__ size_t ksplit_index(int bh, int Nb, int j, int c) {
   const int tl = j >> 4, n = j & 15, s = c >> 5, g = (c >> 3) & 3, e = c & 7;
-  return ((size_t)bh * ((Nb + 15) >> 4) + tl) * kSplitTileElems + (size_t)s * 3 * 512 + (16 * g + n) * 8 + e;
+  return ((size_t)bh * ((Nb + 15) >> 4) + tl) * kSplitTileElems + (size_t)s * 2 * 512 + (16 * g + n) * 8 + e;
 }
 
 // ---------------------------------------------------------------------------
@@ -70,9 +74,10 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int N, int Nb,
     double* __restrict__ ksum, float* __restrict__ qbar, float* __restrict__ kbar,
     int8_t* __restrict__ q8, float* __restrict__ sq, uint16_t* __restrict__ ksplit,
-    uint8_t* __restrict__ kflag, float* __restrict__ kbar_rm) {
+    uint8_t* __restrict__ kflag, float* __restrict__ kbar_rm, float* __restrict__ knorm) {
   __shared__ __align__(16) uint16_t tile[2][kBlk][kD];  // bf16 Q, K rows of the block
   __shared__ float red[4];
+  __shared__ double nsq[2];
   const int t = threadIdx.x;
   const int blk = blockIdx.x;
   const int bh = blockIdx.y;
@@ -124,20 +129,27 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
       kbar[((size_t)bh * kD + c) * Nb + blk] = mean;
       ksum[((size_t)bh * Nb + blk) * kD + c] = acc;
       if (ksplit) {
-        __bf16 h, l, a;
-        split_bf16(mean, h, l, a);
+        __bf16 h, l;
+        split_bf16(mean, h, l);
         uint16_t* d = ksplit + ksplit_index(bh, Nb, blk, c);
         d[0] = __builtin_bit_cast(uint16_t, h);
         d[512] = __builtin_bit_cast(uint16_t, l);
-        d[1024] = __builtin_bit_cast(uint16_t, a);
         kbad = out_of_range(mean);
         kbar_rm[((size_t)bh * Nb + blk) * kD + c] = mean;  // row-major, for the filter's fp64 scores
+        // the block's squared norm (fp64), over the two waves holding K
+        double q2 = (double)mean * (double)mean;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) q2 += __shfl_xor(q2, off);
+        if ((t & 63) == 0) nsq[(t >> 6) - 2] = q2;
       }
     }
   }
   if (ksplit) {
     const int any_bad = __syncthreads_or(kbad ? 1 : 0);
-    if (t == 0) kflag[(size_t)bh * Nb + blk] = any_bad ? 1 : 0;
+    if (t == 0) {
+      kflag[(size_t)bh * Nb + blk] = any_bad ? 1 : 0;
+      knorm[(size_t)bh * Nb + blk] = next_up((float)sqrt(nsq[0] + nsq[1]));  // an upper bound
+    }
   }
   if (!q8) return;
   float scale, inv;
@@ -474,19 +486,20 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 // ---------------------------------------------------------------------------
 // Filtered block top-k: the same kept lists as block_topk_kernel, with the
 // fp64 scores computed only for the key blocks whose fate they decide.
-// block_scores_approx_kernel (matrix cores, 32 query blocks per workgroup):
+// block_scores_approx_kernel (matrix cores, 64 query blocks per workgroup):
 // with the bf16 splits x = x_h + x_l + e of the means (split_bf16; the K ones
 // written by the statistics pass), the approximate score s~_ij = sum_c q_h k_h
-// + q_h k_l + q_l k_h takes exact bf16 products with fp32 accumulation, and
-// a_ij = sum_c |q_h||k_h| is accumulated beside it.  The dropped terms (q_l k_l
-// and the e parts) are below 2^-16.4 sum|q||k|, the fp32 accumulation of the
-// 384 products below 2^-14.4 sum|q||k| even with truncating adds, and
-// sum|q||k| <= a_ij (1 + 2^-7), so the exact fp64 score s_ij of
-// block_topk_kernel lies within E_i = 2^-12 max_j a_ij + 2^-100 of s~_ij for
-// every key block j of row i.  (Inside the range of out_of_range no product
-// overflows, and denormal products are covered by the 2^-100.)  It writes s~
-// (fp32 [Nb][Nb] per head) and, per row and wave, the largest a_ij (NaN when
-// a mean of the row or of the head's K is out of range).
+// + q_h k_l + q_l k_h takes exact bf16 products with fp32 accumulation.  The
+// dropped terms (q_l k_l and the e parts) are below 2^-16.4 sum|q||k|, the
+// fp32 accumulation of the 384 products below 2^-14.4 sum|q||k| even with
+// truncating adds, and sum|q||k| <= |q_i| |k_j| (Cauchy-Schwarz; the norms
+// rounded up), so the exact fp64 score s_ij of block_topk_kernel lies within
+// E_i = 2^-12 |q_i| max_j |k_j| + 2^-100 of s~_ij for every key block j of
+// row i.  (Inside the range of out_of_range no product overflows, and
+// denormal products are covered by the 2^-100.)  It writes s~ (fp32 [Nb][Nb]
+// per head) and, per row and wave, |q_i| times the largest |k_j| of the
+// wave's key blocks (NaN when a mean of the row or of those key blocks is out
+// of range).
 // block_topk_approx_select_kernel (one wave per row): T = the k-th largest s~
 // (the histogram of block_topk_kernel on s~).  At least k key blocks have s >=
 // T - E and fewer than k have s > T + E, so the k-th largest s lies in
@@ -498,15 +511,21 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 // (large groups of equal scores), or with means out of range, sets its redo
 // flag instead, and block_topk_kernel (redo mode) selects it afterwards.
 // ---------------------------------------------------------------------------
-constexpr int kSRows = 32;   // query blocks per scoring workgroup (two row tiles)
-constexpr int kSWaves = 4;   // waves per scoring workgroup
+constexpr int kSRows = 64;   // query blocks per scoring workgroup (four row tiles)
+constexpr int kSWaves = 8;   // waves per scoring workgroup
 constexpr int kFSlots = 27;  // key blocks per lane of a row held in registers (Nb <= 1728)
 constexpr int kBWaves = 4;   // rows per selecting workgroup (one wave each)
 
 __global__ __launch_bounds__(64 * kSWaves) void block_scores_approx_kernel(
     const float* __restrict__ qbar, const uint16_t* __restrict__ ksplit,
-    const uint8_t* __restrict__ kflag, int Nb, float* __restrict__ scores,
-    float* __restrict__ amaxp) {
+    const uint8_t* __restrict__ kflag, const float* __restrict__ knorm, int Nb,
+    float* __restrict__ scores, float* __restrict__ amaxp) {
+  // the workgroup's A operands in LDS as the matrix core's lanes hold them:
+  // [row tile][k-step][hi, lo][64 lanes][8 bf16], lane 16g + l16 = row
+  // 16 rt + l16, channels 32s + 8g ..; then the rows' norms and range flags
+  __shared__ __align__(16) unsigned char alds[4 * 4 * 2 * 1024];
+  __shared__ float qnorm[kSRows];
+  __shared__ uint32_t qflag[kSRows];
   const int t = threadIdx.x;
   // the wave index in a scalar register: tile offsets are uniform
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -514,108 +533,102 @@ __global__ __launch_bounds__(64 * kSWaves) void block_scores_approx_kernel(
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * kSRows;
   const int ntiles = (Nb + 15) >> 4;
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-  // A operands: row tile rt, row l16 (query block i0 + 16 rt + l16), channels 32s + 8g + e
-  bf16x8 ah[2][4], al[2][4], aa[2][4];
-  bool qbad[2] = {false, false};
+  {
+    // thread t: row t / 8, channels 16 (t % 8) .. + 15 (two 8-channel groups)
+    const int r = t >> 3, c0 = 16 * (t & 7);
+    const int iq = min(i0 + r, Nb - 1);
+    const float* qp = qbar + ((size_t)bh * Nb + iq) * kD + c0;
+    bool bad = false;
+    double n2 = 0.0;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int iq = min(i0 + 16 * rt + l16, Nb - 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float* qp = qbar + ((size_t)bh * Nb + iq) * kD + 32 * s + 8 * g;
-      const float4v u0 = *reinterpret_cast<const float4v*>(qp);
-      const float4v u1 = *reinterpret_cast<const float4v*>(qp + 4);
+    for (int hf = 0; hf < 2; ++hf) {
+      const float4v u0 = *reinterpret_cast<const float4v*>(qp + 8 * hf);
+      const float4v u1 = *reinterpret_cast<const float4v*>(qp + 8 * hf + 4);
       const float x[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+      bf16x8 h8, l8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        qbad[rt] |= out_of_range(x[e]);
-        __bf16 h, l, a;
-        split_bf16(x[e], h, l, a);
-        ah[rt][s][e] = h;
-        al[rt][s][e] = l;
-        aa[rt][s][e] = a;
+        bad |= out_of_range(x[e]);
+        n2 += (double)x[e] * (double)x[e];
+        __bf16 h, l;
+        split_bf16(x[e], h, l);
+        h8[e] = h;
+        l8[e] = l;
       }
+      const int c = c0 + 8 * hf, s = c >> 5, gg = (c >> 3) & 3, rt = r >> 4;
+      unsigned char* dst = alds + ((rt * 4 + s) * 2) * 1024 + (16 * gg + (r & 15)) * 16;
+      *(lds_bf16x8*)dst = h8;
+      *(lds_bf16x8*)(dst + 1024) = l8;
+    }
+    // the row's eight threads are consecutive lanes
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      n2 += __shfl_xor(n2, off);
+      bad |= __shfl_xor(bad ? 1 : 0, off) != 0;
+    }
+    if ((t & 7) == 0) {
+      qnorm[r] = next_up((float)sqrt(n2));  // an upper bound
+      qflag[r] = bad ? 1u : 0u;
     }
   }
+  __syncthreads();
 
-  // B operands of tile t: 12 whole 16-byte loads per lane from the split
-  // layout (several workgroups per CU hide their latency)
+  // B operands of tile t: 8 whole 16-byte loads per lane from the split layout
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(ksplit) + (size_t)bh * ntiles * kSplitTileElems, 0,
       ntiles * kSplitTileElems * 2, 0x00020000);
-  float amx[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float kmax = 0.0f;
   bool kbad = false;
-  auto load_tile = [&](v4i (&kv)[12], int tile) {
+  for (int tile = wave; tile < ntiles; tile += kSWaves) {
+    v4i kv[8];
 #pragma unroll
-    for (int m = 0; m < 12; ++m)
+    for (int m = 0; m < 8; ++m)
       kv[m] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                           sr, 16 * lane, (tile * kSplitTileElems + 512 * m) * 2, 0));
-  };
-  auto run_tile = [&](const v4i (&kv)[12], int tile) {
     const int j = 16 * tile + l16;
-    if (j < Nb) kbad |= kflag[(size_t)bh * Nb + j] != 0;
-    float4v acc[2], aca[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) acc[rt] = aca[rt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 bh8 = __builtin_bit_cast(bf16x8, kv[3 * s]);
-      const bf16x8 bl8 = __builtin_bit_cast(bf16x8, kv[3 * s + 1]);
-      const bf16x8 ba8 = __builtin_bit_cast(bf16x8, kv[3 * s + 2]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rt][s], bh8, acc[rt], 0, 0, 0);
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rt][s], bl8, acc[rt], 0, 0, 0);
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[rt][s], bh8, acc[rt], 0, 0, 0);
-        aca[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa[rt][s], ba8, aca[rt], 0, 0, 0);
-      }
-    }
-    // the lane holds rows 16 rt + 4g + r of key block j
     if (j < Nb) {
+      kbad |= kflag[(size_t)bh * Nb + j] != 0;
+      kmax = fmaxf(kmax, knorm[(size_t)bh * Nb + j]);
+    }
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
+      float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const unsigned char* ap = alds + ((rt * 4 + s) * 2) * 1024 + 16 * lane;
+        const bf16x8 ah = *(const lds_bf16x8*)ap;
+        const bf16x8 al = *(const lds_bf16x8*)(ap + 1024);
+        const bf16x8 bh8 = __builtin_bit_cast(bf16x8, kv[2 * s]);
+        const bf16x8 bl8 = __builtin_bit_cast(bf16x8, kv[2 * s + 1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh8, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl8, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh8, acc, 0, 0, 0);
+      }
+      // the lane holds rows 16 rt + 4g + r of key block j
+      if (j < Nb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + 16 * rt + 4 * g + r;
-          if (i < Nb) scores[((size_t)bh * Nb + i) * Nb + j] = acc[rt][r];
-          amx[rt][r] = fmaxf(amx[rt][r], aca[rt][r]);
+          if (i < Nb) scores[((size_t)bh * Nb + i) * Nb + j] = acc[r];
         }
+      }
     }
-  };
-  for (int tile = wave; tile < ntiles; tile += kSWaves) {
-    v4i kv[12];
-    load_tile(kv, tile);
-    run_tile(kv, tile);
   }
-  // per row and wave: the largest a over the 16 lanes of the row group, NaN
-  // when the row's means or any K mean this wave met are out of range
+  // per row and wave: |q_i| max |k_j| over the wave's key blocks (rounded
+  // up), NaN when the row's means or any of those K means are out of range
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off));
   const bool kbw = __builtin_amdgcn_ballot_w64(kbad) != 0;
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const uint64_t qm = __builtin_amdgcn_ballot_w64(qbad[rt]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float m = amx[rt][r];
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const int x = 4 * g + r;  // the row within the tile
-      const bool rbad = ((qm >> x) | (qm >> (x + 16)) | (qm >> (x + 32)) | (qm >> (x + 48))) & 1ull;
-      const int i = i0 + 16 * rt + x;
-      if (l16 == 0 && i < Nb)
-        amaxp[((size_t)bh * Nb + i) * kSWaves + wave] = (rbad || kbw) ? __builtin_nanf("") : m;
-    }
-  }
+  const int i = i0 + lane;
+  if (i < Nb)
+    amaxp[((size_t)bh * Nb + i) * kSWaves + wave] =
+        (qflag[lane] || kbw) ? __builtin_nanf("") : next_up(qnorm[lane] * kmax);
 }
 
 // fp32 bounds of a window [lo, hi] given in fp64: for every fp32 x,
 // lo <= x <= hi exactly when lo32 <= x <= hi32, and x > hi exactly when x > hi32.
-__device__ __forceinline__ float next_up(float x) {  // the least float above a finite x
-  if (x == 0.0f) return __uint_as_float(1u);
-  const uint32_t u = __float_as_uint(x);
-  return __uint_as_float(x > 0.0f ? u + 1u : u - 1u);
-}
-
 __device__ __forceinline__ void window_f32(double lo, double hi, float& lo32, float& hi32) {
   lo32 = (float)lo;
   if ((double)lo32 < lo) lo32 = next_up(lo32);
@@ -1195,10 +1208,11 @@ __global__ __launch_bounds__(256) void linear_cvt_kernel(const float* __restrict
 
 hipError_t launch_block_stats(const uint16_t* q, const uint16_t* k, const Shape& sh,
                               double* ksum, float* qbar, float* kbar, int8_t* q8, float* sq,
-                              uint16_t* ksplit, uint8_t* kflag, float* kbar_rm, hipStream_t s) {
+                              uint16_t* ksplit, uint8_t* kflag, float* kbar_rm, float* knorm,
+                              hipStream_t s) {
   dim3 grid(sh.Nb, sh.BH);
   block_stats_kernel<<<grid, 256, 0, s>>>(q, k, sh.N, sh.Nb, ksum, qbar, kbar, q8, sq, ksplit, kflag,
-                                          kbar_rm);
+                                          kbar_rm, knorm);
   return hipGetLastError();
 }
 
@@ -1245,10 +1259,10 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFil
   // the filtered passes where they apply; then the exact kernel for the rows
   // they hand over (all rows without them)
   const uint8_t* todo = nullptr;
-  if (f.scores && f.ksplit && f.kflag && f.kbar_rm && f.redo && sh.Nb <= 64 * kFSlots) {
+  if (f.scores && f.ksplit && f.kflag && f.kbar_rm && f.knorm && f.redo && sh.Nb <= 64 * kFSlots) {
     float* amaxp = f.scores + (size_t)sh.BH * sh.Nb * sh.Nb;
     block_scores_approx_kernel<<<dim3((sh.Nb + kSRows - 1) / kSRows, sh.BH), 64 * kSWaves, 0, s>>>(
-        qbar, f.ksplit, f.kflag, sh.Nb, f.scores, amaxp);
+        qbar, f.ksplit, f.kflag, f.knorm, sh.Nb, f.scores, amaxp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     block_topk_approx_select_kernel<<<dim3((sh.Nb + kBWaves - 1) / kBWaves, sh.BH), 64 * kBWaves, 0, s>>>(
