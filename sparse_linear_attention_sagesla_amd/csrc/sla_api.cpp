@@ -76,7 +76,7 @@ size_t carve(int op, const Shape& s, int phi, unsigned char* base, Workspace* w,
     ws.kflag = take(BH * Nb);
     ws.kbar_rm = reinterpret_cast<float*>(take(BH * Nb * D * sizeof(float)));
     ws.knorm = reinterpret_cast<float*>(take(BH * Nb * sizeof(float)));
-    ws.redo = take(BH * Nb);
+    ws.redo = reinterpret_cast<uint32_t*>(take((1 + BH * Nb) * sizeof(uint32_t)));
     ws.topk_scores = reinterpret_cast<float*>(take(fb));
   }
   if (op == SLA_OP_ATTENTION_BWD) {

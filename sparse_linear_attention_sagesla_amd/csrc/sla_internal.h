@@ -43,7 +43,7 @@ struct Workspace {
   float* kbar_rm = nullptr;   // [BH, Nb, D]   fp32 K block means, row-major
   float* knorm = nullptr;     // [BH, Nb]      upper bound of each K block mean's 2-norm
   float* topk_scores = nullptr;  // [BH, Nb, Nb] approximate scores, then [BH, Nb, 8] row maxima
-  uint8_t* redo = nullptr;    // [BH, Nb]      rows handed to the exact top-k
+  uint32_t* redo = nullptr;   // [1 + BH * Nb] rows handed to the exact top-k: count, rows
   float* mu = nullptr;        // [BH, D]       K channel mean
   int8_t* q8 = nullptr;       // [BH, Np, D]   INT8 codes
   int8_t* k8 = nullptr;       // [BH, Np, D]
@@ -102,7 +102,7 @@ struct TopkFilter {
   const uint8_t* kflag = nullptr;
   const float* kbar_rm = nullptr;
   const float* knorm = nullptr;
-  uint8_t* redo = nullptr;
+  uint32_t* redo = nullptr;
 };
 // Bytes of TopkFilter::scores for BH heads of Nb blocks; 0 where the filter does not run.
 size_t topk_filter_bytes(int BH, int Nb);

@@ -260,11 +260,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kBins = 1024;
 
+// Rows i0 .. i0 + R - 1 of head bh (the workgroup's 256 threads, `smem` its LDS).
 template <int R>
-__global__ __launch_bounds__(256) void block_topk_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int Nb, int k,
-    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, const uint8_t* __restrict__ redo) {
-  extern __shared__ __align__(16) unsigned char smem[];
+__device__ __forceinline__ void topk_rows(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                          int Nb, int k, int32_t* __restrict__ idx,
+                                          uint32_t* __restrict__ mask, int bh, int i0,
+                                          unsigned char* smem) {
   double* qs = reinterpret_cast<double*>(smem);                              // [128][R]
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + R * kD * 8);           // [4][kBins]
   double* cand_s = reinterpret_cast<double*>(smem + R * kD * 8 + 4 * kBins * 4);   // [4][64]
@@ -273,15 +274,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * R;
   const float* kb = kbar + (size_t)bh * kD * Nb;  // [128][Nb]
-  if (redo) {
-    // after the filtered pass: only the rows it handed over
-    bool any = false;
-    for (int r = 0; r < R && i0 + r < Nb; ++r) any |= redo[(size_t)bh * Nb + i0 + r] != 0;
-    if (!any) return;  // uniform over the workgroup
-  }
 
   for (int e = t; e < R * kD; e += 256) {
     const int r = e % R, c = e / R;
@@ -344,7 +337,6 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   for (int r = wave; r < R; r += 4) {
     const int i = i0 + r;
     if (i >= Nb) break;  // wave-uniform; no block barrier follows
-    if (redo && !redo[(size_t)bh * Nb + i]) continue;
     const double* sr = sc + (size_t)r * Nb;
     double mn = INFINITY, mx = -INFINITY;
     for (int j = lane; j < Nb; j += 64) {
@@ -483,6 +475,27 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
   }
 }
 
+// One workgroup per R rows; or, with `list` (a count, then packed rows bh *
+// Nb + i), the rows the filtered pass handed back, one at a time per
+// workgroup over a small grid (R = 1), so that a pass with nothing to redo
+// costs a few microseconds.
+template <int R>
+__global__ __launch_bounds__(256) void block_topk_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int Nb, int k,
+    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, const uint32_t* __restrict__ list) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (!list) {
+    topk_rows<R>(qbar, kbar, Nb, k, idx, mask, blockIdx.y, blockIdx.x * R, smem);
+    return;
+  }
+  const uint32_t n = list[0];
+  for (uint32_t e = blockIdx.x; e < n; e += gridDim.x) {
+    const uint32_t row = list[1 + e];
+    topk_rows<R>(qbar, kbar, Nb, k, idx, mask, (int)(row / (uint32_t)Nb), (int)(row % (uint32_t)Nb), smem);
+    __syncthreads();  // the LDS serves the next row
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Filtered block top-k: the same kept lists as block_topk_kernel, with the
 // fp64 scores computed only for the key blocks whose fate they decide.
@@ -508,18 +521,20 @@ __global__ __launch_bounds__(256) void block_topk_kernel(
 // score, computed as block_topk_kernel does, and are ranked by (score desc,
 // index asc) for the places the certain ones leave.  A row with more than 64
 // such key blocks or more than 64 approximate scores in the threshold bucket
-// (large groups of equal scores), or with means out of range, sets its redo
-// flag instead, and block_topk_kernel (redo mode) selects it afterwards.
+// (large groups of equal scores), or with means out of range, is appended to
+// a list instead, and block_topk_kernel (list mode) selects it afterwards.
 // ---------------------------------------------------------------------------
 constexpr int kSRows = 64;   // query blocks per scoring workgroup (four row tiles)
 constexpr int kSWaves = 8;   // waves per scoring workgroup
 constexpr int kFSlots = 27;  // key blocks per lane of a row held in registers (Nb <= 1728)
 constexpr int kBWaves = 4;   // rows per selecting workgroup (one wave each)
+constexpr int kRedoGrid = 512;  // workgroups of the exact kernel over the hand-back list
 
 __global__ __launch_bounds__(64 * kSWaves) void block_scores_approx_kernel(
     const float* __restrict__ qbar, const uint16_t* __restrict__ ksplit,
     const uint8_t* __restrict__ kflag, const float* __restrict__ knorm, int Nb,
-    float* __restrict__ scores, float* __restrict__ amaxp) {
+    float* __restrict__ scores, float* __restrict__ amaxp, uint32_t* __restrict__ redo) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) redo[0] = 0;  // the hand-back list
   // the workgroup's A operands in LDS as the matrix core's lanes hold them:
   // [row tile][k-step][hi, lo][64 lanes][8 bf16], lane 16g + l16 = row
   // 16 rt + l16, channels 32s + 8g ..; then the rows' norms and range flags
@@ -639,7 +654,7 @@ __device__ __forceinline__ void window_f32(double lo, double hi, float& lo32, fl
 __global__ __launch_bounds__(64 * kBWaves) void block_topk_approx_select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar_rm,
     const float* __restrict__ scores, const float* __restrict__ amaxp, int Nb, int k,
-    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, uint8_t* __restrict__ redo) {
+    int32_t* __restrict__ idx, uint32_t* __restrict__ mask, uint32_t* __restrict__ redo) {
   __shared__ uint32_t hist_all[kBWaves][kBins];
   __shared__ double cand_s_all[kBWaves][64];
   __shared__ int cand_j_all[kBWaves][64];
@@ -663,7 +678,6 @@ __global__ __launch_bounds__(64 * kBWaves) void block_topk_approx_select_kernel(
     if (mrow)
       for (int w = lane; w < mwords; w += 64)
         mrow[w] = (w + 1) * 32 <= Nb ? 0xffffffffu : ((1u << (Nb - 32 * w)) - 1u);
-    if (lane == 0) redo[row] = 0;
     return;
   }
   // the row's approximate scores in registers (key block 64u + lane in slot u)
@@ -793,7 +807,7 @@ __global__ __launch_bounds__(64 * kBWaves) void block_topk_approx_select_kernel(
     bad |= n_amb > 64 || n_in >= (uint32_t)k || (uint32_t)k - n_in > n_amb;
   }
   if (bad) {
-    if (lane == 0) redo[row] = 1;
+    if (lane == 0) redo[1 + atomicAdd(redo, 1u)] = (uint32_t)row;
     return;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
@@ -855,7 +869,6 @@ __global__ __launch_bounds__(64 * kBWaves) void block_topk_approx_select_kernel(
     }
     base += (uint32_t)__popcll(sb);
   }
-  if (lane == 0) redo[row] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1229,14 +1242,16 @@ hipError_t launch_quantize(const uint16_t* q, const uint16_t* k, const float* mu
   return hipGetLastError();
 }
 
+// LDS bytes of block_topk_kernel<R>.
+static size_t topk_bytes(int Nb, int R) {
+  return (size_t)R * Nb * 8 + (size_t)R * kD * 8 + 4 * kBins * 4 + 4 * 64 * 12;
+}
+
 size_t topk_lds_bytes(int Nb, int* rows_per_group) {
-  auto bytes = [&](int R) {
-    return (size_t)R * Nb * 8 + (size_t)R * kD * 8 + 4 * kBins * 4 + 4 * 64 * 12;
-  };
   int R = 8;
-  while (R > 1 && bytes(R) > 96 * 1024) R >>= 1;
+  while (R > 1 && topk_bytes(Nb, R) > 96 * 1024) R >>= 1;
   if (rows_per_group) *rows_per_group = R;
-  return bytes(R);
+  return topk_bytes(Nb, R);
 }
 
 // Bytes of the filtered top-k's approximate scores and row maxima, 0 where
@@ -1248,35 +1263,37 @@ size_t topk_filter_bytes(int BH, int Nb) {
 
 hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFilter& f,
                              const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s) {
-  int R = 1;
-  const size_t lds = topk_lds_bytes(sh.Nb, &R);
-  const void* fn = R == 8   ? reinterpret_cast<const void*>(block_topk_kernel<8>)
-                   : R == 4 ? reinterpret_cast<const void*>(block_topk_kernel<4>)
-                   : R == 2 ? reinterpret_cast<const void*>(block_topk_kernel<2>)
-                            : reinterpret_cast<const void*>(block_topk_kernel<1>);
-  hipError_t e = allow_lds(fn, (int)lds);
-  if (e != hipSuccess) return e;
-  // the filtered passes where they apply; then the exact kernel for the rows
-  // they hand over (all rows without them)
-  const uint8_t* todo = nullptr;
   if (f.scores && f.ksplit && f.kflag && f.kbar_rm && f.knorm && f.redo && sh.Nb <= 64 * kFSlots) {
+    // the filtered passes, then the exact kernel on the rows they hand back
+    const size_t lds1 = topk_bytes(sh.Nb, 1);
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(block_topk_kernel<1>), (int)lds1);
+    if (e != hipSuccess) return e;
     float* amaxp = f.scores + (size_t)sh.BH * sh.Nb * sh.Nb;
     block_scores_approx_kernel<<<dim3((sh.Nb + kSRows - 1) / kSRows, sh.BH), 64 * kSWaves, 0, s>>>(
-        qbar, f.ksplit, f.kflag, f.knorm, sh.Nb, f.scores, amaxp);
+        qbar, f.ksplit, f.kflag, f.knorm, sh.Nb, f.scores, amaxp, f.redo);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     block_topk_approx_select_kernel<<<dim3((sh.Nb + kBWaves - 1) / kBWaves, sh.BH), 64 * kBWaves, 0, s>>>(
         qbar, f.kbar_rm, f.scores, amaxp, sh.Nb, sh.k, idx, mask, f.redo);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    todo = f.redo;
+    block_topk_kernel<1><<<kRedoGrid, 256, lds1, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, f.redo);
+    return hipGetLastError();
   }
+  int R = 1;
+  const size_t lds = topk_lds_bytes(sh.Nb, &R);
+  const void* fn = R == 8   ? reinterpret_cast<const void*>(block_topk_kernel<8>)
+                   : R == 4 ? reinterpret_cast<const void*>(block_topk_kernel<4>)
+                   : R == 2 ? reinterpret_cast<const void*>(block_topk_kernel<2>)
+                            : reinterpret_cast<const void*>(block_topk_kernel<1>);
+  const hipError_t e = allow_lds(fn, (int)lds);
+  if (e != hipSuccess) return e;
   dim3 grid((sh.Nb + R - 1) / R, sh.BH);
   switch (R) {
-    case 8: block_topk_kernel<8><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
-    case 4: block_topk_kernel<4><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
-    case 2: block_topk_kernel<2><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
-    default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, todo); break;
+    case 8: block_topk_kernel<8><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, nullptr); break;
+    case 4: block_topk_kernel<4><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, nullptr); break;
+    case 2: block_topk_kernel<2><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, nullptr); break;
+    default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, nullptr); break;
   }
   return hipGetLastError();
 }
