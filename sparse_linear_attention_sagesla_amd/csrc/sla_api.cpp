@@ -397,12 +397,24 @@ sla_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, i
       e = hipEventRecord(fork, hs);
       if (e == hipSuccess) e = hipStreamWaitEvent(sel, fork, 0);
     }
+    // the selection; rows the filtered top-k hands back to the exact kernel
+    // (none on smooth inputs) are redone after the walk schedule, which is
+    // then rebuilt only if there were any, so that the exact kernel's grid
+    // does not wait for the CUs in front of the schedule
+    const uint32_t* handed_back = nullptr;
     stage(SLA_STAGE_TOPK, [&] {
-      return sla::launch_block_topk(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, sel);
+      return sla::launch_block_topk_first(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, sel,
+                                          &handed_back);
     });
     // the aligned walks of the query-block groups, from the kept lists alone
-    if (!direct)
-      stage(SLA_STAGE_SCHEDULE, [&] { return sla::launch_group_schedule(w.idx, s, w.sched, sel); });
+    stage(SLA_STAGE_SCHEDULE, [&] {
+      hipError_t r = direct ? hipSuccess : sla::launch_group_schedule(w.idx, s, w.sched, sel);
+      if (r == hipSuccess && handed_back) {
+        r = sla::launch_block_topk_redo(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, sel);
+        if (r == hipSuccess && !direct) r = sla::launch_group_schedule(w.idx, s, w.sched, sel, handed_back);
+      }
+      return r;
+    });
     if (join && e == hipSuccess) e = hipEventRecord(join, sel);
     stage(SLA_STAGE_KMEAN, [&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
@@ -578,8 +590,15 @@ sla_status bwd_impl(const void* q, const void* k, const void* v, const void* dou
     }
   } else if (kk > 0) {
     run([&] { return sla::launch_block_stats(qb, kb, s, w.ksum, w.qbar, w.kbar, w.q8, w.sq, w.ksplit, w.kflag, w.kbar_rm, w.knorm, hs); });
-    run([&] { return sla::launch_block_topk(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, hs); });
+    const uint32_t* handed_back = nullptr;
+    run([&] {
+      return sla::launch_block_topk_first(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, hs, &handed_back);
+    });
     run([&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs); });
+    if (handed_back) {
+      run([&] { return sla::launch_block_topk_redo(w.qbar, w.kbar, topk_filter(w), s, w.idx, nullptr, hs); });
+      run([&] { return sla::launch_group_schedule(w.idx, s, w.sched, hs, handed_back); });
+    }
     run([&] { return sla::launch_key_mean(w.ksum, s, w.mu, hs); });
   }
   if (!res)

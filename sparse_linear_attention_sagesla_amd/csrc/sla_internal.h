@@ -111,6 +111,15 @@ size_t topk_filter_bytes(int BH, int Nb);
 // applies, else the exact kernel on every row.
 hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFilter& f,
                              const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s);
+// The same selection in two parts, for callers that build the walk schedule
+// in between: the first pass (the filtered kernels where they apply, else the
+// exact kernel on every row; *handed_back is the hand-back list, or null when
+// the exact kernel already did everything), then the exact kernel on that list.
+hipError_t launch_block_topk_first(const float* qbar, const float* kbar, const TopkFilter& f,
+                                   const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s,
+                                   const uint32_t** handed_back);
+hipError_t launch_block_topk_redo(const float* qbar, const float* kbar, const TopkFilter& f,
+                                  const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s);
 size_t topk_lds_bytes(int Nb, int* rows_per_group);
 // fp8: stage phi(K) as e4m3 codes (8 KB per block, a head's blocks at the
 // start of its fk16 slice) with per-block decode scales in fkscale.
@@ -130,7 +139,7 @@ inline bool linear_direct(const Shape& sh) { return sh.Nb - sh.k <= sh.k; }
 // Aligned walks of the query-block groups from the kept lists (ws.sched);
 // needed by launch_sparse_fwd unless the linear branch takes the direct form.
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
-                                 hipStream_t s);
+                                 hipStream_t s, const uint32_t* only_if = nullptr);
 // What a training forward keeps for the backward (sla_attention_fwd_train);
 // m and zm only in the subtraction form.
 struct TrainResiduals {

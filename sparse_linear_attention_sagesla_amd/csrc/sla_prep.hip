@@ -1261,24 +1261,25 @@ size_t topk_filter_bytes(int BH, int Nb) {
   return (size_t)BH * Nb * ((size_t)Nb + kSWaves) * 4;
 }
 
-hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFilter& f,
-                             const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s) {
-  if (f.scores && f.ksplit && f.kflag && f.kbar_rm && f.knorm && f.redo && sh.Nb <= 64 * kFSlots) {
-    // the filtered passes, then the exact kernel on the rows they hand back
-    const size_t lds1 = topk_bytes(sh.Nb, 1);
-    hipError_t e = allow_lds(reinterpret_cast<const void*>(block_topk_kernel<1>), (int)lds1);
-    if (e != hipSuccess) return e;
+static bool filter_applies(const TopkFilter& f, const Shape& sh) {
+  return f.scores && f.ksplit && f.kflag && f.kbar_rm && f.knorm && f.redo && sh.Nb <= 64 * kFSlots;
+}
+
+hipError_t launch_block_topk_first(const float* qbar, const float* kbar, const TopkFilter& f,
+                                   const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s,
+                                   const uint32_t** handed_back) {
+  *handed_back = nullptr;
+  if (filter_applies(f, sh)) {
     float* amaxp = f.scores + (size_t)sh.BH * sh.Nb * sh.Nb;
     block_scores_approx_kernel<<<dim3((sh.Nb + kSRows - 1) / kSRows, sh.BH), 64 * kSWaves, 0, s>>>(
         qbar, f.ksplit, f.kflag, f.knorm, sh.Nb, f.scores, amaxp, f.redo);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     block_topk_approx_select_kernel<<<dim3((sh.Nb + kBWaves - 1) / kBWaves, sh.BH), 64 * kBWaves, 0, s>>>(
         qbar, f.kbar_rm, f.scores, amaxp, sh.Nb, sh.k, idx, mask, f.redo);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    block_topk_kernel<1><<<kRedoGrid, 256, lds1, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, f.redo);
-    return hipGetLastError();
+    if (e == hipSuccess) *handed_back = f.redo;
+    return e;
   }
   int R = 1;
   const size_t lds = topk_lds_bytes(sh.Nb, &R);
@@ -1296,6 +1297,23 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFil
     default: block_topk_kernel<1><<<grid, 256, lds, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, nullptr); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_block_topk_redo(const float* qbar, const float* kbar, const TopkFilter& f,
+                                  const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s) {
+  const size_t lds1 = topk_bytes(sh.Nb, 1);
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(block_topk_kernel<1>), (int)lds1);
+  if (e != hipSuccess) return e;
+  block_topk_kernel<1><<<kRedoGrid, 256, lds1, s>>>(qbar, kbar, sh.Nb, sh.k, idx, mask, f.redo);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_topk(const float* qbar, const float* kbar, const TopkFilter& f,
+                             const Shape& sh, int32_t* idx, uint32_t* mask, hipStream_t s) {
+  const uint32_t* list = nullptr;
+  const hipError_t e = launch_block_topk_first(qbar, kbar, f, sh, idx, mask, s, &list);
+  if (e != hipSuccess || !list) return e;
+  return launch_block_topk_redo(qbar, kbar, f, sh, idx, mask, s);
 }
 
 hipError_t launch_linear_prep(const uint16_t* k, const uint16_t* v, const Shape& sh, int phi,

@@ -1234,7 +1234,9 @@ __device__ __forceinline__ void greedy_general(uint32_t* uni, int n, int k, uint
 template <int kG>
 __global__ __launch_bounds__(64) void group_schedule_kernel(const int32_t* __restrict__ idx,
                                                             int Nb, int k, int ragged,
-                                                            int32_t* __restrict__ sched) {
+                                                            int32_t* __restrict__ sched,
+                                                            const uint32_t* __restrict__ only_if) {
+  if (only_if && only_if[0] == 0u) return;  // a rebuild with nothing to rebuild
   extern __shared__ uint32_t gsm[];
   const int lane = threadIdx.x;
   const int grp = blockIdx.x;
@@ -1273,7 +1275,9 @@ inline size_t group_schedule_x4_lds(int Nb, int k) {
 // greedy (the same schedule as the one-group kernel gives).
 __global__ __launch_bounds__(64) void group_schedule_x4_kernel(const int32_t* __restrict__ idx, int Nb,
                                                                int k, int ragged,
-                                                               int32_t* __restrict__ sched) {
+                                                               int32_t* __restrict__ sched,
+                                                               const uint32_t* __restrict__ only_if) {
+  if (only_if && only_if[0] == 0u) return;  // a rebuild with nothing to rebuild
   extern __shared__ uint32_t gsm[];
   const int lane = threadIdx.x, row = lane >> 4, l16 = lane & 15;
   const size_t bh = blockIdx.y;
@@ -2465,7 +2469,7 @@ hipError_t launch_bwd_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v
 }
 
 hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* sched,
-                                 hipStream_t s) {
+                                 hipStream_t s, const uint32_t* only_if) {
   if (sh.k <= 0) return hipSuccess;
   const int ngroups = (sh.Nb + kGroup - 1) / kGroup;
   const int ragged = sh.N != sh.Nb * kBlk ? 1 : 0;
@@ -2473,13 +2477,14 @@ hipError_t launch_group_schedule(const int32_t* idx, const Shape& sh, int32_t* s
   if (lds4 <= 32 * 1024) {
     const hipError_t e = allow_lds(reinterpret_cast<const void*>(group_schedule_x4_kernel), (int)lds4);
     if (e != hipSuccess) return e;
-    group_schedule_x4_kernel<<<dim3((ngroups + 3) / 4, sh.BH), 64, lds4, s>>>(idx, sh.Nb, sh.k, ragged, sched);
+    group_schedule_x4_kernel<<<dim3((ngroups + 3) / 4, sh.BH), 64, lds4, s>>>(idx, sh.Nb, sh.k, ragged, sched,
+                                                                            only_if);
     return hipGetLastError();
   }
   const size_t lds = group_schedule_lds(sh.Nb, sh.k, kGroup);
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(group_schedule_kernel<kGroup>), (int)lds);
   if (e != hipSuccess) return e;
-  group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, lds, s>>>(idx, sh.Nb, sh.k, ragged, sched);
+  group_schedule_kernel<kGroup><<<dim3(ngroups, sh.BH), 64, lds, s>>>(idx, sh.Nb, sh.k, ragged, sched, only_if);
   return hipGetLastError();
 }
 
