@@ -249,7 +249,7 @@ sla_status sla_attention_fwd_lowbit(const void *q, const void *k,
  * numerics and errors, bit-identical output).  Shapes whose workspace
  * (sla_workspace_bytes) exceeds the scratch are rejected with
  * SLA_ERR_SCRATCH before anything is enqueued (e.g. B*H = 2 at N = 2048 needs
- * 6.3 MiB, one head at N = 32760 27 MiB).  Every call on a device shares its
+ * 6.4 MiB, one head at N = 32760 28.6 MiB).  Every call on a device shares its
  * scratch and nothing in it needs to start at zero; calls that overlap on one
  * device (other streams, other threads) race on it, so the caller orders
  * them.  The first call on a device looks up the scratch's device address
