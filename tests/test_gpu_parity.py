@@ -104,6 +104,36 @@ def test_block_select_exact_ties_keep_lower_index():
     assert (idx[0, 0] == np.arange(4)).all()
 
 
+@pytest.mark.parametrize("keep,phi", [(0.1, "elu1"), (0.3, "relu")])
+def test_rows_handed_back_to_the_exact_selection(keep, phi):
+    """Query blocks whose Q is zero score every key block 0; the filtered
+    top-k hands such rows to the exact kernel (which keeps the lowest
+    indices) while the rows around them stay with the filter.  Checked through
+    the selection, the forward (whose walk schedule is built from the filter's
+    lists before those rows are redone, then rebuilt) and the forked forward."""
+    N = 64 * 40 - 11
+    Q, K, V = (random_bf16((1, 2, N, 128), s) for s in (41, 42, 43))
+    zero = {0: (5, 17, 39), 1: (0, 2, 3, 30)}   # block 39 is the ragged last one
+    for h, blocks in zero.items():
+        for i in blocks:
+            Q[0, h, 64 * i:64 * (i + 1)] = 0
+    q, k, v = _case(f"handed-back rows keep={keep} {phi}", Q, K, V)
+    idx = sla.block_select(q, k, keep).cpu().numpy()
+    out = sla.attention(q, k, v, keep, phi, torch.float32).cpu().numpy()
+    side = torch.cuda.Stream()
+    outf = sla.attention(q, k, v, keep, phi, torch.float32, side_stream=side)
+    torch.cuda.synchronize()
+    assert np.array_equal(outf.cpu().numpy(), out)
+    kk = O.topk_count(O.n_blocks(N, 64), keep)
+    for h in range(2):
+        oidx, _ = O.select_head(Q[0, h], K[0, h], 64, keep)
+        assert np.array_equal(idx[0, h], oidx)
+        for i in zero[h]:
+            assert (oidx[i] == np.arange(kk)).all()
+        r = O.sla_forward_head(Q[0, h], K[0, h], V[0, h], 64, keep, phi)
+        assert_parity(out[0, h], r["out"], what=f"handed-back rows h{h}")
+
+
 # --------------------------------------------------------- integer QK tiles
 def test_int8_accumulators_bit_exact_all_tiles(tiny):
     """Every integer tile of the tiny workload against the oracle's integer
