@@ -537,13 +537,23 @@ def streaming_ceiling(dev, stream, mib=1024, reps=5):
             times.append(start.elapsed_time(end) * 1e-3)
         return min(times)
 
+    # three reads per write (about the statistics pass's mix, 4:1): d = a + b * c
+    # over four bf16 tensors of a quarter of the buffer each
+    m = n // 8
+    ta, tb, tc, td = (torch.empty(m, dtype=torch.bfloat16, device=dev) for _ in range(4))
+    for t_ in (ta, tb, tc):
+        t_.fill_(1.0)
     with torch.cuda.stream(stream):
         t_copy = best(lambda: b.copy_(a))
         t_read = best(lambda: torch.sum(x, dtype=torch.float32))
-    del a, b, x
+        t_rw3 = best(lambda: torch.addcmul(ta, tb, tc, out=td))
+    del a, b, x, ta, tb, tc, td
     return {"copy_gbps": round(2 * n / t_copy / 1e9, 1), "read_gbps": round(n / t_read / 1e9, 1),
-            "bytes": n, "note": "device copy (read + write bytes) and bf16 sum (read bytes), best of "
-                                f"{reps}; stage_frac_of_copy divides each streaming stage's rate by the copy rate"}
+            "read3_write1_gbps": round(4 * 2 * m / t_rw3 / 1e9, 1),
+            "bytes": n, "note": "device copy (read + write bytes), bf16 sum (read bytes) and an "
+                                "elementwise d = a + b*c (3 reads : 1 write), best of "
+                                f"{reps}; stage_frac_of_copy divides each streaming stage's rate by the "
+                                "copy rate, stage_frac_of_mix by the reference closest to its read/write mix"}
 
 
 def main():
@@ -720,6 +730,9 @@ def main():
     gemm_ref = dense_gemm_reference(dev, stream)
     roofline["frac_of_dense_gemm"] = round(achieved / gemm_ref["achieved"], 4)
     ceil_frac = {n: round(g / ceiling["copy_gbps"], 3) for n, g in bw.items()}
+    # the statistics pass reads 4 bytes per byte written, the staging pass about 1:1.25
+    mix_ref = {"stats": ceiling["read3_write1_gbps"], "linear_prep": ceiling["copy_gbps"]}
+    mix_frac = {n: round(g / mix_ref[n], 3) for n, g in bw.items() if n in mix_ref}
     # whole call against its ideal: sparse work at the MFMA peaks, streaming
     # stages at the HBM peak, block scores at the fp64 vector peak
     ideal_s = ops_i8 / PEAK_I8_OPS + ops_16 / PEAK_F16_FLOPS
@@ -742,6 +755,7 @@ def main():
         "streaming_ceiling": ceiling,
         "dense_gemm_reference": gemm_ref,
         "stage_frac_of_copy": ceil_frac,
+        "stage_frac_of_mix": mix_frac,
         "call_roofline_frac": round(ideal_s / (ms_step * 1e-3), 4),
         "roofline": roofline,
         "call": {"entry": "sla_attention_fwd", "fork_ms": round(ms_fork, 4),
