@@ -259,6 +259,10 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
   if (kSoft) {
     v4i s[4];
+    // The score products gate everything else in the tile: the wave running
+    // them gets issue priority over the other workgroup's wave on this SIMD,
+    // whose P.V and M products then fill the slots between them.
+    __builtin_amdgcn_s_setprio(1);
     qk_tile(st, qf, lo.rd8, s);
     if (kMask) {
 #pragma unroll
@@ -272,6 +276,7 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mi = max(mi, s[kt][r]);
+    __builtin_amdgcn_s_setprio(0);
     mi = rows_max(mi);
     const float mx = (float)mi * cs;  // cs >= 0, so this is the tile's largest logit
     const bool up = mx > S.m_run;
@@ -324,10 +329,7 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
       }
     S.zk += (double)zj;
   }
-  // The products below are most of the tile's matrix-core work.  The wave
-  // running them gets issue priority over the other workgroup's wave on this
-  // SIMD, whose softmax steps then fill the issue slots between them.
-  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_s_setprio(0);  // the products below run at normal priority
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -341,7 +343,6 @@ __device__ __forceinline__ void compute_tile(State& S, const lds_byte* st, const
       }
     }
   }
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // Key blocks of an ascending list, one per call (wave-uniform, in scalar
